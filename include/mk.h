@@ -1,0 +1,207 @@
+/* mk.h - C ABI of a persistent decode megakernel for AMD Instinct MI355X
+ * (CDNA4, gfx950).
+ *
+ * One call runs one decode step of a Llama-style dense decoder (batch 1 to
+ * 8): RMSNorm, QKV matvec, RoPE with K/V append, GQA attention over a paged
+ * K/V cache, O projection with residual, SiLU-gated MLP with residual, and
+ * (for models with an embedding) the tied LM head with greedy argmax.
+ *
+ * The operation follows "Inference MegaKernel" (shaojiemike.top):
+ *   - section "why conventional inference still has bubbles": the op chain of
+ *     a step, and the end-to-end time equation T_e2e = sum of kernel, launch,
+ *     tail and materialisation times plus communication, whose launch, tail
+ *     and materialisation terms a resident kernel removes;
+ *   - section "unified framework": the lowering chain kernel graph -> tile
+ *     graph -> per-SM queue + event counters -> resident worker, and the
+ *     four obligations (data visibility, progress, capacity, resources);
+ *   - section "hand-written whole-model MegaKernel / principle, schedule and
+ *     dataflow": a host script builds the tile DAG and writes one instruction
+ *     queue per compute unit; one model binding passes weights, K/V cache,
+ *     activations and counters in as objects; a grid sized to the unit count
+ *     runs an interpreter loop that fetches an instruction, waits on its
+ *     counters, leases on-chip pages, runs the op body, fences and publishes
+ *     completions; and the object table (queue [S,Q,32] int32 for the whole
+ *     kernel, weights per model instance, paged K/V per request, counters per
+ *     dependency interval).
+ *
+ * Conventions for every call:
+ *   - Return value: MK_OK (0) or a positive mk_status code. The text of the
+ *     last error on the calling thread is returned by mk_last_error().
+ *   - No C++ exception crosses the ABI. One host thread uses a handle at a
+ *     time.
+ *   - "device pointer" means memory on the handle's HIP device; "host
+ *     pointer" means ordinary process memory. The library never frees memory
+ *     it did not allocate.
+ *   - Streams are passed as `void *` holding a hipStream_t (NULL = the null
+ *     stream).
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mk_status {
+    MK_OK = 0,
+    MK_EINVAL = 1,      /* an argument is invalid (null, shape, range) */
+    MK_ENOSCHED = 2,    /* mk_decode_step before a successful mk_build_schedule */
+    MK_ECAPACITY = 3,   /* queue, LDS ring, attention chunking or K/V pages
+                           cannot cover the configured maximum (capacity
+                           obligation of the "unified framework" section) */
+    MK_ERESOURCE = 4,   /* the resident grid cannot be co-resident at one
+                           workgroup per CU (resource obligation) */
+    MK_EHIP = 5,        /* a HIP runtime call failed */
+    MK_ETIMEOUT = 6,    /* sticky: a device wait exceeded the watchdog bound
+                           and the grid bailed out instead of hanging */
+    MK_EDEVICE = 7      /* sticky: the device raised an error (invalid opcode,
+                           token or page id out of range, NaN logit) */
+} mk_status;
+
+typedef enum mk_mode {
+    MK_MODE_MEGAKERNEL = 0, /* one resident grid per step */
+    MK_MODE_UNFUSED = 1     /* one kernel launch per op (comparison baseline) */
+} mk_mode;
+
+/* Model shape and capacity. Requirements: head_dim == 64; n_q_heads a
+ * multiple of n_kv_heads with n_q_heads / n_kv_heads <= 8; hidden, ffn and
+ * n_q_heads * head_dim each a multiple of 512 or equal to 256; page_tokens
+ * == 16; 1 <= max_batch <= 8. */
+typedef struct mk_config {
+    int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+    int32_t has_embed;          /* 1: token in, tied LM head, greedy token
+                                   out; 0: hidden vector in and out, no head */
+    float rms_eps, rope_theta;
+    int32_t max_batch;
+    int32_t page_tokens;        /* K/V positions per page, 16 */
+    int32_t max_pages_per_req;  /* page-table columns; a request may hold up
+                                   to max_pages_per_req * page_tokens positions */
+    int32_t device;             /* HIP device ordinal */
+} mk_config;
+
+/* Per-layer weights: device pointers to bf16, row-major [out, in]. */
+typedef struct mk_layer_weights {
+    const void *attn_norm;  /* [H] */
+    const void *wqkv;       /* [(nq + 2 nkv) d, H], rows [q heads | k heads | v heads] */
+    const void *wo;         /* [H, nq d] */
+    const void *mlp_norm;   /* [H] */
+    const void *w_gate;     /* [F, H] */
+    const void *w_up;       /* [F, H] */
+    const void *w_down;     /* [H, F] */
+} mk_layer_weights;
+
+typedef struct mk_weights {
+    const void *embed;                /* device [V, H] bf16, also the LM head; NULL if has_embed == 0 */
+    const void *final_norm;           /* device [H] bf16; NULL if has_embed == 0 */
+    const mk_layer_weights *layers;   /* host array of n_layers entries */
+} mk_weights;
+
+typedef struct mk_schedule_desc {
+    int32_t batch;           /* requests per step, 1..max_batch */
+    int32_t n_cus;           /* compute units of the grid; 0 = the device's count */
+    int32_t mode;            /* mk_mode */
+    int32_t max_kv_len;      /* the largest kv_lens[b] a step will see; sizes
+                                the attention split; <= capacity - 1 */
+    int32_t attn_chunks;     /* K/V chunks per (request, kv head); 0 = auto */
+    int32_t trace;           /* 1: record per-instruction device timestamps */
+    int64_t watchdog_spins;  /* bound of every device wait loop; 0 = default */
+} mk_schedule_desc;
+
+/* Buffers of one step. All device pointers; the caller owns them. The new
+ * K/V entry of request b is written at position kv_lens[b]. tokens_out may
+ * alias tokens_in and kv_lens_out may alias kv_lens (the step writes them
+ * after its last read). */
+typedef struct mk_step_io {
+    const int32_t *tokens_in;   /* [B] (has_embed == 1) */
+    const float *hidden_in;     /* [B, H] fp32 (has_embed == 0) */
+    const int32_t *kv_lens;     /* [B], current lengths */
+    void *k_pool;               /* bf16 [L, n_pages, nkv, page_tokens, d] */
+    void *v_pool;               /* same shape */
+    int32_t n_pages;            /* pages per layer in each pool */
+    const int32_t *page_table;  /* [B, max_pages_per_req] page ids */
+    int32_t *tokens_out;        /* [B] greedy tokens (has_embed == 1) */
+    int32_t *kv_lens_out;       /* [B] = kv_lens + 1, or NULL */
+    float *logits_out;          /* [B, V] fp32, or NULL */
+    float *hidden_out;          /* [B, H] fp32 residual stream after the last layer, or NULL */
+} mk_step_io;
+
+typedef struct mk_handle mk_handle;
+
+/* Binds a model to a device ("hand-written whole-model MegaKernel" section:
+ * the one model-specific binding; weights live in HBM for the model
+ * instance). Weights are BORROWED: the caller keeps them alive and
+ * unchanged until mk_destroy. The handle owns its RoPE table, activation
+ * scratch and counters. Errors: MK_EINVAL (null pointer, unsupported shape),
+ * MK_EHIP (no device, allocation failure). *out is set only on MK_OK. */
+int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out);
+
+/* Builds the tile DAG of a step for a batch size, validates it, linearises
+ * it into one instruction queue per CU ([n_cus, Q, 32] int32, a subsequence
+ * of one global topological order each) and uploads it ("principle,
+ * schedule and dataflow" section: the host script that builds the DAG and
+ * tensorises each SM's plan). Rebuilding replaces the previous schedule and
+ * resets the counters. Errors: MK_EINVAL, MK_ECAPACITY (over capacity),
+ * MK_ERESOURCE (not co-resident at one workgroup per CU), MK_EHIP. */
+int mk_build_schedule(mk_handle *h, const mk_schedule_desc *s);
+
+/* Runs one decode step on `stream` (a hipStream_t), asynchronously: no host
+ * synchronisation ("principle, schedule and dataflow" section: the resident
+ * grid and its interpreter loop). In MK_MODE_MEGAKERNEL this is one
+ * cooperative launch of 256 (n_cus) workgroups. Errors: MK_ENOSCHED,
+ * MK_EINVAL, MK_EHIP, and the sticky MK_ETIMEOUT / MK_EDEVICE raised by an
+ * earlier step's device watchdog or error flag (seen once that step has
+ * finished; mk_sync_status waits for it). After a sticky error the handle
+ * needs mk_build_schedule before the next step. */
+int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream);
+
+/* Frees everything the handle owns; never touches borrowed buffers. NULL is
+ * a no-op. */
+void mk_destroy(mk_handle *h);
+
+/* Thread-local text of the last error, valid until the next call on the
+ * same thread. Never NULL. */
+const char *mk_last_error(void);
+
+/* Waits for the handle's device work on `stream` and returns the sticky
+ * status (MK_OK, MK_ETIMEOUT or MK_EDEVICE) with the failing CU and
+ * instruction in mk_last_error(). */
+int mk_sync_status(mk_handle *h, void *stream);
+
+/* Schedule facts for reports and tests. */
+typedef struct mk_schedule_info {
+    int32_t n_cus, queue_len, n_instr, n_events, n_counters;
+    int32_t attn_chunks, ring_granules, lds_bytes, block_threads;
+    int64_t stream_bytes_max_cu;   /* largest per-CU streamed byte count of a step at max_kv_len */
+    int64_t stream_bytes_total;    /* streamed bytes of a step over all CUs at max_kv_len */
+    int32_t launches_per_step;     /* 1 for the megakernel, kernel count for MK_MODE_UNFUSED */
+} mk_schedule_info;
+
+int mk_get_schedule_info(const mk_handle *h, mk_schedule_info *out);
+
+/* Copies the trace of the last step (when built with trace = 1) into the
+ * host buffer `out` of `cap` int64 values: for each CU and queue slot,
+ * {start, deps_ready, end} device-clock stamps. Returns the number of values
+ * written through *n. */
+int mk_read_trace(mk_handle *h, int64_t *out, size_t cap, size_t *n);
+
+/* ---- host-only planning (no HIP call; usable without a GPU) ---- */
+
+typedef struct mk_plan mk_plan;
+
+/* Builds the same schedule mk_build_schedule would, on the host only.
+ * `s->n_cus` must be given (non-zero). Errors as mk_build_schedule. */
+int mk_plan_create(const mk_config *cfg, const mk_schedule_desc *s, mk_plan **out);
+void mk_plan_destroy(mk_plan *p);
+int mk_plan_info(const mk_plan *p, mk_schedule_info *out);
+/* Copies the encoded queues [n_cus, Q, 32] int32 into `out` (cap int32s). */
+int mk_plan_queue(const mk_plan *p, int32_t *out, size_t cap);
+/* Copies the event table [n_events, 16] int32 into `out`. */
+int mk_plan_events(const mk_plan *p, int32_t *out, size_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

@@ -1,0 +1,54 @@
+"""Builds the HIP library libmk.so for gfx950, in-tree.
+
+Usage: python -m persistent_megakernel_decode_cu_amd.build
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OUT = os.path.join(PKG, "libmk.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+SOURCES = ["mk_api.cpp", "mk_sched.cpp", "mk_megakernel.hip", "mk_unfused.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
+          "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+          # no packed fp32 instructions in device code
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-Wno-unused-command-line-argument"]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    cmd = [HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = OUT + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, OUT)
+    if verbose:
+        print("built", OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

@@ -1,0 +1,393 @@
+// mk_api.cpp - the C ABI (include/mk.h): model binding, schedule upload,
+// step launch, sticky device errors.
+//
+// "Inference MegaKernel" (shaojiemike.top), section "hand-written
+// whole-model MegaKernel / principle, schedule and dataflow": one
+// model-specific binding passes weights, K/V cache, activations and counters
+// to the resident run as objects; its object table fixes their lifetimes
+// (weights per model instance, K/V per request, queue and counters per
+// kernel). The "unified framework" section's capacity and resource
+// obligations are checked here before any launch.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "mk.h"
+#include "mk_isa.h"
+#include "mk_kernels.h"
+#include "mk_sched.h"
+
+namespace mk {
+
+namespace {
+thread_local std::string g_last_error = "no error";
+}
+
+int set_error(int code, const std::string &msg) {
+    g_last_error = msg;
+    return code;
+}
+
+}  // namespace mk
+
+using mk::set_error;
+
+#define MK_HIP(call)                                                                                \
+    do {                                                                                            \
+        hipError_t e_ = (call);                                                                     \
+        if (e_ != hipSuccess)                                                                       \
+            return set_error(MK_EHIP, std::string(#call) + " failed: " + hipGetErrorString(e_)); \
+    } while (0)
+
+struct mk_handle {
+    mk_config cfg{};
+    int n_cus_dev = 0;
+    uint64_t *wtab = nullptr;
+    const void *embed = nullptr, *final_norm = nullptr;
+    float2 *rope = nullptr;
+    int capacity = 0;
+    int32_t *err = nullptr;
+    int32_t *host_err = nullptr;      // pinned, mapped
+    int32_t *host_err_dev = nullptr;  // device view of host_err
+    // schedule
+    bool built = false;
+    mk::Plan plan;
+    int32_t *queue = nullptr, *events = nullptr, *counters = nullptr;
+    float *x = nullptr, *qkv = nullptr, *o = nullptr, *act = nullptr, *attn_part = nullptr, *lm_part = nullptr;
+    float *u = nullptr, *qrot = nullptr;
+    int64_t *trace = nullptr;
+    int64_t epoch = 0;
+    int32_t max_need = 1;
+    int sticky = MK_OK;
+};
+
+namespace {
+
+template <typename T>
+void dfree(T *&p) {
+    if (p) (void)hipFree((void *)p);
+    p = nullptr;
+}
+
+void free_schedule(mk_handle *h) {
+    dfree(h->queue);
+    dfree(h->events);
+    dfree(h->counters);
+    dfree(h->x);
+    dfree(h->qkv);
+    dfree(h->o);
+    dfree(h->act);
+    dfree(h->attn_part);
+    dfree(h->lm_part);
+    dfree(h->u);
+    dfree(h->qrot);
+    dfree(h->trace);
+    h->built = false;
+}
+
+template <typename T>
+int dalloc(T *&p, size_t count) {
+    void *v = nullptr;
+    hipError_t e = hipMalloc(&v, count * sizeof(T) + 256);
+    if (e != hipSuccess) return set_error(MK_EHIP, std::string("hipMalloc failed: ") + hipGetErrorString(e));
+    e = hipMemset(v, 0, count * sizeof(T) + 256);
+    if (e != hipSuccess) return set_error(MK_EHIP, std::string("hipMemset failed: ") + hipGetErrorString(e));
+    p = (T *)v;
+    return MK_OK;
+}
+
+int decode_err(int32_t v) {
+    const int code = (v >> 28) & 0xf;
+    const int cu = (v >> 16) & 0xfff, pc = v & 0xffff;
+    const char *what = code == mk::ERR_TIMEOUT ? "watchdog timeout"
+                       : code == mk::ERR_OPCODE ? "invalid opcode"
+                       : code == mk::ERR_RANGE ? "token, length or page id out of range"
+                       : code == mk::ERR_NAN ? "NaN logit"
+                                             : "device error";
+    const int rc = code == mk::ERR_TIMEOUT ? MK_ETIMEOUT : MK_EDEVICE;
+    return set_error(rc, std::string("device reported ") + what + " (cu " + std::to_string(cu) + ", instruction " +
+                             std::to_string(pc) + "); rebuild the schedule");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mk_last_error(void) { return mk::g_last_error.c_str(); }
+
+int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out) {
+    try {
+        if (!cfg || !w || !out) return set_error(MK_EINVAL, "null argument");
+        if (int rc = mk::check_config(*cfg)) return rc;
+        if (!w->layers) return set_error(MK_EINVAL, "weights.layers is null");
+        if (cfg->has_embed && (!w->embed || !w->final_norm))
+            return set_error(MK_EINVAL, "embed and final_norm are required with has_embed = 1");
+        for (int l = 0; l < cfg->n_layers; ++l) {
+            const mk_layer_weights &lw = w->layers[l];
+            if (!lw.attn_norm || !lw.wqkv || !lw.wo || !lw.mlp_norm || !lw.w_gate || !lw.w_up || !lw.w_down)
+                return set_error(MK_EINVAL, "null weight pointer in layer " + std::to_string(l));
+        }
+        int ndev = 0;
+        MK_HIP(hipGetDeviceCount(&ndev));
+        if (cfg->device < 0 || cfg->device >= ndev) return set_error(MK_EINVAL, "device ordinal out of range");
+        MK_HIP(hipSetDevice(cfg->device));
+        hipDeviceProp_t prop;
+        MK_HIP(hipGetDeviceProperties(&prop, cfg->device));
+        if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+            return set_error(MK_EINVAL, std::string("built for gfx950, device is ") + prop.gcnArchName);
+
+        mk_handle *h = new (std::nothrow) mk_handle();
+        if (!h) return set_error(MK_EINVAL, "out of host memory");
+        h->cfg = *cfg;
+        h->n_cus_dev = prop.multiProcessorCount;
+        h->embed = w->embed;
+        h->final_norm = w->final_norm;
+        auto fail = [&](int rc) {
+            mk_destroy(h);
+            return rc;
+        };
+        std::vector<uint64_t> tab((size_t)cfg->n_layers * 8, 0);
+        for (int l = 0; l < cfg->n_layers; ++l) {
+            const mk_layer_weights &lw = w->layers[l];
+            const void *ptrs[7] = {lw.attn_norm, lw.wqkv, lw.wo, lw.mlp_norm, lw.w_gate, lw.w_up, lw.w_down};
+            for (int k = 0; k < 7; ++k) tab[(size_t)l * 8 + k] = (uint64_t)(uintptr_t)ptrs[k];
+        }
+        if (int rc = dalloc(h->wtab, tab.size())) return fail(rc);
+        if (hipMemcpy(h->wtab, tab.data(), tab.size() * 8, hipMemcpyHostToDevice) != hipSuccess)
+            return fail(set_error(MK_EHIP, "hipMemcpy of the weight table failed"));
+        h->capacity = cfg->max_pages_per_req * cfg->page_tokens;
+        if (int rc = dalloc(h->rope, (size_t)h->capacity * (cfg->head_dim / 2))) return fail(rc);
+        if (mk::launch_rope_table(h->rope, h->capacity, cfg->head_dim, (double)cfg->rope_theta, nullptr) !=
+            hipSuccess)
+            return fail(set_error(MK_EHIP, "RoPE table kernel failed to launch"));
+        if (int rc = dalloc(h->err, 1)) return fail(rc);
+        if (hipHostMalloc((void **)&h->host_err, 64, hipHostMallocMapped) != hipSuccess)
+            return fail(set_error(MK_EHIP, "hipHostMalloc failed"));
+        *h->host_err = 0;
+        if (hipHostGetDevicePointer((void **)&h->host_err_dev, h->host_err, 0) != hipSuccess)
+            return fail(set_error(MK_EHIP, "hipHostGetDevicePointer failed"));
+        if (hipDeviceSynchronize() != hipSuccess) return fail(set_error(MK_EHIP, "device synchronisation failed"));
+        *out = h;
+        return MK_OK;
+    } catch (...) {
+        return set_error(MK_EINVAL, "internal error in mk_create");
+    }
+}
+
+int mk_build_schedule(mk_handle *h, const mk_schedule_desc *s) {
+    try {
+        if (!h || !s) return set_error(MK_EINVAL, "null argument");
+        MK_HIP(hipSetDevice(h->cfg.device));
+        mk_schedule_desc d = *s;
+        if (d.n_cus == 0) d.n_cus = h->n_cus_dev;
+        if (d.n_cus < 0) return set_error(MK_EINVAL, "n_cus must be >= 0");
+        if (d.watchdog_spins <= 0) d.watchdog_spins = (int64_t)1 << 22;
+        mk::Plan plan;
+        if (int rc = mk::build_plan(h->cfg, d, plan)) return rc;
+        if (d.mode == MK_MODE_MEGAKERNEL) {
+            MK_HIP(mk::setup_megakernel(plan.lds_bytes));
+            int per_cu = 0;
+            MK_HIP(mk::megakernel_occupancy(plan.lds_bytes, &per_cu));
+            if (per_cu < 1 || d.n_cus > h->n_cus_dev * per_cu)
+                return set_error(MK_ERESOURCE, "resident grid of " + std::to_string(d.n_cus) +
+                                                   " workgroups is not co-resident (" + std::to_string(per_cu) +
+                                                   " per CU, " + std::to_string(h->n_cus_dev) + " CUs)");
+        }
+        MK_HIP(hipDeviceSynchronize());
+        free_schedule(h);
+        h->plan = plan;
+        const mk_config &c = h->cfg;
+        const int B = d.batch, G = c.n_q_heads / c.n_kv_heads;
+        const size_t QKV = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim, QD = (size_t)c.n_q_heads * c.head_dim;
+        const size_t kmax = std::max<size_t>(c.hidden, std::max<size_t>(c.ffn, QD));
+        const size_t lm_slots =
+            c.has_embed ? std::max<size_t>((size_t)plan.n_lm_slots, (size_t)(c.vocab + 3) / 4) : 1;
+        int rc = MK_OK;
+        if (!rc) rc = dalloc(h->queue, std::max<size_t>(plan.queue.size(), 32));
+        if (!rc) rc = dalloc(h->events, std::max<size_t>(plan.events.size(), 16));
+        if (!rc) rc = dalloc(h->counters, (size_t)std::max(plan.n_counters, 1) * mk::CTR_STRIDE);
+        if (!rc) rc = dalloc(h->x, (size_t)B * c.hidden);
+        if (!rc) rc = dalloc(h->qkv, (size_t)B * QKV);
+        if (!rc) rc = dalloc(h->o, (size_t)B * QD);
+        if (!rc) rc = dalloc(h->act, (size_t)B * c.ffn);
+        if (!rc) rc = dalloc(h->attn_part, (size_t)B * c.n_kv_heads * plan.attn_chunks * G * mk::ATTN_PART_STRIDE);
+        if (!rc) rc = dalloc(h->lm_part, lm_slots * B * 2);
+        if (!rc) rc = dalloc(h->u, (size_t)B * kmax);
+        if (!rc) rc = dalloc(h->qrot, (size_t)B * QD);
+        if (!rc && d.trace) rc = dalloc(h->trace, (size_t)plan.n_cus * plan.Q * 3);
+        if (rc) {
+            free_schedule(h);
+            return rc;
+        }
+        if (!plan.queue.empty())
+            MK_HIP(hipMemcpy(h->queue, plan.queue.data(), plan.queue.size() * 4, hipMemcpyHostToDevice));
+        if (!plan.events.empty())
+            MK_HIP(hipMemcpy(h->events, plan.events.data(), plan.events.size() * 4, hipMemcpyHostToDevice));
+        h->max_need = 1;
+        for (int e = 0; e < plan.n_events; ++e)
+            h->max_need = std::max(h->max_need, plan.events[(size_t)e * mk::EV_WORDS + mk::EV_NEED]);
+        MK_HIP(hipMemset(h->err, 0, 4));
+        *h->host_err = 0;
+        h->sticky = MK_OK;
+        h->epoch = 0;
+        MK_HIP(hipDeviceSynchronize());
+        h->built = true;
+        return MK_OK;
+    } catch (...) {
+        return set_error(MK_EINVAL, "internal error in mk_build_schedule");
+    }
+}
+
+int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream) {
+    try {
+        if (!h || !io) return set_error(MK_EINVAL, "null argument");
+        if (!h->built) return set_error(MK_ENOSCHED, "mk_decode_step before mk_build_schedule");
+        if (h->sticky != MK_OK) return set_error(h->sticky, "a previous step failed; rebuild the schedule");
+        const int32_t herr = __atomic_load_n(h->host_err, __ATOMIC_ACQUIRE);
+        if (herr != 0) {
+            h->sticky = decode_err(herr);
+            return h->sticky;
+        }
+        const mk_config &c = h->cfg;
+        if (!io->kv_lens || !io->k_pool || !io->v_pool || !io->page_table)
+            return set_error(MK_EINVAL, "kv_lens, k_pool, v_pool and page_table are required");
+        if (c.has_embed && (!io->tokens_in || !io->tokens_out))
+            return set_error(MK_EINVAL, "tokens_in and tokens_out are required with an embedding");
+        if (!c.has_embed && !io->hidden_in) return set_error(MK_EINVAL, "hidden_in is required without an embedding");
+        if (io->n_pages < 1) return set_error(MK_EINVAL, "n_pages must be positive");
+        hipStream_t st = (hipStream_t)stream;
+        const mk::Plan &P = h->plan;
+        // epoch-based counters: re-zero before the int32 counts could wrap
+        if ((h->epoch + 1) * (int64_t)h->max_need >= ((int64_t)1 << 30)) {
+            MK_HIP(hipMemsetAsync(h->counters, 0, (size_t)std::max(P.n_counters, 1) * mk::CTR_STRIDE * 4, st));
+            h->epoch = 0;
+        }
+        h->epoch++;
+        mk::KParams k{};
+        k.queue = h->queue;
+        k.events = h->events;
+        k.counters = h->counters;
+        k.Q = P.Q;
+        k.epoch = (int32_t)h->epoch;
+        k.n_cus = P.n_cus;
+        k.ring_granules = P.ring_granules;
+        k.act_off = mk::MISC_BYTES;
+        k.ring_off = P.lds_bytes - P.ring_granules * mk::GRANULE;
+        {
+            const int QD = c.n_q_heads * c.head_dim;
+            const int kmax = std::max(c.hidden, std::max(c.ffn, QD));
+            k.act_stride = (kmax + 511) / 512 * 512;
+        }
+        k.watchdog = P.desc.watchdog_spins;
+        k.L = c.n_layers;
+        k.H = c.hidden;
+        k.nq = c.n_q_heads;
+        k.nkv = c.n_kv_heads;
+        k.d = c.head_dim;
+        k.F = c.ffn;
+        k.V = c.vocab;
+        k.has_embed = c.has_embed;
+        k.B = P.desc.batch;
+        k.T = c.page_tokens;
+        k.max_pages = c.max_pages_per_req;
+        k.eps = c.rms_eps;
+        k.embed = (const uint16_t *)h->embed;
+        k.final_norm = (const uint16_t *)h->final_norm;
+        k.wtab = h->wtab;
+        k.rope = h->rope;
+        k.tokens_in = io->tokens_in;
+        k.hidden_in = io->hidden_in;
+        k.kv_lens = io->kv_lens;
+        k.k_pool = (uint16_t *)io->k_pool;
+        k.v_pool = (uint16_t *)io->v_pool;
+        k.n_pages = io->n_pages;
+        k.page_table = io->page_table;
+        k.tokens_out = io->tokens_out;
+        k.kv_lens_out = io->kv_lens_out;
+        k.logits_out = io->logits_out;
+        k.hidden_out = io->hidden_out;
+        k.x = h->x;
+        k.qkv = h->qkv;
+        k.o = h->o;
+        k.act = h->act;
+        k.attn_part = h->attn_part;
+        k.lm_part = h->lm_part;
+        k.attn_chunks = P.attn_chunks;
+        k.err = h->err;
+        k.host_err = h->host_err_dev;
+        k.trace = h->trace;
+        hipError_t e;
+        if (P.desc.mode == MK_MODE_MEGAKERNEL) {
+            e = mk::launch_megakernel(k, P.lds_bytes, st);
+        } else {
+            e = mk::launch_unfused(k, h->u, h->qrot, st);
+        }
+        if (e != hipSuccess) return set_error(MK_EHIP, std::string("launch failed: ") + hipGetErrorString(e));
+        return MK_OK;
+    } catch (...) {
+        return set_error(MK_EINVAL, "internal error in mk_decode_step");
+    }
+}
+
+int mk_sync_status(mk_handle *h, void *stream) {
+    if (!h) return set_error(MK_EINVAL, "null argument");
+    MK_HIP(hipSetDevice(h->cfg.device));
+    MK_HIP(hipStreamSynchronize((hipStream_t)stream));
+    int32_t v = 0;
+    MK_HIP(hipMemcpy(&v, h->err, 4, hipMemcpyDeviceToHost));
+    if (v != 0) {
+        h->sticky = decode_err(v);
+        return h->sticky;
+    }
+    if (h->sticky != MK_OK) return set_error(h->sticky, "a previous step failed; rebuild the schedule");
+    return MK_OK;
+}
+
+void mk_destroy(mk_handle *h) {
+    if (!h) return;
+    (void)hipSetDevice(h->cfg.device);
+    (void)hipDeviceSynchronize();
+    free_schedule(h);
+    dfree(h->wtab);
+    dfree(h->rope);
+    dfree(h->err);
+    if (h->host_err) (void)hipHostFree(h->host_err);
+    delete h;
+}
+
+int mk_get_schedule_info(const mk_handle *h, mk_schedule_info *out) {
+    if (!h || !out) return set_error(MK_EINVAL, "null argument");
+    if (!h->built) return set_error(MK_ENOSCHED, "no schedule");
+    const mk::Plan &P = h->plan;
+    std::memset(out, 0, sizeof *out);
+    out->n_cus = P.n_cus;
+    out->queue_len = P.Q;
+    out->n_instr = P.n_instr;
+    out->n_events = P.n_events;
+    out->n_counters = P.n_counters;
+    out->attn_chunks = P.attn_chunks;
+    out->ring_granules = P.ring_granules;
+    out->lds_bytes = P.lds_bytes;
+    out->block_threads = mk::BLOCK_THREADS;
+    out->stream_bytes_max_cu = P.stream_max_cu;
+    out->stream_bytes_total = P.stream_total;
+    out->launches_per_step = P.launches;
+    return MK_OK;
+}
+
+int mk_read_trace(mk_handle *h, int64_t *out, size_t cap, size_t *n) {
+    if (!h || !out || !n) return set_error(MK_EINVAL, "null argument");
+    if (!h->built || !h->trace) return set_error(MK_EINVAL, "schedule was not built with trace = 1");
+    const size_t need = (size_t)h->plan.n_cus * h->plan.Q * 3;
+    if (cap < need) return set_error(MK_EINVAL, "buffer too small");
+    MK_HIP(hipSetDevice(h->cfg.device));
+    MK_HIP(hipDeviceSynchronize());
+    MK_HIP(hipMemcpy(out, h->trace, need * 8, hipMemcpyDeviceToHost));
+    *n = need;
+    return MK_OK;
+}
+
+}  // extern "C"

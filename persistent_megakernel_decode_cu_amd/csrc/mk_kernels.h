@@ -1,0 +1,55 @@
+// mk_kernels.h - kernel parameter block and host launchers (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mk {
+
+// Everything a step needs, passed by value as the kernel argument block.
+struct KParams {
+    // schedule
+    const int32_t *queue;     // [n_cus, Q, INSTR_WORDS]
+    const int32_t *events;    // [n_events, EV_WORDS]
+    int32_t *counters;        // [n_counters * CTR_STRIDE]
+    int32_t Q, epoch, n_cus, ring_granules;
+    int32_t act_off, ring_off;   // LDS byte offsets
+    int32_t act_stride;          // floats per request in the activation area
+    int64_t watchdog;
+    // model
+    int32_t L, H, nq, nkv, d, F, V, has_embed, B, T, max_pages;
+    float eps;
+    const uint16_t *embed;
+    const uint16_t *final_norm;
+    const uint64_t *wtab;     // [L, 8]: attn_norm, wqkv, wo, mlp_norm, w_gate, w_up, w_down, -
+    const float2 *rope;       // [capacity, d/2] (cos, sin)
+    // step io
+    const int32_t *tokens_in;
+    const float *hidden_in;
+    const int32_t *kv_lens;
+    uint16_t *k_pool, *v_pool;
+    int32_t n_pages;
+    const int32_t *page_table;
+    int32_t *tokens_out, *kv_lens_out;
+    float *logits_out, *hidden_out;
+    // scratch
+    float *x;          // [B, H] residual stream
+    float *qkv;        // [B, (nq + 2 nkv) d]
+    float *o;          // [B, nq d] attention output
+    float *act;        // [B, F] gated MLP activation
+    float *attn_part;  // [B, nkv, chunks, G, ATTN_PART_STRIDE]
+    float *lm_part;    // [lm slots, B, 2]
+    int32_t attn_chunks;
+    int32_t *err;      // device error word
+    int32_t *host_err; // mapped host mirror of the error word
+    int64_t *trace;    // [n_cus, Q, 3] or null
+};
+
+constexpr int ATTN_PART_STRIDE = 68;
+
+hipError_t launch_megakernel(const KParams &p, int lds_bytes, hipStream_t s);
+hipError_t setup_megakernel(int lds_bytes);
+hipError_t megakernel_occupancy(int lds_bytes, int *blocks_per_cu);
+hipError_t launch_unfused(const KParams &p, float *u_scratch, float *qrot, hipStream_t s);
+hipError_t launch_rope_table(float2 *table, int capacity, int d, double theta, hipStream_t s);
+
+}  // namespace mk

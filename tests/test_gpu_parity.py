@@ -1,0 +1,120 @@
+"""GPU parity: the HIP path (megakernel and unfused baseline) against the CPU
+oracle on every workload shape, through the C ABI.
+
+Bar (from the benchmark spec of the method): max |logit difference| <=
+5e-2 and the greedy token equal wherever the oracle's top-2 gap exceeds
+1e-2; hidden outputs of the one-layer block within the same 5e-2; appended
+K/V entries within one bf16 step of the oracle's (both round the same
+binary32 value to nearest even, from differently ordered sums).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def inputs(name_or_cfg):
+    cfg = synthetic.workload(name_or_cfg) if isinstance(name_or_cfg, str) else name_or_cfg
+    key = cfg.name + str(cfg.cid)
+    if key not in _cache:
+        _cache.clear()
+        _cache[key] = (synthetic.make_model(cfg), synthetic.make_state(cfg))
+    m, st = _cache[key]
+    return cfg, m, st
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_compare(cfg, m, st, oracle64, mode, steps=1, check_kv=True):
+    wdev = gu.upload_model(m)
+    ds = gu.DevState(st)
+    dec = gu.make_decoder(m, st, wdev)
+    maxlen = int(st.kv_lens.max()) + steps - 1
+    dec.build_schedule(st.batch, mode=mode, max_kv_len=maxlen)
+    ost = st.copy()
+    worst = 0.0
+    for s in range(steps):
+        print(f"[{cfg.name} {mode}] step {s}", flush=True)
+        g = gu.run_step(dec, ds, cfg, want_hidden=True)
+        o = oracle64.decode_step(m, ost, want_hidden=True)
+        assert o["rc"] == 0
+        if cfg.has_embed:
+            diff, _ = gu.check_logits(g["logits"], o["logits"], g["tokens"], o["tokens"])
+            worst = max(worst, diff)
+        hd = float(np.max(np.abs(g["hidden"].astype(np.float64) - o["hidden"])))
+        assert hd <= gu.LOGIT_TOL, f"hidden diff {hd}"
+        assert np.array_equal(g["kv_lens"], ost.kv_lens + 1)
+        if check_kv:
+            kp = ds.k_pool.cpu().numpy().view(np.uint16)
+            vp = ds.v_pool.cpu().numpy().view(np.uint16)
+            assert gu.bf16_ulp_diff(kp, ost.k_pool) <= 1
+            assert gu.bf16_ulp_diff(vp, ost.v_pool) <= 1
+        # next step: the oracle's token (teacher-forced), lengths + 1
+        ost.kv_lens = ost.kv_lens + 1
+        if cfg.has_embed:
+            ost.tokens = o["tokens"].copy()
+            ds.tokens.copy_(torch.from_numpy(ost.tokens))
+        ds.kv_lens.copy_(torch.from_numpy(ost.kv_lens))
+    dec.close()
+    return worst
+
+
+@pytest.mark.parametrize("mode", ["unfused", "megakernel"])
+def test_tiny_step(mode, oracle64):
+    cfg, m, st = inputs("tiny-2l")
+    diff = run_compare(cfg, m, st, oracle64, mode, steps=3)
+    print(f"tiny {mode}: max |dlogit| = {diff:.3g}")
+    assert diff < 1e-3
+
+
+@pytest.mark.parametrize("mode", ["unfused", "megakernel"])
+def test_tiny_batched_paged(mode, oracle64):
+    cfg = synthetic.Workload(11, "tiny-b4-paged", n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2,
+                             head_dim=64, ffn=1024, vocab=4096, has_embed=True, batch=4,
+                             kv_len_range=(1, 300), steps=2, paged_random=True)
+    cfg, m, st = inputs(cfg)
+    run_compare(cfg, m, st, oracle64, mode, steps=2)
+
+
+@pytest.mark.parametrize("mode", ["unfused", "megakernel"])
+def test_tiny_gqa8_first_position(mode, oracle64):
+    """Eight query heads per kv head (two attention passes) and an empty cache
+    (the new token attends to itself only)."""
+    cfg = synthetic.Workload(12, "tiny-g8", n_layers=1, hidden=512, n_q_heads=8, n_kv_heads=1, head_dim=64,
+                             ffn=512, vocab=1000, has_embed=True, batch=2, kv_len=0, steps=1)
+    cfg, m, st = inputs(cfg)
+    run_compare(cfg, m, st, oracle64, mode)
+
+
+@pytest.mark.parametrize("mode", ["unfused", "megakernel"])
+def test_one_1b_layer(mode, oracle64):
+    cfg, m, st = inputs("1b-layer-kv512")
+    run_compare(cfg, m, st, oracle64, mode)
+
+
+@pytest.mark.parametrize("mode", ["unfused", "megakernel"])
+def test_1b_kv1024(mode, oracle64):
+    cfg, m, st = inputs("1b-kv1024")
+    diff = run_compare(cfg, m, st, oracle64, mode, steps=2, check_kv=False)
+    print(f"1b-kv1024 {mode}: max |dlogit| = {diff:.3g}")
+
+
+@pytest.mark.parametrize("mode", ["unfused", "megakernel"])
+def test_1b_kv8192(mode, oracle64):
+    cfg, m, st = inputs("1b-kv8192")
+    run_compare(cfg, m, st, oracle64, mode, check_kv=False)
+
+
+def test_1b_batch8_paged_unfused(oracle64):
+    cfg, m, st = inputs("1b-b8-paged")
+    run_compare(cfg, m, st, oracle64, "unfused", check_kv=False)
