@@ -108,6 +108,11 @@ typedef struct mk_schedule_desc {
     int32_t attn_chunks;     /* K/V chunks per (request, kv head); 0 = auto */
     int32_t trace;           /* 1: record per-instruction device timestamps */
     int64_t watchdog_spins;  /* bound of every device wait loop; 0 = default */
+    int32_t ring_kib;        /* LDS weight ring in KiB; 0 = all the LDS left
+                                after the activation area */
+    int32_t dma_inflight;    /* 1 KiB HBM -> LDS transfers the loader keeps
+                                in flight (1..57, rounded down to one of
+                                1, 5, 9, 17, 25, 33, 41, 49, 57); 0 = 41 */
 } mk_schedule_desc;
 
 /* Buffers of one step. All device pointers; the caller owns them. The new
@@ -186,6 +191,42 @@ int mk_get_schedule_info(const mk_handle *h, mk_schedule_info *out);
  * {start, deps_ready, end} device-clock stamps. Returns the number of values
  * written through *n. */
 int mk_read_trace(mk_handle *h, int64_t *out, size_t cap, size_t *n);
+
+/* ---- debugging aids ---- */
+
+/* Copies the handle's scratch buffer `which` (0: residual stream x [B, H],
+ * 1: qkv [B, (nq + 2 nkv) d], 2: attention output o [B, nq d], 3: gated MLP
+ * activation [B, F]) into the host buffer `out` of `bytes` bytes, after
+ * synchronising the device. Errors: MK_EINVAL, MK_ENOSCHED, MK_EHIP. */
+int mk_debug_copy_scratch(mk_handle *h, int which, void *out, size_t bytes);
+
+/* Runs the weight loader's HBM -> LDS transfer on one wave: copies `n_kib`
+ * KiB from device `src` into LDS at byte offset 1024 * lds_offset_kib with
+ * the 16-byte-per-lane DMA the resident loop uses (workgroup LDS of 160
+ * KiB), then writes those LDS bytes back to device `dst`. Synchronous.
+ * Errors: MK_EINVAL (n_kib + lds_offset_kib > 160), MK_EHIP. */
+int mk_debug_dma_probe(const void *src, void *dst, int n_kib, int lds_offset_kib);
+
+/* Streams `n_granules` KiB from device `src` through an LDS ring of
+ * `ring_granules` (2..150) KiB with the resident loop's loader protocol
+ * (`depth` transfers in flight: 0, 8, 40 or 56) while the compute waves check
+ * every word they read against `src`; `variant` 2 or 3 makes another wave
+ * issue agent-scope acquire or release fences meanwhile. Adds the number of
+ * mismatching words to errs_dev[0], granules checked to errs_dev[1] and
+ * timed-out waits to errs_dev[2] (device int32[4]). Synchronous. Errors:
+ * MK_EINVAL, MK_EHIP. */
+int mk_debug_ring_probe(const void *src, int n_granules, int ring_granules, int depth, int variant,
+                        int32_t *errs_dev);
+
+/* Cross-XCD message-passing litmus of the counter protocol: `pairs`
+ * writer/reader workgroup pairs (co-resident, cooperative launch) run
+ * `rounds` rounds over `n_words` int32 words each (data_dev: pairs * n_words
+ * int32; flags_dev: pairs * 64 int32, zeroed). The reader plants stale
+ * copies, waits for the writer's released flag, acquires, and counts words
+ * that are not the round's value: res_dev[0] with plain loads, res_dev[1]
+ * with device-coherent loads; res_dev[2] counts watchdog expiries (device
+ * int32[4], zeroed). Synchronous. Errors: MK_EINVAL, MK_EHIP. */
+int mk_debug_litmus(int pairs, int n_words, int rounds, int32_t *data_dev, int32_t *flags_dev, int32_t *res_dev);
 
 /* ---- host-only planning (no HIP call; usable without a GPU) ---- */
 

@@ -41,7 +41,8 @@ class MkWeights(ctypes.Structure):
 
 class MkScheduleDesc(ctypes.Structure):
     _fields_ = [("batch", i32), ("n_cus", i32), ("mode", i32), ("max_kv_len", i32),
-                ("attn_chunks", i32), ("trace", i32), ("watchdog_spins", i64)]
+                ("attn_chunks", i32), ("trace", i32), ("watchdog_spins", i64), ("ring_kib", i32),
+                ("dma_inflight", i32)]
 
 
 class MkStepIO(ctypes.Structure):
@@ -78,6 +79,10 @@ _SIGS = {
     "mk_sync_status": (i32, [vp, vp]),
     "mk_get_schedule_info": (i32, [vp, ctypes.POINTER(MkScheduleInfo)]),
     "mk_read_trace": (i32, [vp, ctypes.POINTER(ctypes.c_int64), ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]),
+    "mk_debug_copy_scratch": (i32, [vp, i32, vp, ctypes.c_size_t]),
+    "mk_debug_dma_probe": (i32, [vp, vp, i32, i32]),
+    "mk_debug_ring_probe": (i32, [vp, i32, i32, i32, i32, vp]),
+    "mk_debug_litmus": (i32, [i32, i32, i32, vp, vp, vp]),
     "mk_plan_create": (i32, [ctypes.POINTER(MkConfig), ctypes.POINTER(MkScheduleDesc), ctypes.POINTER(vp)]),
     "mk_plan_destroy": (None, [vp]),
     "mk_plan_info": (i32, [vp, ctypes.POINTER(MkScheduleInfo)]),
@@ -146,6 +151,19 @@ def mk_read_trace(handle: int) -> np.ndarray:
     n = ctypes.c_size_t()
     _check(lib().mk_read_trace(handle, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), cap, ctypes.byref(n)))
     return buf.reshape(info.n_cus, info.queue_len, 3)
+
+
+SCRATCH = {"x": 0, "qkv": 1, "o": 2, "act": 3}
+
+
+def mk_debug_copy_scratch(handle: int, which: str, n_floats: int) -> np.ndarray:
+    out = np.zeros(n_floats, dtype=np.float32)
+    _check(lib().mk_debug_copy_scratch(handle, SCRATCH[which], out.ctypes.data, out.nbytes))
+    return out
+
+
+def mk_debug_dma_probe(src_ptr: int, dst_ptr: int, n_kib: int, lds_offset_kib: int = 0) -> None:
+    _check(lib().mk_debug_dma_probe(src_ptr, dst_ptr, n_kib, lds_offset_kib))
 
 
 class Plan:

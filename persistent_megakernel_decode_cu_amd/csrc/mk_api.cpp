@@ -282,6 +282,14 @@ int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream) {
             k.act_stride = (kmax + 511) / 512 * 512;
         }
         k.watchdog = P.desc.watchdog_spins;
+        {
+            const int want = P.desc.dma_inflight > 0 ? P.desc.dma_inflight - 1 : 40;
+            const int allowed[] = {0, 4, 8, 16, 24, 32, 40, 48, 56};
+            int d = 0;
+            for (int a : allowed)
+                if (a <= want) d = a;
+            k.dma_depth = d;
+        }
         k.L = c.n_layers;
         k.H = c.hidden;
         k.nq = c.n_q_heads;
@@ -375,6 +383,49 @@ int mk_get_schedule_info(const mk_handle *h, mk_schedule_info *out) {
     out->stream_bytes_max_cu = P.stream_max_cu;
     out->stream_bytes_total = P.stream_total;
     out->launches_per_step = P.launches;
+    return MK_OK;
+}
+
+int mk_debug_copy_scratch(mk_handle *h, int which, void *out, size_t bytes) {
+    if (!h || !out) return set_error(MK_EINVAL, "null argument");
+    if (!h->built) return set_error(MK_ENOSCHED, "no schedule");
+    const mk_config &c = h->cfg;
+    const size_t B = (size_t)h->plan.desc.batch;
+    const float *src = nullptr;
+    size_t n = 0;
+    switch (which) {
+        case 0: src = h->x; n = B * c.hidden; break;
+        case 1: src = h->qkv; n = B * (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim; break;
+        case 2: src = h->o; n = B * c.n_q_heads * c.head_dim; break;
+        case 3: src = h->act; n = B * c.ffn; break;
+        default: return set_error(MK_EINVAL, "unknown scratch buffer");
+    }
+    if (bytes < n * 4) return set_error(MK_EINVAL, "buffer too small");
+    MK_HIP(hipSetDevice(c.device));
+    MK_HIP(hipDeviceSynchronize());
+    MK_HIP(hipMemcpy(out, src, n * 4, hipMemcpyDeviceToHost));
+    return MK_OK;
+}
+
+int mk_debug_dma_probe(const void *src, void *dst, int n_kib, int lds_offset_kib) {
+    if (!src || !dst || n_kib < 1 || lds_offset_kib < 0 || n_kib + lds_offset_kib > mk::LDS_LIMIT / 1024)
+        return set_error(MK_EINVAL, "bad probe arguments");
+    MK_HIP(mk::dma_probe(src, dst, n_kib, lds_offset_kib));
+    return MK_OK;
+}
+
+int mk_debug_ring_probe(const void *src, int n_granules, int ring_granules, int depth, int variant,
+                        int32_t *errs_dev) {
+    if (!src || !errs_dev || n_granules < 1 || ring_granules < 2 || ring_granules > 150 || depth < 0)
+        return set_error(MK_EINVAL, "bad probe arguments");
+    MK_HIP(mk::ring_probe(src, n_granules, ring_granules, depth, variant, errs_dev));
+    return MK_OK;
+}
+
+int mk_debug_litmus(int pairs, int n_words, int rounds, int32_t *data_dev, int32_t *flags_dev, int32_t *res_dev) {
+    if (pairs < 1 || pairs > 128 || n_words < 1 || rounds < 1 || !data_dev || !flags_dev || !res_dev)
+        return set_error(MK_EINVAL, "bad litmus arguments");
+    MK_HIP(mk::litmus(pairs, n_words, rounds, data_dev, flags_dev, res_dev));
     return MK_OK;
 }
 

@@ -15,6 +15,7 @@ struct KParams {
     int32_t act_off, ring_off;   // LDS byte offsets
     int32_t act_stride;          // floats per request in the activation area
     int64_t watchdog;
+    int32_t dma_depth;           // one of 0, 4, 8, 16, 24, 32, 40, 48, 56
     // model
     int32_t L, H, nq, nkv, d, F, V, has_embed, B, T, max_pages;
     float eps;
@@ -50,6 +51,9 @@ hipError_t launch_megakernel(const KParams &p, int lds_bytes, hipStream_t s);
 hipError_t setup_megakernel(int lds_bytes);
 hipError_t megakernel_occupancy(int lds_bytes, int *blocks_per_cu);
 hipError_t launch_unfused(const KParams &p, float *u_scratch, float *qrot, hipStream_t s);
+hipError_t dma_probe(const void *src, void *dst, int n_kib, int off_kib);
+hipError_t ring_probe(const void *src, int n, int ring, int depth, int variant, int32_t *errs);
+hipError_t litmus(int pairs, int n, int rounds, int32_t *data, int32_t *flags, int32_t *res);
 hipError_t launch_rope_table(float2 *table, int capacity, int d, double theta, hipStream_t s);
 
 }  // namespace mk

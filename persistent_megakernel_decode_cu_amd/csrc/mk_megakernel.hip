@@ -50,7 +50,8 @@ enum : int {
 };
 
 constexpr int NC = N_COMPUTE_WAVES;
-constexpr int DMA_DEPTH = 40;  // DMA instructions a loader keeps in flight
+// DMA instructions the loader may keep in flight after each issue
+constexpr int DMA_DEPTH_DEFAULT = 40;
 
 __device__ __forceinline__ uint32_t lds_ld(MK_LDS uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -65,25 +66,25 @@ __device__ __forceinline__ uint32_t lds_add(MK_LDS uint32_t *p, uint32_t v) {
 // HBM -> LDS, 16 bytes per active lane at lds_addr + 16 * lane. Issued from
 // inline assembly so that the compiler does not conservatively wait for the
 // transfer before unrelated LDS accesses; the loader tracks completion with
-// its own vmcnt waits. m0 is restored after issue.
+// its own vmcnt waits. m0 carries the LDS base; nothing else in this kernel
+// uses m0.
 __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_addr) {
-    uint32_t saved;
     asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %2, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 1\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
         : "s"(lds_addr), "v"(gptr)
         : "memory");
 }
 
-// s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt left open)
+// s_waitcnt vmcnt(n), also a compiler barrier: no memory access moves across
+// it (the plain builtin is not one, and stores sinking below it, or a flag
+// store rising above it, would publish data that has not arrived)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (N & 0xF));
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 __device__ __forceinline__ void raise_error(const KParams &P, MK_LDS uint32_t *misc, int code, int cu, int pc) {
@@ -147,8 +148,9 @@ __device__ __forceinline__ void run_loader(const KParams &P, const Ctx &c) {
     const int lane = c.lane;
     const uint32_t RING = (uint32_t)P.ring_granules;
     const uint32_t ring_lds = (uint32_t)(uintptr_t)c.ring;
-    uint32_t issued = 0, slot = 0, lim = RING;
+    uint32_t issued = 0, slot = 0, lim = RING, pub = 0;
     MK_LDS uint32_t *landed = c.misc + M_LANDED;
+    const int depth = P.dma_depth;
     __builtin_amdgcn_s_setprio(3);
     for (int pc = 0;; ++pc) {
         const int32_t *ins = instr(P, c.cu, pc);
@@ -186,6 +188,7 @@ __device__ __forceinline__ void run_loader(const KParams &P, const Ctx &c) {
                 int64_t spins = 0;
                 for (;;) {
                     wait_vmcnt<0>();
+                    pub = issued;
                     lds_st(landed, issued);
                     uint32_t mn = lds_ld(c.misc + M_WPOS);
 #pragma unroll
@@ -224,8 +227,22 @@ __device__ __forceinline__ void run_loader(const KParams &P, const Ctx &c) {
             if (valid) dma16(src, __builtin_amdgcn_readfirstlane(ring_lds + slot * GRANULE));
             ++issued;
             slot = (slot + 1 == RING) ? 0 : slot + 1;
-            wait_vmcnt<DMA_DEPTH>();
-            if (issued > DMA_DEPTH) lds_st(landed, issued - DMA_DEPTH);
+            // at most `depth` transfers outstanding: the older ones have landed
+            switch (depth) {
+                case 0: wait_vmcnt<0>(); break;
+                case 4: wait_vmcnt<4>(); break;
+                case 8: wait_vmcnt<8>(); break;
+                case 16: wait_vmcnt<16>(); break;
+                case 24: wait_vmcnt<24>(); break;
+                case 32: wait_vmcnt<32>(); break;
+                case 40: wait_vmcnt<40>(); break;
+                case 48: wait_vmcnt<48>(); break;
+                default: wait_vmcnt<56>(); break;
+            }
+            if (issued > (uint32_t)depth && issued - depth > pub) {
+                pub = issued - depth;
+                lds_st(landed, pub);
+            }
         }
     }
     wait_vmcnt<0>();
@@ -260,7 +277,11 @@ __device__ __forceinline__ void run_poller(const KParams &P, const Ctx &c) {
                 __builtin_amdgcn_s_sleep(1);
             }
         }
+        // The acquire is a cache invalidate that completes asynchronously
+        // (vmcnt); the compute waves load only after READY, so wait for it
+        // to finish before publishing READY to them.
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        wait_vmcnt<0>();
         lds_st(c.misc + M_READY, (uint32_t)(pc + 1));
     }
 }
@@ -275,7 +296,7 @@ struct CW {
 
 __device__ __forceinline__ bool cbar(CW &s, int pc) {
     s.nbar++;
-    lds_add(s.c.misc + M_ARRIVE, 1u);
+    if (s.c.lane == 0) lds_add(s.c.misc + M_ARRIVE, 1u);  // one arrival per wave
     return lds_wait_ge(s.c, s.c.misc + M_ARRIVE, (uint32_t)NC * s.nbar, pc);
 }
 
@@ -368,6 +389,8 @@ __device__ __forceinline__ void matvec_rows(const KParams &P, CW &s, const int32
     bool bad_nan = false;
     for (int u = s.w; u < nu; u += NC) {
         const uint32_t sb0 = (uint32_t)u * unitb;
+        // nothing before this unit is needed any more: let the loader reuse it
+        if (lane == 0) lds_st(c.misc + M_WPOS + s.w, g0 + sb0 / GRANULE);
         if (!lds_wait_ge(c, c.misc + M_LANDED, g0 + (sb0 + unitb + GRANULE - 1) / GRANULE, pc)) return;
         const uint32_t rbase = (g0 * GRANULE + sb0) % c.ring_bytes;
         float dot[2][NB];
@@ -479,6 +502,7 @@ __device__ __forceinline__ void attn_body(const KParams &P, CW &s, const int32_t
     attn_init(st);
     const int nu = bhi - blo;
     for (int u = s.w; u < nu; u += NC) {
+        if (lane == 0) lds_st(c.misc + M_WPOS + s.w, g0 + (uint32_t)u * 4);
         if (!lds_wait_ge(c, c.misc + M_LANDED, g0 + (uint32_t)(u + 1) * 4, pc)) return;
         const uint32_t kb = (g0 * GRANULE + (uint32_t)u * 4096u) % c.ring_bytes;
         uint32_t vb = kb + 2048;
@@ -501,7 +525,10 @@ __device__ __forceinline__ void attn_body(const KParams &P, CW &s, const int32_t
     attn_store(st, wpart + s.w * G * 68, G, lane);
 }
 
-__device__ __forceinline__ void publish(const KParams &P, const int32_t *ins) {
+// One completion per event: only lane 0 bumps (an atomic issued by every
+// lane would count once per lane).
+__device__ __forceinline__ void publish(const KParams &P, const int32_t *ins, int lane) {
+    if (lane != 0) return;
     const int np = sload(ins, W_NPUB);
     for (int k = 0; k < np; ++k) {
         const int e = sload(ins, W_PUB + k);
@@ -552,7 +579,7 @@ __device__ __forceinline__ void finish(const KParams &P, CW &s, const int32_t *i
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const int merge = sload(ins, W_MERGE);
     if (merge < 0) {
-        publish(P, ins);
+        publish(P, ins, lane);
         return;
     }
     // last-finisher election across compute units
@@ -592,7 +619,7 @@ __device__ __forceinline__ void finish(const KParams &P, CW &s, const int32_t *i
     }
     if ((flags & F_STEP_FINAL) && P.kv_lens_out && lane < P.B) P.kv_lens_out[lane] = sload(P.kv_lens, lane) + 1;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    publish(P, ins);
+    publish(P, ins, lane);
     (void)p;
 }
 
@@ -654,7 +681,10 @@ __device__ __forceinline__ void run_compute(const KParams &P, CW &s) {
         if (lds_ld(c.misc + M_ABORT)) return;
         g0 += ng;
         if (lane == 0) lds_st(c.misc + M_WPOS + s.w, g0);
-        // body done: make this wave's global stores complete, then count in
+        // body done: wait until this wave's global stores are acknowledged
+        // (a workgroup-scope release does not wait for them), so that the
+        // finisher's agent-scope release covers every wave's results
+        wait_vmcnt<0>();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         uint32_t old = 0;
         if (lane == 0) old = lds_add(c.misc + M_FIN, 1u);
@@ -692,6 +722,218 @@ __global__ __launch_bounds__(BLOCK_THREADS, 1) void mk_megakernel(KParams P) {
         CW s{c, wave - 2, 0};
         run_compute(P, s);
     }
+}
+
+// One wave: DMA n granules into LDS at byte offset `off` exactly as the
+// loader does, wait, then copy those LDS bytes out with ordinary loads.
+__global__ __launch_bounds__(64) void mk_dma_probe(const char *src, char *dst, int n, int off) {
+    extern __shared__ char lds_raw[];
+    MK_LDS char *lds = (MK_LDS char *)lds_raw;
+    const int lane = threadIdx.x;
+    for (int i = lane; i < LDS_LIMIT / 4; i += 64) ((MK_LDS uint32_t *)lds)[i] = 0u;
+    __syncthreads();
+    const uint32_t base = (uint32_t)(uintptr_t)lds + (uint32_t)off;
+    for (int k = 0; k < n; ++k)
+        dma16(src + (size_t)k * GRANULE + lane * 16, __builtin_amdgcn_readfirstlane(base + k * GRANULE));
+    wait_vmcnt<0>();
+    for (int k = 0; k < n; ++k) {
+        const v4u v = *(const MK_LDS v4u *)(lds + off + k * GRANULE + lane * 16);
+        *(v4u *)(dst + (size_t)k * GRANULE + lane * 16) = v;
+    }
+}
+
+hipError_t dma_probe(const void *src, void *dst, int n_kib, int off_kib) {
+    hipError_t e = hipFuncSetAttribute((const void *)mk_dma_probe, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       LDS_LIMIT);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mk_dma_probe, dim3(1), dim3(64), LDS_LIMIT, 0, (const char *)src, (char *)dst, n_kib,
+                       off_kib * GRANULE);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return hipDeviceSynchronize();
+}
+
+// Ring protocol probe: wave 0 streams n granules of a known pattern through
+// a ring of `ring` granules exactly as the loader does (issue, keep `depth`
+// in flight, publish landed); NC consumer waves take granules round-robin,
+// wait for them to land, check every word and release them. `variant` 1
+// makes the loader read back one word of the newest landed granule before
+// publishing. Counts mismatching words into errs[0] and granules checked
+// into errs[1].
+__global__ __launch_bounds__(BLOCK_THREADS, 1) void mk_ring_probe(const uint32_t *src, int n, int ring, int depth,
+                                                                   int variant, int64_t watchdog, int32_t *errs) {
+    extern __shared__ char lds_raw[];
+    MK_LDS char *lds = (MK_LDS char *)lds_raw;
+    MK_LDS uint32_t *misc = (MK_LDS uint32_t *)lds;
+    MK_LDS char *rb = lds + MISC_BYTES;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int i = threadIdx.x; i < MISC_BYTES / 4; i += BLOCK_THREADS) misc[i] = 0;
+    __syncthreads();
+    if (wave == 0) {
+        const uint32_t ring_lds = (uint32_t)(uintptr_t)rb;
+        uint32_t issued = 0, slot = 0, lim = ring, pub = 0;
+        for (int k = 0; k < n; ++k) {
+            if (issued >= lim) {
+                int64_t spins = 0;
+                for (;;) {
+                    wait_vmcnt<0>();
+                    pub = issued;
+                    lds_st(misc + M_LANDED, issued);
+                    uint32_t mn = lds_ld(misc + M_WPOS);
+                    for (int w = 1; w < NC; ++w) mn = min(mn, lds_ld(misc + M_WPOS + w));
+                    lim = __builtin_amdgcn_readfirstlane(mn + ring);
+                    if (issued < lim) break;
+                    if (++spins > watchdog) {
+                        lds_st(misc + M_ABORT, 1u);
+                        return;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            dma16(src + (size_t)k * 256 + lane * 4, __builtin_amdgcn_readfirstlane(ring_lds + slot * GRANULE));
+            ++issued;
+            slot = (slot + 1 == (uint32_t)ring) ? 0 : slot + 1;
+            switch (depth) {
+                case 0: wait_vmcnt<0>(); break;
+                case 8: wait_vmcnt<8>(); break;
+                case 40: wait_vmcnt<40>(); break;
+                default: wait_vmcnt<56>(); break;
+            }
+            if (issued > (uint32_t)depth && issued - depth > pub) {
+                pub = issued - depth;
+                if (variant == 1) {
+                    const uint32_t s2 = (pub - 1) % ring;
+                    const uint32_t v = *(volatile MK_LDS uint32_t *)(rb + s2 * GRANULE + lane * 16);
+                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                    if (v == 0xdeadbeefu) misc[M_ABORT] = 2;
+                }
+                lds_st(misc + M_LANDED, pub);
+            }
+        }
+        wait_vmcnt<0>();
+        lds_st(misc + M_LANDED, issued);
+    } else if (wave == 1) {
+        // variant 2: agent-scope acquire fences, variant 3: release fences,
+        // issued by a second wave while the loader streams
+        if (variant >= 2) {
+            int64_t spins = 0;
+            while (lds_ld(misc + M_LANDED) < (uint32_t)n && lds_ld(misc + M_ABORT) != 1u && ++spins < watchdog) {
+                (void)__hip_atomic_load(errs + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (variant == 2) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                else __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+    } else if (wave >= 2) {
+        const int w = wave - 2;
+        int bad = 0, seen = 0;
+        for (int g = w; g < n; g += NC) {
+            int64_t spins = 0;
+            while (lds_ld(misc + M_LANDED) < (uint32_t)(g + 1)) {
+                if (lds_ld(misc + M_ABORT) == 1u || ++spins > watchdog) {
+                    if (lane == 0) atomicAdd(errs + 2, 1);
+                    return;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            const v4u v = *(const MK_LDS v4u *)(rb + (g % ring) * GRANULE + lane * 16);
+            const uint32_t e = (uint32_t)g * 256u + lane * 4u;
+            bad += (v.x != src[e]) + (v.y != src[e + 1]) + (v.z != src[e + 2]) + (v.w != src[e + 3]);
+            ++seen;
+            const int gn = g + NC;
+            if (lane == 0) lds_st(misc + M_WPOS + w, (uint32_t)(gn < n ? gn : n));
+        }
+        if (lane == 0) lds_st(misc + M_WPOS + w, (uint32_t)n);
+        bad = (int)wave_sum((float)bad);
+        if (lane == 0) {
+            atomicAdd(errs, bad);
+            atomicAdd(errs + 1, seen);
+        }
+    }
+}
+
+hipError_t ring_probe(const void *src, int n, int ring, int depth, int variant, int32_t *errs) {
+    const int lds = MISC_BYTES + ring * GRANULE;
+    hipError_t e = hipFuncSetAttribute((const void *)mk_ring_probe, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mk_ring_probe, dim3(1), dim3(BLOCK_THREADS), lds, 0, (const uint32_t *)src, n, ring, depth,
+                       variant, (int64_t)1 << 22, errs);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return hipDeviceSynchronize();
+}
+
+// Cross-XCD message-passing litmus. Workgroup 2k writes, workgroup 2k+1 (on
+// another XCD under the round-robin placement) reads. Per round r the writer
+// stores r into n words, releases at agent scope and raises a flag; the reader
+// first reads the words (planting possibly stale copies in its caches), then
+// waits for the flag, acquires at agent scope and reads them again with plain
+// loads (counted into res[0]) and with device-coherent loads (res[1]); then it
+// acknowledges the round. res[2] counts watchdog expiries.
+__global__ __launch_bounds__(256) void mk_litmus(int32_t *data, int32_t *flags, int n, int rounds, int64_t watchdog,
+                                                 int32_t *res) {
+    const int pair = blockIdx.x >> 1, role = blockIdx.x & 1, tid = threadIdx.x;
+    int32_t *d = data + (size_t)pair * n;
+    int32_t *flag = flags + pair * 64, *ack = flags + pair * 64 + 32;
+    int stale_plain = 0, stale_coh = 0, sink = 0;
+    for (int r = 1; r <= rounds; ++r) {
+        if (role == 0) {
+            if (tid == 0) {
+                int64_t spins = 0;
+                while (__hip_atomic_load(ack, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < r - 1) {
+                    if (++spins > watchdog) {
+                        atomicAdd(res + 2, 1);
+                        __hip_atomic_store(flag, 1 << 30, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            __syncthreads();
+            for (int i = tid; i < n; i += 256) d[i] = r;
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (tid == 0) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                __hip_atomic_store(flag, r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        } else {
+            for (int i = tid; i < n; i += 256) sink += d[i];
+            if (tid == 0) {
+                int64_t spins = 0;
+                while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < r) {
+                    if (++spins > watchdog) {
+                        atomicAdd(res + 2, 1);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                wait_vmcnt<0>();
+            }
+            __syncthreads();
+            for (int i = tid; i < n; i += 256) {
+                stale_plain += d[i] != r;
+                stale_coh += __hip_atomic_load(d + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != r;
+            }
+            wait_vmcnt<0>();
+            __syncthreads();
+            if (tid == 0) __hip_atomic_store(ack, r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (stale_plain) atomicAdd(res, stale_plain);
+    if (stale_coh) atomicAdd(res + 1, stale_coh);
+    if (sink == 0x7fffffff) res[3] = sink;
+}
+
+hipError_t litmus(int pairs, int n, int rounds, int32_t *data, int32_t *flags, int32_t *res) {
+    void *args[] = {&data, &flags, &n, &rounds, nullptr, &res};
+    int64_t wd = (int64_t)1 << 22;
+    args[4] = &wd;
+    hipError_t e = hipLaunchCooperativeKernel((const void *)mk_litmus, dim3(2 * pairs), dim3(256), args, 0, nullptr);
+    if (e != hipSuccess) return e;
+    return hipDeviceSynchronize();
 }
 
 hipError_t setup_megakernel(int lds_bytes) {

@@ -165,6 +165,13 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     P.act_floats = std::max(B * ((kmax + 511) / 512 * 512), attn_floats);
     const int act_bytes = ceil_div((int64_t)P.act_floats * 4, 1024) * 1024;
     P.ring_granules = (LDS_LIMIT - MISC_BYTES - act_bytes) / GRANULE;
+    if (desc.ring_kib < 0) return set_error(MK_EINVAL, "ring_kib must be >= 0");
+    if (desc.dma_inflight < 0 || desc.dma_inflight > 57) return set_error(MK_EINVAL, "dma_inflight must be in 0..57");
+    if (desc.ring_kib > 0) {
+        if (desc.ring_kib > P.ring_granules)
+            return set_error(MK_ECAPACITY, "ring_kib exceeds the LDS left next to the activation area");
+        P.ring_granules = desc.ring_kib;
+    }
     P.lds_bytes = MISC_BYTES + act_bytes + P.ring_granules * GRANULE;
 
     if (desc.mode == MK_MODE_UNFUSED) {

@@ -53,7 +53,7 @@ def test_shape_checks(field, value):
     w = synthetic.workload("tiny-2l")
     cfg = cfg_of(w)
     setattr(cfg, field, value)
-    desc = _mk.MkScheduleDesc(1, 8, 0, 0, 0, 0, 0)
+    desc = _mk.MkScheduleDesc(1, 8, 0, 0, 0, 0, 0, 0, 0)
     with pytest.raises(_mk.MkError) as e:
         _mk.Plan(cfg, desc)
     assert e.value.code == _mk.MK_EINVAL
@@ -63,14 +63,14 @@ def test_capacity_checks():
     w = synthetic.workload("tiny-2l")
     cfg = cfg_of(w, pages=5)
     with pytest.raises(_mk.MkError) as e:
-        _mk.Plan(cfg, _mk.MkScheduleDesc(1, 8, 0, 80, 0, 0, 0))   # 80 >= 5 * 16
+        _mk.Plan(cfg, _mk.MkScheduleDesc(1, 8, 0, 80, 0, 0, 0, 0, 0))   # 80 >= 5 * 16
     assert e.value.code == _mk.MK_ECAPACITY
     with pytest.raises(_mk.MkError) as e:
-        _mk.Plan(cfg_of(w, max_batch=2), _mk.MkScheduleDesc(3, 8, 0, 0, 0, 0, 0))  # batch > max_batch
+        _mk.Plan(cfg_of(w, max_batch=2), _mk.MkScheduleDesc(3, 8, 0, 0, 0, 0, 0, 0, 0))  # batch > max_batch
     assert e.value.code == _mk.MK_EINVAL
     big = synthetic.workload("1b-b8-paged")
     with pytest.raises(_mk.MkError) as e:   # 8 activation rows of 8192 fp32 do not fit next to the ring
-        _mk.Plan(cfg_of(big, max_batch=8, pages=258), _mk.MkScheduleDesc(8, 256, 0, 0, 0, 0, 0))
+        _mk.Plan(cfg_of(big, max_batch=8, pages=258), _mk.MkScheduleDesc(8, 256, 0, 0, 0, 0, 0, 0, 0))
     assert e.value.code == _mk.MK_ECAPACITY
 
 

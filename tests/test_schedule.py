@@ -23,7 +23,7 @@ def plan_for(name, n_cus, batch=None, max_kv_len=None, chunks=0):
     if max_kv_len is not None:
         maxlen = max_kv_len
     cfg = cfg_of(w, max_batch=max(B, 1), pages=pages)
-    p = _mk.Plan(cfg, _mk.MkScheduleDesc(B, n_cus, 0, maxlen, chunks, 0, 0))
+    p = _mk.Plan(cfg, _mk.MkScheduleDesc(B, n_cus, 0, maxlen, chunks, 0, 0, 0, 0))
     return w, B, maxlen, p
 
 
