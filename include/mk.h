@@ -207,16 +207,24 @@ int mk_debug_copy_scratch(mk_handle *h, int which, void *out, size_t bytes);
  * Errors: MK_EINVAL (n_kib + lds_offset_kib > 160), MK_EHIP. */
 int mk_debug_dma_probe(const void *src, void *dst, int n_kib, int lds_offset_kib);
 
-/* Streams `n_granules` KiB from device `src` through an LDS ring of
+/* Streams `n_granules` KiB per workgroup (`blocks` workgroups, 1..256,
+ * workgroup b reading from src + b * n_granules KiB; the request must fit in
+ * the `src_bytes` of the source buffer, else MK_EINVAL) through an LDS ring of
  * `ring_granules` (2..150) KiB with the resident loop's loader protocol
  * (`depth` transfers in flight: 0, 8, 40 or 56) while the compute waves check
  * every word they read against `src`; `variant` 2 or 3 makes another wave
- * issue agent-scope acquire or release fences meanwhile. Adds the number of
- * mismatching words to errs_dev[0], granules checked to errs_dev[1] and
- * timed-out waits to errs_dev[2] (device int32[4]). Synchronous. Errors:
+ * issue agent-scope acquire or release fences meanwhile, `variant` 4 consumes
+ * without checking (for timing). Adds the number of mismatching words to
+ * errs_dev[0], granules checked to errs_dev[1] and timed-out waits to
+ * errs_dev[2] (device int32[4]). Asynchronous on the null stream. Errors:
  * MK_EINVAL, MK_EHIP. */
-int mk_debug_ring_probe(const void *src, int n_granules, int ring_granules, int depth, int variant,
-                        int32_t *errs_dev);
+int mk_debug_ring_probe(const void *src, size_t src_bytes, int n_granules, int ring_granules, int depth,
+                        int variant, int32_t *errs_dev, int blocks, void *stream);
+
+/* Plain HBM streaming read of `bytes` from device `src` by `blocks`
+ * workgroups of 256 threads (16-byte loads), for the achievable read
+ * bandwidth. Asynchronous on the null stream. Errors: MK_EINVAL, MK_EHIP. */
+int mk_debug_stream_probe(const void *src, size_t bytes, int blocks, void *out_dev);
 
 /* Cross-XCD message-passing litmus of the counter protocol: `pairs`
  * writer/reader workgroup pairs (co-resident, cooperative launch) run

@@ -81,7 +81,8 @@ _SIGS = {
     "mk_read_trace": (i32, [vp, ctypes.POINTER(ctypes.c_int64), ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]),
     "mk_debug_copy_scratch": (i32, [vp, i32, vp, ctypes.c_size_t]),
     "mk_debug_dma_probe": (i32, [vp, vp, i32, i32]),
-    "mk_debug_ring_probe": (i32, [vp, i32, i32, i32, i32, vp]),
+    "mk_debug_ring_probe": (i32, [vp, ctypes.c_size_t, i32, i32, i32, i32, vp, i32, vp]),
+    "mk_debug_stream_probe": (i32, [vp, ctypes.c_size_t, i32, vp]),
     "mk_debug_litmus": (i32, [i32, i32, i32, vp, vp, vp]),
     "mk_plan_create": (i32, [ctypes.POINTER(MkConfig), ctypes.POINTER(MkScheduleDesc), ctypes.POINTER(vp)]),
     "mk_plan_destroy": (None, [vp]),

@@ -408,17 +408,31 @@ int mk_debug_copy_scratch(mk_handle *h, int which, void *out, size_t bytes) {
 }
 
 int mk_debug_dma_probe(const void *src, void *dst, int n_kib, int lds_offset_kib) {
+    if (n_kib == -1 && src && dst && lds_offset_kib >= 0 && lds_offset_kib + 2 <= mk::LDS_LIMIT / 1024) {
+        MK_HIP(mk::dma_probe(src, dst, -1, lds_offset_kib));
+        return MK_OK;
+    }
     if (!src || !dst || n_kib < 1 || lds_offset_kib < 0 || n_kib + lds_offset_kib > mk::LDS_LIMIT / 1024)
         return set_error(MK_EINVAL, "bad probe arguments");
     MK_HIP(mk::dma_probe(src, dst, n_kib, lds_offset_kib));
     return MK_OK;
 }
 
-int mk_debug_ring_probe(const void *src, int n_granules, int ring_granules, int depth, int variant,
-                        int32_t *errs_dev) {
-    if (!src || !errs_dev || n_granules < 1 || ring_granules < 2 || ring_granules > 150 || depth < 0)
+int mk_debug_ring_probe(const void *src, size_t src_bytes, int n_granules, int ring_granules, int depth,
+                        int variant, int32_t *errs_dev, int blocks, void *stream) {
+    if (!src || !errs_dev || n_granules < 1 || ring_granules < 2 || ring_granules > 150 || depth < 0 || blocks < 1 ||
+        blocks > 256)
         return set_error(MK_EINVAL, "bad probe arguments");
-    MK_HIP(mk::ring_probe(src, n_granules, ring_granules, depth, variant, errs_dev));
+    if ((size_t)blocks * (size_t)n_granules * mk::GRANULE > src_bytes)
+        return set_error(MK_EINVAL, "blocks * n_granules KiB exceeds the source buffer");
+    (void)stream;
+    MK_HIP(mk::ring_probe(src, n_granules, ring_granules, depth, variant, errs_dev, blocks));
+    return MK_OK;
+}
+
+int mk_debug_stream_probe(const void *src, size_t bytes, int blocks, void *out_dev) {
+    if (!src || !out_dev || blocks < 1 || bytes < 16) return set_error(MK_EINVAL, "bad probe arguments");
+    MK_HIP(mk::stream_probe(src, bytes, blocks, (uint32_t *)out_dev));
     return MK_OK;
 }
 

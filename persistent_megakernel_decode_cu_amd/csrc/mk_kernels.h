@@ -52,7 +52,8 @@ hipError_t setup_megakernel(int lds_bytes);
 hipError_t megakernel_occupancy(int lds_bytes, int *blocks_per_cu);
 hipError_t launch_unfused(const KParams &p, float *u_scratch, float *qrot, hipStream_t s);
 hipError_t dma_probe(const void *src, void *dst, int n_kib, int off_kib);
-hipError_t ring_probe(const void *src, int n, int ring, int depth, int variant, int32_t *errs);
+hipError_t ring_probe(const void *src, int n, int ring, int depth, int variant, int32_t *errs, int blocks);
+hipError_t stream_probe(const void *src, size_t bytes, int blocks, uint32_t *out);
 hipError_t litmus(int pairs, int n, int rounds, int32_t *data, int32_t *flags, int32_t *res);
 hipError_t launch_rope_table(float2 *table, int capacity, int d, double theta, hipStream_t s);
 

@@ -733,8 +733,22 @@ __global__ __launch_bounds__(64) void mk_dma_probe(const char *src, char *dst, i
     for (int i = lane; i < LDS_LIMIT / 4; i += 64) ((MK_LDS uint32_t *)lds)[i] = 0u;
     __syncthreads();
     const uint32_t base = (uint32_t)(uintptr_t)lds + (uint32_t)off;
-    for (int k = 0; k < n; ++k)
-        dma16(src + (size_t)k * GRANULE + lane * 16, __builtin_amdgcn_readfirstlane(base + k * GRANULE));
+    if (n < 0) {
+        // two transfers, one m0 value, the second with instruction offset 1024
+        const char *g = src + lane * 16;
+        asm volatile(
+            "s_mov_b32 m0, %0\n\t"
+            "s_nop 1\n\t"
+            "global_load_lds_dwordx4 %1, off\n\t"
+            "global_load_lds_dwordx4 %1, off offset:1024"
+            :
+            : "s"(base), "v"(g)
+            : "memory");
+        n = 2;
+    } else {
+        for (int k = 0; k < n; ++k)
+            dma16(src + (size_t)k * GRANULE + lane * 16, __builtin_amdgcn_readfirstlane(base + k * GRANULE));
+    }
     wait_vmcnt<0>();
     for (int k = 0; k < n; ++k) {
         const v4u v = *(const MK_LDS v4u *)(lds + off + k * GRANULE + lane * 16);
@@ -768,8 +782,207 @@ __global__ __launch_bounds__(BLOCK_THREADS, 1) void mk_ring_probe(const uint32_t
     MK_LDS char *rb = lds + MISC_BYTES;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    src += (size_t)blockIdx.x * n * 256;
     for (int i = threadIdx.x; i < MISC_BYTES / 4; i += BLOCK_THREADS) misc[i] = 0;
     __syncthreads();
+    const int nl = (variant >> 8) & 15;
+    const int gb = ((variant >> 12) & 15) ? ((variant >> 12) & 15) : 1;  // granules per DMA batch: 1 or 4
+    const bool regs = (variant >> 16) & 1;                                // register-staged loaders
+    const bool inter = (variant >> 17) & 1;  // batch t of workgroup b at (t * gridDim.x + b) * 4 KiB
+    const bool plain = (variant >> 18) & 1;  // ordinary loads instead of non-temporal ones
+    variant &= 255;
+    if (inter) src -= (size_t)blockIdx.x * n * 256;  // undo the per-block slice
+    if (regs && nl >= 1) {
+        // nl loader waves; batch t = 4 granules issued by loader t % nl with
+        // ordinary 16-byte loads into registers, 4 batches in flight, then
+        // written into the ring once its slots are free
+        const int ncons = N_WAVES - nl;
+        const int nbatch = n / 4;
+        if (wave < nl) {
+            uint32_t mine = 0, lim = ring;
+            v4u ra[4], rbuf[4], rc[4], rd[4];
+            auto issue = [&](v4u (&r)[4], int t) {
+                if (t < nbatch) {
+                    const size_t bt = inter ? (size_t)t * gridDim.x + blockIdx.x : (size_t)t;
+                    const v4u *g = (const v4u *)(src + bt * 4 * 256) + lane;
+                    if (plain) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) r[i] = g[i * 64];
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) r[i] = __builtin_nontemporal_load(g + i * 64);
+                    }
+                }
+            };
+            auto commit = [&](v4u (&r)[4], int t) -> bool {
+                if (t >= nbatch) return true;
+                const uint32_t k = (uint32_t)t * 4;
+                if (k + 4 > lim) {
+                    int64_t spins = 0;
+                    for (;;) {
+                        uint32_t mn = lds_ld(misc + M_WPOS);
+                        for (int w = 1; w < ncons; ++w) mn = min(mn, lds_ld(misc + M_WPOS + w));
+                        lim = __builtin_amdgcn_readfirstlane(mn + ring);
+                        if (k + 4 <= lim) break;
+                        if (++spins > watchdog) {
+                            lds_st(misc + M_ABORT, 1u);
+                            return false;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) *(MK_LDS v4u *)(rb + ((k + i) % ring) * GRANULE + lane * 16) = r[i];
+                mine += 4;
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                __hip_atomic_store(misc + M_LANDED + 32 + wave, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                return true;
+            };
+            const int step = nl;
+            int t = wave;
+            issue(ra, t);
+            issue(rbuf, t + step);
+            issue(rc, t + 2 * step);
+            issue(rd, t + 3 * step);
+            for (; t < nbatch; t += 4 * step) {
+                if (!commit(ra, t)) return;
+                issue(ra, t + 4 * step);
+                if (!commit(rbuf, t + step)) return;
+                issue(rbuf, t + 5 * step);
+                if (!commit(rc, t + 2 * step)) return;
+                issue(rc, t + 6 * step);
+                if (!commit(rd, t + 3 * step)) return;
+                issue(rd, t + 7 * step);
+            }
+        } else {
+            const int w = wave - nl;
+            int bad = 0, seen = 0;
+            for (int g = w; g < nbatch * 4; g += ncons) {
+                const int tb = g / 4;
+                const int j = tb % nl;
+                const uint32_t need = (uint32_t)((tb / nl + 1) * 4);
+                int64_t spins = 0;
+                while (lds_ld(misc + M_LANDED + 32 + j) < need) {
+                    if (lds_ld(misc + M_ABORT) == 1u || ++spins > watchdog) {
+                        if (lane == 0) atomicAdd(errs + 2, 1);
+                        return;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                const v4u v = *(const MK_LDS v4u *)(rb + (g % ring) * GRANULE + lane * 16);
+                const uint32_t e = (uint32_t)g * 256u + lane * 4u;
+                if (variant == 4)
+                    bad += (v.x ^ v.y ^ v.z ^ v.w) == 0x12345678u;
+                else
+                    bad += (v.x != src[e]) + (v.y != src[e + 1]) + (v.z != src[e + 2]) + (v.w != src[e + 3]);
+                ++seen;
+                const int gn = g + ncons;
+                if (lane == 0) lds_st(misc + M_WPOS + w, (uint32_t)(gn < nbatch * 4 ? gn : nbatch * 4));
+            }
+            if (lane == 0) lds_st(misc + M_WPOS + w, (uint32_t)(nbatch * 4));
+            bad = (int)wave_sum((float)bad);
+            if (lane == 0) {
+                atomicAdd(errs, bad);
+                atomicAdd(errs + 1, seen);
+            }
+        }
+        return;
+    }
+    if (nl >= 1) {
+        // nl loader waves; batch t (granules [t*gb, t*gb+gb)) is issued by
+        // loader t % nl with one m0 write; consumers are waves nl .. N_WAVES-1
+        // and wait on the issuing loader's own landed count (in granules)
+        const int ncons = N_WAVES - nl;
+        const int nbatch = n / gb;
+        if (wave < nl) {
+            const uint32_t ring_lds = (uint32_t)(uintptr_t)rb;
+            uint32_t mine = 0, pub = 0, lim = ring;
+            for (int t = wave; t < nbatch; t += nl) {
+                const uint32_t k = (uint32_t)t * gb;  // first granule of the batch
+                if (k + gb > lim) {
+                    int64_t spins = 0;
+                    for (;;) {
+                        wait_vmcnt<0>();
+                        pub = mine;
+                        lds_st(misc + M_LANDED + 32 + wave, mine);
+                        uint32_t mn = lds_ld(misc + M_WPOS);
+                        for (int w = 1; w < ncons; ++w) mn = min(mn, lds_ld(misc + M_WPOS + w));
+                        lim = __builtin_amdgcn_readfirstlane(mn + ring);
+                        if (k + gb <= lim) break;
+                        if (++spins > watchdog) {
+                            lds_st(misc + M_ABORT, 1u);
+                            return;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                }
+                const size_t kk = inter ? ((size_t)t * gridDim.x + blockIdx.x) * gb : (size_t)k;
+                const char *g = (const char *)(src + kk * 256 + lane * 4);
+                const uint32_t l = __builtin_amdgcn_readfirstlane(ring_lds + (k % ring) * GRANULE);
+                if (gb == 4) {
+                    asm volatile(
+                        "s_mov_b32 m0, %0\n\t"
+                        "s_nop 1\n\t"
+                        "global_load_lds_dwordx4 %1, off\n\t"
+                        "global_load_lds_dwordx4 %1, off offset:1024\n\t"
+                        "global_load_lds_dwordx4 %1, off offset:2048\n\t"
+                        "global_load_lds_dwordx4 %1, off offset:3072"
+                        :
+                        : "s"(l), "v"(g)
+                        : "memory");
+                } else {
+                    dma16(g, l);
+                }
+                mine += gb;
+                uint32_t dd;
+                switch (depth) {
+                    case 8: wait_vmcnt<8>(); dd = 8; break;
+                    case 32: wait_vmcnt<32>(); dd = 32; break;
+                    case 48: wait_vmcnt<48>(); dd = 48; break;
+                    case 56: wait_vmcnt<56>(); dd = 56; break;
+                    default: wait_vmcnt<16>(); dd = 16; break;
+                }
+                if (mine > dd && mine - dd > pub) {
+                    pub = mine - dd;
+                    lds_st(misc + M_LANDED + 32 + wave, pub);
+                }
+            }
+            wait_vmcnt<0>();
+            lds_st(misc + M_LANDED + 32 + wave, mine);
+        } else {
+            const int w = wave - nl;
+            int bad = 0, seen = 0;
+            for (int g = w; g < nbatch * gb; g += ncons) {
+                const int t = g / gb;
+                const int j = t % nl;
+                const uint32_t need = (uint32_t)((t / nl + 1) * gb);
+                int64_t spins = 0;
+                while (lds_ld(misc + M_LANDED + 32 + j) < need) {
+                    if (lds_ld(misc + M_ABORT) == 1u || ++spins > watchdog) {
+                        if (lane == 0) atomicAdd(errs + 2, 1);
+                        return;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                const v4u v = *(const MK_LDS v4u *)(rb + (g % ring) * GRANULE + lane * 16);
+                const uint32_t e = (uint32_t)g * 256u + lane * 4u;
+                if (variant == 4)
+                    bad += (v.x ^ v.y ^ v.z ^ v.w) == 0x12345678u;
+                else
+                    bad += (v.x != src[e]) + (v.y != src[e + 1]) + (v.z != src[e + 2]) + (v.w != src[e + 3]);
+                ++seen;
+                const int gn = g + ncons;
+                if (lane == 0) lds_st(misc + M_WPOS + w, (uint32_t)(gn < nbatch * gb ? gn : nbatch * gb));
+            }
+            if (lane == 0) lds_st(misc + M_WPOS + w, (uint32_t)(nbatch * gb));
+            bad = (int)wave_sum((float)bad);
+            if (lane == 0) {
+                atomicAdd(errs, bad);
+                atomicAdd(errs + 1, seen);
+            }
+        }
+        return;
+    }
     if (wave == 0) {
         const uint32_t ring_lds = (uint32_t)(uintptr_t)rb;
         uint32_t issued = 0, slot = 0, lim = ring, pub = 0;
@@ -839,7 +1052,10 @@ __global__ __launch_bounds__(BLOCK_THREADS, 1) void mk_ring_probe(const uint32_t
             }
             const v4u v = *(const MK_LDS v4u *)(rb + (g % ring) * GRANULE + lane * 16);
             const uint32_t e = (uint32_t)g * 256u + lane * 4u;
-            bad += (v.x != src[e]) + (v.y != src[e + 1]) + (v.z != src[e + 2]) + (v.w != src[e + 3]);
+            if (variant == 4)
+                bad += (v.x ^ v.y ^ v.z ^ v.w) == 0x12345678u;
+            else
+                bad += (v.x != src[e]) + (v.y != src[e + 1]) + (v.z != src[e + 2]) + (v.w != src[e + 3]);
             ++seen;
             const int gn = g + NC;
             if (lane == 0) lds_st(misc + M_WPOS + w, (uint32_t)(gn < n ? gn : n));
@@ -853,15 +1069,13 @@ __global__ __launch_bounds__(BLOCK_THREADS, 1) void mk_ring_probe(const uint32_t
     }
 }
 
-hipError_t ring_probe(const void *src, int n, int ring, int depth, int variant, int32_t *errs) {
+hipError_t ring_probe(const void *src, int n, int ring, int depth, int variant, int32_t *errs, int blocks) {
     const int lds = MISC_BYTES + ring * GRANULE;
     hipError_t e = hipFuncSetAttribute((const void *)mk_ring_probe, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mk_ring_probe, dim3(1), dim3(BLOCK_THREADS), lds, 0, (const uint32_t *)src, n, ring, depth,
-                       variant, (int64_t)1 << 22, errs);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return hipDeviceSynchronize();
+    hipLaunchKernelGGL(mk_ring_probe, dim3(blocks), dim3(BLOCK_THREADS), lds, 0, (const uint32_t *)src, n, ring,
+                       depth, variant, (int64_t)1 << 22, errs);
+    return hipGetLastError();
 }
 
 // Cross-XCD message-passing litmus. Workgroup 2k writes, workgroup 2k+1 (on
@@ -934,6 +1148,28 @@ hipError_t litmus(int pairs, int n, int rounds, int32_t *data, int32_t *flags, i
     hipError_t e = hipLaunchCooperativeKernel((const void *)mk_litmus, dim3(2 * pairs), dim3(256), args, 0, nullptr);
     if (e != hipSuccess) return e;
     return hipDeviceSynchronize();
+}
+
+// Plain HBM streaming read: every thread sums 16-byte loads; the achievable
+// read bandwidth of the chip.
+__global__ __launch_bounds__(256) void mk_stream_probe(const v4u *src, size_t n16, uint32_t *out) {
+    uint32_t acc = 0;
+    const size_t stride = (size_t)gridDim.x * 256;
+    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const v4u a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    }
+    for (; i < n16; i += stride) {
+        const v4u a = src[i];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    if (acc == 0x9e3779b9u) out[0] = acc;
+}
+
+hipError_t stream_probe(const void *src, size_t bytes, int blocks, uint32_t *out) {
+    hipLaunchKernelGGL(mk_stream_probe, dim3(blocks), dim3(256), 0, 0, (const v4u *)src, bytes / 16, out);
+    return hipGetLastError();
 }
 
 hipError_t setup_megakernel(int lds_bytes) {
