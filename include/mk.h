@@ -49,9 +49,10 @@ typedef enum mk_status {
     MK_OK = 0,
     MK_EINVAL = 1,      /* an argument is invalid (null, shape, range) */
     MK_ENOSCHED = 2,    /* mk_decode_step before a successful mk_build_schedule */
-    MK_ECAPACITY = 3,   /* queue, LDS ring, attention chunking or K/V pages
-                           cannot cover the configured maximum (capacity
-                           obligation of the "unified framework" section) */
+    MK_ECAPACITY = 3,   /* queue, LDS staging, attention chunking or K/V
+                           pages cannot cover the configured maximum
+                           (capacity obligation of the "unified framework"
+                           section) */
     MK_ERESOURCE = 4,   /* the resident grid cannot be co-resident at one
                            workgroup per CU (resource obligation) */
     MK_EHIP = 5,        /* a HIP runtime call failed */
@@ -108,11 +109,8 @@ typedef struct mk_schedule_desc {
     int32_t attn_chunks;     /* K/V chunks per (request, kv head); 0 = auto */
     int32_t trace;           /* 1: record per-instruction device timestamps */
     int64_t watchdog_spins;  /* bound of every device wait loop; 0 = default */
-    int32_t ring_kib;        /* LDS weight ring in KiB; 0 = all the LDS left
-                                after the activation area */
-    int32_t dma_inflight;    /* 1 KiB HBM -> LDS transfers the loader keeps
-                                in flight (1..57, rounded down to one of
-                                1, 5, 9, 17, 25, 33, 41, 49, 57); 0 = 41 */
+    int32_t reserved0;       /* must be 0 */
+    int32_t reserved1;       /* must be 0 */
 } mk_schedule_desc;
 
 /* Buffers of one step. All device pointers; the caller owns them. The new
@@ -178,7 +176,7 @@ int mk_sync_status(mk_handle *h, void *stream);
 /* Schedule facts for reports and tests. */
 typedef struct mk_schedule_info {
     int32_t n_cus, queue_len, n_instr, n_events, n_counters;
-    int32_t attn_chunks, ring_granules, lds_bytes, block_threads;
+    int32_t attn_chunks, prefetch_slices, lds_bytes, block_threads;
     int64_t stream_bytes_max_cu;   /* largest per-CU streamed byte count of a step at max_kv_len */
     int64_t stream_bytes_total;    /* streamed bytes of a step over all CUs at max_kv_len */
     int32_t launches_per_step;     /* 1 for the megakernel, kernel count for MK_MODE_UNFUSED */
@@ -226,15 +224,50 @@ int mk_debug_ring_probe(const void *src, size_t src_bytes, int n_granules, int r
  * bandwidth. Asynchronous on the null stream. Errors: MK_EINVAL, MK_EHIP. */
 int mk_debug_stream_probe(const void *src, size_t bytes, int blocks, void *out_dev);
 
-/* Cross-XCD message-passing litmus of the counter protocol: `pairs`
- * writer/reader workgroup pairs (co-resident, cooperative launch) run
- * `rounds` rounds over `n_words` int32 words each (data_dev: pairs * n_words
- * int32; flags_dev: pairs * 64 int32, zeroed). The reader plants stale
- * copies, waits for the writer's released flag, acquires, and counts words
- * that are not the round's value: res_dev[0] with plain loads, res_dev[1]
- * with device-coherent loads; res_dev[2] counts watchdog expiries (device
- * int32[4], zeroed). Synchronous. Errors: MK_EINVAL, MK_EHIP. */
-int mk_debug_litmus(int pairs, int n_words, int rounds, int32_t *data_dev, int32_t *flags_dev, int32_t *res_dev);
+/* Cross-XCD message-passing litmus: `pairs` writer/reader workgroup pairs
+ * (co-resident, cooperative launch) run `rounds` rounds over `n_words` int32
+ * words each (data_dev: pairs * n_words int32; flags_dev: pairs * 64 int32,
+ * zeroed). The reader plants possibly stale copies with plain loads, waits
+ * for the writer's flag and counts words that are not the round's value:
+ * res_dev[0] with plain loads, res_dev[1] with device-coherent loads;
+ * res_dev[2] counts watchdog expiries (device int32[4], zeroed).
+ * mode 0: plain stores, agent-scope release fence before the flag and
+ * acquire fence after it. mode 1: device-coherent stores, completion wait
+ * before the flag, no fences (the protocol of the resident interpreter, in
+ * which only the device-coherent count must be zero). Synchronous. Errors:
+ * MK_EINVAL, MK_EHIP. */
+int mk_debug_litmus(int pairs, int n_words, int rounds, int mode, int32_t *data_dev, int32_t *flags_dev,
+                    int32_t *res_dev);
+
+/* Dependency-hop latency: a cooperative grid of n_cus one-wave workgroups
+ * runs `rounds` grid-wide hops (wait for every workgroup's previous round,
+ * optionally acquire, optionally exchange 8 floats per workgroup, optionally
+ * release, signal). ctr_dev: ctr_words int32, zeroed by the caller, at least
+ * max((rounds + 1) * 32, (17 + ceil(n_cus / 16)) * 1024); xbuf_dev:
+ * xbuf_floats floats, at least 2 * ceil(n_cus / 4) * 1024; res_dev: 2 int32
+ * (res[0] counts watchdog expiries). variant bits: 0 no release fence, 1 no
+ * acquire fence, 2 exchange the floats, 3 tree of 16-way counters with
+ * replicated release flags instead of one shared counter, 4 spread the
+ * exchanged vector one 128-byte line per 4 KiB, 5 plain loads and stores for
+ * the exchange instead of device-coherent ones. Asynchronous on the null
+ * stream. */
+int mk_debug_hop_probe(int32_t *ctr_dev, size_t ctr_words, float *xbuf_dev, size_t xbuf_floats, int n_cus,
+                       int rounds, int variant, int32_t *res_dev);
+/* Epoch-tagged exchange latency: a cooperative grid of n_cus one-wave
+ * workgroups runs `rounds` rounds; in each, every workgroup writes `per`
+ * 64-bit (value, round) words into each of `copies` (1..16) copies of the
+ * exchange vector and then reads all n_cus * per words of copy
+ * (workgroup % copies) until each carries the round. buf_dev: buf_words
+ * uint64, at least 2 * copies * n_cus * per, zeroed by the caller; res_dev:
+ * 2 int32 (res[0] counts watchdog expiries). Asynchronous on the null
+ * stream. */
+int mk_debug_ll_probe(uint64_t *buf_dev, size_t buf_words, int n_cus, int per, int copies, int rounds,
+                      int32_t *res_dev);
+/* Read bandwidth of `blocks` workgroups of `threads` threads streaming the
+ * first floor(bytes / 4096) 4 KiB slices of src through registers with
+ * `depth` (1..6) slices in flight per wave. out_dev: one uint32 sink.
+ * Asynchronous on the null stream. */
+int mk_debug_regstream_probe(const void *src, size_t bytes, int blocks, int threads, int depth, void *out_dev);
 
 /* ---- host-only planning (no HIP call; usable without a GPU) ---- */
 

@@ -84,10 +84,8 @@ class Decoder:
         self.batch = 0
 
     def build_schedule(self, batch: int, mode: str = "megakernel", max_kv_len: int = 0, attn_chunks: int = 0,
-                       n_cus: int = 0, trace: bool = False, watchdog_spins: int = 0, ring_kib: int = 0,
-                       dma_inflight: int = 0) -> dict:
-        desc = MkScheduleDesc(batch, n_cus, _MODES[mode], max_kv_len, attn_chunks, int(trace), watchdog_spins,
-                              ring_kib, dma_inflight)
+                       n_cus: int = 0, trace: bool = False, watchdog_spins: int = 0) -> dict:
+        desc = MkScheduleDesc(batch, n_cus, _MODES[mode], max_kv_len, attn_chunks, int(trace), watchdog_spins, 0, 0)
         mk_build_schedule(self.handle, desc)
         self.batch = batch
         self.mode = mode

@@ -41,8 +41,8 @@ class MkWeights(ctypes.Structure):
 
 class MkScheduleDesc(ctypes.Structure):
     _fields_ = [("batch", i32), ("n_cus", i32), ("mode", i32), ("max_kv_len", i32),
-                ("attn_chunks", i32), ("trace", i32), ("watchdog_spins", i64), ("ring_kib", i32),
-                ("dma_inflight", i32)]
+                ("attn_chunks", i32), ("trace", i32), ("watchdog_spins", i64), ("reserved0", i32),
+                ("reserved1", i32)]
 
 
 class MkStepIO(ctypes.Structure):
@@ -53,7 +53,7 @@ class MkStepIO(ctypes.Structure):
 
 class MkScheduleInfo(ctypes.Structure):
     _fields_ = [("n_cus", i32), ("queue_len", i32), ("n_instr", i32), ("n_events", i32),
-                ("n_counters", i32), ("attn_chunks", i32), ("ring_granules", i32), ("lds_bytes", i32),
+                ("n_counters", i32), ("attn_chunks", i32), ("prefetch_slices", i32), ("lds_bytes", i32),
                 ("block_threads", i32), ("stream_bytes_max_cu", i64), ("stream_bytes_total", i64),
                 ("launches_per_step", i32)]
 
@@ -83,7 +83,10 @@ _SIGS = {
     "mk_debug_dma_probe": (i32, [vp, vp, i32, i32]),
     "mk_debug_ring_probe": (i32, [vp, ctypes.c_size_t, i32, i32, i32, i32, vp, i32, vp]),
     "mk_debug_stream_probe": (i32, [vp, ctypes.c_size_t, i32, vp]),
-    "mk_debug_litmus": (i32, [i32, i32, i32, vp, vp, vp]),
+    "mk_debug_litmus": (i32, [i32, i32, i32, i32, vp, vp, vp]),
+    "mk_debug_hop_probe": (i32, [vp, ctypes.c_size_t, vp, ctypes.c_size_t, i32, i32, i32, vp]),
+    "mk_debug_ll_probe": (i32, [vp, ctypes.c_size_t, i32, i32, i32, i32, vp]),
+    "mk_debug_regstream_probe": (i32, [vp, ctypes.c_size_t, i32, i32, i32, vp]),
     "mk_plan_create": (i32, [ctypes.POINTER(MkConfig), ctypes.POINTER(MkScheduleDesc), ctypes.POINTER(vp)]),
     "mk_plan_destroy": (None, [vp]),
     "mk_plan_info": (i32, [vp, ctypes.POINTER(MkScheduleInfo)]),

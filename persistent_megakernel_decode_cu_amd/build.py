@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libmk.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["mk_api.cpp", "mk_sched.cpp", "mk_megakernel.hip", "mk_unfused.hip"]
+SOURCES = ["mk_api.cpp", "mk_sched.cpp", "mk_megakernel.hip", "mk_interp_b1.hip", "mk_interp_b2.hip",
+           "mk_interp_b4.hip", "mk_interp_b8.hip", "mk_unfused.hip", "mk_probes.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
@@ -36,7 +37,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]

@@ -1,3 +1,4 @@
+#include <algorithm>
 // mk_api.cpp - the C ABI (include/mk.h): model binding, schedule upload,
 // step launch, sticky device errors.
 //
@@ -58,6 +59,8 @@ struct mk_handle {
     int32_t *queue = nullptr, *events = nullptr, *counters = nullptr;
     float *x = nullptr, *qkv = nullptr, *o = nullptr, *act = nullptr, *attn_part = nullptr, *lm_part = nullptr;
     float *u = nullptr, *qrot = nullptr;
+    uint64_t *tx = nullptr, *tqkv = nullptr, *to = nullptr, *tact = nullptr, *tpart = nullptr, *tlm = nullptr;
+    uint32_t tag = 0;  // tag of the last step's activations (never 0 on the device)
     int64_t *trace = nullptr;
     int64_t epoch = 0;
     int32_t max_need = 1;
@@ -84,6 +87,12 @@ void free_schedule(mk_handle *h) {
     dfree(h->lm_part);
     dfree(h->u);
     dfree(h->qrot);
+    dfree(h->tx);
+    dfree(h->tqkv);
+    dfree(h->to);
+    dfree(h->tact);
+    dfree(h->tpart);
+    dfree(h->tlm);
     dfree(h->trace);
     h->built = false;
 }
@@ -187,10 +196,13 @@ int mk_build_schedule(mk_handle *h, const mk_schedule_desc *s) {
         if (d.watchdog_spins <= 0) d.watchdog_spins = (int64_t)1 << 22;
         mk::Plan plan;
         if (int rc = mk::build_plan(h->cfg, d, plan)) return rc;
+        const int G = h->cfg.n_q_heads / h->cfg.n_kv_heads;
         if (d.mode == MK_MODE_MEGAKERNEL) {
-            MK_HIP(mk::setup_megakernel(plan.lds_bytes));
+            if (!mk::megakernel_supports(d.batch, G))
+                return set_error(MK_EINVAL, "no resident interpreter for this batch and head grouping");
+            MK_HIP(mk::setup_megakernel(d.batch, G, plan.lds_bytes));
             int per_cu = 0;
-            MK_HIP(mk::megakernel_occupancy(plan.lds_bytes, &per_cu));
+            MK_HIP(mk::megakernel_occupancy(d.batch, G, plan.lds_bytes, &per_cu));
             if (per_cu < 1 || d.n_cus > h->n_cus_dev * per_cu)
                 return set_error(MK_ERESOURCE, "resident grid of " + std::to_string(d.n_cus) +
                                                    " workgroups is not co-resident (" + std::to_string(per_cu) +
@@ -200,7 +212,7 @@ int mk_build_schedule(mk_handle *h, const mk_schedule_desc *s) {
         free_schedule(h);
         h->plan = plan;
         const mk_config &c = h->cfg;
-        const int B = d.batch, G = c.n_q_heads / c.n_kv_heads;
+        const int B = d.batch;
         const size_t QKV = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim, QD = (size_t)c.n_q_heads * c.head_dim;
         const size_t kmax = std::max<size_t>(c.hidden, std::max<size_t>(c.ffn, QD));
         const size_t lm_slots =
@@ -217,6 +229,15 @@ int mk_build_schedule(mk_handle *h, const mk_schedule_desc *s) {
         if (!rc) rc = dalloc(h->lm_part, lm_slots * B * 2);
         if (!rc) rc = dalloc(h->u, (size_t)B * kmax);
         if (!rc) rc = dalloc(h->qrot, (size_t)B * QD);
+        if (d.mode == MK_MODE_MEGAKERNEL) {  // tagged activations, each written once per step
+            const size_t L = (size_t)c.n_layers;
+            if (!rc) rc = dalloc(h->tx, 2 * L * B * c.hidden);
+            if (!rc) rc = dalloc(h->tqkv, L * B * QKV);
+            if (!rc) rc = dalloc(h->to, L * B * QD);
+            if (!rc) rc = dalloc(h->tact, L * B * c.ffn);
+            if (!rc) rc = dalloc(h->tpart, L * B * c.n_kv_heads * plan.attn_chunks * G * mk::ATTN_PART);
+            if (!rc) rc = dalloc(h->tlm, (size_t)std::max(plan.n_lm_slots, 1) * B * 2);
+        }
         if (!rc && d.trace) rc = dalloc(h->trace, (size_t)plan.n_cus * plan.Q * 3);
         if (rc) {
             free_schedule(h);
@@ -233,6 +254,7 @@ int mk_build_schedule(mk_handle *h, const mk_schedule_desc *s) {
         *h->host_err = 0;
         h->sticky = MK_OK;
         h->epoch = 0;
+        h->tag = 0;
         MK_HIP(hipDeviceSynchronize());
         h->built = true;
         return MK_OK;
@@ -266,6 +288,7 @@ int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream) {
             h->epoch = 0;
         }
         h->epoch++;
+        if (++h->tag == 0) h->tag = 1;  // the buffers start at tag 0, which no step uses
         mk::KParams k{};
         k.queue = h->queue;
         k.events = h->events;
@@ -273,23 +296,13 @@ int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream) {
         k.Q = P.Q;
         k.epoch = (int32_t)h->epoch;
         k.n_cus = P.n_cus;
-        k.ring_granules = P.ring_granules;
-        k.act_off = mk::MISC_BYTES;
-        k.ring_off = P.lds_bytes - P.ring_granules * mk::GRANULE;
-        {
-            const int QD = c.n_q_heads * c.head_dim;
-            const int kmax = std::max(c.hidden, std::max(c.ffn, QD));
-            k.act_stride = (kmax + 511) / 512 * 512;
-        }
+        k.tag = h->tag;
+        k.xrow_off = P.xrow_off;
+        k.part_off = P.part_off;
+        k.act_off = P.act_off;
+        k.act_stride = P.act_stride;
+        k.xrow_stride = P.xrow_stride;
         k.watchdog = P.desc.watchdog_spins;
-        {
-            const int want = P.desc.dma_inflight > 0 ? P.desc.dma_inflight - 1 : 40;
-            const int allowed[] = {0, 4, 8, 16, 24, 32, 40, 48, 56};
-            int d = 0;
-            for (int a : allowed)
-                if (a <= want) d = a;
-            k.dma_depth = d;
-        }
         k.L = c.n_layers;
         k.H = c.hidden;
         k.nq = c.n_q_heads;
@@ -323,6 +336,12 @@ int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream) {
         k.act = h->act;
         k.attn_part = h->attn_part;
         k.lm_part = h->lm_part;
+        k.tx = h->tx;
+        k.tqkv = h->tqkv;
+        k.to = h->to;
+        k.tact = h->tact;
+        k.tpart = h->tpart;
+        k.tlm = h->tlm;
         k.attn_chunks = P.attn_chunks;
         k.err = h->err;
         k.host_err = h->host_err_dev;
@@ -377,7 +396,7 @@ int mk_get_schedule_info(const mk_handle *h, mk_schedule_info *out) {
     out->n_events = P.n_events;
     out->n_counters = P.n_counters;
     out->attn_chunks = P.attn_chunks;
-    out->ring_granules = P.ring_granules;
+    out->prefetch_slices = mk::PREFETCH_SLICES;
     out->lds_bytes = P.lds_bytes;
     out->block_threads = mk::BLOCK_THREADS;
     out->stream_bytes_max_cu = P.stream_max_cu;
@@ -423,7 +442,7 @@ int mk_debug_ring_probe(const void *src, size_t src_bytes, int n_granules, int r
     if (!src || !errs_dev || n_granules < 1 || ring_granules < 2 || ring_granules > 150 || depth < 0 || blocks < 1 ||
         blocks > 256)
         return set_error(MK_EINVAL, "bad probe arguments");
-    if ((size_t)blocks * (size_t)n_granules * mk::GRANULE > src_bytes)
+    if ((size_t)blocks * (size_t)n_granules * 1024 > src_bytes)
         return set_error(MK_EINVAL, "blocks * n_granules KiB exceeds the source buffer");
     (void)stream;
     MK_HIP(mk::ring_probe(src, n_granules, ring_granules, depth, variant, errs_dev, blocks));
@@ -436,10 +455,43 @@ int mk_debug_stream_probe(const void *src, size_t bytes, int blocks, void *out_d
     return MK_OK;
 }
 
-int mk_debug_litmus(int pairs, int n_words, int rounds, int32_t *data_dev, int32_t *flags_dev, int32_t *res_dev) {
-    if (pairs < 1 || pairs > 128 || n_words < 1 || rounds < 1 || !data_dev || !flags_dev || !res_dev)
+int mk_debug_litmus(int pairs, int n_words, int rounds, int mode, int32_t *data_dev, int32_t *flags_dev,
+                    int32_t *res_dev) {
+    if (pairs < 1 || pairs > 128 || n_words < 1 || rounds < 1 || mode < 0 || mode > 1 || !data_dev || !flags_dev ||
+        !res_dev)
         return set_error(MK_EINVAL, "bad litmus arguments");
-    MK_HIP(mk::litmus(pairs, n_words, rounds, data_dev, flags_dev, res_dev));
+    MK_HIP(mk::litmus(pairs, n_words, rounds, mode, data_dev, flags_dev, res_dev));
+    return MK_OK;
+}
+
+int mk_debug_hop_probe(int32_t *ctr_dev, size_t ctr_words, float *xbuf_dev, size_t xbuf_floats, int n_cus,
+                       int rounds, int variant, int32_t *res_dev) {
+    if (!ctr_dev || !xbuf_dev || !res_dev || n_cus < 1 || n_cus > 1024 || rounds < 1 || rounds > 100000 ||
+        variant < 0 || variant > 63)
+        return set_error(MK_EINVAL, "bad probe arguments");
+    const size_t groups = (size_t)(n_cus + 15) / 16;
+    const size_t need_ctr = std::max((size_t)(rounds + 1) * 32, (1 + groups + 16) * 1024);
+    const size_t need_x = 2 * (((size_t)n_cus * 8 + 31) / 32) * 1024;
+    if (ctr_words < need_ctr || xbuf_floats < need_x) return set_error(MK_EINVAL, "probe buffers too small");
+    MK_HIP(mk::hop_probe(ctr_dev, xbuf_dev, n_cus, rounds, variant, res_dev));
+    return MK_OK;
+}
+
+int mk_debug_ll_probe(uint64_t *buf_dev, size_t buf_words, int n_cus, int per, int copies, int rounds,
+                      int32_t *res_dev) {
+    if (!buf_dev || !res_dev || n_cus < 1 || n_cus > 1024 || per < 1 || per > 4096 || copies < 1 || copies > 16 ||
+        rounds < 1 || rounds > 100000 || (size_t)n_cus * per * copies * 8 >= ((size_t)1 << 31))
+        return set_error(MK_EINVAL, "bad probe arguments");
+    if (buf_words < 2 * (size_t)n_cus * per * copies) return set_error(MK_EINVAL, "probe buffer too small");
+    MK_HIP(mk::ll_probe(buf_dev, n_cus, per, copies, rounds, res_dev));
+    return MK_OK;
+}
+
+int mk_debug_regstream_probe(const void *src, size_t bytes, int blocks, int threads, int depth, void *out_dev) {
+    if (!src || !out_dev || blocks < 1 || bytes < 4096 || threads < 64 || threads > mk::BLOCK_THREADS ||
+        threads % 64 != 0 || depth < 1 || depth > 6)
+        return set_error(MK_EINVAL, "bad probe arguments");
+    MK_HIP(mk::regstream_probe(src, bytes, blocks, threads, depth, (uint32_t *)out_dev));
     return MK_OK;
 }
 

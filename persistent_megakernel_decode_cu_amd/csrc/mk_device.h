@@ -24,6 +24,58 @@ __device__ __forceinline__ T sload(const T *p, int64_t i) {
     return ((const MK_CONST T *)p)[i];
 }
 
+// s_waitcnt vmcnt(n) that is also a compiler barrier: no memory access moves
+// across it (the plain builtin is not one, and a store sinking below it, or a
+// flag store rising above it, would publish data that has not arrived).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Device-coherent vector accesses (scope bit sc1): they neither hit nor
+// leave behind lines that another XCD's L2 may hold stale, so data exchanged
+// between workgroups within one launch can move through them without the
+// agent-scope cache write-back and invalidate that a release or acquire fence
+// costs. Completion (s_waitcnt vmcnt(0)) of such a store makes it visible at
+// device scope; the compiler tracks these loads and stores like any other.
+constexpr int CP_SC1 = 16;  // cache-policy operand: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ v4f coherent_load16f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP_SC1);
+    return v4f{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+}
+__device__ __forceinline__ float coherent_load4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CP_SC1));
+}
+__device__ __forceinline__ void coherent_store4f(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, CP_SC1);
+}
+__device__ __forceinline__ void coherent_store16f(__amdgpu_buffer_rsrc_t r, uint32_t off, v4f v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v4u{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                                               __float_as_uint(v.w)},
+                                           r, off, 0, CP_SC1);
+}
+
+// Tagged activations: one 64-bit word per value, low half the fp32 bits,
+// high half the tag of the step that wrote it. A single 64-bit access is
+// atomic, so a reader that sees the tag sees the value written with it.
+__device__ __forceinline__ void tput(__amdgpu_buffer_rsrc_t r, uint32_t idx, float v, uint32_t tag) {
+    __builtin_amdgcn_raw_buffer_store_b64(v2u{__float_as_uint(v), tag}, r, idx * 8u, 0, CP_SC1);
+}
+__device__ __forceinline__ v2u tget(__amdgpu_buffer_rsrc_t r, uint32_t idx) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, idx * 8u, 0, CP_SC1);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tres(const uint64_t *base, uint32_t words) {
+    return coherent_rsrc(base, words * 8u);
+}
+// ordinary (cached) buffer resource over `bytes` bytes; loads beyond return 0
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t plain_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -75,93 +127,108 @@ __device__ __forceinline__ int act_index(int i) {
     return ((((ci >> 6) << 1) + (e8 >> 2)) << 8) + ((ci & 63) << 2) + (e8 & 3);
 }
 
+// Rotate-half RoPE of element i (lane) of a 64-wide head: x_i cos - x_{i+32}
+// sin for i < 32, x_i cos + x_{i-32} sin above; xp is the partner element.
+// Written with explicit fmaf so that every kernel rounds it the same way.
+__device__ __forceinline__ float rope_rotate(float xi, float xp, float2 cs, bool low_half) {
+    return low_half ? fmaf(xi, cs.x, -(xp * cs.y)) : fmaf(xi, cs.x, xp * cs.y);
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// Online-softmax state of one wave for up to 8 query heads of one kv group:
-// lanes are (head-in-pass hl = lane / 16, j = lane % 16); pass p covers heads
-// 4p .. 4p+3. m and l are replicated over the 16 lanes of a head; o holds
-// dims 4j .. 4j+3 of that head.
-struct AttnState {
-    float m[2], l[2], o[2][4];
+// Online-softmax state of one lane for the G query heads of one kv group. A 16-position K/V block (page) is spread over the wave as 16-byte
+// chunks: lane l holds dims 8 (l % 8) .. 8 (l % 8) + 7 of positions l / 8
+// (t0) and 8 + l / 8 (t1), for K and for V. Scores are reduced over the 8
+// lanes that share a position; m and l are wave-uniform; o[h] holds the
+// lane's own positions' share of dims 8 (l % 8) .. +7, summed over the 8
+// position groups only when the state is stored.
+template <int G>
+struct AttnLaneT {
+    float m[G], l[G], o[G][8];
 };
 
-__device__ __forceinline__ void attn_init(AttnState &s) {
+template <int G>
+__device__ __forceinline__ void attn_lane_init(AttnLaneT<G> &s) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        s.m[p] = -1e30f;
-        s.l[p] = 0.0f;
+    for (int h = 0; h < G; ++h) {
+        s.m[h] = -1e30f;
+        s.l[h] = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s.o[p][e] = 0.0f;
+        for (int e = 0; e < 8; ++e) s.o[h][e] = 0.0f;
     }
 }
 
-// One 16-position K/V block. `kchunk(j, ch)` returns 16 bytes (8 bf16) of K
-// row j, dims 8ch .. 8ch+7; `vpart(j, q)` returns 8 bytes (4 bf16) of V row
-// j, dims 4q .. 4q+3. q_lds: rotated queries [G][68] fp32. nvalid: positions
-// of the block that exist (the rest are masked).
-template <typename KF, typename VF>
-__device__ __forceinline__ void attn_block(AttnState &st, const MK_LDS float *q_lds, int G, int nvalid, int lane,
-                                           KF kchunk, VF vpart) {
-    const int hl = lane >> 4, j = lane & 15;
-    const int npass = (G + 3) >> 2;
+__device__ __forceinline__ float sum8lanes(float v) {
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    return v;
+}
+__device__ __forceinline__ float sum_groups(float v) {
+    v += __shfl_xor(v, 8, 64);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+__device__ __forceinline__ float max_groups(float v) {
+    v = fmaxf(v, __shfl_xor(v, 8, 64));
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    v = fmaxf(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+
+// One block: k0/v0 are this lane's K/V chunks of position t0, k1/v1 of t1;
+// ok0/ok1 say whether those positions exist (<= the new position). q: the
+// group's rotated queries, [G][64] fp32 in LDS.
+template <int G>
+__device__ __forceinline__ void attn_lane_block(AttnLaneT<G> &st, const MK_LDS float *q, int lane, v4u k0, v4u k1,
+                                                v4u v0, v4u v1, bool ok0, bool ok1) {
+    const int dd = (lane & 7) * 8;
+    if (!ok0) v0 = v4u{0u, 0u, 0u, 0u};  // a missing position may hold any bit pattern
+    if (!ok1) v1 = v4u{0u, 0u, 0u, 0u};
+    const float va[8] = {bf_lo(v0.x), bf_hi(v0.x), bf_lo(v0.y), bf_hi(v0.y),
+                         bf_lo(v0.z), bf_hi(v0.z), bf_lo(v0.w), bf_hi(v0.w)};
+    const float vb[8] = {bf_lo(v1.x), bf_hi(v1.x), bf_lo(v1.y), bf_hi(v1.y),
+                         bf_lo(v1.z), bf_hi(v1.z), bf_lo(v1.w), bf_hi(v1.w)};
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        if (p >= npass) break;
-        const int hq = p * 4 + hl;
-        const bool active = hq < G;
-        float s = 0.0f;
-        if (active && j < nvalid) {
-            const MK_LDS float *qh = q_lds + hq * 68;
+    for (int h = 0; h < G; ++h) {
+        const v4f qa = *(const MK_LDS v4f *)(q + h * 64 + dd);
+        const v4f qb = *(const MK_LDS v4f *)(q + h * 64 + dd + 4);
+        float s0 = sum8lanes(dot8(k0, qa, qb)) * 0.125f;  // 1 / sqrt(64)
+        float s1 = sum8lanes(dot8(k1, qa, qb)) * 0.125f;
+        if (!ok0) s0 = -INFINITY;
+        if (!ok1) s1 = -INFINITY;
+        const float mb = max_groups(fmaxf(s0, s1));
+        const float mnew = fmaxf(st.m[h], mb);
+        const float alpha = __expf(st.m[h] - mnew);
+        const float p0 = ok0 ? __expf(s0 - mnew) : 0.0f;
+        const float p1 = ok1 ? __expf(s1 - mnew) : 0.0f;
+        st.l[h] = st.l[h] * alpha + sum_groups(p0 + p1);
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const int ch = (kk + j) & 7;  // rotate the chunk order across lanes: fewer bank conflicts
-                v4u kw = kchunk(j, ch);
-                v4f a0 = *(const MK_LDS v4f *)(qh + ch * 8);
-                v4f a1 = *(const MK_LDS v4f *)(qh + ch * 8 + 4);
-                s += dot8(kw, a0, a1);
-            }
-            s *= 0.125f;  // 1 / sqrt(64)
-        } else {
-            s = -INFINITY;
-        }
-        const float mb = group16_max(s);
-        const float mnew = fmaxf(st.m[p], mb);
-        const float alpha = __expf(st.m[p] - mnew);
-        const float pj = (s == -INFINITY) ? 0.0f : __expf(s - mnew);
-        const float ls = group16_sum(pj);
-        st.l[p] = st.l[p] * alpha + ls;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st.o[p][e] *= alpha;
-        for (int jj = 0; jj < nvalid; ++jj) {
-            const float pw = __shfl(pj, (hl << 4) + jj, 64);
-            v2u vv = vpart(jj, j);
-            st.o[p][0] = fmaf(pw, bf_lo(vv.x), st.o[p][0]);
-            st.o[p][1] = fmaf(pw, bf_hi(vv.x), st.o[p][1]);
-            st.o[p][2] = fmaf(pw, bf_lo(vv.y), st.o[p][2]);
-            st.o[p][3] = fmaf(pw, bf_hi(vv.y), st.o[p][3]);
-        }
-        st.m[p] = mnew;
+        for (int e = 0; e < 8; ++e) st.o[h][e] = fmaf(p1, vb[e], fmaf(p0, va[e], st.o[h][e] * alpha));
+        st.m[h] = mnew;
     }
 }
 
-// Writes a wave's state as partials [G][68] (o[64], m, l).
-__device__ __forceinline__ void attn_store(const AttnState &st, MK_LDS float *part, int G, int lane) {
-    const int hl = lane >> 4, j = lane & 15;
+// Writes a wave's state as partials [G][ATTN_WAVE_PART] (o[64], m, l) after
+// summing o over the position groups.
+template <int G>
+__device__ __forceinline__ void attn_lane_store(AttnLaneT<G> &st, MK_LDS float *part, int lane) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int hq = p * 4 + hl;
-        if (hq < G) {
-            MK_LDS float *ph = part + hq * 68;
+    for (int h = 0; h < G; ++h) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ph[j * 4 + e] = st.o[p][e];
-            if (j == 0) {
-                ph[64] = st.m[p];
-                ph[65] = st.l[p];
-            }
+        for (int e = 0; e < 8; ++e) st.o[h][e] = sum_groups(st.o[h][e]);
+        if (lane < 8) {
+            MK_LDS float *ph = part + h * ATTN_WAVE_PART + lane * 8;
+            *(MK_LDS v4f *)ph = v4f{st.o[h][0], st.o[h][1], st.o[h][2], st.o[h][3]};
+            *(MK_LDS v4f *)(ph + 4) = v4f{st.o[h][4], st.o[h][5], st.o[h][6], st.o[h][7]};
+        }
+        if (lane == 0) {
+            part[h * ATTN_WAVE_PART + 64] = st.m[h];
+            part[h * ATTN_WAVE_PART + 65] = st.l[h];
         }
     }
 }
-
 
 // Merge partial softmax states (o, m, l) of `n` sources in source order;
 // lanes are dims. Sources are global (gsrc) or LDS (lsrc), `stride` floats

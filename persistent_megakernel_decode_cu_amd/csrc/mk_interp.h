@@ -1,0 +1,827 @@
+// mk_interp.h - the resident decode interpreter for gfx950 (device code).
+//
+// Included once per padded batch size by mk_interp_b{1,2,4,8}.hip, which
+// instantiate the kernel for each supported head grouping.
+//
+// "Inference MegaKernel" (shaojiemike.top), section "hand-written whole-model
+// MegaKernel / principle, schedule and dataflow": one grid sized to the
+// compute-unit count stays resident for the step; each workgroup walks its
+// own instruction queue, waits for the inputs of each instruction, runs the
+// op body and publishes its results for the consumers on other units. The
+// page's design targets one-die GPUs with a coherent L2, so its waits are on
+// counters that producers bump after a fence. gfx950 has eight L2s, one per
+// XCD, kept coherent only by agent-scope cache write-back / invalidate, and
+// measured on this chip a fenced counter hop across 256 workgroups costs
+// 7-15 us. So this interpreter moves every activation that crosses compute
+// units as a tagged 64-bit word (fp32 value, step tag) written and read with
+// device-coherent (sc1) accesses: a consumer polls the data itself, with no
+// fence and no counter, and a single 64-bit access makes value and tag
+// atomic. Counters are kept only to elect the one workgroup that merges split
+// attention chunks and the LM-head argmax.
+//
+// One workgroup per compute unit, N_COMPUTE_WAVES wave64s, all alike. The
+// page leases on-chip pages to prefetch the next op's weights while the
+// counter wait is still pending; here each wave keeps PREFETCH_SLICES 4 KiB
+// weight slices (or 16-position K/V blocks) in flight in its own registers,
+// and the stream of slices runs straight across instruction boundaries: the
+// weights and K/V blocks of the next instruction are already landing while
+// the wave polls that instruction's inputs. At an instruction boundary the
+// waves stage the inputs into LDS together (RMSNorm recomputed where the op
+// consumes a norm; RoPE and the K/V append for attention), then each takes
+// its round-robin share of rows (or K/V blocks) from the slice stream. The
+// last wave to finish an instruction runs its merges. Waves synchronise
+// through LDS counters only; every wait loop is bounded by a watchdog, after
+// which the wave records an error and the grid drains instead of hanging.
+#pragma once
+#include "mk_device.h"
+
+namespace mk {
+
+namespace {
+
+// LDS misc area, in 32-bit words
+enum : int {
+    M_ABORT = 0,
+    M_ARRIVE = 1,  // compute-wave barrier arrivals
+    M_FIN = 2,     // waves finished with an instruction's slices
+    M_DONE = 3,    // instructions fully finished (incl. their merges)
+    M_NORM = 16,   // [4][MAX_B] sums of squares
+    M_AMAX = 64,   // [NC][MAX_B][2] per-wave argmax (value, index)
+};
+
+constexpr int NC = N_COMPUTE_WAVES;
+constexpr int D = PREFETCH_SLICES;
+
+// Every lane reads the same LDS word; readfirstlane makes that visible to the
+// compiler, so that control flow on these flags stays uniform (and the slice
+// cursors stay in scalar registers).
+__device__ __forceinline__ uint32_t lds_ld(MK_LDS uint32_t *p) {
+    return __builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+}
+__device__ __forceinline__ void lds_st(MK_LDS uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ uint32_t lds_add(MK_LDS uint32_t *p, uint32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+struct Ctx {
+    MK_LDS uint32_t *misc;
+    MK_LDS float *act;   // matvec inputs of all requests, or the attention staging
+    MK_LDS float *xrow;  // residual rows of the instruction (O projection, down projection)
+    MK_LDS float *part;  // per-wave attention states; merge staging
+    int cu, lane, w;
+    uint32_t nbar;
+    uint32_t tag;        // copies of kernel arguments the helpers need: taking
+    int64_t watchdog;    // the argument block's address would move it to
+    int32_t *err;        // private memory
+    int32_t *host_err;
+};
+
+__device__ __forceinline__ void raise_err(Ctx &c, int code, int pc) {
+    const int32_t v = (code << 28) | ((c.cu & 0xfff) << 16) | (pc & 0xffff);
+    if (atomicCAS(c.err, 0, v) == 0 && c.host_err)
+        __hip_atomic_store(c.host_err, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    lds_st(c.misc + M_ABORT, 1u);
+}
+
+// A boolean every lane agrees on, made visibly uniform: return paths that
+// pass through lane-conditional code (an error report by lane 0) would
+// otherwise make the compiler treat the caller's loop control as divergent.
+__device__ __forceinline__ bool uni(bool b) { return __builtin_amdgcn_readfirstlane((int)b) != 0; }
+
+// Wait until *p >= v; false (after raising an error on timeout) if the
+// workgroup aborts.
+__device__ __forceinline__ bool lds_wait_ge(Ctx &c, MK_LDS uint32_t *p, uint32_t v, int pc) {
+    if (lds_ld(p) >= v) return true;
+    int64_t spins = 0;
+    while (lds_ld(p) < v) {
+        if (lds_ld(c.misc + M_ABORT)) return false;
+        if (++spins > c.watchdog) {
+            raise_err(c, ERR_TIMEOUT, pc);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return true;
+}
+
+// barrier of the workgroup's waves (one arrival per wave)
+__device__ __forceinline__ bool cbar(Ctx &c, int pc) {
+    c.nbar++;
+    if (c.lane == 0) lds_add(c.misc + M_ARRIVE, 1u);
+    return lds_wait_ge(c, c.misc + M_ARRIVE, (uint32_t)NC * c.nbar, pc);
+}
+
+__device__ __forceinline__ const int32_t *instr(const KParams &P, int cu, int pc) {
+    return P.queue + ((int64_t)cu * P.Q + pc) * INSTR_WORDS;
+}
+
+__device__ __forceinline__ const char *wptr(const KParams &P, int layer, int k) {
+    return (const char *)(uintptr_t)sload(P.wtab, (int64_t)layer * 8 + k);
+}
+
+__device__ __forceinline__ void chunk_blocks(int p, int c, int nch, int *lo, int *hi) {
+    const int nb = (p + 1 + 15) >> 4;
+    *lo = (int)((int64_t)c * nb / nch);
+    *hi = (int)((int64_t)(c + 1) * nb / nch);
+}
+
+// Reads the tagged words idx(k), k < n (n <= N, per lane), until each
+// carries the step's tag, handing every value to put(k, v). All outstanding
+// loads are issued before any tag is checked. False on abort or timeout.
+template <int N, typename IDX, typename PUT>
+__device__ __forceinline__ bool tgather(Ctx &c, __amdgpu_buffer_rsrc_t r, int n, IDX idx, PUT put, int pc) {
+    static_assert(N >= 1 && N <= 16, "gather width");
+    const uint32_t tag = c.tag;
+    uint32_t pend = n <= 0 ? 0u : (n >= N ? ((1u << N) - 1u) : ((1u << n) - 1u));
+    int64_t spins = 0;
+    for (;;) {
+        v2u wv[N];
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+            if (pend & (1u << k)) wv[k] = tget(r, idx(k));
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+            if ((pend & (1u << k)) && wv[k].y == tag) {
+                put(k, __uint_as_float(wv[k].x));
+                pend &= ~(1u << k);
+            }
+        if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) return true;
+        if (lds_ld(c.misc + M_ABORT)) return false;
+        // a producer on another unit may have failed: then this data never comes
+        if ((++spins & 63) == 0 &&
+            __builtin_amdgcn_readfirstlane(__hip_atomic_load(c.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+            lds_st(c.misc + M_ABORT, 1u);
+            return false;
+        }
+        if (spins > c.watchdog) {
+            raise_err(c, ERR_TIMEOUT, pc);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// Gathers words [lo, hi) of a tagged vector into fn(i, v), the lane taking
+// i = lo + lane + 64 k, in rounds of up to 16 words per lane.
+template <typename FN>
+__device__ __forceinline__ bool tgather_range(Ctx &c, __amdgpu_buffer_rsrc_t r, int lo, int hi, FN fn, int pc) {
+    for (int base = lo; base < hi; base += 64 * 16) {
+        const int first = base + c.lane;
+        const int n = first < hi ? min(16, (hi - first + 63) / 64) : 0;
+        if (!tgather<16>(
+                c, r, n, [&](int k) { return (uint32_t)(first + 64 * k); },
+                [&](int k, float v) { fn(first + 64 * k, v); }, pc))
+            return false;
+    }
+    return true;
+}
+
+// ------------------------------------------------------------ slice stream
+
+// A wave's position in its stream of slices: instruction pc, unit u (a row,
+// a row pair, or a K/V block; the wave's units are w, w + NC, ...), slice s
+// of the unit. An instruction in which the wave has no unit still yields one
+// empty slice, so that the wave passes through its staging and merges.
+struct Cur {
+    int pc, op, layer, r0, nu, sp, spm, u, s, K;
+    int b, g, blo, p;
+    uint32_t rowb;
+};
+
+__device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k, int pc) {
+    k.pc = pc;
+    const int32_t *ins = instr(P, c.cu, pc);
+    k.op = sload(ins, W_OP);
+    k.u = c.w;
+    k.s = 0;
+    k.nu = 0;
+    k.sp = 1;
+    k.spm = 1;
+    k.K = 0;
+    k.rowb = 0;
+    if (k.op == OP_END) return;
+    k.layer = sload(ins, W_LAYER);
+    k.r0 = sload(ins, W_R0);
+    if (k.op == OP_ATTN) {
+        k.b = sload(ins, W_B);
+        k.g = sload(ins, W_G);
+        int p = sload(P.kv_lens, k.b);
+        if (p < 0 || p >= P.T * P.max_pages) p = 0;  // the staging raises the error
+        k.p = p;
+        int lo, hi;
+        chunk_blocks(p, sload(ins, W_C), sload(ins, W_NCH), &lo, &hi);
+        k.blo = lo;
+        k.nu = hi - lo;
+    } else if (k.op > OP_END && k.op < OP_COUNT) {
+        k.K = op_k(P, k.op);
+        k.rowb = (uint32_t)k.K * 2;
+        k.spm = (int)((k.rowb + SLICE_BYTES - 1) / SLICE_BYTES);
+        k.sp = (k.op == OP_UPGATE ? 2 : 1) * k.spm;
+        k.nu = sload(ins, W_R1) - k.r0;
+    }
+    // an unknown opcode yields one empty slice; its staging raises the error
+}
+
+__device__ __forceinline__ void cur_next(const KParams &P, const Ctx &c, Cur &k) {
+    if (k.op == OP_END) return;
+    if (k.u < k.nu) {
+        if (++k.s == k.sp) {
+            k.s = 0;
+            k.u += NC;
+        }
+        if (k.u < k.nu) return;
+    }
+    cur_load(P, c, k, k.pc + 1);
+}
+
+// Issues the loads of the slice at the cursor into r: always four 16-byte
+// buffer loads per lane (two per 2 KiB half), so that the count of loads in
+// flight per slice is fixed; bytes outside the slice read as zero.
+__device__ __forceinline__ void issue(const KParams &P, const Cur &k, v4u (&r)[4], int lane) {
+    const char *a = (const char *)P.wtab, *b = (const char *)P.wtab;
+    uint32_t na = 0, nb = 0;
+    if (k.op != OP_END && k.u < k.nu) {
+        if (k.op == OP_ATTN) {
+            const int blk = k.blo + k.u;
+            int page = sload(P.page_table, (int64_t)k.b * P.max_pages + blk);
+            if (page < 0 || page >= P.n_pages) page = 0;  // the staging raises the error
+            const size_t off = (((size_t)k.layer * P.n_pages + page) * P.nkv + k.g) * 2048;
+            a = (const char *)P.k_pool + off;
+            b = (const char *)P.v_pool + off;
+            na = nb = 2048;
+        } else {
+            const int m = k.s >= k.spm ? 1 : 0, part = k.s - m * k.spm;
+            const uint32_t col0 = (uint32_t)part * SLICE_BYTES;
+            const int which = k.op == OP_QKV ? 1 : k.op == OP_OPROJ ? 2 : k.op == OP_UPGATE ? 4 + m : 6;
+            const char *base = k.op == OP_LMHEAD ? (const char *)P.embed : wptr(P, k.layer, which);
+            a = base + ((uint32_t)(k.r0 + k.u) * k.rowb + col0);
+            const uint32_t nbytes = min((uint32_t)SLICE_BYTES, k.rowb - col0);
+            na = min(nbytes, 2048u);
+            nb = nbytes - na;
+            b = a + 2048;
+        }
+    }
+    const __amdgpu_buffer_rsrc_t ra = plain_rsrc(a, na), rb = plain_rsrc(b, nb);
+    const uint32_t o = (uint32_t)lane * 16;
+    r[0] = __builtin_amdgcn_raw_buffer_load_b128(ra, o, 0, 0);
+    r[1] = __builtin_amdgcn_raw_buffer_load_b128(ra, o + 1024, 0, 0);
+    r[2] = __builtin_amdgcn_raw_buffer_load_b128(rb, o, 0, 0);
+    r[3] = __builtin_amdgcn_raw_buffer_load_b128(rb, o + 1024, 0, 0);
+}
+
+// ------------------------------------------------------------ instruction
+
+struct Ins {
+    int pc, op, layer, r0, r1, flags, b, g, c, nch, p, merge, slot, nslot;
+    int64_t *tr;
+};
+
+template <int NB>
+struct Acc {
+    float a0[NB], a1[NB];  // dot products of the current unit (gate/up for UPGATE)
+    float bv[NB];          // LM head: best value and index so far
+    int bi[NB];
+    bool nan;
+};
+
+__device__ __forceinline__ int token_of(const KParams &P, Ctx &c, int b, int pc) {
+    int t = sload(P.tokens_in, b);
+    if (t < 0 || t >= P.V) {
+        if (c.lane == 0) raise_err(c, ERR_RANGE, pc);
+        t = 0;
+    }
+    return t;
+}
+
+// act[b] <- rmsnorm(x_v[b]) * wn in the matvec layout (x_0: the layer-0
+// input). Waves 0..3 each gather the elements i = 64 w + lane + 256 k and
+// sum their squares in that order, which is the reduction of the
+// one-kernel-per-op baseline's norm, so both paths agree bit for bit.
+__device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &in, const uint16_t *wn, int xv) {
+    const int H = P.H, lane = c.lane, w = c.w;
+    MK_LDS float *norm = (MK_LDS float *)(c.misc + M_NORM);
+    if (w < 4) {
+        for (int b = 0; b < P.B; ++b) {
+            MK_LDS float *a = c.act + b * P.act_stride;
+            if (xv == 0) {
+                const int tok = P.has_embed ? token_of(P, c, b, in.pc) : 0;
+                for (int i = w * 64 + lane; i < H; i += 256) a[act_index(i)] = x_input(P, b, i, true, tok);
+            } else {
+                const __amdgpu_buffer_rsrc_t r = tres(P.tx + ((size_t)(xv - 1) * P.B + b) * H, (uint32_t)H);
+                const int first = w * 64 + lane;
+                const int n = first < H ? (H - first + 255) / 256 : 0;  // this lane's words
+                const int nmax = (H - w * 64 + 255) / 256;               // lane 0's: the most
+                // the loop bound is uniform: an early return from a loop whose
+                // trip count differs per lane would make the caller's control
+                // flow divergent
+                for (int k0 = 0; k0 < nmax; k0 += 16)
+                    if (!tgather<16>(
+                            c, r, n - k0, [&](int k) { return (uint32_t)(first + 256 * (k0 + k)); },
+                            [&](int k, float v) { a[act_index(first + 256 * (k0 + k))] = v; }, in.pc))
+                        return false;
+            }
+            float ss = 0.0f;
+            for (int i = w * 64 + lane; i < H; i += 256) {
+                const float v = a[act_index(i)];
+                ss = fmaf(v, v, ss);
+            }
+            ss = wave_sum(ss);
+            if (lane == 0) norm[w * MAX_B + b] = ss;
+        }
+    }
+    if (!cbar(c, in.pc)) return false;
+    if (w < 4) {
+        for (int b = 0; b < P.B; ++b) {
+            float tot = 0.0f;
+            for (int v = 0; v < 4; ++v) tot += norm[v * MAX_B + b];
+            const float inv = 1.0f / sqrtf(tot / (float)H + P.eps);
+            MK_LDS float *a = c.act + b * P.act_stride;
+            for (int i = w * 64 + lane; i < H; i += 256) a[act_index(i)] = a[act_index(i)] * inv * bf2f(wn[i]);
+        }
+    }
+    return cbar(c, in.pc);
+}
+
+// xrow[b][j] <- x_v[b][r0 + j] for the instruction's rows (x_0: the input)
+__device__ __forceinline__ bool stage_rows(const KParams &P, Ctx &c, const Ins &in, int xv) {
+    const int nr = in.r1 - in.r0;
+    for (int b = 0; b < P.B; ++b) {
+        MK_LDS float *xr = c.xrow + b * P.xrow_stride;
+        if (xv == 0) {
+            const int tok = P.has_embed ? token_of(P, c, b, in.pc) : 0;
+            for (int j = c.w * 64 + c.lane; j < nr; j += NC * 64) xr[j] = x_input(P, b, in.r0 + j, true, tok);
+        } else {
+            const __amdgpu_buffer_rsrc_t r = tres(P.tx + ((size_t)(xv - 1) * P.B + b) * P.H, (uint32_t)P.H);
+            for (int j0 = c.w * 64; j0 < nr; j0 += NC * 64) {
+                const int j = j0 + c.lane;
+                if (!tgather<1>(
+                        c, r, j < nr ? 1 : 0, [&](int) { return (uint32_t)(in.r0 + j); },
+                        [&](int, float v) { xr[j] = v; }, in.pc))
+                    return false;
+            }
+        }
+    }
+    return true;
+}
+
+// act[b] <- src[b][0, K) in the matvec layout; src: tagged [B][K]
+__device__ __forceinline__ bool stage_copy(const KParams &P, Ctx &c, const Ins &in, const uint64_t *src, int K) {
+    const int per = K / NC;
+    for (int b = 0; b < P.B; ++b) {
+        MK_LDS float *a = c.act + b * P.act_stride;
+        const __amdgpu_buffer_rsrc_t r = tres(src + (size_t)b * K, (uint32_t)K);
+        if (!tgather_range(
+                c, r, c.w * per, (c.w + 1) * per, [&](int i, float v) { a[act_index(i)] = v; }, in.pc))
+            return false;
+    }
+    return true;
+}
+
+// Attention staging: the group's queries rotated (fp32, act[0, G*64)), and
+// the new K/V entry rotated and rounded to bf16 (act + G*64 as uint16 [2][64]);
+// the last chunk also appends that entry to the cache.
+template <int G>
+__device__ __forceinline__ bool stage_attn(const KParams &P, Ctx &c, const Ins &in) {
+    const int lane = c.lane;
+    const int QD = P.nq * P.d, QKVN = QD + 2 * P.nkv * P.d;
+    const int b = in.b, g = in.g, p = in.p;
+    const bool last = in.c == in.nch - 1;
+    MK_LDS uint16_t *kvn = (MK_LDS uint16_t *)(c.act + G * 64);
+    const __amdgpu_buffer_rsrc_t r = tres(P.tqkv + ((size_t)in.layer * P.B + b) * QKVN, (uint32_t)QKVN);
+    const float2 cs = P.rope[(int64_t)p * 32 + (lane & 31)];
+    for (int t = c.w; t < G + 2; t += NC) {
+        const int row0 = t < G ? (g * G + t) * 64 : (t == G ? QD + g * 64 : QD + P.nkv * 64 + g * 64);
+        float xi = 0.0f;
+        if (!tgather<1>(
+                c, r, 1, [&](int) { return (uint32_t)(row0 + lane); }, [&](int, float v) { xi = v; }, in.pc))
+            return false;
+        float out = xi;
+        if (t <= G) {  // queries and the key are rotated; the value is not
+            const float xp = __shfl_xor(xi, 32, 64);
+            out = rope_rotate(xi, xp, cs, lane < 32);
+        }
+        if (t < G) {
+            c.act[t * 64 + lane] = out;
+        } else {
+            const uint16_t hb = f2bf(out);
+            kvn[(t - G) * 64 + lane] = hb;
+            if (last) {
+                int page = sload(P.page_table, (int64_t)b * P.max_pages + (p >> 4));
+                if (page < 0 || page >= P.n_pages) {
+                    if (lane == 0) raise_err(c, ERR_RANGE, in.pc);
+                    page = 0;
+                }
+                uint16_t *pool = t == G ? P.k_pool : P.v_pool;
+                pool[(((size_t)in.layer * P.n_pages + page) * P.nkv + g) * 1024 + (p & 15) * 64 + lane] = hb;
+            }
+        }
+    }
+    return cbar(c, in.pc);
+}
+
+template <int NB, int G>
+__device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, Ins &in, Acc<NB> &acc,
+                                      AttnLaneT<G> &at) {
+    const int pc = k.pc;
+    const int32_t *ins = instr(P, c.cu, pc);
+    in.pc = pc;
+    in.op = sload(ins, W_OP);
+    in.layer = sload(ins, W_LAYER);
+    in.r0 = sload(ins, W_R0);
+    in.r1 = sload(ins, W_R1);
+    in.flags = sload(ins, W_FLAGS);
+    in.b = sload(ins, W_B);
+    in.g = sload(ins, W_G);
+    in.c = sload(ins, W_C);
+    in.nch = sload(ins, W_NCH);
+    in.merge = sload(ins, W_MERGE);
+    in.slot = sload(ins, W_SLOT);
+    in.nslot = sload(ins, W_NSLOT);
+    in.tr = P.trace ? P.trace + ((int64_t)c.cu * P.Q + pc) * 3 : nullptr;
+    const bool tracer = in.tr && c.w == 0 && c.lane == 0;
+    if (tracer) in.tr[0] = wall_clock64();
+    // the previous instruction is finished, merges included: its LDS areas are free
+    if (!lds_wait_ge(c, c.misc + M_DONE, (uint32_t)pc, pc)) return false;
+    bool ok = true;
+    switch (in.op) {
+        case OP_QKV:
+            ok = stage_norm(P, c, in, (const uint16_t *)wptr(P, in.layer, 0),
+                            (in.flags & F_X_FROM_INPUT) ? 0 : 2 * in.layer);
+            break;
+        case OP_UPGATE: ok = stage_norm(P, c, in, (const uint16_t *)wptr(P, in.layer, 3), 2 * in.layer + 1); break;
+        case OP_LMHEAD: ok = stage_norm(P, c, in, P.final_norm, 2 * P.L); break;
+        case OP_OPROJ:
+            ok = stage_rows(P, c, in, (in.flags & F_X_FROM_INPUT) ? 0 : 2 * in.layer) &&
+                 stage_copy(P, c, in, P.to + (size_t)in.layer * P.B * P.nq * P.d, P.nq * P.d) && cbar(c, pc);
+            break;
+        case OP_DOWN:
+            ok = stage_rows(P, c, in, 2 * in.layer + 1) &&
+                 stage_copy(P, c, in, P.tact + (size_t)in.layer * P.B * P.F, P.F) && cbar(c, pc);
+            break;
+        case OP_ATTN: {
+            const int p = sload(P.kv_lens, in.b);
+            if (p < 0 || p >= P.T * P.max_pages) {
+                if (c.lane == 0) raise_err(c, ERR_RANGE, pc);
+                return false;
+            }
+            in.p = p;
+            ok = stage_attn<G>(P, c, in);
+            break;
+        }
+        default:
+            if (c.lane == 0) raise_err(c, ERR_OPCODE, pc);
+            return false;
+    }
+    if (!ok) return false;
+    if (tracer) in.tr[1] = wall_clock64();
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        acc.a0[b] = 0.0f;
+        acc.a1[b] = 0.0f;
+        acc.bv[b] = -INFINITY;
+        acc.bi[b] = 0x7fffffff;
+    }
+    acc.nan = false;
+    attn_lane_init(at);
+    return true;
+}
+
+// Output of row `row` for request b (lane b), v0 the row's dot product, v1
+// the up projection's for UPGATE.
+__device__ __forceinline__ void emit_row(const KParams &P, Ctx &c, const Ins &in, int row, int b, float v0, float v1) {
+    const uint32_t tag = P.tag;
+    switch (in.op) {
+        case OP_QKV: {
+            const int QKVN = (P.nq + 2 * P.nkv) * P.d;
+            tput(tres(P.tqkv + ((size_t)in.layer * P.B + b) * QKVN, (uint32_t)QKVN), (uint32_t)row, v0, tag);
+            break;
+        }
+        case OP_OPROJ: {
+            const float nx = c.xrow[b * P.xrow_stride + (row - in.r0)] + v0;
+            tput(tres(P.tx + ((size_t)(2 * in.layer) * P.B + b) * P.H, (uint32_t)P.H), (uint32_t)row, nx, tag);
+            break;
+        }
+        case OP_UPGATE:
+            tput(tres(P.tact + ((size_t)in.layer * P.B + b) * P.F, (uint32_t)P.F), (uint32_t)row, silu(v0) * v1, tag);
+            break;
+        case OP_DOWN: {
+            const float nx = c.xrow[b * P.xrow_stride + (row - in.r0)] + v0;
+            tput(tres(P.tx + ((size_t)(2 * in.layer + 1) * P.B + b) * P.H, (uint32_t)P.H), (uint32_t)row, nx, tag);
+            if ((in.flags & F_WRITE_HIDDEN) && P.hidden_out) P.hidden_out[(int64_t)b * P.H + row] = nx;
+            break;
+        }
+        default:
+            if (P.logits_out) P.logits_out[(int64_t)b * P.V + row] = v0;
+            break;
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &k, const Ins &in, const v4u (&r)[4],
+                                           Acc<NB> &acc) {
+    const int lane = c.lane;
+    const int m = k.s >= k.spm ? 1 : 0, part = k.s - m * k.spm;
+    const int nchunk = k.K >> 3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int ci = part * 256 + j * 64 + lane;
+        if (ci < nchunk) {
+            const int base = ((ci >> 6) << 9) + ((ci & 63) << 2);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const MK_LDS float *a = c.act + b * P.act_stride + base;
+                const float d = dot8(r[j], *(const MK_LDS v4f *)a, *(const MK_LDS v4f *)(a + 256));
+                if (m == 0) acc.a0[b] += d;
+                else acc.a1[b] += d;
+            }
+        }
+    }
+    if (k.s != k.sp - 1) return;
+    // unit complete: reduce, write, reset
+    const int row = k.r0 + k.u;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const float v0 = wave_sum(acc.a0[b]);
+        const float v1 = in.op == OP_UPGATE ? wave_sum(acc.a1[b]) : 0.0f;
+        acc.a0[b] = 0.0f;
+        acc.a1[b] = 0.0f;
+        if (b < P.B) {
+            if (lane == b) emit_row(P, c, in, row, b, v0, v1);
+            if (in.op == OP_LMHEAD) {
+                if (v0 != v0) acc.nan = true;
+                if (v0 > acc.bv[b]) {  // a wave's rows rise, so ties keep the lowest index
+                    acc.bv[b] = v0;
+                    acc.bi[b] = row;
+                }
+            }
+        }
+    }
+}
+
+template <int G>
+__device__ __forceinline__ void consume_attn(const KParams &P, Ctx &c, const Cur &k, const Ins &in, const v4u (&r)[4],
+                                             AttnLaneT<G> &at) {
+    const int lane = c.lane;
+    const int blk = k.blo + k.u;
+    v4u k0 = r[0], k1 = r[1], v0 = r[2], v1 = r[3];
+    const int t0 = lane >> 3;
+    if (blk == (in.p >> 4)) {  // the new entry replaces whatever the cache slot held
+        const int j = in.p & 15, dd = (lane & 7) * 8;
+        const MK_LDS uint16_t *kvn = (const MK_LDS uint16_t *)(c.act + G * 64);
+        const v4u nk = *(const MK_LDS v4u *)(kvn + dd), nv = *(const MK_LDS v4u *)(kvn + 64 + dd);
+        if (t0 == j) {
+            k0 = nk;
+            v0 = nv;
+        }
+        if (t0 + 8 == j) {
+            k1 = nk;
+            v1 = nv;
+        }
+    }
+    const int pos0 = blk * 16 + t0;
+    attn_lane_block(at, c.act, lane, k0, k1, v0, v1, pos0 <= in.p, pos0 + 8 <= in.p);
+}
+
+// Elects the last of `need` finishers of a merge event (one per step).
+__device__ __forceinline__ bool elect_last(const KParams &P, Ctx &c, int merge) {
+    const int ctr = sload(P.events, (int64_t)merge * EV_WORDS + EV_CTR);
+    const int32_t need = (int32_t)((int64_t)P.epoch * sload(P.events, (int64_t)merge * EV_WORDS + EV_NEED));
+    int32_t old = 0;
+    if (c.lane == 0)
+        old = __hip_atomic_fetch_add(P.counters + (int64_t)ctr * CTR_STRIDE, 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(__shfl(old, 0, 64));
+    return old + 1 == need;
+}
+
+// Run by the last wave to finish an instruction's slices.
+template <int G>
+__device__ __forceinline__ bool finish(const KParams &P, Ctx &c, const Ins &in) {
+    const int lane = c.lane;
+    const uint32_t tag = P.tag;
+    if (in.op == OP_ATTN) {
+        const int QD = P.nq * P.d;
+        const int b = in.b, g = in.g, nch = in.nch;
+        const __amdgpu_buffer_rsrc_t ro = tres(P.to + ((size_t)in.layer * P.B + b) * QD, (uint32_t)QD);
+        const size_t pbase = (((size_t)in.layer * P.B + b) * P.nkv + g) * nch * G * ATTN_PART;
+        const __amdgpu_buffer_rsrc_t rp = tres(P.tpart + pbase, (uint32_t)(nch * G * ATTN_PART));
+        for (int h = 0; h < G; ++h) {
+            float o, m, l;
+            merge_parts(nullptr, c.part + h * ATTN_WAVE_PART, NC, G * ATTN_WAVE_PART, lane, &o, &m, &l);
+            if (nch == 1) {
+                tput(ro, (uint32_t)((g * G + h) * 64 + lane), o / l, tag);
+            } else {
+                const uint32_t e = (uint32_t)((in.c * G + h) * ATTN_PART);
+                tput(rp, e + lane, o, tag);
+                if (lane == 0) {
+                    tput(rp, e + 64, m, tag);
+                    tput(rp, e + 65, l, tag);
+                }
+            }
+        }
+        if (nch == 1 || !elect_last(P, c, in.merge)) return true;
+        // the last chunk to finish merges all chunks, in chunk order
+        if (!tgather_range(
+                c, rp, 0, nch * G * ATTN_PART, [&](int i, float v) { c.part[i] = v; }, in.pc))
+            return false;
+        for (int h = 0; h < G; ++h) {
+            float o, m, l;
+            merge_parts(nullptr, c.part + h * ATTN_PART, nch, G * ATTN_PART, lane, &o, &m, &l);
+            tput(ro, (uint32_t)((g * G + h) * 64 + lane), o / l, tag);
+        }
+        return true;
+    }
+    if (in.op == OP_LMHEAD) {
+        const MK_LDS float *am = (const MK_LDS float *)(c.misc + M_AMAX);
+        const __amdgpu_buffer_rsrc_t rl = tres(P.tlm, (uint32_t)(in.nslot * P.B * 2));
+        if (lane < P.B) {
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
+            for (int w = 0; w < NC; ++w) {
+                const float v = am[(w * MAX_B + lane) * 2];
+                const int i = ((const MK_LDS int32_t *)am)[(w * MAX_B + lane) * 2 + 1];
+                if (amax_better(v, i, bv, bi)) {
+                    bv = v;
+                    bi = i;
+                }
+            }
+            tput(rl, (uint32_t)((in.slot * P.B + lane) * 2), bv, tag);
+            tput(rl, (uint32_t)((in.slot * P.B + lane) * 2 + 1), __int_as_float(bi), tag);
+        }
+        if (!elect_last(P, c, in.merge)) return true;
+        // the argmax is a maximum under a total order: any combination order gives the same token
+        if (!tgather_range(
+                c, rl, 0, in.nslot * P.B * 2, [&](int i, float v) { c.act[i] = v; }, in.pc))
+            return false;
+        if (lane < P.B) {
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
+            for (int t = 0; t < in.nslot; ++t) {
+                const float v = c.act[(t * P.B + lane) * 2];
+                const int i = __float_as_int(c.act[(t * P.B + lane) * 2 + 1]);
+                if (amax_better(v, i, bv, bi)) {
+                    bv = v;
+                    bi = i;
+                }
+            }
+            P.tokens_out[lane] = bi;
+            if (P.kv_lens_out) P.kv_lens_out[lane] = sload(P.kv_lens, lane) + 1;
+        }
+        return true;
+    }
+    if ((in.flags & F_STEP_FINAL) && in.merge >= 0) {  // last layer's down projection without an LM head
+        if (elect_last(P, c, in.merge) && P.kv_lens_out && lane < P.B)
+            P.kv_lens_out[lane] = sload(P.kv_lens, lane) + 1;
+    }
+    return true;
+}
+
+template <int NB, int G>
+__device__ __forceinline__ bool leave(const KParams &P, Ctx &c, const Ins &in, Acc<NB> &acc, AttnLaneT<G> &at) {
+    const int lane = c.lane;
+    if (in.op == OP_LMHEAD) {
+        MK_LDS float *am = (MK_LDS float *)(c.misc + M_AMAX);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            if (lane == b && b < P.B) {
+                am[(c.w * MAX_B + b) * 2] = acc.bv[b];
+                ((MK_LDS int32_t *)am)[(c.w * MAX_B + b) * 2 + 1] = acc.bi[b];
+            }
+        if (acc.nan && lane == 0) raise_err(c, ERR_NAN, in.pc);
+    } else if (in.op == OP_ATTN) {
+        attn_lane_store(at, c.part + c.w * G * ATTN_WAVE_PART, lane);
+    }
+    uint32_t old = 0;
+    if (lane == 0) old = lds_add(c.misc + M_FIN, 1u);
+    old = __builtin_amdgcn_readfirstlane(__shfl(old, 0, 64));
+    if (old != (uint32_t)NC * (in.pc + 1) - 1) return true;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (!finish<G>(P, c, in)) return false;
+    if (in.tr && lane == 0) in.tr[2] = wall_clock64();
+    if (lane == 0) lds_add(c.misc + M_DONE, 1u);
+    return true;
+}
+
+// Runs one slice of the stream from register slot `buf`: consume it, refill
+// the slot with the slice D positions ahead, advance. True when the slice was the
+// wave's last of its instruction (the caller then handles the boundary).
+template <int NB, int G>
+__device__ __forceinline__ bool slot_step(const KParams &P, Ctx &c, Cur &ic, Cur &cc, const Ins &in, v4u (&buf)[4],
+                                          Acc<NB> &acc, AttnLaneT<G> &at) {
+    const bool empty = cc.u >= cc.nu;
+    if (!empty) {
+        if (cc.op == OP_ATTN) consume_attn<G>(P, c, cc, in, buf, at);
+        else consume_mv<NB>(P, c, cc, in, buf, acc);
+    }
+    const bool last = empty || (cc.s == cc.sp - 1 && cc.u + NC >= cc.nu);
+    issue(P, ic, buf, c.lane);
+    cur_next(P, c, ic);
+    cur_next(P, c, cc);
+    return last;
+}
+
+__device__ __forceinline__ void rot4(v4u (&a)[4], v4u (&b)[4], v4u (&c)[4], v4u (&d)[4], int by) {
+    // by 1: (a, b, c, d) <- (b, c, d, a); by 2 and 3 likewise
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const v4u t0 = a[j], t1 = b[j], t2 = c[j], t3 = d[j];
+        if (by == 1) {
+            a[j] = t1;
+            b[j] = t2;
+            c[j] = t3;
+            d[j] = t0;
+        } else if (by == 2) {
+            a[j] = t2;
+            b[j] = t3;
+            c[j] = t0;
+            d[j] = t1;
+        } else if (by == 3) {
+            a[j] = t3;
+            b[j] = t0;
+            c[j] = t1;
+            d[j] = t2;
+        }
+    }
+}
+
+// The wave's main loop. Between instruction boundaries the four slots are
+// consumed in order 0, 1, 2, 3, 0, ..., so that the compiler counts the loads
+// in flight exactly (the slot being consumed always has three slices issued
+// after it). At a boundary the wave leaves the previous instruction and
+// enters the next one -- that code exists once -- and, since entering waits
+// for the instruction's inputs anyway, it then renames the slots so that the
+// next slice to consume is in slot 0 again.
+template <int NB, int G>
+__device__ __forceinline__ void run(const KParams &P, Ctx &c) {
+    static_assert(D == 4, "the slot sequence below is written out for four slots");
+    v4u b0[4], b1[4], b2[4], b3[4];
+    Cur ic, cc;
+    cur_load(P, c, ic, 0);
+    cur_load(P, c, cc, 0);
+    issue(P, ic, b0, c.lane);
+    cur_next(P, c, ic);
+    issue(P, ic, b1, c.lane);
+    cur_next(P, c, ic);
+    issue(P, ic, b2, c.lane);
+    cur_next(P, c, ic);
+    issue(P, ic, b3, c.lane);
+    cur_next(P, c, ic);
+    Ins in{};
+    Acc<NB> acc;
+    AttnLaneT<G> at;
+    bool first = true;
+    int rot = 0;
+    for (;;) {
+        if (!first && !uni(leave<NB, G>(P, c, in, acc, at))) return;
+        first = false;
+        if (cc.op == OP_END) return;
+        if (!uni(enter<NB, G>(P, c, cc, in, acc, at))) return;
+        if (rot) rot4(b0, b1, b2, b3, rot);
+        for (;;) {
+            if (uni(slot_step<NB, G>(P, c, ic, cc, in, b0, acc, at))) {
+                rot = 1;
+                break;
+            }
+            if (uni(slot_step<NB, G>(P, c, ic, cc, in, b1, acc, at))) {
+                rot = 2;
+                break;
+            }
+            if (uni(slot_step<NB, G>(P, c, ic, cc, in, b2, acc, at))) {
+                rot = 3;
+                break;
+            }
+            if (uni(slot_step<NB, G>(P, c, ic, cc, in, b3, acc, at))) {
+                rot = 0;
+                break;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+template <int NB, int G>
+__global__ __launch_bounds__(BLOCK_THREADS, 1) void mk_megakernel(KParams P) {
+    extern __shared__ char lds_raw[];
+    MK_LDS char *lds = (MK_LDS char *)lds_raw;
+    Ctx c;
+    c.misc = (MK_LDS uint32_t *)lds;
+    c.xrow = (MK_LDS float *)(lds + P.xrow_off);
+    c.part = (MK_LDS float *)(lds + P.part_off);
+    c.act = (MK_LDS float *)(lds + P.act_off);
+    c.cu = blockIdx.x;
+    c.lane = threadIdx.x & 63;
+    c.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    c.nbar = 0;
+    c.tag = P.tag;
+    c.watchdog = P.watchdog;
+    c.err = P.err;
+    c.host_err = P.host_err;
+    for (int i = threadIdx.x; i < MISC_BYTES / 4; i += BLOCK_THREADS) c.misc[i] = 0;
+    __syncthreads();
+    run<NB, G>(P, c);
+}
+
+}  // namespace mk

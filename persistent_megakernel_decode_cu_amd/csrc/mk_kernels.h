@@ -9,13 +9,14 @@ namespace mk {
 struct KParams {
     // schedule
     const int32_t *queue;     // [n_cus, Q, INSTR_WORDS]
-    const int32_t *events;    // [n_events, EV_WORDS]
+    const int32_t *events;    // [n_events, EV_WORDS] merge events
     int32_t *counters;        // [n_counters * CTR_STRIDE]
-    int32_t Q, epoch, n_cus, ring_granules;
-    int32_t act_off, ring_off;   // LDS byte offsets
-    int32_t act_stride;          // floats per request in the activation area
+    int32_t Q, epoch, n_cus;
+    uint32_t tag;             // this step's tag on every exchanged activation (never 0)
+    int32_t xrow_off, part_off, act_off;  // LDS byte offsets
+    int32_t act_stride;       // floats per request in the activation area
+    int32_t xrow_stride;      // floats per request in the residual-row area
     int64_t watchdog;
-    int32_t dma_depth;           // one of 0, 4, 8, 16, 24, 32, 40, 48, 56
     // model
     int32_t L, H, nq, nkv, d, F, V, has_embed, B, T, max_pages;
     float eps;
@@ -32,14 +33,22 @@ struct KParams {
     const int32_t *page_table;
     int32_t *tokens_out, *kv_lens_out;
     float *logits_out, *hidden_out;
-    // scratch
+    // resident interpreter: tagged activations, 64-bit words (low: fp32 bits,
+    // high: tag), each written once per step
+    uint64_t *tx;      // [2L][B][H]: x_1 .. x_{2L} (x_v at index v - 1)
+    uint64_t *tqkv;    // [L][B][(nq + 2 nkv) d]
+    uint64_t *to;      // [L][B][nq d]
+    uint64_t *tact;    // [L][B][F]
+    uint64_t *tpart;   // [L][B][nkv][chunks][G][ATTN_PART] attention chunk partials
+    uint64_t *tlm;     // [lm slots][B][2] argmax partials (value, index)
+    int32_t attn_chunks;
+    // one-kernel-per-op baseline scratch (fp32, overwritten in place)
     float *x;          // [B, H] residual stream
     float *qkv;        // [B, (nq + 2 nkv) d]
     float *o;          // [B, nq d] attention output
     float *act;        // [B, F] gated MLP activation
     float *attn_part;  // [B, nkv, chunks, G, ATTN_PART_STRIDE]
     float *lm_part;    // [lm slots, B, 2]
-    int32_t attn_chunks;
     int32_t *err;      // device error word
     int32_t *host_err; // mapped host mirror of the error word
     int64_t *trace;    // [n_cus, Q, 3] or null
@@ -47,14 +56,19 @@ struct KParams {
 
 constexpr int ATTN_PART_STRIDE = 68;
 
+// The resident interpreter exists for B in 1..8 and G = nq / nkv in {1, 2, 4, 8}.
+bool megakernel_supports(int B, int G);
 hipError_t launch_megakernel(const KParams &p, int lds_bytes, hipStream_t s);
-hipError_t setup_megakernel(int lds_bytes);
-hipError_t megakernel_occupancy(int lds_bytes, int *blocks_per_cu);
+hipError_t setup_megakernel(int B, int G, int lds_bytes);
+hipError_t megakernel_occupancy(int B, int G, int lds_bytes, int *blocks_per_cu);
 hipError_t launch_unfused(const KParams &p, float *u_scratch, float *qrot, hipStream_t s);
 hipError_t dma_probe(const void *src, void *dst, int n_kib, int off_kib);
 hipError_t ring_probe(const void *src, int n, int ring, int depth, int variant, int32_t *errs, int blocks);
 hipError_t stream_probe(const void *src, size_t bytes, int blocks, uint32_t *out);
-hipError_t litmus(int pairs, int n, int rounds, int32_t *data, int32_t *flags, int32_t *res);
+hipError_t litmus(int pairs, int n, int rounds, int mode, int32_t *data, int32_t *flags, int32_t *res);
+hipError_t hop_probe(int32_t *ctr, float *xbuf, int n_cus, int rounds, int variant, int32_t *res);
+hipError_t ll_probe(uint64_t *buf, int n_cus, int per, int copies, int rounds, int32_t *res);
+hipError_t regstream_probe(const void *src, size_t bytes, int blocks, int threads, int depth, uint32_t *out);
 hipError_t launch_rope_table(float2 *table, int capacity, int d, double theta, hipStream_t s);
 
 }  // namespace mk

@@ -1,1191 +1,47 @@
-// mk_megakernel.hip - the resident decode interpreter for gfx950.
-//
-// "Inference MegaKernel" (shaojiemike.top), section "hand-written whole-model
-// MegaKernel / principle, schedule and dataflow": one grid sized to the
-// compute-unit count stays resident for the step; each workgroup reads its
-// own instruction queue, waits on global counters for its inputs, leases
-// on-chip pages for the op body, runs it, fences, and bumps the counters of
-// its consumers. The page's design targets H100/B200; what follows is the
-// gfx950 shape of the same loop.
-//
-// One workgroup per CU, N_WAVES wave64s with fixed roles:
-//   wave 0, loader: walks the queue and streams each instruction's weights
-//     (or K/V blocks) HBM -> LDS with global_load_lds_dwordx4 into a ring of
-//     1 KiB granules. Weights do not depend on activations, so the loader
-//     runs ahead of the counter waits by up to the whole ring; that is the
-//     page's "page lease" with the lease taken as early as the ring allows.
-//     It counts its own in-flight DMAs with vmcnt and publishes how many
-//     granules have landed.
-//   wave 1, poller: walks the queue and, per instruction, spins on the
-//     global counters it waits for (device-scope relaxed loads), then takes
-//     an agent-scope acquire fence and marks the instruction ready in LDS.
-//   waves 2.., compute: per instruction, stage the activation vector into
-//     LDS (recomputing RMSNorm where the op consumes a norm), take their
-//     round-robin share of rows (or K/V blocks) as their granules land, run
-//     the op body, and release ring space as they go. The last compute wave
-//     to finish an instruction publishes it: agent-scope release fence, then
-//     an atomic add per completion event (the page's "fence, then
-//     atomic_add").
-// Waves of a workgroup never use s_barrier: they synchronise through LDS
-// counters only, so the loader and poller never stall the compute waves.
-// Every wait loop is bounded by a watchdog; on expiry the wave records an
-// error and the whole grid drains instead of hanging.
+// mk_megakernel.hip - host side of the resident decode interpreter: picks the
+// kernel variant (padded batch, q heads per kv head), sets its LDS size,
+// checks co-residency and launches it cooperatively. The device code is in
+// mk_interp.h, instantiated by mk_interp_b{1,2,4,8}.hip.
 #include "mk_device.h"
 
 namespace mk {
 
+const void *interp_kernel_b1(int G);
+const void *interp_kernel_b2(int G);
+const void *interp_kernel_b4(int G);
+const void *interp_kernel_b8(int G);
+
 namespace {
 
-// LDS misc area, in 32-bit words
-enum : int {
-    M_READY = 0,    // poller: instructions whose inputs are visible
-    M_LANDED = 1,   // loader: granules landed in the ring
-    M_ABORT = 2,
-    M_ARRIVE = 3,   // compute-wave barrier arrivals
-    M_FIN = 4,      // compute waves finished with an instruction (body)
-    M_DONE = 5,     // instructions fully finished (incl. publication)
-    M_WPOS = 16,    // [N_COMPUTE_WAVES] first granule each compute wave still needs
-    M_NORM = 32,    // [N_COMPUTE_WAVES][MAX_B] partial sums of squares
-    M_AMAX = 128,   // [N_COMPUTE_WAVES][MAX_B][2] partial argmax (value, index)
-};
-
-constexpr int NC = N_COMPUTE_WAVES;
-// DMA instructions the loader may keep in flight after each issue
-constexpr int DMA_DEPTH_DEFAULT = 40;
-
-__device__ __forceinline__ uint32_t lds_ld(MK_LDS uint32_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ __forceinline__ void lds_st(MK_LDS uint32_t *p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ __forceinline__ uint32_t lds_add(MK_LDS uint32_t *p, uint32_t v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-// HBM -> LDS, 16 bytes per active lane at lds_addr + 16 * lane. Issued from
-// inline assembly so that the compiler does not conservatively wait for the
-// transfer before unrelated LDS accesses; the loader tracks completion with
-// its own vmcnt waits. m0 carries the LDS base; nothing else in this kernel
-// uses m0.
-__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_addr) {
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "s_nop 1\n\t"
-        "global_load_lds_dwordx4 %1, off"
-        :
-        : "s"(lds_addr), "v"(gptr)
-        : "memory");
-}
-
-// s_waitcnt vmcnt(n), also a compiler barrier: no memory access moves across
-// it (the plain builtin is not one, and stores sinking below it, or a flag
-// store rising above it, would publish data that has not arrived)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ void raise_error(const KParams &P, MK_LDS uint32_t *misc, int code, int cu, int pc) {
-    const int32_t v = (code << 28) | ((cu & 0xfff) << 16) | (pc & 0xffff);
-    if (atomicCAS(P.err, 0, v) == 0 && P.host_err)
-        __hip_atomic_store(P.host_err, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    lds_st(misc + M_ABORT, 1u);
-}
-
-struct Ctx {
-    const KParams *P;
-    MK_LDS uint32_t *misc;
-    MK_LDS float *act;
-    MK_LDS char *ring;
-    uint32_t ring_bytes;
-    int cu, lane;
-};
-
-// Wait until *p >= v. Returns false (after raising an error on timeout) if
-// the workgroup aborts.
-__device__ __forceinline__ bool lds_wait_ge(const Ctx &c, MK_LDS uint32_t *p, uint32_t v, int pc) {
-    if (lds_ld(p) >= v) return true;
-    int64_t spins = 0;
-    while (lds_ld(p) < v) {
-        if (lds_ld(c.misc + M_ABORT)) return false;
-        if (++spins > c.P->watchdog) {
-            raise_error(*c.P, c.misc, ERR_TIMEOUT, c.cu, pc);
-            return false;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-    return true;
-}
-
-__device__ __forceinline__ const int32_t *instr(const KParams &P, int cu, int pc) {
-    return P.queue + ((int64_t)cu * P.Q + pc) * INSTR_WORDS;
-}
-
-__device__ __forceinline__ const uint16_t *wptr(const KParams &P, int layer, int k) {
-    return (const uint16_t *)(uintptr_t)sload(P.wtab, (int64_t)layer * 8 + k);
-}
-
-// bytes one instruction streams, identical in the loader and compute waves
-__device__ __forceinline__ uint32_t stream_bytes(const KParams &P, int op, int r0, int r1, int blo, int bhi) {
-    switch (op) {
-        case OP_ATTN: return (uint32_t)(bhi - blo) * 4096u;
-        case OP_UPGATE: return (uint32_t)(r1 - r0) * (uint32_t)P.H * 4u;
-        default: return (uint32_t)(r1 - r0) * (uint32_t)op_k(P, op) * 2u;
-    }
-}
-
-__device__ __forceinline__ void chunk_blocks(int p, int c, int nch, int *lo, int *hi) {
-    const int nb = (p + 1 + 15) >> 4;
-    *lo = (int)((int64_t)c * nb / nch);
-    *hi = (int)((int64_t)(c + 1) * nb / nch);
-}
-
-// ------------------------------------------------------------------ loader
-
-__device__ __forceinline__ void run_loader(const KParams &P, const Ctx &c) {
-    const int lane = c.lane;
-    const uint32_t RING = (uint32_t)P.ring_granules;
-    const uint32_t ring_lds = (uint32_t)(uintptr_t)c.ring;
-    uint32_t issued = 0, slot = 0, lim = RING, pub = 0;
-    MK_LDS uint32_t *landed = c.misc + M_LANDED;
-    const int depth = P.dma_depth;
-    __builtin_amdgcn_s_setprio(3);
-    for (int pc = 0;; ++pc) {
-        const int32_t *ins = instr(P, c.cu, pc);
-        const int op = sload(ins, W_OP);
-        if (op == OP_END) break;
-        const int layer = sload(ins, W_LAYER);
-        const int r0 = sload(ins, W_R0), r1 = sload(ins, W_R1);
-        int blo = 0, bhi = 0, b = 0, g = 0, p = 0;
-        if (op == OP_ATTN) {
-            b = sload(ins, W_B);
-            g = sload(ins, W_G);
-            p = sload(P.kv_lens, b);
-            if (p < 0 || p >= P.T * P.max_pages) p = 0;  // the compute side raises the error
-            chunk_blocks(p, sload(ins, W_C), sload(ins, W_NCH), &blo, &bhi);
-        }
-        const uint32_t nbytes = stream_bytes(P, op, r0, r1, blo, bhi);
-        const uint32_t ng = (nbytes + GRANULE - 1) / GRANULE;
-        // per-op source walk
-        const char *base = nullptr;
-        const char *base2 = nullptr;
-        uint32_t rb = 0;
-        if (op == OP_QKV) base = (const char *)wptr(P, layer, 1) + (size_t)r0 * P.H * 2;
-        else if (op == OP_OPROJ) base = (const char *)wptr(P, layer, 2) + (size_t)r0 * P.nq * P.d * 2;
-        else if (op == OP_DOWN) base = (const char *)wptr(P, layer, 6) + (size_t)r0 * P.F * 2;
-        else if (op == OP_LMHEAD) base = (const char *)P.embed + (size_t)r0 * P.H * 2;
-        else if (op == OP_UPGATE) {
-            rb = (uint32_t)P.H * 2;
-            base = (const char *)wptr(P, layer, 4) + (size_t)r0 * rb;
-            base2 = (const char *)wptr(P, layer, 5) + (size_t)r0 * rb;
-        }
-        const size_t layer_pool = (size_t)P.n_pages * P.nkv * 16 * 64;
-        for (uint32_t k = 0; k < ng; ++k) {
-            // ring space: granules below min(wpos) are free
-            if (issued >= lim) {
-                int64_t spins = 0;
-                for (;;) {
-                    wait_vmcnt<0>();
-                    pub = issued;
-                    lds_st(landed, issued);
-                    uint32_t mn = lds_ld(c.misc + M_WPOS);
-#pragma unroll
-                    for (int w = 1; w < NC; ++w) mn = min(mn, lds_ld(c.misc + M_WPOS + w));
-                    lim = __builtin_amdgcn_readfirstlane(mn + RING);
-                    if (issued < lim) break;
-                    if (lds_ld(c.misc + M_ABORT)) return;
-                    if (++spins > P.watchdog) {
-                        raise_error(P, c.misc, ERR_TIMEOUT, c.cu, pc);
-                        return;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-            }
-            const uint32_t off = k * GRANULE + lane * 16;
-            const char *src = nullptr;
-            bool valid = off < nbytes;
-            if (op == OP_UPGATE) {
-                if (rb >= GRANULE) {
-                    const uint32_t rbg = rb / GRANULE;
-                    const uint32_t pair = k / (2 * rbg), m = (k / rbg) & 1, col = k % rbg;
-                    src = (m ? base2 : base) + (size_t)pair * rb + col * GRANULE + lane * 16;
-                } else {  // 512-byte rows: one pair per granule
-                    src = (lane < 32 ? base : base2) + (size_t)k * rb + (lane & 31) * 16;
-                }
-            } else if (op == OP_ATTN) {
-                const int blk = blo + (int)(k >> 2);
-                int page = sload(P.page_table, (int64_t)b * P.max_pages + blk);
-                if (page < 0 || page >= P.n_pages) page = 0;
-                const uint16_t *pool = ((k >> 1) & 1) ? P.v_pool : P.k_pool;
-                src = (const char *)(pool + (size_t)layer * layer_pool + ((size_t)page * P.nkv + g) * 1024) +
-                      (k & 1) * GRANULE + lane * 16;
-            } else {
-                src = base + off;
-            }
-            if (valid) dma16(src, __builtin_amdgcn_readfirstlane(ring_lds + slot * GRANULE));
-            ++issued;
-            slot = (slot + 1 == RING) ? 0 : slot + 1;
-            // at most `depth` transfers outstanding: the older ones have landed
-            switch (depth) {
-                case 0: wait_vmcnt<0>(); break;
-                case 4: wait_vmcnt<4>(); break;
-                case 8: wait_vmcnt<8>(); break;
-                case 16: wait_vmcnt<16>(); break;
-                case 24: wait_vmcnt<24>(); break;
-                case 32: wait_vmcnt<32>(); break;
-                case 40: wait_vmcnt<40>(); break;
-                case 48: wait_vmcnt<48>(); break;
-                default: wait_vmcnt<56>(); break;
-            }
-            if (issued > (uint32_t)depth && issued - depth > pub) {
-                pub = issued - depth;
-                lds_st(landed, pub);
-            }
-        }
-    }
-    wait_vmcnt<0>();
-    lds_st(landed, issued);
-}
-
-// ------------------------------------------------------------------ poller
-
-__device__ __forceinline__ void run_poller(const KParams &P, const Ctx &c) {
-    const int64_t epoch = P.epoch;
-    for (int pc = 0;; ++pc) {
-        const int32_t *ins = instr(P, c.cu, pc);
-        if (sload(ins, W_OP) == OP_END) break;
-        const int nw = sload(ins, W_NWAIT);
-        for (int k = 0; k < nw; ++k) {
-            const int e = sload(ins, W_WAIT + k);
-            const int ctr = sload(P.events, (int64_t)e * EV_WORDS + EV_CTR);
-            const int32_t need = (int32_t)(epoch * sload(P.events, (int64_t)e * EV_WORDS + EV_NEED));
-            int32_t *cp = P.counters + (int64_t)ctr * CTR_STRIDE;
-            int64_t spins = 0;
-            while (__hip_atomic_load(cp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
-                if (lds_ld(c.misc + M_ABORT)) return;
-                if ((++spins & 255) == 0 &&
-                    __hip_atomic_load(P.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-                    lds_st(c.misc + M_ABORT, 1u);
-                    return;
-                }
-                if (spins > P.watchdog) {
-                    raise_error(P, c.misc, ERR_TIMEOUT, c.cu, pc);
-                    return;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-        }
-        // The acquire is a cache invalidate that completes asynchronously
-        // (vmcnt); the compute waves load only after READY, so wait for it
-        // to finish before publishing READY to them.
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        wait_vmcnt<0>();
-        lds_st(c.misc + M_READY, (uint32_t)(pc + 1));
-    }
-}
-
-// ------------------------------------------------------------- compute waves
-
-struct CW {
-    Ctx c;
-    int w;          // compute wave index
-    uint32_t nbar;  // barriers passed
-};
-
-__device__ __forceinline__ bool cbar(CW &s, int pc) {
-    s.nbar++;
-    if (s.c.lane == 0) lds_add(s.c.misc + M_ARRIVE, 1u);  // one arrival per wave
-    return lds_wait_ge(s.c, s.c.misc + M_ARRIVE, (uint32_t)NC * s.nbar, pc);
-}
-
-__device__ __forceinline__ v4u ring16(const Ctx &c, uint32_t off) {
-    if (off >= c.ring_bytes) off -= c.ring_bytes;
-    return *(const MK_LDS v4u *)(c.ring + off);
-}
-__device__ __forceinline__ v2u ring8(const Ctx &c, uint32_t off) {
-    if (off >= c.ring_bytes) off -= c.ring_bytes;
-    return *(const MK_LDS v2u *)(c.ring + off);
-}
-
-__device__ __forceinline__ int token_of(const KParams &P, CW &s, int b, int pc) {
-    int t = sload(P.tokens_in, b);
-    if (t < 0 || t >= P.V) {
-        if (s.c.lane == 0) raise_error(P, s.c.misc, ERR_RANGE, s.c.cu, pc);
-        t = 0;
-    }
-    return t;
-}
-
-// act[b] <- rmsnorm(x_b) * w, in the matvec layout; every compute wave
-// takes a slice and the sums of squares are combined in wave order.
-__device__ __forceinline__ bool stage_norm(const KParams &P, CW &s, int pc, const uint16_t *wn, bool from_input) {
-    const int H = P.H, lane = s.c.lane;
-    MK_LDS float *norm = (MK_LDS float *)(s.c.misc + M_NORM);
-    for (int b = 0; b < P.B; ++b) {
-        const int tok = (from_input && P.has_embed) ? token_of(P, s, b, pc) : 0;
-        float ss = 0.0f;
-        for (int i = (s.w * 64 + lane) * 4; i < H; i += NC * 256) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float v = x_input(P, b, i + e, from_input, tok);
-                ss = fmaf(v, v, ss);
-            }
-        }
-        ss = wave_sum(ss);
-        if (lane == 0) norm[s.w * MAX_B + b] = ss;
-    }
-    if (!cbar(s, pc)) return false;
-    for (int b = 0; b < P.B; ++b) {
-        const int tok = (from_input && P.has_embed) ? token_of(P, s, b, pc) : 0;
-        float ss = 0.0f;
-        for (int w = 0; w < NC; ++w) ss += norm[w * MAX_B + b];
-        const float inv = 1.0f / sqrtf(ss / (float)H + P.eps);
-        MK_LDS float *a = s.c.act + b * P.act_stride;
-        for (int i = (s.w * 64 + lane) * 4; i < H; i += NC * 256) {
-            v4f u;
-            u.x = x_input(P, b, i + 0, from_input, tok) * inv * bf2f(wn[i + 0]);
-            u.y = x_input(P, b, i + 1, from_input, tok) * inv * bf2f(wn[i + 1]);
-            u.z = x_input(P, b, i + 2, from_input, tok) * inv * bf2f(wn[i + 2]);
-            u.w = x_input(P, b, i + 3, from_input, tok) * inv * bf2f(wn[i + 3]);
-            *(MK_LDS v4f *)(a + act_index(i)) = u;
-        }
-    }
-    return cbar(s, pc);
-}
-
-// act[b] <- src[b] (length K), in the matvec layout
-__device__ __forceinline__ bool stage_copy(const KParams &P, CW &s, int pc, const float *src, int K) {
-    const int lane = s.c.lane;
-    for (int b = 0; b < P.B; ++b) {
-        MK_LDS float *a = s.c.act + b * P.act_stride;
-        for (int i = (s.w * 64 + lane) * 4; i < K; i += NC * 256)
-            *(MK_LDS v4f *)(a + act_index(i)) = *(const v4f *)(src + (int64_t)b * K + i);
-    }
-    return cbar(s, pc);
-}
-
-// One matvec instruction: rows [r0, r1) of one (or, for UPGATE, two)
-// matrices against the staged activations of all requests.
-template <int NB>
-__device__ __forceinline__ void matvec_rows(const KParams &P, CW &s, const int32_t *ins, int op, int pc, uint32_t g0) {
-    const Ctx &c = s.c;
-    const int lane = c.lane;
-    const int r0 = sload(ins, W_R0), r1 = sload(ins, W_R1);
-    const int layer = sload(ins, W_LAYER), flags = sload(ins, W_FLAGS);
-    const int K = op_k(P, op);
-    const int nchunk = K >> 3;
-    const uint32_t rowb = (uint32_t)K * 2;
-    const uint32_t unitb = op == OP_UPGATE ? 2 * rowb : rowb;
-    const int nu = r1 - r0;
-    float best_v[NB];
-    int best_i[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        best_v[b] = -INFINITY;
-        best_i[b] = 0x7fffffff;
-    }
-    bool bad_nan = false;
-    for (int u = s.w; u < nu; u += NC) {
-        const uint32_t sb0 = (uint32_t)u * unitb;
-        // nothing before this unit is needed any more: let the loader reuse it
-        if (lane == 0) lds_st(c.misc + M_WPOS + s.w, g0 + sb0 / GRANULE);
-        if (!lds_wait_ge(c, c.misc + M_LANDED, g0 + (sb0 + unitb + GRANULE - 1) / GRANULE, pc)) return;
-        const uint32_t rbase = (g0 * GRANULE + sb0) % c.ring_bytes;
-        float dot[2][NB];
-        const int nm = op == OP_UPGATE ? 2 : 1;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            if (m >= nm) break;
-            float acc[NB];
-#pragma unroll
-            for (int b = 0; b < NB; ++b) acc[b] = 0.0f;
-            const uint32_t mb = rbase + m * rowb;
-            for (int j = 0; (j << 6) < nchunk; ++j) {
-                const int ci = lane + (j << 6);
-                if (ci < nchunk) {
-                    const v4u w = ring16(c, mb + (uint32_t)ci * 16);
-#pragma unroll
-                    for (int b = 0; b < NB; ++b) {
-                        const MK_LDS float *a = c.act + b * P.act_stride + (j << 9) + (lane << 2);
-                        const v4f a0 = *(const MK_LDS v4f *)a;
-                        const v4f a1 = *(const MK_LDS v4f *)(a + 256);
-                        acc[b] += dot8(w, a0, a1);
-                    }
-                }
-            }
-#pragma unroll
-            for (int b = 0; b < NB; ++b) dot[m][b] = wave_sum(acc[b]);
-        }
-        // release the unit's ring space before the epilogue's global traffic
-        {
-            const int un = u + NC;
-            const uint32_t nxt = un < nu ? g0 + ((uint32_t)un * unitb) / GRANULE
-                                         : g0 + (stream_bytes(P, op, r0, r1, 0, 0) + GRANULE - 1) / GRANULE;
-            if (lane == 0) lds_st(c.misc + M_WPOS + s.w, nxt);
-        }
-        const int r = r0 + u;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            if (lane != b) continue;  // lane b writes request b
-            const float v = dot[0][b];
-            row_epilogue(P, op, flags, r, b, v, op == OP_UPGATE ? dot[1][b] : 0.0f);
-            if (op == OP_LMHEAD) {
-                if (v != v) bad_nan = true;
-                if (v > best_v[b]) {  // rows rise, so ties keep the lowest index
-                    best_v[b] = v;
-                    best_i[b] = r;
-                }
-            }
-        }
-    }
-    if (op == OP_LMHEAD) {
-        MK_LDS float *am = (MK_LDS float *)(c.misc + M_AMAX);
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-            if (lane == b) {
-                am[(s.w * MAX_B + b) * 2] = best_v[b];
-                ((MK_LDS int32_t *)am)[(s.w * MAX_B + b) * 2 + 1] = best_i[b];
-            }
-        if (bad_nan) raise_error(P, c.misc, ERR_NAN, c.cu, pc);
-    }
-}
-
-// ATTN staging: rotated queries of the group, and (last chunk only) the new
-// K/V entry rounded to bf16, written to the cache and kept for the patch.
-__device__ __forceinline__ bool stage_attn(const KParams &P, CW &s, const int32_t *ins, int pc, int p) {
-    const int lane = s.c.lane;
-    const int b = sload(ins, W_B), g = sload(ins, W_G), layer = sload(ins, W_LAYER);
-    const bool last = sload(ins, W_C) == sload(ins, W_NCH) - 1;
-    const int G = P.nq / P.nkv, QKVN = (P.nq + 2 * P.nkv) * P.d, QD = P.nq * P.d;
-    MK_LDS float *q = s.c.act;
-    MK_LDS uint16_t *kvn = (MK_LDS uint16_t *)(s.c.act + G * 68);
-    const float *row = P.qkv + (int64_t)b * QKVN;
-    const float2 cs = P.rope[(int64_t)p * 32 + (lane & 31)];
-    const int ntask = G + (last ? 2 : 0);
-    for (int t = s.w; t < ntask; t += NC) {
-        const float *src = t < G ? row + (g * G + t) * 64 : (t == G ? row + QD + g * 64 : row + QD + P.nkv * 64 + g * 64);
-        const float xi = src[lane];
-        float out = xi;
-        if (t <= G) {  // queries and the key are rotated; the value is not
-            const float xp = src[lane ^ 32];
-            out = lane < 32 ? xi * cs.x - xp * cs.y : xi * cs.x + xp * cs.y;
-        }
-        if (t < G) {
-            q[t * 68 + lane] = out;
-        } else {
-            const uint16_t hb = f2bf(out);
-            kvn[(t - G) * 64 + lane] = hb;
-            int page = sload(P.page_table, (int64_t)b * P.max_pages + (p >> 4));
-            if (page < 0 || page >= P.n_pages) {
-                if (lane == 0) raise_error(P, s.c.misc, ERR_RANGE, s.c.cu, pc);
-                page = 0;
-            }
-            uint16_t *pool = t == G ? P.k_pool : P.v_pool;
-            const size_t layer_pool = (size_t)P.n_pages * P.nkv * 16 * 64;
-            pool[(size_t)layer * layer_pool + ((size_t)page * P.nkv + g) * 1024 + (p & 15) * 64 + lane] = hb;
-        }
-    }
-    return cbar(s, pc);
-}
-
-__device__ __forceinline__ void attn_body(const KParams &P, CW &s, const int32_t *ins, int pc, uint32_t g0, int p, int blo,
-                          int bhi) {
-    const Ctx &c = s.c;
-    const int lane = c.lane;
-    const int G = P.nq / P.nkv;
-    const MK_LDS float *q = c.act;
-    const MK_LDS uint16_t *kvn = (const MK_LDS uint16_t *)(c.act + G * 68);
-    MK_LDS float *wpart = c.act + G * 68 + 64;
-    AttnState st;
-    attn_init(st);
-    const int nu = bhi - blo;
-    for (int u = s.w; u < nu; u += NC) {
-        if (lane == 0) lds_st(c.misc + M_WPOS + s.w, g0 + (uint32_t)u * 4);
-        if (!lds_wait_ge(c, c.misc + M_LANDED, g0 + (uint32_t)(u + 1) * 4, pc)) return;
-        const uint32_t kb = (g0 * GRANULE + (uint32_t)u * 4096u) % c.ring_bytes;
-        uint32_t vb = kb + 2048;
-        if (vb >= c.ring_bytes) vb -= c.ring_bytes;
-        const int blk = blo + u;
-        if (blk == (p >> 4)) {  // patch the new entry over the stale cache row
-            const int j = p & 15;
-            const int half = lane >> 5, li = lane & 31;
-            const uint32_t at = (half ? vb : kb) + j * 128 + li * 4;
-            const uint32_t v = (uint32_t)kvn[half * 64 + li * 2] | ((uint32_t)kvn[half * 64 + li * 2 + 1] << 16);
-            *(MK_LDS uint32_t *)(c.ring + (at >= c.ring_bytes ? at - c.ring_bytes : at)) = v;
-        }
-        const int nvalid = min(16, p + 1 - blk * 16);
-        attn_block(
-            st, q, G, nvalid, lane, [&](int j, int ch) { return ring16(c, kb + j * 128 + ch * 16); },
-            [&](int j, int qq) { return ring8(c, vb + j * 128 + qq * 8); });
-        const int un = u + NC;
-        if (lane == 0) lds_st(c.misc + M_WPOS + s.w, g0 + (un < nu ? (uint32_t)un * 4 : (uint32_t)nu * 4));
-    }
-    attn_store(st, wpart + s.w * G * 68, G, lane);
-}
-
-// One completion per event: only lane 0 bumps (an atomic issued by every
-// lane would count once per lane).
-__device__ __forceinline__ void publish(const KParams &P, const int32_t *ins, int lane) {
-    if (lane != 0) return;
-    const int np = sload(ins, W_NPUB);
-    for (int k = 0; k < np; ++k) {
-        const int e = sload(ins, W_PUB + k);
-        const int ctr = sload(P.events, (int64_t)e * EV_WORDS + EV_CTR);
-        __hip_atomic_fetch_add(P.counters + (int64_t)ctr * CTR_STRIDE, 1, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    }
-}
-
-// Run by the last compute wave to finish an instruction's body.
-__device__ __forceinline__ void finish(const KParams &P, CW &s, const int32_t *ins, int pc, int p) {
-    const Ctx &c = s.c;
-    const int lane = c.lane;
-    const int op = sload(ins, W_OP);
-    const int G = P.nq / P.nkv;
-    // local combination of the compute waves' partials
-    if (op == OP_ATTN) {
-        const int b = sload(ins, W_B), g = sload(ins, W_G), ch = sload(ins, W_C), nch = sload(ins, W_NCH);
-        const MK_LDS float *wpart = c.act + G * 68 + 64;
-        for (int hq = 0; hq < G; ++hq) {
-            float o, m, l;
-            merge_parts(nullptr, wpart + hq * 68, NC, G * 68, lane, &o, &m, &l);
-            float *dst = P.attn_part + ((((int64_t)b * P.nkv + g) * nch + ch) * G + hq) * ATTN_PART_STRIDE;
-            dst[lane] = o;
-            if (lane == 0) {
-                dst[64] = m;
-                dst[65] = l;
-            }
-        }
-    } else if (op == OP_LMHEAD) {
-        const MK_LDS float *am = (const MK_LDS float *)(c.misc + M_AMAX);
-        if (lane < P.B) {
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;
-            for (int w = 0; w < NC; ++w) {
-                const float v = am[(w * MAX_B + lane) * 2];
-                const int i = ((const MK_LDS int32_t *)am)[(w * MAX_B + lane) * 2 + 1];
-                if (amax_better(v, i, bv, bi)) {
-                    bv = v;
-                    bi = i;
-                }
-            }
-            const int slot = sload(ins, W_SLOT);
-            P.lm_part[((int64_t)slot * P.B + lane) * 2] = bv;
-            ((int32_t *)P.lm_part)[((int64_t)slot * P.B + lane) * 2 + 1] = bi;
-        }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const int merge = sload(ins, W_MERGE);
-    if (merge < 0) {
-        publish(P, ins, lane);
-        return;
-    }
-    // last-finisher election across compute units
-    const int ctr = sload(P.events, (int64_t)merge * EV_WORDS + EV_CTR);
-    const int32_t need = (int32_t)((int64_t)P.epoch * sload(P.events, (int64_t)merge * EV_WORDS + EV_NEED));
-    int32_t old = 0;
-    if (lane == 0)
-        old = __hip_atomic_fetch_add(P.counters + (int64_t)ctr * CTR_STRIDE, 1, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-    old = __shfl(old, 0, 64);
-    if (old + 1 != need) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    const int flags = sload(ins, W_FLAGS);
-    if (op == OP_ATTN) {
-        const int b = sload(ins, W_B), g = sload(ins, W_G), nch = sload(ins, W_NCH);
-        for (int hq = 0; hq < G; ++hq) {
-            const float *src = P.attn_part + (((int64_t)b * P.nkv + g) * nch * G + hq) * ATTN_PART_STRIDE;
-            float o, m, l;
-            merge_parts(src, nullptr, nch, G * ATTN_PART_STRIDE, lane, &o, &m, &l);
-            P.o[(int64_t)b * P.nq * P.d + (g * G + hq) * 64 + lane] = o / l;
-        }
-    } else if (op == OP_LMHEAD) {
-        const int nslot = sload(ins, W_NSLOT);
-        if (lane < P.B) {
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;
-            for (int t = 0; t < nslot; ++t) {
-                const float v = P.lm_part[((int64_t)t * P.B + lane) * 2];
-                const int i = ((const int32_t *)P.lm_part)[((int64_t)t * P.B + lane) * 2 + 1];
-                if (amax_better(v, i, bv, bi)) {
-                    bv = v;
-                    bi = i;
-                }
-            }
-            P.tokens_out[lane] = bi;
-        }
-    }
-    if ((flags & F_STEP_FINAL) && P.kv_lens_out && lane < P.B) P.kv_lens_out[lane] = sload(P.kv_lens, lane) + 1;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    publish(P, ins, lane);
-    (void)p;
-}
-
-__device__ __forceinline__ void run_compute(const KParams &P, CW &s) {
-    const Ctx &c = s.c;
-    const int lane = c.lane;
-    uint32_t g0 = 0;
-    const bool tracer = s.w == 0 && lane == 0 && P.trace != nullptr;
-    for (int pc = 0;; ++pc) {
-        const int32_t *ins = instr(P, c.cu, pc);
-        const int op = sload(ins, W_OP);
-        if (op == OP_END) break;
-        int64_t *tr = P.trace ? P.trace + ((int64_t)c.cu * P.Q + pc) * 3 : nullptr;
-        if (tracer) tr[0] = wall_clock64();
-        int p = 0, blo = 0, bhi = 0;
-        if (op == OP_ATTN) {
-            const int b = sload(ins, W_B);
-            p = sload(P.kv_lens, b);
-            if (p < 0 || p >= P.T * P.max_pages) {
-                if (lane == 0) raise_error(P, c.misc, ERR_RANGE, c.cu, pc);
-                p = 0;
-            }
-            chunk_blocks(p, sload(ins, W_C), sload(ins, W_NCH), &blo, &bhi);
-        }
-        const uint32_t ng = (stream_bytes(P, op, sload(ins, W_R0), sload(ins, W_R1), blo, bhi) + GRANULE - 1) / GRANULE;
-        // inputs visible, and the previous instruction fully finished (its
-        // finisher may still read the activation area)
-        if (!lds_wait_ge(c, c.misc + M_READY, (uint32_t)pc + 1, pc)) return;
-        if (!lds_wait_ge(c, c.misc + M_DONE, (uint32_t)pc, pc)) return;
-        if (tracer) tr[1] = wall_clock64();
-        const int layer = sload(ins, W_LAYER), flags = sload(ins, W_FLAGS);
-        bool ok = true;
-        switch (op) {
-            case OP_QKV: ok = stage_norm(P, s, pc, wptr(P, layer, 0), (flags & F_X_FROM_INPUT) != 0); break;
-            case OP_UPGATE: ok = stage_norm(P, s, pc, wptr(P, layer, 3), false); break;
-            case OP_LMHEAD: ok = stage_norm(P, s, pc, P.final_norm, false); break;
-            case OP_OPROJ: ok = stage_copy(P, s, pc, P.o, P.nq * P.d); break;
-            case OP_DOWN: ok = stage_copy(P, s, pc, P.act, P.F); break;
-            case OP_ATTN: ok = stage_attn(P, s, ins, pc, p); break;
-            default:
-                if (lane == 0) raise_error(P, c.misc, ERR_OPCODE, c.cu, pc);
-                return;
-        }
-        if (!ok) return;
-        if (op == OP_ATTN) {
-            attn_body(P, s, ins, pc, g0, p, blo, bhi);
-        } else {
-            switch (P.B) {
-                case 1: matvec_rows<1>(P, s, ins, op, pc, g0); break;
-                case 2: matvec_rows<2>(P, s, ins, op, pc, g0); break;
-                case 3: matvec_rows<3>(P, s, ins, op, pc, g0); break;
-                case 4: matvec_rows<4>(P, s, ins, op, pc, g0); break;
-                case 5: matvec_rows<5>(P, s, ins, op, pc, g0); break;
-                case 6: matvec_rows<6>(P, s, ins, op, pc, g0); break;
-                case 7: matvec_rows<7>(P, s, ins, op, pc, g0); break;
-                default: matvec_rows<8>(P, s, ins, op, pc, g0); break;
-            }
-        }
-        if (lds_ld(c.misc + M_ABORT)) return;
-        g0 += ng;
-        if (lane == 0) lds_st(c.misc + M_WPOS + s.w, g0);
-        // body done: wait until this wave's global stores are acknowledged
-        // (a workgroup-scope release does not wait for them), so that the
-        // finisher's agent-scope release covers every wave's results
-        wait_vmcnt<0>();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        uint32_t old = 0;
-        if (lane == 0) old = lds_add(c.misc + M_FIN, 1u);
-        old = __shfl(old, 0, 64);
-        if (old == (uint32_t)NC * (pc + 1) - 1) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            finish(P, s, ins, pc, p);
-            if (P.trace && lane == 0) tr[2] = wall_clock64();
-            if (lane == 0) lds_add(c.misc + M_DONE, 1u);
-        }
-    }
+const void *kernel_for(int B, int G) {
+    if (B <= 1) return interp_kernel_b1(G);
+    if (B <= 2) return interp_kernel_b2(G);
+    if (B <= 4) return interp_kernel_b4(G);
+    return interp_kernel_b8(G);
 }
 
 }  // namespace
 
-__global__ __launch_bounds__(BLOCK_THREADS, 1) void mk_megakernel(KParams P) {
-    extern __shared__ char lds_raw[];
-    MK_LDS char *lds = (MK_LDS char *)lds_raw;
-    Ctx c;
-    c.P = &P;
-    c.misc = (MK_LDS uint32_t *)lds;
-    c.act = (MK_LDS float *)(lds + P.act_off);
-    c.ring = lds + P.ring_off;
-    c.ring_bytes = (uint32_t)P.ring_granules * GRANULE;
-    c.cu = blockIdx.x;
-    c.lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    for (int i = threadIdx.x; i < MISC_BYTES / 4; i += BLOCK_THREADS) c.misc[i] = 0;
-    __syncthreads();
-    if (wave == 0) {
-        run_loader(P, c);
-    } else if (wave == 1) {
-        run_poller(P, c);
-    } else {
-        CW s{c, wave - 2, 0};
-        run_compute(P, s);
-    }
+bool megakernel_supports(int B, int G) { return B >= 1 && B <= MAX_B && kernel_for(B, G) != nullptr; }
+
+hipError_t setup_megakernel(int B, int G, int lds_bytes) {
+    const void *k = kernel_for(B, G);
+    if (!k) return hipErrorInvalidValue;
+    return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
 }
 
-// One wave: DMA n granules into LDS at byte offset `off` exactly as the
-// loader does, wait, then copy those LDS bytes out with ordinary loads.
-__global__ __launch_bounds__(64) void mk_dma_probe(const char *src, char *dst, int n, int off) {
-    extern __shared__ char lds_raw[];
-    MK_LDS char *lds = (MK_LDS char *)lds_raw;
-    const int lane = threadIdx.x;
-    for (int i = lane; i < LDS_LIMIT / 4; i += 64) ((MK_LDS uint32_t *)lds)[i] = 0u;
-    __syncthreads();
-    const uint32_t base = (uint32_t)(uintptr_t)lds + (uint32_t)off;
-    if (n < 0) {
-        // two transfers, one m0 value, the second with instruction offset 1024
-        const char *g = src + lane * 16;
-        asm volatile(
-            "s_mov_b32 m0, %0\n\t"
-            "s_nop 1\n\t"
-            "global_load_lds_dwordx4 %1, off\n\t"
-            "global_load_lds_dwordx4 %1, off offset:1024"
-            :
-            : "s"(base), "v"(g)
-            : "memory");
-        n = 2;
-    } else {
-        for (int k = 0; k < n; ++k)
-            dma16(src + (size_t)k * GRANULE + lane * 16, __builtin_amdgcn_readfirstlane(base + k * GRANULE));
-    }
-    wait_vmcnt<0>();
-    for (int k = 0; k < n; ++k) {
-        const v4u v = *(const MK_LDS v4u *)(lds + off + k * GRANULE + lane * 16);
-        *(v4u *)(dst + (size_t)k * GRANULE + lane * 16) = v;
-    }
-}
-
-hipError_t dma_probe(const void *src, void *dst, int n_kib, int off_kib) {
-    hipError_t e = hipFuncSetAttribute((const void *)mk_dma_probe, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       LDS_LIMIT);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mk_dma_probe, dim3(1), dim3(64), LDS_LIMIT, 0, (const char *)src, (char *)dst, n_kib,
-                       off_kib * GRANULE);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return hipDeviceSynchronize();
-}
-
-// Ring protocol probe: wave 0 streams n granules of a known pattern through
-// a ring of `ring` granules exactly as the loader does (issue, keep `depth`
-// in flight, publish landed); NC consumer waves take granules round-robin,
-// wait for them to land, check every word and release them. `variant` 1
-// makes the loader read back one word of the newest landed granule before
-// publishing. Counts mismatching words into errs[0] and granules checked
-// into errs[1].
-__global__ __launch_bounds__(BLOCK_THREADS, 1) void mk_ring_probe(const uint32_t *src, int n, int ring, int depth,
-                                                                   int variant, int64_t watchdog, int32_t *errs) {
-    extern __shared__ char lds_raw[];
-    MK_LDS char *lds = (MK_LDS char *)lds_raw;
-    MK_LDS uint32_t *misc = (MK_LDS uint32_t *)lds;
-    MK_LDS char *rb = lds + MISC_BYTES;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    src += (size_t)blockIdx.x * n * 256;
-    for (int i = threadIdx.x; i < MISC_BYTES / 4; i += BLOCK_THREADS) misc[i] = 0;
-    __syncthreads();
-    const int nl = (variant >> 8) & 15;
-    const int gb = ((variant >> 12) & 15) ? ((variant >> 12) & 15) : 1;  // granules per DMA batch: 1 or 4
-    const bool regs = (variant >> 16) & 1;                                // register-staged loaders
-    const bool inter = (variant >> 17) & 1;  // batch t of workgroup b at (t * gridDim.x + b) * 4 KiB
-    const bool plain = (variant >> 18) & 1;  // ordinary loads instead of non-temporal ones
-    variant &= 255;
-    if (inter) src -= (size_t)blockIdx.x * n * 256;  // undo the per-block slice
-    if (regs && nl >= 1) {
-        // nl loader waves; batch t = 4 granules issued by loader t % nl with
-        // ordinary 16-byte loads into registers, 4 batches in flight, then
-        // written into the ring once its slots are free
-        const int ncons = N_WAVES - nl;
-        const int nbatch = n / 4;
-        if (wave < nl) {
-            uint32_t mine = 0, lim = ring;
-            v4u ra[4], rbuf[4], rc[4], rd[4];
-            auto issue = [&](v4u (&r)[4], int t) {
-                if (t < nbatch) {
-                    const size_t bt = inter ? (size_t)t * gridDim.x + blockIdx.x : (size_t)t;
-                    const v4u *g = (const v4u *)(src + bt * 4 * 256) + lane;
-                    if (plain) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) r[i] = g[i * 64];
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) r[i] = __builtin_nontemporal_load(g + i * 64);
-                    }
-                }
-            };
-            auto commit = [&](v4u (&r)[4], int t) -> bool {
-                if (t >= nbatch) return true;
-                const uint32_t k = (uint32_t)t * 4;
-                if (k + 4 > lim) {
-                    int64_t spins = 0;
-                    for (;;) {
-                        uint32_t mn = lds_ld(misc + M_WPOS);
-                        for (int w = 1; w < ncons; ++w) mn = min(mn, lds_ld(misc + M_WPOS + w));
-                        lim = __builtin_amdgcn_readfirstlane(mn + ring);
-                        if (k + 4 <= lim) break;
-                        if (++spins > watchdog) {
-                            lds_st(misc + M_ABORT, 1u);
-                            return false;
-                        }
-                        __builtin_amdgcn_s_sleep(1);
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) *(MK_LDS v4u *)(rb + ((k + i) % ring) * GRANULE + lane * 16) = r[i];
-                mine += 4;
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                __hip_atomic_store(misc + M_LANDED + 32 + wave, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                return true;
-            };
-            const int step = nl;
-            int t = wave;
-            issue(ra, t);
-            issue(rbuf, t + step);
-            issue(rc, t + 2 * step);
-            issue(rd, t + 3 * step);
-            for (; t < nbatch; t += 4 * step) {
-                if (!commit(ra, t)) return;
-                issue(ra, t + 4 * step);
-                if (!commit(rbuf, t + step)) return;
-                issue(rbuf, t + 5 * step);
-                if (!commit(rc, t + 2 * step)) return;
-                issue(rc, t + 6 * step);
-                if (!commit(rd, t + 3 * step)) return;
-                issue(rd, t + 7 * step);
-            }
-        } else {
-            const int w = wave - nl;
-            int bad = 0, seen = 0;
-            for (int g = w; g < nbatch * 4; g += ncons) {
-                const int tb = g / 4;
-                const int j = tb % nl;
-                const uint32_t need = (uint32_t)((tb / nl + 1) * 4);
-                int64_t spins = 0;
-                while (lds_ld(misc + M_LANDED + 32 + j) < need) {
-                    if (lds_ld(misc + M_ABORT) == 1u || ++spins > watchdog) {
-                        if (lane == 0) atomicAdd(errs + 2, 1);
-                        return;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                const v4u v = *(const MK_LDS v4u *)(rb + (g % ring) * GRANULE + lane * 16);
-                const uint32_t e = (uint32_t)g * 256u + lane * 4u;
-                if (variant == 4)
-                    bad += (v.x ^ v.y ^ v.z ^ v.w) == 0x12345678u;
-                else
-                    bad += (v.x != src[e]) + (v.y != src[e + 1]) + (v.z != src[e + 2]) + (v.w != src[e + 3]);
-                ++seen;
-                const int gn = g + ncons;
-                if (lane == 0) lds_st(misc + M_WPOS + w, (uint32_t)(gn < nbatch * 4 ? gn : nbatch * 4));
-            }
-            if (lane == 0) lds_st(misc + M_WPOS + w, (uint32_t)(nbatch * 4));
-            bad = (int)wave_sum((float)bad);
-            if (lane == 0) {
-                atomicAdd(errs, bad);
-                atomicAdd(errs + 1, seen);
-            }
-        }
-        return;
-    }
-    if (nl >= 1) {
-        // nl loader waves; batch t (granules [t*gb, t*gb+gb)) is issued by
-        // loader t % nl with one m0 write; consumers are waves nl .. N_WAVES-1
-        // and wait on the issuing loader's own landed count (in granules)
-        const int ncons = N_WAVES - nl;
-        const int nbatch = n / gb;
-        if (wave < nl) {
-            const uint32_t ring_lds = (uint32_t)(uintptr_t)rb;
-            uint32_t mine = 0, pub = 0, lim = ring;
-            for (int t = wave; t < nbatch; t += nl) {
-                const uint32_t k = (uint32_t)t * gb;  // first granule of the batch
-                if (k + gb > lim) {
-                    int64_t spins = 0;
-                    for (;;) {
-                        wait_vmcnt<0>();
-                        pub = mine;
-                        lds_st(misc + M_LANDED + 32 + wave, mine);
-                        uint32_t mn = lds_ld(misc + M_WPOS);
-                        for (int w = 1; w < ncons; ++w) mn = min(mn, lds_ld(misc + M_WPOS + w));
-                        lim = __builtin_amdgcn_readfirstlane(mn + ring);
-                        if (k + gb <= lim) break;
-                        if (++spins > watchdog) {
-                            lds_st(misc + M_ABORT, 1u);
-                            return;
-                        }
-                        __builtin_amdgcn_s_sleep(1);
-                    }
-                }
-                const size_t kk = inter ? ((size_t)t * gridDim.x + blockIdx.x) * gb : (size_t)k;
-                const char *g = (const char *)(src + kk * 256 + lane * 4);
-                const uint32_t l = __builtin_amdgcn_readfirstlane(ring_lds + (k % ring) * GRANULE);
-                if (gb == 4) {
-                    asm volatile(
-                        "s_mov_b32 m0, %0\n\t"
-                        "s_nop 1\n\t"
-                        "global_load_lds_dwordx4 %1, off\n\t"
-                        "global_load_lds_dwordx4 %1, off offset:1024\n\t"
-                        "global_load_lds_dwordx4 %1, off offset:2048\n\t"
-                        "global_load_lds_dwordx4 %1, off offset:3072"
-                        :
-                        : "s"(l), "v"(g)
-                        : "memory");
-                } else {
-                    dma16(g, l);
-                }
-                mine += gb;
-                uint32_t dd;
-                switch (depth) {
-                    case 8: wait_vmcnt<8>(); dd = 8; break;
-                    case 32: wait_vmcnt<32>(); dd = 32; break;
-                    case 48: wait_vmcnt<48>(); dd = 48; break;
-                    case 56: wait_vmcnt<56>(); dd = 56; break;
-                    default: wait_vmcnt<16>(); dd = 16; break;
-                }
-                if (mine > dd && mine - dd > pub) {
-                    pub = mine - dd;
-                    lds_st(misc + M_LANDED + 32 + wave, pub);
-                }
-            }
-            wait_vmcnt<0>();
-            lds_st(misc + M_LANDED + 32 + wave, mine);
-        } else {
-            const int w = wave - nl;
-            int bad = 0, seen = 0;
-            for (int g = w; g < nbatch * gb; g += ncons) {
-                const int t = g / gb;
-                const int j = t % nl;
-                const uint32_t need = (uint32_t)((t / nl + 1) * gb);
-                int64_t spins = 0;
-                while (lds_ld(misc + M_LANDED + 32 + j) < need) {
-                    if (lds_ld(misc + M_ABORT) == 1u || ++spins > watchdog) {
-                        if (lane == 0) atomicAdd(errs + 2, 1);
-                        return;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                const v4u v = *(const MK_LDS v4u *)(rb + (g % ring) * GRANULE + lane * 16);
-                const uint32_t e = (uint32_t)g * 256u + lane * 4u;
-                if (variant == 4)
-                    bad += (v.x ^ v.y ^ v.z ^ v.w) == 0x12345678u;
-                else
-                    bad += (v.x != src[e]) + (v.y != src[e + 1]) + (v.z != src[e + 2]) + (v.w != src[e + 3]);
-                ++seen;
-                const int gn = g + ncons;
-                if (lane == 0) lds_st(misc + M_WPOS + w, (uint32_t)(gn < nbatch * gb ? gn : nbatch * gb));
-            }
-            if (lane == 0) lds_st(misc + M_WPOS + w, (uint32_t)(nbatch * gb));
-            bad = (int)wave_sum((float)bad);
-            if (lane == 0) {
-                atomicAdd(errs, bad);
-                atomicAdd(errs + 1, seen);
-            }
-        }
-        return;
-    }
-    if (wave == 0) {
-        const uint32_t ring_lds = (uint32_t)(uintptr_t)rb;
-        uint32_t issued = 0, slot = 0, lim = ring, pub = 0;
-        for (int k = 0; k < n; ++k) {
-            if (issued >= lim) {
-                int64_t spins = 0;
-                for (;;) {
-                    wait_vmcnt<0>();
-                    pub = issued;
-                    lds_st(misc + M_LANDED, issued);
-                    uint32_t mn = lds_ld(misc + M_WPOS);
-                    for (int w = 1; w < NC; ++w) mn = min(mn, lds_ld(misc + M_WPOS + w));
-                    lim = __builtin_amdgcn_readfirstlane(mn + ring);
-                    if (issued < lim) break;
-                    if (++spins > watchdog) {
-                        lds_st(misc + M_ABORT, 1u);
-                        return;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-            }
-            dma16(src + (size_t)k * 256 + lane * 4, __builtin_amdgcn_readfirstlane(ring_lds + slot * GRANULE));
-            ++issued;
-            slot = (slot + 1 == (uint32_t)ring) ? 0 : slot + 1;
-            switch (depth) {
-                case 0: wait_vmcnt<0>(); break;
-                case 8: wait_vmcnt<8>(); break;
-                case 40: wait_vmcnt<40>(); break;
-                default: wait_vmcnt<56>(); break;
-            }
-            if (issued > (uint32_t)depth && issued - depth > pub) {
-                pub = issued - depth;
-                if (variant == 1) {
-                    const uint32_t s2 = (pub - 1) % ring;
-                    const uint32_t v = *(volatile MK_LDS uint32_t *)(rb + s2 * GRANULE + lane * 16);
-                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-                    if (v == 0xdeadbeefu) misc[M_ABORT] = 2;
-                }
-                lds_st(misc + M_LANDED, pub);
-            }
-        }
-        wait_vmcnt<0>();
-        lds_st(misc + M_LANDED, issued);
-    } else if (wave == 1) {
-        // variant 2: agent-scope acquire fences, variant 3: release fences,
-        // issued by a second wave while the loader streams
-        if (variant >= 2) {
-            int64_t spins = 0;
-            while (lds_ld(misc + M_LANDED) < (uint32_t)n && lds_ld(misc + M_ABORT) != 1u && ++spins < watchdog) {
-                (void)__hip_atomic_load(errs + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (variant == 2) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                else __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-                __builtin_amdgcn_s_sleep(2);
-            }
-        }
-    } else if (wave >= 2) {
-        const int w = wave - 2;
-        int bad = 0, seen = 0;
-        for (int g = w; g < n; g += NC) {
-            int64_t spins = 0;
-            while (lds_ld(misc + M_LANDED) < (uint32_t)(g + 1)) {
-                if (lds_ld(misc + M_ABORT) == 1u || ++spins > watchdog) {
-                    if (lane == 0) atomicAdd(errs + 2, 1);
-                    return;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-            const v4u v = *(const MK_LDS v4u *)(rb + (g % ring) * GRANULE + lane * 16);
-            const uint32_t e = (uint32_t)g * 256u + lane * 4u;
-            if (variant == 4)
-                bad += (v.x ^ v.y ^ v.z ^ v.w) == 0x12345678u;
-            else
-                bad += (v.x != src[e]) + (v.y != src[e + 1]) + (v.z != src[e + 2]) + (v.w != src[e + 3]);
-            ++seen;
-            const int gn = g + NC;
-            if (lane == 0) lds_st(misc + M_WPOS + w, (uint32_t)(gn < n ? gn : n));
-        }
-        if (lane == 0) lds_st(misc + M_WPOS + w, (uint32_t)n);
-        bad = (int)wave_sum((float)bad);
-        if (lane == 0) {
-            atomicAdd(errs, bad);
-            atomicAdd(errs + 1, seen);
-        }
-    }
-}
-
-hipError_t ring_probe(const void *src, int n, int ring, int depth, int variant, int32_t *errs, int blocks) {
-    const int lds = MISC_BYTES + ring * GRANULE;
-    hipError_t e = hipFuncSetAttribute((const void *)mk_ring_probe, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mk_ring_probe, dim3(blocks), dim3(BLOCK_THREADS), lds, 0, (const uint32_t *)src, n, ring,
-                       depth, variant, (int64_t)1 << 22, errs);
-    return hipGetLastError();
-}
-
-// Cross-XCD message-passing litmus. Workgroup 2k writes, workgroup 2k+1 (on
-// another XCD under the round-robin placement) reads. Per round r the writer
-// stores r into n words, releases at agent scope and raises a flag; the reader
-// first reads the words (planting possibly stale copies in its caches), then
-// waits for the flag, acquires at agent scope and reads them again with plain
-// loads (counted into res[0]) and with device-coherent loads (res[1]); then it
-// acknowledges the round. res[2] counts watchdog expiries.
-__global__ __launch_bounds__(256) void mk_litmus(int32_t *data, int32_t *flags, int n, int rounds, int64_t watchdog,
-                                                 int32_t *res) {
-    const int pair = blockIdx.x >> 1, role = blockIdx.x & 1, tid = threadIdx.x;
-    int32_t *d = data + (size_t)pair * n;
-    int32_t *flag = flags + pair * 64, *ack = flags + pair * 64 + 32;
-    int stale_plain = 0, stale_coh = 0, sink = 0;
-    for (int r = 1; r <= rounds; ++r) {
-        if (role == 0) {
-            if (tid == 0) {
-                int64_t spins = 0;
-                while (__hip_atomic_load(ack, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < r - 1) {
-                    if (++spins > watchdog) {
-                        atomicAdd(res + 2, 1);
-                        __hip_atomic_store(flag, 1 << 30, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-            }
-            __syncthreads();
-            for (int i = tid; i < n; i += 256) d[i] = r;
-            wait_vmcnt<0>();
-            __syncthreads();
-            if (tid == 0) {
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-                __hip_atomic_store(flag, r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        } else {
-            for (int i = tid; i < n; i += 256) sink += d[i];
-            if (tid == 0) {
-                int64_t spins = 0;
-                while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < r) {
-                    if (++spins > watchdog) {
-                        atomicAdd(res + 2, 1);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                wait_vmcnt<0>();
-            }
-            __syncthreads();
-            for (int i = tid; i < n; i += 256) {
-                stale_plain += d[i] != r;
-                stale_coh += __hip_atomic_load(d + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != r;
-            }
-            wait_vmcnt<0>();
-            __syncthreads();
-            if (tid == 0) __hip_atomic_store(ack, r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-    if (stale_plain) atomicAdd(res, stale_plain);
-    if (stale_coh) atomicAdd(res + 1, stale_coh);
-    if (sink == 0x7fffffff) res[3] = sink;
-}
-
-hipError_t litmus(int pairs, int n, int rounds, int32_t *data, int32_t *flags, int32_t *res) {
-    void *args[] = {&data, &flags, &n, &rounds, nullptr, &res};
-    int64_t wd = (int64_t)1 << 22;
-    args[4] = &wd;
-    hipError_t e = hipLaunchCooperativeKernel((const void *)mk_litmus, dim3(2 * pairs), dim3(256), args, 0, nullptr);
-    if (e != hipSuccess) return e;
-    return hipDeviceSynchronize();
-}
-
-// Plain HBM streaming read: every thread sums 16-byte loads; the achievable
-// read bandwidth of the chip.
-__global__ __launch_bounds__(256) void mk_stream_probe(const v4u *src, size_t n16, uint32_t *out) {
-    uint32_t acc = 0;
-    const size_t stride = (size_t)gridDim.x * 256;
-    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const v4u a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
-    }
-    for (; i < n16; i += stride) {
-        const v4u a = src[i];
-        acc ^= a.x ^ a.y ^ a.z ^ a.w;
-    }
-    if (acc == 0x9e3779b9u) out[0] = acc;
-}
-
-hipError_t stream_probe(const void *src, size_t bytes, int blocks, uint32_t *out) {
-    hipLaunchKernelGGL(mk_stream_probe, dim3(blocks), dim3(256), 0, 0, (const v4u *)src, bytes / 16, out);
-    return hipGetLastError();
-}
-
-hipError_t setup_megakernel(int lds_bytes) {
-    return hipFuncSetAttribute((const void *)mk_megakernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-}
-
-hipError_t megakernel_occupancy(int lds_bytes, int *blocks_per_cu) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void *)mk_megakernel, BLOCK_THREADS,
-                                                        lds_bytes);
+hipError_t megakernel_occupancy(int B, int G, int lds_bytes, int *blocks_per_cu) {
+    const void *k = kernel_for(B, G);
+    if (!k) return hipErrorInvalidValue;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, k, BLOCK_THREADS, lds_bytes);
 }
 
 hipError_t launch_megakernel(const KParams &p, int lds_bytes, hipStream_t s) {
+    const void *k = kernel_for(p.B, p.nq / p.nkv);
+    if (!k) return hipErrorInvalidValue;
     KParams arg = p;
     void *args[] = {&arg};
-    return hipLaunchCooperativeKernel((const void *)mk_megakernel, dim3(p.n_cus), dim3(BLOCK_THREADS), args,
-                                      (unsigned)lds_bytes, s);
+    return hipLaunchCooperativeKernel(k, dim3(p.n_cus), dim3(BLOCK_THREADS), args, (unsigned)lds_bytes, s);
 }
 
 }  // namespace mk

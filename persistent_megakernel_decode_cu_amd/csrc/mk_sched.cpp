@@ -3,8 +3,8 @@
 // "Inference MegaKernel" (shaojiemike.top):
 //   - "unified framework": kernel graph -> tile/task graph -> per-SM queue +
 //     event counters -> resident worker; the capacity obligation (queues,
-//     rings and K/V pages must cover the configured maximum) and the
-//     resource obligation (the largest body must not stop the launch).
+//     on-chip buffers and K/V pages must cover the configured maximum) and
+//     the resource obligation (the largest body must not stop the launch).
 //   - "hand-written whole-model MegaKernel / principle, schedule and
 //     dataflow": start from a fixed Llama configuration, cut every op into
 //     tiles, build the dependency DAG, assign tiles statically to each SM's
@@ -20,16 +20,17 @@
 //      fill over streamed bytes, so compute units that also carry attention
 //      chunks get fewer rows of the next op), and one tile per (request, kv
 //      head, K/V chunk) for attention;
-//   2. create the events: one per (layer, kv group) for the QKV -> attention
-//      edges (only the QKV tiles whose rows feed that group bump it), one per
-//      layer for each later op boundary, and last-finisher merge counters for
-//      the attention chunks and the LM-head argmax;
+//   2. create the merge events: last-finisher counters for the attention
+//      chunks of each (layer, request, kv head), the LM-head argmax, and the
+//      end of a step without an LM head. The data edges need no event: every
+//      activation carries the step's tag, a consumer waits for the tags of
+//      exactly what it reads, and each buffer is written once per step;
 //   3. order all tiles in one global topological order (layer by layer, op
 //      by op); each compute unit's queue is the subsequence of its tiles,
 //      which makes every queue consistent with one order and so rules out
 //      deadlock while all workgroups are co-resident (progress obligation);
-//   4. encode each queue as [Q, 32] int32 words (mk_isa.h) and size the LDS
-//      split between the activation area and the weight ring.
+//   4. encode each queue as [Q, 32] int32 words (mk_isa.h) and lay out the
+//      LDS of a workgroup (residual rows, attention states, activations).
 #include "mk_sched.h"
 
 #include <algorithm>
@@ -46,15 +47,9 @@ bool k_supported(int k) { return k == 256 || (k >= 512 && k % 512 == 0); }
 
 struct Tile {
     int op = OP_END, layer = 0, r0 = 0, r1 = 0, b = 0, g = 0, c = 0, nch = 0, flags = 0;
-    std::vector<int> waits, pubs;
     int merge = -1, slot = 0, nslot = 0;
     int cu = 0;
     int64_t bytes = 0;
-};
-
-struct Ev {
-    int kind = EVK_WAIT;
-    int need = 0;
 };
 
 // Least-loaded-first: hand out n units of `unit_bytes` one at a time to the
@@ -143,13 +138,17 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     if (S < 1) return set_error(MK_EINVAL, "n_cus must be positive");
     if (desc.mode != MK_MODE_MEGAKERNEL && desc.mode != MK_MODE_UNFUSED)
         return set_error(MK_EINVAL, "unknown mode");
+    if (desc.reserved0 != 0 || desc.reserved1 != 0) return set_error(MK_EINVAL, "reserved fields must be 0");
     const int T = cfg.page_tokens, cap = cfg.max_pages_per_req * T;
     int maxlen = desc.max_kv_len > 0 ? desc.max_kv_len : cap - 1;
     if (maxlen > cap - 1 || maxlen < 0)
         return set_error(MK_ECAPACITY, "max_kv_len exceeds the page capacity of a request");
     P.max_kv_len = maxlen;
     const int nb_max = (maxlen + 1 + T - 1) / T;
-    int C = desc.attn_chunks > 0 ? desc.attn_chunks : std::max(1, ceil_div(nb_max, 16));
+    // enough chunks that one chunk's K/V blocks fit in its workgroup's
+    // prefetch window (N_COMPUTE_WAVES waves x PREFETCH_SLICES blocks)
+    int C = desc.attn_chunks > 0 ? desc.attn_chunks
+                                 : std::max(1, ceil_div(nb_max, N_COMPUTE_WAVES * PREFETCH_SLICES));
     C = std::min(C, nb_max);
     P.attn_chunks = C;
     P.n_cus = S;
@@ -158,44 +157,25 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     const int nq = cfg.n_q_heads, nkv = cfg.n_kv_heads, G = nq / nkv, QD = nq * d;
     const int QKV = (nq + 2 * nkv) * d;
 
-    // LDS split: activation area (matvec inputs of all requests, or the
-    // attention staging) + misc flags + the weight ring.
-    const int kmax = std::max(H, std::max(F, QD));
-    const int attn_floats = G * 68 + 2 * 64 + N_COMPUTE_WAVES * G * 68;
-    P.act_floats = std::max(B * ((kmax + 511) / 512 * 512), attn_floats);
-    const int act_bytes = ceil_div((int64_t)P.act_floats * 4, 1024) * 1024;
-    P.ring_granules = (LDS_LIMIT - MISC_BYTES - act_bytes) / GRANULE;
-    if (desc.ring_kib < 0) return set_error(MK_EINVAL, "ring_kib must be >= 0");
-    if (desc.dma_inflight < 0 || desc.dma_inflight > 57) return set_error(MK_EINVAL, "dma_inflight must be in 0..57");
-    if (desc.ring_kib > 0) {
-        if (desc.ring_kib > P.ring_granules)
-            return set_error(MK_ECAPACITY, "ring_kib exceeds the LDS left next to the activation area");
-        P.ring_granules = desc.ring_kib;
-    }
-    P.lds_bytes = MISC_BYTES + act_bytes + P.ring_granules * GRANULE;
-
     if (desc.mode == MK_MODE_UNFUSED) {
         P.launches = unfused_launches(cfg);
         P.n_lm_slots = cfg.has_embed ? ceil_div(cfg.vocab, 64) : 0;
         return MK_OK;
     }
     P.launches = 1;
-
-    // largest unit a compute wave holds in the ring at once
-    const int max_unit = std::max({ceil_div((int64_t)2 * H * 2, GRANULE), ceil_div((int64_t)F * 2, GRANULE),
-                                   ceil_div((int64_t)QD * 2, GRANULE), ceil_div((int64_t)2 * T * d * 2, GRANULE)});
-    if (P.ring_granules < 2 * max_unit + 2)
-        return set_error(MK_ECAPACITY, "batch too large: the LDS ring cannot hold two units of the largest op "
-                                       "next to the activation area (" + std::to_string(P.act_floats * 4) + " B)");
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return set_error(MK_EINVAL, "the resident interpreter needs n_q_heads / n_kv_heads in {1, 2, 4, 8}");
 
     std::vector<Tile> tiles;
-    std::vector<Ev> evs;
-    auto new_ev = [&](int kind) { evs.push_back(Ev{kind, 0}); return (int)evs.size() - 1; };
+    std::vector<int> ev_need;  // merge events
+    auto new_merge = [&](int need) {
+        ev_need.push_back(need);
+        return (int)ev_need.size() - 1;
+    };
     std::vector<int64_t> cum(S, 0);
 
     // rows of one matvec op, one tile per compute unit that receives rows
-    auto matvec_op = [&](int op, int layer, int rows, int64_t unit_bytes, const std::vector<int> &waits,
-                         int flags) -> std::vector<int> {
+    auto matvec_op = [&](int op, int layer, int rows, int64_t unit_bytes, int flags) -> std::vector<int> {
         std::vector<int> cnt = fill_units(rows, unit_bytes, cum);
         std::vector<int> ids;
         int r = 0;
@@ -207,7 +187,6 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
             t.r0 = r;
             t.r1 = r + cnt[c];
             t.cu = c;
-            t.waits = waits;
             t.flags = flags;
             t.bytes = (int64_t)cnt[c] * unit_bytes;
             r += cnt[c];
@@ -217,43 +196,14 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
         return ids;
     };
 
-    int ev_prev = -1;  // event: residual stream of this layer is complete
     for (int l = 0; l < L; ++l) {
         const int first = l == 0 ? F_X_FROM_INPUT : 0;
-        // --- QKV
-        std::vector<int> w0;
-        if (ev_prev >= 0) w0.push_back(ev_prev);
-        std::vector<int> qkv_ids = matvec_op(OP_QKV, l, QKV, (int64_t)H * 2, w0, first);
-        // per-group events when every tile feeds few groups, else one event
-        auto groups_of = [&](const Tile &t) {
-            std::vector<int> gs;
-            for (int g = 0; g < nkv; ++g) {
-                const int rq0 = g * G * d, rq1 = (g + 1) * G * d;
-                const int rk0 = QD + g * d, rk1 = rk0 + d;
-                const int rv0 = QD + nkv * d + g * d, rv1 = rv0 + d;
-                auto hit = [&](int a, int b) { return t.r0 < b && a < t.r1; };
-                if (hit(rq0, rq1) || hit(rk0, rk1) || hit(rv0, rv1)) gs.push_back(g);
-            }
-            return gs;
-        };
-        bool per_group = true;
-        for (int id : qkv_ids)
-            if ((int)groups_of(tiles[id]).size() > MAX_PUB) per_group = false;
-        std::vector<int> ev_qkv(nkv);
-        if (per_group) {
-            for (int g = 0; g < nkv; ++g) ev_qkv[g] = new_ev(EVK_WAIT);
-            for (int id : qkv_ids)
-                for (int g : groups_of(tiles[id])) tiles[id].pubs.push_back(ev_qkv[g]);
-        } else {
-            int e = new_ev(EVK_WAIT);
-            for (int g = 0; g < nkv; ++g) ev_qkv[g] = e;
-            for (int id : qkv_ids) tiles[id].pubs.push_back(e);
-        }
-        // --- attention chunks; the last chunk of each (b, g) to finish merges
-        const int ev_attn = new_ev(EVK_WAIT);
+        matvec_op(OP_QKV, l, QKV, (int64_t)H * 2, first);
+        // attention chunks; with several chunks the last of each (b, g) to
+        // finish merges them
         for (int b = 0; b < B; ++b)
             for (int g = 0; g < nkv; ++g) {
-                const int ev_merge = new_ev(EVK_MERGE);
+                const int ev = C > 1 ? new_merge(C) : -1;
                 for (int c = 0; c < C; ++c) {
                     Tile t;
                     t.op = OP_ATTN;
@@ -262,9 +212,7 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
                     t.g = g;
                     t.c = c;
                     t.nch = C;
-                    t.waits = {ev_qkv[g]};
-                    t.pubs = {ev_attn};
-                    t.merge = ev_merge;
+                    t.merge = ev;
                     t.slot = c;
                     t.nslot = C;
                     int lo, hi;
@@ -275,24 +223,15 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
                     tiles.push_back(t);
                 }
             }
-        // --- O projection + residual
-        const int ev_o = new_ev(EVK_WAIT);
-        for (int id : matvec_op(OP_OPROJ, l, H, (int64_t)QD * 2, {ev_attn}, first)) tiles[id].pubs.push_back(ev_o);
-        // --- up/gate + SiLU
-        const int ev_ug = new_ev(EVK_WAIT);
-        for (int id : matvec_op(OP_UPGATE, l, F, (int64_t)H * 4, {ev_o}, 0)) tiles[id].pubs.push_back(ev_ug);
-        // --- down + residual
+        matvec_op(OP_OPROJ, l, H, (int64_t)QD * 2, first);
+        matvec_op(OP_UPGATE, l, F, (int64_t)H * 4, 0);
         const bool last = l == L - 1;
-        std::vector<int> down_ids = matvec_op(OP_DOWN, l, H, (int64_t)F * 2, {ev_ug}, last ? F_WRITE_HIDDEN : 0);
-        if (!last || cfg.has_embed) {
-            const int ev_d = new_ev(EVK_WAIT);
-            for (int id : down_ids) tiles[id].pubs.push_back(ev_d);
-            ev_prev = ev_d;
-        } else {
-            const int ev_fin = new_ev(EVK_MERGE);
+        std::vector<int> down_ids = matvec_op(OP_DOWN, l, H, (int64_t)F * 2, last ? F_WRITE_HIDDEN : 0);
+        if (last && !cfg.has_embed) {  // the last down-projection tile to finish ends the step
+            const int ev = new_merge((int)down_ids.size());
             for (size_t i = 0; i < down_ids.size(); ++i) {
                 Tile &t = tiles[down_ids[i]];
-                t.merge = ev_fin;
+                t.merge = ev;
                 t.slot = (int)i;
                 t.nslot = (int)down_ids.size();
                 t.flags |= F_STEP_FINAL;
@@ -300,29 +239,15 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
         }
     }
     if (cfg.has_embed) {
-        std::vector<int> lm_ids = matvec_op(OP_LMHEAD, L, cfg.vocab, (int64_t)H * 2, {ev_prev}, F_STEP_FINAL);
-        const int ev_lm = new_ev(EVK_MERGE);
+        std::vector<int> lm_ids = matvec_op(OP_LMHEAD, L, cfg.vocab, (int64_t)H * 2, F_STEP_FINAL);
+        const int ev = new_merge((int)lm_ids.size());
         for (size_t i = 0; i < lm_ids.size(); ++i) {
             Tile &t = tiles[lm_ids[i]];
-            t.merge = ev_lm;
+            t.merge = ev;
             t.slot = (int)i;
             t.nslot = (int)lm_ids.size();
         }
         P.n_lm_slots = (int)lm_ids.size();
-    }
-
-    // event needs: producers per step
-    for (const Tile &t : tiles) {
-        if (t.op == OP_ATTN) continue;  // attention publishes once per (b, g), below
-        for (int e : t.pubs) evs[e].need++;
-    }
-    for (const Tile &t : tiles)
-        if (t.op == OP_ATTN && t.c == 0) evs[t.pubs[0]].need++;
-    for (const Tile &t : tiles)
-        if (t.merge >= 0) evs[t.merge].need = t.nslot;
-    for (const Tile &t : tiles) {
-        if ((int)t.waits.size() > MAX_WAIT || (int)t.pubs.size() > MAX_PUB)
-            return set_error(MK_ECAPACITY, "instruction has too many waits or completions");
     }
 
     // per-CU queues in the global order
@@ -333,6 +258,7 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     P.Q = Q;
     P.n_instr = (int)tiles.size();
     P.queue.assign((size_t)S * Q * INSTR_WORDS, 0);
+    int max_rows_x = 1;  // residual rows an O- or down-projection tile stages
     for (int c = 0; c < S; ++c) {
         int64_t bytes = 0;
         for (size_t k = 0; k < per_cu[c].size(); ++k) {
@@ -348,28 +274,49 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
             w[W_C] = t.c;
             w[W_NCH] = t.nch;
             w[W_FLAGS] = t.flags;
-            w[W_NWAIT] = (int)t.waits.size();
-            for (size_t j = 0; j < t.waits.size(); ++j) w[W_WAIT + j] = t.waits[j];
-            w[W_NPUB] = (int)t.pubs.size();
-            for (size_t j = 0; j < t.pubs.size(); ++j) w[W_PUB + j] = t.pubs[j];
             w[W_MERGE] = t.merge;
             w[W_SLOT] = t.slot;
             w[W_NSLOT] = t.nslot;
             w[W_SEQ] = id;
             bytes += t.bytes;
+            if (t.op == OP_OPROJ || t.op == OP_DOWN) max_rows_x = std::max(max_rows_x, t.r1 - t.r0);
         }
         // END is the zero-filled word after the last instruction
         P.stream_total += bytes;
         P.stream_max_cu = std::max(P.stream_max_cu, bytes);
     }
-    P.n_events = (int)evs.size();
+    P.n_events = (int)ev_need.size();
     P.n_counters = P.n_events;
     P.events.assign((size_t)P.n_events * EV_WORDS, 0);
     for (int e = 0; e < P.n_events; ++e) {
         P.events[(size_t)e * EV_WORDS + EV_CTR] = e;
-        P.events[(size_t)e * EV_WORDS + EV_NEED] = evs[e].need;
-        P.events[(size_t)e * EV_WORDS + EV_KIND] = evs[e].kind;
+        P.events[(size_t)e * EV_WORDS + EV_NEED] = ev_need[e];
+        P.events[(size_t)e * EV_WORDS + EV_KIND] = EVK_MERGE;
     }
+
+    // LDS layout (capacity obligation: everything a tile stages must fit)
+    const int NBP = B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8;  // requests the interpreter is compiled for
+    const int kmax = std::max(H, std::max(F, QD));
+    P.act_stride = (kmax + 511) / 512 * 512;
+    P.xrow_stride = (max_rows_x + 3) / 4 * 4;
+    const int64_t part_floats = std::max<int64_t>((int64_t)N_COMPUTE_WAVES * G * ATTN_WAVE_PART,
+                                                  (int64_t)C * G * ATTN_PART);
+    const int64_t act_floats = std::max<int64_t>({(int64_t)NBP * P.act_stride, (int64_t)G * 64 + 64,
+                                                  (int64_t)P.n_lm_slots * B * 2});
+    auto up256 = [](int64_t x) { return (x + 255) / 256 * 256; };
+    const int64_t xrow_off = MISC_BYTES;
+    const int64_t part_off = xrow_off + up256((int64_t)NBP * P.xrow_stride * 4);
+    const int64_t act_off = part_off + up256(part_floats * 4);
+    const int64_t lds = act_off + up256(act_floats * 4);
+    if (lds > LDS_LIMIT)
+        return set_error(MK_ECAPACITY, "a tile's on-chip staging needs " + std::to_string(lds) +
+                                           " bytes of LDS (limit " + std::to_string(LDS_LIMIT) +
+                                           "): the activation area holds " + std::to_string(NBP) + " x " +
+                                           std::to_string(P.act_stride) + " floats");
+    P.xrow_off = (int)xrow_off;
+    P.part_off = (int)part_off;
+    P.act_off = (int)act_off;
+    P.lds_bytes = (int)lds;
     return MK_OK;
 }
 
@@ -409,7 +356,7 @@ int mk_plan_info(const mk_plan *p, mk_schedule_info *out) {
     out->n_events = P.n_events;
     out->n_counters = P.n_counters;
     out->attn_chunks = P.attn_chunks;
-    out->ring_granules = P.ring_granules;
+    out->prefetch_slices = mk::PREFETCH_SLICES;
     out->lds_bytes = P.lds_bytes;
     out->block_threads = mk::BLOCK_THREADS;
     out->stream_bytes_max_cu = P.stream_max_cu;

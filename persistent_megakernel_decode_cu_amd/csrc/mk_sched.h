@@ -18,7 +18,10 @@ struct Plan {
     int n_cus = 0, Q = 0, n_instr = 0, n_events = 0, n_counters = 0;
     int attn_chunks = 0;
     int max_kv_len = 0;
-    int act_floats = 0, ring_granules = 0, lds_bytes = 0;
+    // LDS layout of a resident workgroup (bytes): misc | residual rows |
+    // attention states / merge staging | activation area
+    int xrow_off = 0, part_off = 0, act_off = 0, lds_bytes = 0;
+    int xrow_stride = 0, act_stride = 0;  // floats per request
     int n_lm_slots = 0;        // LM-head tiles (partial argmax slots)
     std::vector<int32_t> queue;   // [n_cus, Q, INSTR_WORDS]
     std::vector<int32_t> events;  // [n_events, EV_WORDS]
@@ -29,8 +32,8 @@ struct Plan {
 // Shape checks shared by mk_create and the planner.
 int check_config(const mk_config &cfg);
 
-// Bytes one instruction streams through its compute unit's LDS ring, for a
-// request whose current length is `kv_len` (only ATTN depends on it).
+// Bytes one instruction streams (weights or K/V blocks) for a request whose
+// current length is `kv_len` (only ATTN depends on it).
 int64_t instr_stream_bytes(const mk_config &cfg, const int32_t *ins, int kv_len);
 
 // K/V blocks [lo, hi) of chunk c out of nch for a request of length n+1.

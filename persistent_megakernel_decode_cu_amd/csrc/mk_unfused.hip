@@ -141,7 +141,7 @@ __global__ __launch_bounds__(UF_THREADS) void uf_rope_append(KParams P, int laye
         float out = xi;
         if (t < P.nq + P.nkv) {
             const float xp = src[lane ^ 32];
-            out = lane < 32 ? xi * cs.x - xp * cs.y : xi * cs.x + xp * cs.y;
+            out = rope_rotate(xi, xp, cs, lane < 32);
         }
         if (t < P.nq) {
             qrot[(int64_t)b * QD + t * 64 + lane] = out;
@@ -154,40 +154,45 @@ __global__ __launch_bounds__(UF_THREADS) void uf_rope_append(KParams P, int laye
     }
 }
 
-// One (chunk, kv head, request) per block; waves take K/V blocks round-robin.
-__global__ __launch_bounds__(UF_THREADS) void uf_attn(KParams P, int layer, const float *qrot) {
-    __shared__ float q[MAX_G * 68];
-    __shared__ float part[UF_WAVES * MAX_G * 68];
+// One (chunk, kv head, request) per workgroup of N_COMPUTE_WAVES waves that
+// take K/V blocks round-robin and merge their states in wave order: the same
+// split and lane layout as an attention tile of the resident interpreter.
+constexpr int UF_ATTN_THREADS = N_COMPUTE_WAVES * 64;
+
+template <int G>
+__global__ __launch_bounds__(UF_ATTN_THREADS) void uf_attn(KParams P, int layer, const float *qrot) {
+    constexpr int NW = N_COMPUTE_WAVES;
+    __shared__ float q[MAX_G * 64];
+    __shared__ float part[NW * MAX_G * ATTN_WAVE_PART];
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, nch = gridDim.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int G = P.nq / P.nkv;
     const int p = P.kv_lens[b];
     if (p < 0 || p >= P.T * P.max_pages) return;  // flagged by uf_rope_append
-    for (int i = threadIdx.x; i < G * 64; i += UF_THREADS)
-        q[(i >> 6) * 68 + (i & 63)] = qrot[(int64_t)b * P.nq * 64 + (g * G) * 64 + i];
+    for (int i = threadIdx.x; i < G * 64; i += UF_ATTN_THREADS) q[i] = qrot[(int64_t)b * P.nq * 64 + (g * G) * 64 + i];
     __syncthreads();
     const int nb = (p + 1 + 15) >> 4;
     const int blo = (int)((int64_t)c * nb / nch), bhi = (int)((int64_t)(c + 1) * nb / nch);
     const size_t layer_pool = (size_t)P.n_pages * P.nkv * 16 * 64;
-    AttnState st;
-    attn_init(st);
-    for (int blk = blo + wave; blk < bhi; blk += UF_WAVES) {
+    AttnLaneT<G> st;
+    attn_lane_init(st);
+    const int t0 = lane >> 3;
+    for (int blk = blo + wave; blk < bhi; blk += NW) {
         int page = P.page_table[(int64_t)b * P.max_pages + blk];
         if (page < 0 || page >= P.n_pages) page = 0;
-        const uint16_t *kb = P.k_pool + (size_t)layer * layer_pool + ((size_t)page * P.nkv + g) * 1024;
-        const uint16_t *vb = P.v_pool + (size_t)layer * layer_pool + ((size_t)page * P.nkv + g) * 1024;
-        const int nvalid = min(16, p + 1 - blk * 16);
-        attn_block(
-            st, (const MK_LDS float *)q, G, nvalid, lane,
-            [&](int j, int ch) { return *(const v4u *)(kb + j * 64 + ch * 8); },
-            [&](int j, int qq) { return *(const v2u *)(vb + j * 64 + qq * 4); });
+        const size_t off = (size_t)layer * layer_pool + ((size_t)page * P.nkv + g) * 1024;
+        const v4u *kb = (const v4u *)(P.k_pool + off);
+        const v4u *vb = (const v4u *)(P.v_pool + off);
+        const int pos0 = blk * 16 + t0;
+        attn_lane_block(st, (const MK_LDS float *)q, lane, kb[lane], kb[64 + lane], vb[lane], vb[64 + lane],
+                        pos0 <= p, pos0 + 8 <= p);
     }
-    attn_store(st, (MK_LDS float *)(part + wave * G * 68), G, lane);
+    attn_lane_store(st, (MK_LDS float *)(part + wave * G * ATTN_WAVE_PART), lane);
     __syncthreads();
     if (wave == 0) {
         for (int hq = 0; hq < G; ++hq) {
             float o, m, l;
-            merge_parts(nullptr, (const MK_LDS float *)(part + hq * 68), UF_WAVES, G * 68, lane, &o, &m, &l);
+            merge_parts(nullptr, (const MK_LDS float *)(part + hq * ATTN_WAVE_PART), NW, G * ATTN_WAVE_PART, lane, &o,
+                        &m, &l);
             float *dst = P.attn_part + ((((int64_t)b * P.nkv + g) * nch + c) * G + hq) * ATTN_PART_STRIDE;
             dst[lane] = o;
             if (lane == 0) {
@@ -284,7 +289,19 @@ hipError_t launch_unfused(const KParams &p, float *u, float *qrot, hipStream_t s
         MK_TRY(uf_mv_any(p, OP_QKV, l, first, u, s));
         hipLaunchKernelGGL(uf_rope_append, dim3(p.B), dim3(UF_THREADS), 0, s, p, l, qrot);
         MK_TRY(hipGetLastError());
-        hipLaunchKernelGGL(uf_attn, dim3(nch, p.nkv, p.B), dim3(UF_THREADS), 0, s, p, l, (const float *)qrot);
+        {
+            const dim3 grid(nch, p.nkv, p.B), blk(UF_ATTN_THREADS);
+            switch (p.nq / p.nkv) {
+                case 1: hipLaunchKernelGGL(uf_attn<1>, grid, blk, 0, s, p, l, (const float *)qrot); break;
+                case 2: hipLaunchKernelGGL(uf_attn<2>, grid, blk, 0, s, p, l, (const float *)qrot); break;
+                case 3: hipLaunchKernelGGL(uf_attn<3>, grid, blk, 0, s, p, l, (const float *)qrot); break;
+                case 4: hipLaunchKernelGGL(uf_attn<4>, grid, blk, 0, s, p, l, (const float *)qrot); break;
+                case 5: hipLaunchKernelGGL(uf_attn<5>, grid, blk, 0, s, p, l, (const float *)qrot); break;
+                case 6: hipLaunchKernelGGL(uf_attn<6>, grid, blk, 0, s, p, l, (const float *)qrot); break;
+                case 7: hipLaunchKernelGGL(uf_attn<7>, grid, blk, 0, s, p, l, (const float *)qrot); break;
+                default: hipLaunchKernelGGL(uf_attn<8>, grid, blk, 0, s, p, l, (const float *)qrot); break;
+            }
+        }
         MK_TRY(hipGetLastError());
         hipLaunchKernelGGL(uf_attn_merge, dim3(p.nkv, p.B), dim3(64), 0, s, p, nch);
         MK_TRY(hipGetLastError());

@@ -69,9 +69,24 @@ def test_capacity_checks():
         _mk.Plan(cfg_of(w, max_batch=2), _mk.MkScheduleDesc(3, 8, 0, 0, 0, 0, 0, 0, 0))  # batch > max_batch
     assert e.value.code == _mk.MK_EINVAL
     big = synthetic.workload("1b-b8-paged")
-    with pytest.raises(_mk.MkError) as e:   # 8 activation rows of 8192 fp32 do not fit next to the ring
+    with pytest.raises(_mk.MkError) as e:   # 8 activation rows of 8192 fp32 do not fit in the LDS
         _mk.Plan(cfg_of(big, max_batch=8, pages=258), _mk.MkScheduleDesc(8, 256, 0, 0, 0, 0, 0, 0, 0))
     assert e.value.code == _mk.MK_ECAPACITY
+    # the one-kernel-per-op mode has no such limit
+    _mk.Plan(cfg_of(big, max_batch=8, pages=258), _mk.MkScheduleDesc(8, 256, 1, 0, 0, 0, 0, 0, 0))
+    with pytest.raises(_mk.MkError) as e:   # reserved fields
+        _mk.Plan(cfg_of(w), _mk.MkScheduleDesc(1, 8, 0, 0, 0, 0, 0, 1, 0))
+    assert e.value.code == _mk.MK_EINVAL
+
+
+def test_head_grouping_of_the_resident_interpreter():
+    w = synthetic.workload("tiny-2l")
+    cfg = cfg_of(w)
+    cfg.n_q_heads, cfg.n_kv_heads = 24, 8   # 3 q heads per kv head: no interpreter variant
+    with pytest.raises(_mk.MkError) as e:
+        _mk.Plan(cfg, _mk.MkScheduleDesc(1, 8, 0, 0, 0, 0, 0, 0, 0))
+    assert e.value.code == _mk.MK_EINVAL
+    _mk.Plan(cfg, _mk.MkScheduleDesc(1, 8, 1, 0, 0, 0, 0, 0, 0))  # the unfused path takes any grouping
 
 
 def test_create_reports_hip_error_without_gpu():

@@ -1,7 +1,7 @@
-"""Host scheduler: the encoded queues of every workload pass the
-independent validator (coverage, event counts, hazard ordering) and the
-randomised simulator (no deadlock over many steps); injected faults are
-caught and name the blocked compute unit."""
+"""Host scheduler: the encoded queues of every workload pass the independent
+validator (coverage, merge events, every input produced earlier in the global
+order) and the randomised simulator (no deadlock over many steps); injected
+faults are caught and name the blocked compute unit."""
 import numpy as np
 import pytest
 
@@ -37,9 +37,18 @@ def test_plans_validate(name, n_cus):
     assert p.info.lds_bytes <= 160 * 1024
 
 
-def test_tiny_batched_plan_validates():
-    w, B, maxlen, p = plan_for("tiny-2l", 16, batch=4)
+@pytest.mark.parametrize("batch,n_cus,chunks", [(4, 16, 0), (2, 8, 3), (3, 5, 1)])
+def test_tiny_batched_plans_validate(batch, n_cus, chunks):
+    w, B, maxlen, p = plan_for("tiny-2l", n_cus, batch=batch, chunks=chunks)
+    sched_check.validate(w, batch, p.queue, p.events, p.info.attn_chunks, maxlen)
+
+
+def test_1b_batch4_fits_and_batch8_reports_capacity():
+    w, B, maxlen, p = plan_for("1b-kv1024", 256, batch=4)
     sched_check.validate(w, 4, p.queue, p.events, p.info.attn_chunks, maxlen)
+    with pytest.raises(_mk.MkError) as ex:
+        plan_for("1b-kv1024", 256, batch=8)
+    assert ex.value.code == _mk.MK_ECAPACITY and "LDS" in str(ex.value)
 
 
 def test_streamed_bytes_match_the_byte_model():
@@ -51,39 +60,60 @@ def test_streamed_bytes_match_the_byte_model():
     assert p.info.stream_bytes_max_cu <= 1.02 * p.info.stream_bytes_total / 256
 
 
-@pytest.mark.parametrize("name,n_cus,steps", [("tiny-2l", 8, 10000), ("tiny-2l", 256, 200),
-                                              ("1b-layer-kv512", 64, 200), ("1b-kv1024", 256, 2)])
+def test_auto_chunks_fit_the_prefetch_window():
+    # one chunk's K/V blocks fit the waves' register slots (8 waves x 4)
+    for name in ("1b-kv1024", "1b-kv8192"):
+        w, B, maxlen, p = plan_for(name, 256)
+        nb = (maxlen + 1 + 15) // 16
+        assert -(-nb // p.info.attn_chunks) <= 8 * p.info.prefetch_slices
+
+
+@pytest.mark.parametrize("name,n_cus,steps", [("tiny-2l", 8, 2000), ("tiny-2l", 256, 50),
+                                              ("1b-layer-kv512", 64, 20), ("1b-kv1024", 256, 1)])
 def test_simulator_no_deadlock(name, n_cus, steps):
     w, B, maxlen, p = plan_for(name, n_cus)
-    ctr = sched_check.simulate(p.queue, p.events, steps, seed=n_cus)
-    need = p.events[:, sched_check.ISA["EV_NEED"]]
-    assert np.array_equal(ctr[p.events[:, 0]], need * steps)
+    ctr = sched_check.simulate(w, B, p.queue, p.events, steps, seed=n_cus)
+    if len(p.events):
+        assert np.array_equal(ctr[: len(p.events)], p.events[:, sched_check.ISA["EV_NEED"]] * steps)
 
 
 def test_simulator_reports_injected_deadlocks():
-    w, B, maxlen, p = plan_for("tiny-2l", 8)
+    w, B, maxlen, p = plan_for("tiny-2l", 8, chunks=2)
     ins = sched_check.decode(p.queue)
-    waited = next(i for i in ins if i.waits)
-    e = waited.waits[0]
-    need = int(p.events[e, sched_check.ISA["EV_NEED"]])
+    I = sched_check.ISA
+    # a merge that can never complete: its output is never written
+    merged = next(i for i in ins if i.op == I["OP_ATTN"])
+    need = int(p.events[merged.merge, I["EV_NEED"]])
     with pytest.raises(sched_check.Deadlock) as ex:
-        sched_check.simulate(p.queue, p.events, 3, need_override={e: need + 1})
+        sched_check.simulate(w, B, p.queue, p.events, 3, need_override={merged.merge: need + 1})
     assert "blocked" in str(ex.value)
-    producer = next(i for i in ins if i.pubs and i.merge < 0)
+    # a producer whose rows never arrive
+    producer = next(i for i in ins if i.op == I["OP_UPGATE"])
     with pytest.raises(sched_check.Deadlock):
-        sched_check.simulate(p.queue, p.events, 3, drop_pub=(producer.seq, producer.pubs[0]))
+        sched_check.simulate(w, B, p.queue, p.events, 3, drop=producer.seq)
 
 
-def test_validator_catches_a_missing_edge():
+def test_validator_catches_an_out_of_order_consumer():
     w, B, maxlen, p = plan_for("tiny-2l", 8)
     q = p.queue.copy()
     I = sched_check.ISA
-    # drop the wait of the first UPGATE instruction: its norm input is unordered
+    # move the first UPGATE before every O projection in the global order
+    ups = [(cu, pc) for cu in range(q.shape[0]) for pc in range(q.shape[1]) if q[cu, pc, I["W_OP"]] == I["OP_UPGATE"]]
+    cu, pc = ups[0]
+    q[cu, pc, I["W_SEQ"]], q[cu, pc - 1, I["W_SEQ"]] = q[cu, pc - 1, I["W_SEQ"]], q[cu, pc, I["W_SEQ"]]
+    with pytest.raises(sched_check.ScheduleError):
+        sched_check.validate(w, B, q, p.events, p.info.attn_chunks, maxlen)
+
+
+def test_validator_catches_a_coverage_gap():
+    w, B, maxlen, p = plan_for("tiny-2l", 8)
+    q = p.queue.copy()
+    I = sched_check.ISA
     for cu in range(q.shape[0]):
         for pc in range(q.shape[1]):
-            if q[cu, pc, I["W_OP"]] == I["OP_UPGATE"]:
-                q[cu, pc, I["W_NWAIT"]] = 0
+            if q[cu, pc, I["W_OP"]] == I["OP_DOWN"] and q[cu, pc, I["W_R1"]] - q[cu, pc, I["W_R0"]] > 1:
+                q[cu, pc, I["W_R1"]] -= 1
                 with pytest.raises(sched_check.ScheduleError):
                     sched_check.validate(w, B, q, p.events, p.info.attn_chunks, maxlen)
                 return
-    pytest.fail("no UPGATE instruction")
+    pytest.fail("no DOWN instruction with two rows")
