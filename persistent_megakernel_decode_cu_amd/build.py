@@ -22,7 +22,15 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
           # no packed fp32 instructions in device code
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-Wno-unused-command-line-argument"]
+          "-Wno-unused-command-line-argument",
+          # the slot registers sit above the compiler's cap on purpose (mk_interp.h)
+          "-Wno-inline-asm", "-Wno-pass-failed"]
+
+
+# translation units holding the resident interpreter: their gfx950 assembly
+# is kept and checked (check_isa.py) for reads of slice registers whose
+# untracked loads may still be in flight
+INTERP = [s for s in SOURCES if s.startswith("mk_interp_b")]
 
 
 def _compile(src: str) -> str:
@@ -35,10 +43,24 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _assembly(src: str) -> str:
+    out = os.path.join(BUILD_DIR, os.path.basename(src) + ".gfx950.s")
+    cmd = [HIPCC, *COMMON, "-x", "hip", "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"assembly failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return out
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
         objs = list(ex.map(_compile, SOURCES))
+        asms = list(ex.map(_assembly, INTERP))
+    from . import check_isa
+    if check_isa.main(asms) != 0:
+        raise RuntimeError("the resident interpreter reads a slice register before its load has landed "
+                           "(see the check_isa report above)")
     tmp = OUT + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

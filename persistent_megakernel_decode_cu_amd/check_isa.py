@@ -1,0 +1,113 @@
+"""Static check of the resident interpreter's compiled code (gfx950 ISA).
+
+The weight slices are loaded by inline assembly into registers the compiler
+does not allocate (v168 and up: the kernel's occupancy target caps the
+compiler below them), and the compiler does not track those loads. Reading a
+slot register while its load is in flight would return stale data, so the
+code must satisfy, and this check proves on the assembly of every kernel:
+
+1. no compiler-generated instruction names a register at or above the slot
+   base; the only instructions that do are the slice loads (marked
+   `slot_load`) and the slot copies (`slot_take`);
+2. every `slot_take` copy is preceded, on every path from the loads, by a
+   `slot_wait` (an s_waitcnt vmcnt) -- checked locally: each run of copies
+   follows a wait in the same basic block with no label in between;
+3. the kernel descriptor allocates the slot registers.
+
+Usage: python -m persistent_megakernel_decode_cu_amd.check_isa file.s ...
+"""
+from __future__ import annotations
+
+import re
+import sys
+
+SLOT_VGPR0 = 168
+_REG = re.compile(r"\bv\[(\d+):(\d+)\]|\bv(\d+)\b")
+
+
+def _regs(text):
+    out = set()
+    for m in _REG.finditer(text):
+        if m.group(3) is not None:
+            out.add(int(m.group(3)))
+        else:
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return out
+
+
+def _kernels(lines):
+    name, body = None, None
+    for l in lines:
+        m = re.match(r"^(_Z\S+):\s*(;.*)?$", l)
+        if m:
+            name, body = m.group(1), []
+            continue
+        if name is None:
+            continue
+        if l.strip().startswith(".Lfunc_end"):
+            yield name, body
+            name = None
+            continue
+        body.append(l)
+
+
+def check_kernel(body):
+    problems = []
+    waited = False   # a slot_wait seen in this basic block
+    n_load = n_take = 0
+    max_compiler = -1
+    for i, l in enumerate(body):
+        code, _, comment = l.partition(";")
+        code = code.strip()
+        if re.match(r"^\.LBB\S+:", l) or code.startswith("s_branch") or code.startswith("s_cbranch"):
+            waited = False
+            continue
+        if not code or code.startswith("."):
+            continue
+        regs = _regs(code)
+        if "slot_wait" in comment:
+            waited = True
+            continue
+        if "slot_load" in comment:
+            n_load += 1
+            if not code.startswith("buffer_load_dwordx4") or min(_regs(code.split(",")[0])) < SLOT_VGPR0:
+                problems.append(f"line {i}: malformed slot load '{code}'")
+            continue
+        if "slot_take" in comment:
+            n_take += 1
+            src = _regs(code.split(",", 1)[1])
+            if not code.startswith("v_mov_b64") or min(src) < SLOT_VGPR0:
+                problems.append(f"line {i}: malformed slot copy '{code}'")
+            if not waited:
+                problems.append(f"line {i}: slot copy without a preceding slot_wait in its block: '{code}'")
+            continue
+        if regs:
+            hi = max(regs)
+            if hi >= SLOT_VGPR0:
+                problems.append(f"line {i}: compiler instruction names a slot register: '{code}'")
+            max_compiler = max(max_compiler, hi)
+    return problems, n_load, n_take, max_compiler
+
+
+def main(paths):
+    bad = 0
+    for p in paths:
+        txt = open(p).read()
+        lines = txt.split("\n")
+        counts = {m.group(1): int(m.group(2))
+                  for m in re.finditer(r"\.name:\s+(\S+)[\s\S]*?\.vgpr_count:\s+(\d+)", txt)}
+        for name, body in _kernels(lines):
+            pr, n_load, n_take, mx = check_kernel(body)
+            vg = counts.get(name)
+            if n_load and (vg is None or vg < SLOT_VGPR0 + 64):
+                pr.append(f"kernel allocates {vg} VGPRs, below the slot registers")
+            print(f"{p}: {name}: {n_load} slot loads, {n_take} slot copies, compiler VGPRs <= v{mx}, "
+                  f"{vg} allocated: {len(pr)} problems")
+            for x in pr[:10]:
+                print("   ", x)
+            bad += len(pr)
+    return 1 if bad else 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))

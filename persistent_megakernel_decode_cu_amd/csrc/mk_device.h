@@ -88,12 +88,24 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// Butterfly sums and maxima: every lane ends with the same value, and the
+// Sum over the 64 lanes of a wave, returned to every lane (a scalar): DPP
+// row shifts by 1, 2, 4, 8 make lane 15 of each row its row's sum, two row
+// broadcasts carry rows 0 and 2 into rows 1 and 3 and then rows 0-1 into
+// rows 2-3, and lane 63 ends with the total. Every step is a VALU op; the
 // combination order is fixed, so results are bit-reproducible.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_shift0(float v) {
+    // lanes without a source (outside the row, or masked rows) read 0
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, true));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v += dpp_shift0<0x111, 0xf>(v);  // row_shr:1
+    v += dpp_shift0<0x112, 0xf>(v);  // row_shr:2
+    v += dpp_shift0<0x114, 0xf>(v);  // row_shr:4
+    v += dpp_shift0<0x118, 0xf>(v);  // row_shr:8
+    v += dpp_shift0<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_shift0<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 __device__ __forceinline__ float group16_sum(float v) {
 #pragma unroll
@@ -136,12 +148,14 @@ __device__ __forceinline__ float rope_rotate(float xi, float xp, float2 cs, bool
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// Online-softmax state of one lane for the G query heads of one kv group. A 16-position K/V block (page) is spread over the wave as 16-byte
-// chunks: lane l holds dims 8 (l % 8) .. 8 (l % 8) + 7 of positions l / 8
-// (t0) and 8 + l / 8 (t1), for K and for V. Scores are reduced over the 8
-// lanes that share a position; m and l are wave-uniform; o[h] holds the
-// lane's own positions' share of dims 8 (l % 8) .. +7, summed over the 8
-// position groups only when the state is stored.
+// Online-softmax state of one lane for the G query heads of one kv group. A
+// 16-position K/V block (page) is spread over the wave as 16-byte chunks:
+// lane l holds dims 8 (l % 8) .. 8 (l % 8) + 7 of positions l / 8 (t0) and
+// 8 + l / 8 (t1), for K and for V. A score is summed over the 8 lanes that
+// share a position (DPP within the lane group), and each lane group keeps its
+// own running max m, sum l and output share o[h] (dims 8 (l % 8) .. +7) over
+// its positions, so a block needs no exchange between lane groups; the eight
+// group states are merged once, when the wave's state is stored.
 template <int G>
 struct AttnLaneT {
     float m[G], l[G], o[G][8];
@@ -158,22 +172,17 @@ __device__ __forceinline__ void attn_lane_init(AttnLaneT<G> &s) {
     }
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the 8 lanes of a lane group: quad swaps (lane ^ 1, lane ^ 2), then
+// the half-row mirror (lane i <-> 7 - i), which pairs the two quads.
 __device__ __forceinline__ float sum8lanes(float v) {
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    return v;
-}
-__device__ __forceinline__ float sum_groups(float v) {
-    v += __shfl_xor(v, 8, 64);
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
-}
-__device__ __forceinline__ float max_groups(float v) {
-    v = fmaxf(v, __shfl_xor(v, 8, 64));
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    v = fmaxf(v, __shfl_xor(v, 32, 64));
+    v += dpp_f<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v += dpp_f<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v += dpp_f<0x141>(v);  // row_half_mirror
     return v;
 }
 
@@ -198,34 +207,48 @@ __device__ __forceinline__ void attn_lane_block(AttnLaneT<G> &st, const MK_LDS f
         float s1 = sum8lanes(dot8(k1, qa, qb)) * 0.125f;
         if (!ok0) s0 = -INFINITY;
         if (!ok1) s1 = -INFINITY;
-        const float mb = max_groups(fmaxf(s0, s1));
-        const float mnew = fmaxf(st.m[h], mb);
+        const float mnew = fmaxf(st.m[h], fmaxf(s0, s1));
         const float alpha = __expf(st.m[h] - mnew);
         const float p0 = ok0 ? __expf(s0 - mnew) : 0.0f;
         const float p1 = ok1 ? __expf(s1 - mnew) : 0.0f;
-        st.l[h] = st.l[h] * alpha + sum_groups(p0 + p1);
+        st.l[h] = st.l[h] * alpha + (p0 + p1);
 #pragma unroll
         for (int e = 0; e < 8; ++e) st.o[h][e] = fmaf(p1, vb[e], fmaf(p0, va[e], st.o[h][e] * alpha));
         st.m[h] = mnew;
     }
 }
 
-// Writes a wave's state as partials [G][ATTN_WAVE_PART] (o[64], m, l) after
-// summing o over the position groups.
+// Merges the eight lane groups' states (in a fixed butterfly order) and
+// writes the wave's state as partials [G][ATTN_WAVE_PART] (o[64], m, l).
 template <int G>
 __device__ __forceinline__ void attn_lane_store(AttnLaneT<G> &st, MK_LDS float *part, int lane) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+        float M = st.m[h];
+        M = fmaxf(M, __shfl_xor(M, 8, 64));
+        M = fmaxf(M, __shfl_xor(M, 16, 64));
+        M = fmaxf(M, __shfl_xor(M, 32, 64));
+        const float f = __expf(st.m[h] - M);
+        float l = st.l[h] * f;
+        l += __shfl_xor(l, 8, 64);
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        float o[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) st.o[h][e] = sum_groups(st.o[h][e]);
+        for (int e = 0; e < 8; ++e) {
+            o[e] = st.o[h][e] * f;
+            o[e] += __shfl_xor(o[e], 8, 64);
+            o[e] += __shfl_xor(o[e], 16, 64);
+            o[e] += __shfl_xor(o[e], 32, 64);
+        }
         if (lane < 8) {
             MK_LDS float *ph = part + h * ATTN_WAVE_PART + lane * 8;
-            *(MK_LDS v4f *)ph = v4f{st.o[h][0], st.o[h][1], st.o[h][2], st.o[h][3]};
-            *(MK_LDS v4f *)(ph + 4) = v4f{st.o[h][4], st.o[h][5], st.o[h][6], st.o[h][7]};
+            *(MK_LDS v4f *)ph = v4f{o[0], o[1], o[2], o[3]};
+            *(MK_LDS v4f *)(ph + 4) = v4f{o[4], o[5], o[6], o[7]};
         }
         if (lane == 0) {
-            part[h * ATTN_WAVE_PART + 64] = st.m[h];
-            part[h * ATTN_WAVE_PART + 65] = st.l[h];
+            part[h * ATTN_WAVE_PART + 64] = M;
+            part[h * ATTN_WAVE_PART + 65] = l;
         }
     }
 }

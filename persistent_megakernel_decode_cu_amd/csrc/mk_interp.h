@@ -236,10 +236,159 @@ __device__ __forceinline__ void cur_next(const KParams &P, const Ctx &c, Cur &k)
     cur_load(P, c, k, k.pc + 1);
 }
 
-// Issues the loads of the slice at the cursor into r: always four 16-byte
-// buffer loads per lane (two per 2 KiB half), so that the count of loads in
-// flight per slice is fixed; bytes outside the slice read as zero.
-__device__ __forceinline__ void issue(const KParams &P, const Cur &k, v4u (&r)[4], int lane) {
+// Buffer resource words for a byte range (gfx950 raw buffer, stride 0):
+// loads beyond `bytes` read as zero.
+__device__ __forceinline__ v4u rsrc_words(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return v4u{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// The slices live in registers the compiler never allocates: the kernel asks
+// for an occupancy of 3 waves per SIMD, which caps the compiler at 168 VGPRs
+// (v0-v167), and slot k occupies v[SLOT_VGPR0 + 16 k, +16). Only the inline
+// assembly below names them (their clobber lists make the kernel allocate
+// them), so no compiler-generated instruction can read, copy or spill a slot
+// while its loads are in flight; the loads are untracked by the compiler, and
+// the only wait on them is the s_waitcnt in slot_take(). check_isa.py proves
+// these properties on the compiled code.
+constexpr int SLOT_VGPR0 = 168;
+static_assert(SLOT_VGPR0 + 16 * D <= 256, "slots beyond the VGPR file");
+
+template <int K>
+__device__ __forceinline__ void slot_loads(uint32_t o, v4u ra, v4u rb);
+template <int K>
+__device__ __forceinline__ void slot_take(v2u (&x)[8], int n_wait);
+
+template <>
+__device__ __forceinline__ void slot_loads<0>(uint32_t o, v4u ra, v4u rb) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "buffer_load_dwordx4 v[168:171], %0, %1, 0 offen ; slot_load\n\t"
+        "buffer_load_dwordx4 v[172:175], %0, %1, 0 offen offset:1024 ; slot_load\n\t"
+        "buffer_load_dwordx4 v[176:179], %0, %2, 0 offen ; slot_load\n\t"
+        "buffer_load_dwordx4 v[180:183], %0, %2, 0 offen offset:1024 ; slot_load"
+        :
+        : "v"(o), "s"(ra), "s"(rb)
+        : "memory", "v168", "v169", "v170", "v171", "v172", "v173", "v174", "v175", "v176", "v177", "v178", "v179", "v180", "v181", "v182", "v183");
+}
+template <>
+__device__ __forceinline__ void slot_loads<1>(uint32_t o, v4u ra, v4u rb) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "buffer_load_dwordx4 v[184:187], %0, %1, 0 offen ; slot_load\n\t"
+        "buffer_load_dwordx4 v[188:191], %0, %1, 0 offen offset:1024 ; slot_load\n\t"
+        "buffer_load_dwordx4 v[192:195], %0, %2, 0 offen ; slot_load\n\t"
+        "buffer_load_dwordx4 v[196:199], %0, %2, 0 offen offset:1024 ; slot_load"
+        :
+        : "v"(o), "s"(ra), "s"(rb)
+        : "memory", "v184", "v185", "v186", "v187", "v188", "v189", "v190", "v191", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199");
+}
+template <>
+__device__ __forceinline__ void slot_loads<2>(uint32_t o, v4u ra, v4u rb) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "buffer_load_dwordx4 v[200:203], %0, %1, 0 offen ; slot_load\n\t"
+        "buffer_load_dwordx4 v[204:207], %0, %1, 0 offen offset:1024 ; slot_load\n\t"
+        "buffer_load_dwordx4 v[208:211], %0, %2, 0 offen ; slot_load\n\t"
+        "buffer_load_dwordx4 v[212:215], %0, %2, 0 offen offset:1024 ; slot_load"
+        :
+        : "v"(o), "s"(ra), "s"(rb)
+        : "memory", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215");
+}
+template <>
+__device__ __forceinline__ void slot_loads<3>(uint32_t o, v4u ra, v4u rb) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "buffer_load_dwordx4 v[216:219], %0, %1, 0 offen ; slot_load\n\t"
+        "buffer_load_dwordx4 v[220:223], %0, %1, 0 offen offset:1024 ; slot_load\n\t"
+        "buffer_load_dwordx4 v[224:227], %0, %2, 0 offen ; slot_load\n\t"
+        "buffer_load_dwordx4 v[228:231], %0, %2, 0 offen offset:1024 ; slot_load"
+        :
+        : "v"(o), "s"(ra), "s"(rb)
+        : "memory", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231");
+}
+template <>
+__device__ __forceinline__ void slot_take<0>(v2u (&x)[8], int n_wait) {
+    if (n_wait == 0)  // a constant at every call site
+        asm volatile("s_waitcnt vmcnt(0) ; slot_wait" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(12) ; slot_wait" ::: "memory");
+    asm volatile(
+        "v_mov_b64 %0, v[168:169] ; slot_take\n\t"
+        "v_mov_b64 %1, v[170:171] ; slot_take\n\t"
+        "v_mov_b64 %2, v[172:173] ; slot_take\n\t"
+        "v_mov_b64 %3, v[174:175] ; slot_take\n\t"
+        "v_mov_b64 %4, v[176:177] ; slot_take\n\t"
+        "v_mov_b64 %5, v[178:179] ; slot_take\n\t"
+        "v_mov_b64 %6, v[180:181] ; slot_take\n\t"
+        "v_mov_b64 %7, v[182:183] ; slot_take"
+        : "=v"(x[0]), "=v"(x[1]), "=v"(x[2]), "=v"(x[3]), "=v"(x[4]), "=v"(x[5]), "=v"(x[6]), "=v"(x[7])
+        :
+        : "memory", "v168", "v169", "v170", "v171", "v172", "v173", "v174", "v175", "v176", "v177", "v178", "v179", "v180", "v181", "v182", "v183");
+}
+template <>
+__device__ __forceinline__ void slot_take<1>(v2u (&x)[8], int n_wait) {
+    if (n_wait == 0)  // a constant at every call site
+        asm volatile("s_waitcnt vmcnt(0) ; slot_wait" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(12) ; slot_wait" ::: "memory");
+    asm volatile(
+        "v_mov_b64 %0, v[184:185] ; slot_take\n\t"
+        "v_mov_b64 %1, v[186:187] ; slot_take\n\t"
+        "v_mov_b64 %2, v[188:189] ; slot_take\n\t"
+        "v_mov_b64 %3, v[190:191] ; slot_take\n\t"
+        "v_mov_b64 %4, v[192:193] ; slot_take\n\t"
+        "v_mov_b64 %5, v[194:195] ; slot_take\n\t"
+        "v_mov_b64 %6, v[196:197] ; slot_take\n\t"
+        "v_mov_b64 %7, v[198:199] ; slot_take"
+        : "=v"(x[0]), "=v"(x[1]), "=v"(x[2]), "=v"(x[3]), "=v"(x[4]), "=v"(x[5]), "=v"(x[6]), "=v"(x[7])
+        :
+        : "memory", "v184", "v185", "v186", "v187", "v188", "v189", "v190", "v191", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199");
+}
+template <>
+__device__ __forceinline__ void slot_take<2>(v2u (&x)[8], int n_wait) {
+    if (n_wait == 0)  // a constant at every call site
+        asm volatile("s_waitcnt vmcnt(0) ; slot_wait" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(12) ; slot_wait" ::: "memory");
+    asm volatile(
+        "v_mov_b64 %0, v[200:201] ; slot_take\n\t"
+        "v_mov_b64 %1, v[202:203] ; slot_take\n\t"
+        "v_mov_b64 %2, v[204:205] ; slot_take\n\t"
+        "v_mov_b64 %3, v[206:207] ; slot_take\n\t"
+        "v_mov_b64 %4, v[208:209] ; slot_take\n\t"
+        "v_mov_b64 %5, v[210:211] ; slot_take\n\t"
+        "v_mov_b64 %6, v[212:213] ; slot_take\n\t"
+        "v_mov_b64 %7, v[214:215] ; slot_take"
+        : "=v"(x[0]), "=v"(x[1]), "=v"(x[2]), "=v"(x[3]), "=v"(x[4]), "=v"(x[5]), "=v"(x[6]), "=v"(x[7])
+        :
+        : "memory", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215");
+}
+template <>
+__device__ __forceinline__ void slot_take<3>(v2u (&x)[8], int n_wait) {
+    if (n_wait == 0)  // a constant at every call site
+        asm volatile("s_waitcnt vmcnt(0) ; slot_wait" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(12) ; slot_wait" ::: "memory");
+    asm volatile(
+        "v_mov_b64 %0, v[216:217] ; slot_take\n\t"
+        "v_mov_b64 %1, v[218:219] ; slot_take\n\t"
+        "v_mov_b64 %2, v[220:221] ; slot_take\n\t"
+        "v_mov_b64 %3, v[222:223] ; slot_take\n\t"
+        "v_mov_b64 %4, v[224:225] ; slot_take\n\t"
+        "v_mov_b64 %5, v[226:227] ; slot_take\n\t"
+        "v_mov_b64 %6, v[228:229] ; slot_take\n\t"
+        "v_mov_b64 %7, v[230:231] ; slot_take"
+        : "=v"(x[0]), "=v"(x[1]), "=v"(x[2]), "=v"(x[3]), "=v"(x[4]), "=v"(x[5]), "=v"(x[6]), "=v"(x[7])
+        :
+        : "memory", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231");
+}
+
+// Issues the loads of the slice at the cursor into slot K: always four
+// 16-byte buffer loads per lane (two per 2 KiB half), so that the count of
+// loads in flight per slot is fixed; bytes outside the slice read as zero.
+template <int K>
+__device__ __forceinline__ void issue(const KParams &P, const Cur &k, int lane) {
     const char *a = (const char *)P.wtab, *b = (const char *)P.wtab;
     uint32_t na = 0, nb = 0;
     if (k.op != OP_END && k.u < k.nu) {
@@ -263,12 +412,19 @@ __device__ __forceinline__ void issue(const KParams &P, const Cur &k, v4u (&r)[4
             b = a + 2048;
         }
     }
-    const __amdgpu_buffer_rsrc_t ra = plain_rsrc(a, na), rb = plain_rsrc(b, nb);
-    const uint32_t o = (uint32_t)lane * 16;
-    r[0] = __builtin_amdgcn_raw_buffer_load_b128(ra, o, 0, 0);
-    r[1] = __builtin_amdgcn_raw_buffer_load_b128(ra, o + 1024, 0, 0);
-    r[2] = __builtin_amdgcn_raw_buffer_load_b128(rb, o, 0, 0);
-    r[3] = __builtin_amdgcn_raw_buffer_load_b128(rb, o + 1024, 0, 0);
+    slot_loads<K>((uint32_t)lane * 16, rsrc_words(a, na), rsrc_words(b, nb));
+}
+
+// Waits until at most N vector memory operations are outstanding (N = 0 or
+// 4 (D - 1)) and copies slot K into compiler registers. With D slots issued
+// in order and four loads per slot, 4 (D - 1) waits exactly for slot K.
+template <int K, int N>
+__device__ __forceinline__ void take_slot(v4u (&r)[4]) {
+    static_assert(N == 0 || N == 4 * (D - 1), "wait counts");
+    v2u x[8];
+    slot_take<K>(x, N);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = v4u{x[2 * j].x, x[2 * j].y, x[2 * j + 1].x, x[2 * j + 1].y};
 }
 
 // ------------------------------------------------------------ instruction
@@ -704,106 +860,82 @@ __device__ __forceinline__ bool leave(const KParams &P, Ctx &c, const Ins &in, A
     return true;
 }
 
-// Runs one slice of the stream from register slot `buf`: consume it, refill
-// the slot with the slice D positions ahead, advance. True when the slice was the
-// wave's last of its instruction (the caller then handles the boundary).
-template <int NB, int G>
-__device__ __forceinline__ bool slot_step(const KParams &P, Ctx &c, Cur &ic, Cur &cc, const Ins &in, v4u (&buf)[4],
-                                          Acc<NB> &acc, AttnLaneT<G> &at) {
-    const bool empty = cc.u >= cc.nu;
-    if (!empty) {
-        if (cc.op == OP_ATTN) consume_attn<G>(P, c, cc, in, buf, at);
-        else consume_mv<NB>(P, c, cc, in, buf, acc);
+// Slot operations with a run-time slot index (a uniform scalar): one small
+// case per slot, so the code that consumes a slice exists once.
+__device__ __forceinline__ void take_any(int k, v4u (&r)[4]) {
+    switch (k) {
+        case 0: take_slot<0, 4 * (D - 1)>(r); break;
+        case 1: take_slot<1, 4 * (D - 1)>(r); break;
+        case 2: take_slot<2, 4 * (D - 1)>(r); break;
+        default: take_slot<3, 4 * (D - 1)>(r); break;
     }
-    const bool last = empty || (cc.s == cc.sp - 1 && cc.u + NC >= cc.nu);
-    issue(P, ic, buf, c.lane);
-    cur_next(P, c, ic);
-    cur_next(P, c, cc);
-    return last;
 }
-
-__device__ __forceinline__ void rot4(v4u (&a)[4], v4u (&b)[4], v4u (&c)[4], v4u (&d)[4], int by) {
-    // by 1: (a, b, c, d) <- (b, c, d, a); by 2 and 3 likewise
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const v4u t0 = a[j], t1 = b[j], t2 = c[j], t3 = d[j];
-        if (by == 1) {
-            a[j] = t1;
-            b[j] = t2;
-            c[j] = t3;
-            d[j] = t0;
-        } else if (by == 2) {
-            a[j] = t2;
-            b[j] = t3;
-            c[j] = t0;
-            d[j] = t1;
-        } else if (by == 3) {
-            a[j] = t3;
-            b[j] = t0;
-            c[j] = t1;
-            d[j] = t2;
-        }
+__device__ __forceinline__ void issue_any(int k, const KParams &P, const Cur &cur, int lane) {
+    switch (k) {
+        case 0: issue<0>(P, cur, lane); break;
+        case 1: issue<1>(P, cur, lane); break;
+        case 2: issue<2>(P, cur, lane); break;
+        default: issue<3>(P, cur, lane); break;
     }
 }
 
-// The wave's main loop. Between instruction boundaries the four slots are
-// consumed in order 0, 1, 2, 3, 0, ..., so that the compiler counts the loads
-// in flight exactly (the slot being consumed always has three slices issued
-// after it). At a boundary the wave leaves the previous instruction and
-// enters the next one -- that code exists once -- and, since entering waits
-// for the instruction's inputs anyway, it then renames the slots so that the
-// next slice to consume is in slot 0 again.
+// The wave's main loop. Slices are consumed in the order they were issued,
+// so the slot being consumed always has the other three slots issued after
+// it, and a wait for all but the 12 newest loads is a wait for exactly this
+// slot. At an instruction boundary the wave leaves the previous instruction
+// and enters the next one while the slices already issued stay in flight.
 template <int NB, int G>
 __device__ __forceinline__ void run(const KParams &P, Ctx &c) {
-    static_assert(D == 4, "the slot sequence below is written out for four slots");
-    v4u b0[4], b1[4], b2[4], b3[4];
+    static_assert(D == 4, "four slots");
     Cur ic, cc;
     cur_load(P, c, ic, 0);
     cur_load(P, c, cc, 0);
-    issue(P, ic, b0, c.lane);
+    issue<0>(P, ic, c.lane);
     cur_next(P, c, ic);
-    issue(P, ic, b1, c.lane);
+    issue<1>(P, ic, c.lane);
     cur_next(P, c, ic);
-    issue(P, ic, b2, c.lane);
+    issue<2>(P, ic, c.lane);
     cur_next(P, c, ic);
-    issue(P, ic, b3, c.lane);
+    issue<3>(P, ic, c.lane);
     cur_next(P, c, ic);
     Ins in{};
     Acc<NB> acc;
     AttnLaneT<G> at;
     bool first = true;
-    int rot = 0;
+    int slot = 0;
     for (;;) {
-        if (!first && !uni(leave<NB, G>(P, c, in, acc, at))) return;
+        if (!first && !uni(leave<NB, G>(P, c, in, acc, at))) break;
         first = false;
-        if (cc.op == OP_END) return;
-        if (!uni(enter<NB, G>(P, c, cc, in, acc, at))) return;
-        if (rot) rot4(b0, b1, b2, b3, rot);
+        if (cc.op == OP_END) break;
+        if (!uni(enter<NB, G>(P, c, cc, in, acc, at))) break;
         for (;;) {
-            if (uni(slot_step<NB, G>(P, c, ic, cc, in, b0, acc, at))) {
-                rot = 1;
-                break;
+            v4u buf[4];
+            take_any(slot, buf);
+            const bool empty = cc.u >= cc.nu;
+            if (!empty) {
+                if (cc.op == OP_ATTN) consume_attn<G>(P, c, cc, in, buf, at);
+                else consume_mv<NB>(P, c, cc, in, buf, acc);
             }
-            if (uni(slot_step<NB, G>(P, c, ic, cc, in, b1, acc, at))) {
-                rot = 2;
-                break;
-            }
-            if (uni(slot_step<NB, G>(P, c, ic, cc, in, b2, acc, at))) {
-                rot = 3;
-                break;
-            }
-            if (uni(slot_step<NB, G>(P, c, ic, cc, in, b3, acc, at))) {
-                rot = 0;
-                break;
-            }
+            const bool last = empty || (cc.s == cc.sp - 1 && cc.u + NC >= cc.nu);
+            issue_any(slot, P, ic, c.lane);
+            cur_next(P, c, ic);
+            cur_next(P, c, cc);
+            slot = (slot + 1) & 3;
+            if (uni(last)) break;
         }
     }
+    // no load may still be writing a slot register when the wave ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 }  // namespace
 
+// Occupancy target 3 caps the compiler at SLOT_VGPR0 VGPRs; the slot
+// registers above make the kernel's real count 232 (2 waves per SIMD, which
+// one 8-wave workgroup per compute unit needs).
 template <int NB, int G>
-__global__ __launch_bounds__(BLOCK_THREADS, 1) void mk_megakernel(KParams P) {
+__global__ __attribute__((amdgpu_flat_work_group_size(BLOCK_THREADS, BLOCK_THREADS), amdgpu_waves_per_eu(3, 3))) void mk_megakernel(
+    KParams P) {
     extern __shared__ char lds_raw[];
     MK_LDS char *lds = (MK_LDS char *)lds_raw;
     Ctx c;
