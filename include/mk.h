@@ -186,8 +186,11 @@ int mk_get_schedule_info(const mk_handle *h, mk_schedule_info *out);
 
 /* Copies the trace of the last step (when built with trace = 1) into the
  * host buffer `out` of `cap` int64 values: for each CU and queue slot,
- * {start, deps_ready, end} device-clock stamps. Returns the number of values
- * written through *n. */
+ * MK_TRACE_WORDS device-clock stamps (100 MHz): {start, inputs staged, end
+ * (merges included), first wave done, last wave done, merge finisher elected,
+ * merge inputs gathered, unused}; 0 where a stamp does not apply. Returns the
+ * number of values written through *n. */
+#define MK_TRACE_WORDS 8
 int mk_read_trace(mk_handle *h, int64_t *out, size_t cap, size_t *n);
 
 /* ---- debugging aids ---- */

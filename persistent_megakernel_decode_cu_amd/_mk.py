@@ -150,12 +150,14 @@ def mk_get_schedule_info(handle: int) -> MkScheduleInfo:
 
 def mk_read_trace(handle: int) -> np.ndarray:
     info = mk_get_schedule_info(handle)
-    cap = info.n_cus * info.queue_len * 3
+    cap = info.n_cus * info.queue_len * TRACE_WORDS
     buf = np.zeros(cap, dtype=np.int64)
     n = ctypes.c_size_t()
     _check(lib().mk_read_trace(handle, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), cap, ctypes.byref(n)))
-    return buf.reshape(info.n_cus, info.queue_len, 3)
+    return buf.reshape(info.n_cus, info.queue_len, TRACE_WORDS)
 
+
+TRACE_WORDS = 8  # MK_TRACE_WORDS
 
 SCRATCH = {"x": 0, "qkv": 1, "o": 2, "act": 3}
 

@@ -47,6 +47,7 @@ struct mk_handle {
     mk_config cfg{};
     int n_cus_dev = 0;
     uint64_t *wtab = nullptr;
+    std::vector<uint64_t> wtab_host;  // [L, 8] device addresses of the layer weights
     const void *embed = nullptr, *final_norm = nullptr;
     float2 *rope = nullptr;
     int capacity = 0;
@@ -123,6 +124,37 @@ int decode_err(int32_t v) {
 
 }  // namespace
 
+// Writes each instruction's operand addresses (weight matrices, norm
+// weight) into its words, so that the interpreter reads them with the
+// instruction instead of chasing the weight table.
+static void bind_operands(const mk_handle *h, mk::Plan &plan) {
+    auto put64 = [](int32_t *w, int at, uint64_t v) {
+        w[at] = (int32_t)(uint32_t)v;
+        w[at + 1] = (int32_t)(uint32_t)(v >> 32);
+    };
+    for (size_t i = 0; i + mk::INSTR_WORDS <= plan.queue.size(); i += mk::INSTR_WORDS) {
+        int32_t *w = &plan.queue[i];
+        const int op = w[mk::W_OP], l = w[mk::W_LAYER];
+        uint64_t wa = 0, wb = 0, wn = 0;
+        auto tab = [&](int k) { return h->wtab_host[(size_t)l * 8 + k]; };
+        switch (op) {
+            case mk::OP_QKV: wa = tab(1); wn = tab(0); break;
+            case mk::OP_OPROJ: wa = tab(2); break;
+            case mk::OP_UPGATE: wa = tab(4); wb = tab(5); wn = tab(3); break;
+            case mk::OP_DOWN: wa = tab(6); break;
+            case mk::OP_LMHEAD:
+                wa = (uint64_t)(uintptr_t)h->embed;
+                wn = (uint64_t)(uintptr_t)h->final_norm;
+                break;
+            default: break;
+        }
+        if (op != mk::OP_UPGATE) wb = wa;
+        put64(w, mk::W_WA, wa);
+        put64(w, mk::W_WB, wb);
+        put64(w, mk::W_WN, wn);
+    }
+}
+
 extern "C" {
 
 const char *mk_last_error(void) { return mk::g_last_error.c_str(); }
@@ -164,6 +196,7 @@ int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out) {
             const void *ptrs[7] = {lw.attn_norm, lw.wqkv, lw.wo, lw.mlp_norm, lw.w_gate, lw.w_up, lw.w_down};
             for (int k = 0; k < 7; ++k) tab[(size_t)l * 8 + k] = (uint64_t)(uintptr_t)ptrs[k];
         }
+        h->wtab_host = tab;
         if (int rc = dalloc(h->wtab, tab.size())) return fail(rc);
         if (hipMemcpy(h->wtab, tab.data(), tab.size() * 8, hipMemcpyHostToDevice) != hipSuccess)
             return fail(set_error(MK_EHIP, "hipMemcpy of the weight table failed"));
@@ -238,13 +271,14 @@ int mk_build_schedule(mk_handle *h, const mk_schedule_desc *s) {
             if (!rc) rc = dalloc(h->tpart, L * B * c.n_kv_heads * plan.attn_chunks * G * mk::ATTN_PART);
             if (!rc) rc = dalloc(h->tlm, (size_t)std::max(plan.n_lm_slots, 1) * B * 2);
         }
-        if (!rc && d.trace) rc = dalloc(h->trace, (size_t)plan.n_cus * plan.Q * 3);
+        if (!rc && d.trace) rc = dalloc(h->trace, (size_t)plan.n_cus * plan.Q * MK_TRACE_WORDS);
         if (rc) {
             free_schedule(h);
             return rc;
         }
-        if (!plan.queue.empty())
-            MK_HIP(hipMemcpy(h->queue, plan.queue.data(), plan.queue.size() * 4, hipMemcpyHostToDevice));
+        bind_operands(h, h->plan);
+        if (!h->plan.queue.empty())
+            MK_HIP(hipMemcpy(h->queue, h->plan.queue.data(), h->plan.queue.size() * 4, hipMemcpyHostToDevice));
         if (!plan.events.empty())
             MK_HIP(hipMemcpy(h->events, plan.events.data(), plan.events.size() * 4, hipMemcpyHostToDevice));
         h->max_need = 1;
@@ -297,6 +331,7 @@ int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream) {
         k.epoch = (int32_t)h->epoch;
         k.n_cus = P.n_cus;
         k.tag = h->tag;
+        k.queue_off = P.queue_off;
         k.xrow_off = P.xrow_off;
         k.part_off = P.part_off;
         k.act_off = P.act_off;
@@ -498,7 +533,7 @@ int mk_debug_regstream_probe(const void *src, size_t bytes, int blocks, int thre
 int mk_read_trace(mk_handle *h, int64_t *out, size_t cap, size_t *n) {
     if (!h || !out || !n) return set_error(MK_EINVAL, "null argument");
     if (!h->built || !h->trace) return set_error(MK_EINVAL, "schedule was not built with trace = 1");
-    const size_t need = (size_t)h->plan.n_cus * h->plan.Q * 3;
+    const size_t need = (size_t)h->plan.n_cus * h->plan.Q * MK_TRACE_WORDS;
     if (cap < need) return set_error(MK_EINVAL, "buffer too small");
     MK_HIP(hipSetDevice(h->cfg.device));
     MK_HIP(hipDeviceSynchronize());

@@ -156,9 +156,11 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // own running max m, sum l and output share o[h] (dims 8 (l % 8) .. +7) over
 // its positions, so a block needs no exchange between lane groups; the eight
 // group states are merged once, when the wave's state is stored.
+// (o has room for at least four heads: the interpreter keeps a matvec's
+// register activations there while no attention state is live)
 template <int G>
 struct AttnLaneT {
-    float m[G], l[G], o[G][8];
+    float m[G], l[G], o[G < 4 ? 4 : G][8];
 };
 
 template <int G>

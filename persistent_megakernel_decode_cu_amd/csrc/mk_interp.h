@@ -45,6 +45,7 @@ enum : int {
     M_ARRIVE = 1,  // compute-wave barrier arrivals
     M_FIN = 2,     // waves finished with an instruction's slices
     M_DONE = 3,    // instructions fully finished (incl. their merges)
+    M_KVLEN = 8,   // [MAX_B] lengths of the requests (read once at start)
     M_NORM = 16,   // [4][MAX_B] sums of squares
     M_AMAX = 64,   // [NC][MAX_B][2] per-wave argmax (value, index)
 };
@@ -67,6 +68,7 @@ __device__ __forceinline__ uint32_t lds_add(MK_LDS uint32_t *p, uint32_t v) {
 
 struct Ctx {
     MK_LDS uint32_t *misc;
+    const MK_LDS int32_t *q;  // this CU's queue, LDS_INSTR_WORDS words per instruction
     MK_LDS float *act;   // matvec inputs of all requests, or the attention staging
     MK_LDS float *xrow;  // residual rows of the instruction (O projection, down projection)
     MK_LDS float *part;  // per-wave attention states; merge staging
@@ -113,12 +115,12 @@ __device__ __forceinline__ bool cbar(Ctx &c, int pc) {
     return lds_wait_ge(c, c.misc + M_ARRIVE, (uint32_t)NC * c.nbar, pc);
 }
 
-__device__ __forceinline__ const int32_t *instr(const KParams &P, int cu, int pc) {
-    return P.queue + ((int64_t)cu * P.Q + pc) * INSTR_WORDS;
+// word `w` of instruction pc, from the LDS copy of the queue
+__device__ __forceinline__ int32_t iw(const Ctx &c, int pc, int w) {
+    return __builtin_amdgcn_readfirstlane(c.q[pc * LDS_INSTR_WORDS + w]);
 }
-
-__device__ __forceinline__ const char *wptr(const KParams &P, int layer, int k) {
-    return (const char *)(uintptr_t)sload(P.wtab, (int64_t)layer * 8 + k);
+__device__ __forceinline__ uint64_t iw64(const Ctx &c, int pc, int w) {
+    return (uint64_t)(uint32_t)iw(c, pc, w) | ((uint64_t)(uint32_t)iw(c, pc, w + 1) << 32);
 }
 
 __device__ __forceinline__ void chunk_blocks(int p, int c, int nch, int *lo, int *hi) {
@@ -188,12 +190,12 @@ struct Cur {
     int pc, op, layer, r0, nu, sp, spm, u, s, K;
     int b, g, blo, p;
     uint32_t rowb;
+    uint64_t wa, wb;  // matvec: base of the op's first (gate) and second (up) weight matrix
 };
 
 __device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k, int pc) {
     k.pc = pc;
-    const int32_t *ins = instr(P, c.cu, pc);
-    k.op = sload(ins, W_OP);
+    k.op = pc < P.Q ? iw(c, pc, W_OP) : OP_END;
     k.u = c.w;
     k.s = 0;
     k.nu = 0;
@@ -201,17 +203,18 @@ __device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k,
     k.spm = 1;
     k.K = 0;
     k.rowb = 0;
+    k.wa = k.wb = (uint64_t)(uintptr_t)P.wtab;
     if (k.op == OP_END) return;
-    k.layer = sload(ins, W_LAYER);
-    k.r0 = sload(ins, W_R0);
+    k.layer = iw(c, pc, W_LAYER);
+    k.r0 = iw(c, pc, W_R0);
     if (k.op == OP_ATTN) {
-        k.b = sload(ins, W_B);
-        k.g = sload(ins, W_G);
-        int p = sload(P.kv_lens, k.b);
+        k.b = iw(c, pc, W_B);
+        k.g = iw(c, pc, W_G);
+        int p = (int)lds_ld(c.misc + M_KVLEN + (k.b & (MAX_B - 1)));
         if (p < 0 || p >= P.T * P.max_pages) p = 0;  // the staging raises the error
         k.p = p;
         int lo, hi;
-        chunk_blocks(p, sload(ins, W_C), sload(ins, W_NCH), &lo, &hi);
+        chunk_blocks(p, iw(c, pc, W_C), iw(c, pc, W_NCH), &lo, &hi);
         k.blo = lo;
         k.nu = hi - lo;
     } else if (k.op > OP_END && k.op < OP_COUNT) {
@@ -219,7 +222,9 @@ __device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k,
         k.rowb = (uint32_t)k.K * 2;
         k.spm = (int)((k.rowb + SLICE_BYTES - 1) / SLICE_BYTES);
         k.sp = (k.op == OP_UPGATE ? 2 : 1) * k.spm;
-        k.nu = sload(ins, W_R1) - k.r0;
+        k.nu = iw(c, pc, W_R1) - k.r0;
+        k.wa = iw64(c, pc, W_WA);
+        k.wb = iw64(c, pc, W_WB);
     }
     // an unknown opcode yields one empty slice; its staging raises the error
 }
@@ -403,9 +408,7 @@ __device__ __forceinline__ void issue(const KParams &P, const Cur &k, int lane) 
         } else {
             const int m = k.s >= k.spm ? 1 : 0, part = k.s - m * k.spm;
             const uint32_t col0 = (uint32_t)part * SLICE_BYTES;
-            const int which = k.op == OP_QKV ? 1 : k.op == OP_OPROJ ? 2 : k.op == OP_UPGATE ? 4 + m : 6;
-            const char *base = k.op == OP_LMHEAD ? (const char *)P.embed : wptr(P, k.layer, which);
-            a = base + ((uint32_t)(k.r0 + k.u) * k.rowb + col0);
+            a = (const char *)(uintptr_t)(m ? k.wb : k.wa) + ((uint32_t)(k.r0 + k.u) * k.rowb + col0);
             const uint32_t nbytes = min((uint32_t)SLICE_BYTES, k.rowb - col0);
             na = min(nbytes, 2048u);
             nb = nbytes - na;
@@ -430,7 +433,8 @@ __device__ __forceinline__ void take_slot(v4u (&r)[4]) {
 // ------------------------------------------------------------ instruction
 
 struct Ins {
-    int pc, op, layer, r0, r1, flags, b, g, c, nch, p, merge, slot, nslot;
+    int pc, op, layer, r0, r1, flags, b, g, c, nch, p, merge, slot, nslot, mctr, mneed;
+    uint64_t wn;  // norm weight of the op's input
     int64_t *tr;
 };
 
@@ -458,17 +462,22 @@ __device__ __forceinline__ int token_of(const KParams &P, Ctx &c, int b, int pc)
 __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &in, const uint16_t *wn, int xv) {
     const int H = P.H, lane = c.lane, w = c.w;
     MK_LDS float *norm = (MK_LDS float *)(c.misc + M_NORM);
+    const int first = w * 64 + lane;
+    const int n = first < H ? (H - first + 255) / 256 : 0;  // this lane's elements
+    const int nmax = (H - w * 64 + 255) / 256;               // lane 0's: the most
+    // The norm weights of the lane's first 16 elements are loaded with the
+    // inputs: a load issued later would wait behind the weight slices in flight.
+    float wv[16];
     if (w < 4) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) wv[k] = k < n ? bf2f(wn[first + 256 * k]) : 0.0f;
         for (int b = 0; b < P.B; ++b) {
             MK_LDS float *a = c.act + b * P.act_stride;
             if (xv == 0) {
                 const int tok = P.has_embed ? token_of(P, c, b, in.pc) : 0;
-                for (int i = w * 64 + lane; i < H; i += 256) a[act_index(i)] = x_input(P, b, i, true, tok);
+                for (int i = first; i < H; i += 256) a[act_index(i)] = x_input(P, b, i, true, tok);
             } else {
                 const __amdgpu_buffer_rsrc_t r = tres(P.tx + ((size_t)(xv - 1) * P.B + b) * H, (uint32_t)H);
-                const int first = w * 64 + lane;
-                const int n = first < H ? (H - first + 255) / 256 : 0;  // this lane's words
-                const int nmax = (H - w * 64 + 255) / 256;               // lane 0's: the most
                 // the loop bound is uniform: an early return from a loop whose
                 // trip count differs per lane would make the caller's control
                 // flow divergent
@@ -479,7 +488,7 @@ __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &
                         return false;
             }
             float ss = 0.0f;
-            for (int i = w * 64 + lane; i < H; i += 256) {
+            for (int i = first; i < H; i += 256) {
                 const float v = a[act_index(i)];
                 ss = fmaf(v, v, ss);
             }
@@ -494,7 +503,16 @@ __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &
             for (int v = 0; v < 4; ++v) tot += norm[v * MAX_B + b];
             const float inv = 1.0f / sqrtf(tot / (float)H + P.eps);
             MK_LDS float *a = c.act + b * P.act_stride;
-            for (int i = w * 64 + lane; i < H; i += 256) a[act_index(i)] = a[act_index(i)] * inv * bf2f(wn[i]);
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                if (k < n) {
+                    const int ai = act_index(first + 256 * k);
+                    a[ai] = a[ai] * inv * wv[k];
+                }
+            for (int k = 16; k < n; ++k) {
+                const int i = first + 256 * k;
+                a[act_index(i)] = a[act_index(i)] * inv * bf2f(wn[i]);
+            }
         }
     }
     return cbar(c, in.pc);
@@ -581,33 +599,34 @@ template <int NB, int G>
 __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, Ins &in, Acc<NB> &acc,
                                       AttnLaneT<G> &at) {
     const int pc = k.pc;
-    const int32_t *ins = instr(P, c.cu, pc);
     in.pc = pc;
-    in.op = sload(ins, W_OP);
-    in.layer = sload(ins, W_LAYER);
-    in.r0 = sload(ins, W_R0);
-    in.r1 = sload(ins, W_R1);
-    in.flags = sload(ins, W_FLAGS);
-    in.b = sload(ins, W_B);
-    in.g = sload(ins, W_G);
-    in.c = sload(ins, W_C);
-    in.nch = sload(ins, W_NCH);
-    in.merge = sload(ins, W_MERGE);
-    in.slot = sload(ins, W_SLOT);
-    in.nslot = sload(ins, W_NSLOT);
-    in.tr = P.trace ? P.trace + ((int64_t)c.cu * P.Q + pc) * 3 : nullptr;
+    in.op = iw(c, pc, W_OP);
+    in.layer = iw(c, pc, W_LAYER);
+    in.r0 = iw(c, pc, W_R0);
+    in.r1 = iw(c, pc, W_R1);
+    in.flags = iw(c, pc, W_FLAGS);
+    in.b = iw(c, pc, W_B);
+    in.g = iw(c, pc, W_G);
+    in.c = iw(c, pc, W_C);
+    in.nch = iw(c, pc, W_NCH);
+    in.merge = iw(c, pc, W_MERGE);
+    in.slot = iw(c, pc, W_SLOT);
+    in.nslot = iw(c, pc, W_NSLOT);
+    in.mctr = iw(c, pc, W_MCTR);
+    in.mneed = iw(c, pc, W_MNEED);
+    in.wn = iw64(c, pc, W_WN);
+    in.tr = P.trace ? P.trace + ((int64_t)c.cu * P.Q + pc) * TRACE_WORDS : nullptr;
     const bool tracer = in.tr && c.w == 0 && c.lane == 0;
-    if (tracer) in.tr[0] = wall_clock64();
+    if (tracer) in.tr[TR_START] = wall_clock64();
     // the previous instruction is finished, merges included: its LDS areas are free
     if (!lds_wait_ge(c, c.misc + M_DONE, (uint32_t)pc, pc)) return false;
     bool ok = true;
     switch (in.op) {
         case OP_QKV:
-            ok = stage_norm(P, c, in, (const uint16_t *)wptr(P, in.layer, 0),
-                            (in.flags & F_X_FROM_INPUT) ? 0 : 2 * in.layer);
+            ok = stage_norm(P, c, in, (const uint16_t *)(uintptr_t)in.wn, (in.flags & F_X_FROM_INPUT) ? 0 : 2 * in.layer);
             break;
-        case OP_UPGATE: ok = stage_norm(P, c, in, (const uint16_t *)wptr(P, in.layer, 3), 2 * in.layer + 1); break;
-        case OP_LMHEAD: ok = stage_norm(P, c, in, P.final_norm, 2 * P.L); break;
+        case OP_UPGATE: ok = stage_norm(P, c, in, (const uint16_t *)(uintptr_t)in.wn, 2 * in.layer + 1); break;
+        case OP_LMHEAD: ok = stage_norm(P, c, in, (const uint16_t *)(uintptr_t)in.wn, 2 * P.L); break;
         case OP_OPROJ:
             ok = stage_rows(P, c, in, (in.flags & F_X_FROM_INPUT) ? 0 : 2 * in.layer) &&
                  stage_copy(P, c, in, P.to + (size_t)in.layer * P.B * P.nq * P.d, P.nq * P.d) && cbar(c, pc);
@@ -617,7 +636,7 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
                  stage_copy(P, c, in, P.tact + (size_t)in.layer * P.B * P.F, P.F) && cbar(c, pc);
             break;
         case OP_ATTN: {
-            const int p = sload(P.kv_lens, in.b);
+            const int p = in.b >= 0 && in.b < P.B ? (int)lds_ld(c.misc + M_KVLEN + in.b) : -1;
             if (p < 0 || p >= P.T * P.max_pages) {
                 if (c.lane == 0) raise_err(c, ERR_RANGE, pc);
                 return false;
@@ -631,7 +650,7 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
             return false;
     }
     if (!ok) return false;
-    if (tracer) in.tr[1] = wall_clock64();
+    if (tracer) in.tr[TR_READY] = wall_clock64();
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         acc.a0[b] = 0.0f;
@@ -641,6 +660,15 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
     }
     acc.nan = false;
     attn_lane_init(at);
+    if (NB == 1 && in.op != OP_ATTN && k.K == 2048) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const v4f a = *(const MK_LDS v4f *)(c.act + j * 512 + c.lane * 4);
+            const v4f b = *(const MK_LDS v4f *)(c.act + j * 512 + 256 + c.lane * 4);
+            at.o[j][0] = a.x; at.o[j][1] = a.y; at.o[j][2] = a.z; at.o[j][3] = a.w;
+            at.o[j][4] = b.x; at.o[j][5] = b.y; at.o[j][6] = b.z; at.o[j][7] = b.w;
+        }
+    }
     return true;
 }
 
@@ -674,23 +702,63 @@ __device__ __forceinline__ void emit_row(const KParams &P, Ctx &c, const Ins &in
     }
 }
 
-template <int NB>
+// Slice (part, m) of unit u: the lane's 16-byte chunks ci = 256 part + 64 j +
+// lane, j < 4, times the activations of those chunks, added in j order to
+// the unit's dot product (m: gate or up matrix of UPGATE). Three forms with
+// the same arithmetic: at batch 1 with K = 2048 the activations sit in
+// registers, loaded once per instruction into the attention state's output
+// registers (xr.o[j], free during a matvec); a full slice reads them from
+// LDS with every read issued before the products; a slice past the end of a
+// short row guards each chunk.
+template <int NB, int G>
 __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &k, const Ins &in, const v4u (&r)[4],
-                                           Acc<NB> &acc) {
+                                           Acc<NB> &acc, const AttnLaneT<G> &xr) {
     const int lane = c.lane;
     const int m = k.s >= k.spm ? 1 : 0, part = k.s - m * k.spm;
-    const int nchunk = k.K >> 3;
+    if (NB == 1 && k.K == 2048) {
+        float a = m ? acc.a1[0] : acc.a0[0];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int ci = part * 256 + j * 64 + lane;
-        if (ci < nchunk) {
-            const int base = ((ci >> 6) << 9) + ((ci & 63) << 2);
+        for (int j = 0; j < 4; ++j)
+            a += dot8(r[j], v4f{xr.o[j][0], xr.o[j][1], xr.o[j][2], xr.o[j][3]},
+                      v4f{xr.o[j][4], xr.o[j][5], xr.o[j][6], xr.o[j][7]});
+        acc.a0[0] = m ? acc.a0[0] : a;
+        acc.a1[0] = m ? a : acc.a1[0];
+    } else if (k.K >= (part + 1) * 2048) {
+        v4f x0[4][NB], x1[4][NB];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const MK_LDS float *a = c.act + b * P.act_stride + base;
-                const float d = dot8(r[j], *(const MK_LDS v4f *)a, *(const MK_LDS v4f *)(a + 256));
-                if (m == 0) acc.a0[b] += d;
-                else acc.a1[b] += d;
+                const MK_LDS float *ab = c.act + b * P.act_stride + part * 2048 + j * 512 + lane * 4;
+                x0[j][b] = *(const MK_LDS v4f *)ab;
+                x1[j][b] = *(const MK_LDS v4f *)(ab + 256);
+            }
+        float a[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) a[b] = m ? acc.a1[b] : acc.a0[b];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) a[b] += dot8(r[j], x0[j][b], x1[j][b]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            acc.a0[b] = m ? acc.a0[b] : a[b];
+            acc.a1[b] = m ? a[b] : acc.a1[b];
+        }
+    } else {
+        const int nchunk = k.K >> 3;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ci = part * 256 + j * 64 + lane;
+            if (ci < nchunk) {
+                const int base = ((ci >> 6) << 9) + ((ci & 63) << 2);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const MK_LDS float *a = c.act + b * P.act_stride + base;
+                    const float d = dot8(r[j], *(const MK_LDS v4f *)a, *(const MK_LDS v4f *)(a + 256));
+                    if (m == 0) acc.a0[b] += d;
+                    else acc.a1[b] += d;
+                }
             }
         }
     }
@@ -740,13 +808,12 @@ __device__ __forceinline__ void consume_attn(const KParams &P, Ctx &c, const Cur
     attn_lane_block(at, c.act, lane, k0, k1, v0, v1, pos0 <= in.p, pos0 + 8 <= in.p);
 }
 
-// Elects the last of `need` finishers of a merge event (one per step).
-__device__ __forceinline__ bool elect_last(const KParams &P, Ctx &c, int merge) {
-    const int ctr = sload(P.events, (int64_t)merge * EV_WORDS + EV_CTR);
-    const int32_t need = (int32_t)((int64_t)P.epoch * sload(P.events, (int64_t)merge * EV_WORDS + EV_NEED));
+// Elects the last of the instruction's merge-event finishers (one per step).
+__device__ __forceinline__ bool elect_last(const KParams &P, Ctx &c, const Ins &in) {
+    const int32_t need = (int32_t)((int64_t)P.epoch * in.mneed);
     int32_t old = 0;
     if (c.lane == 0)
-        old = __hip_atomic_fetch_add(P.counters + (int64_t)ctr * CTR_STRIDE, 1, __ATOMIC_RELAXED,
+        old = __hip_atomic_fetch_add(P.counters + (int64_t)in.mctr * CTR_STRIDE, 1, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
     old = __builtin_amdgcn_readfirstlane(__shfl(old, 0, 64));
     return old + 1 == need;
@@ -777,11 +844,13 @@ __device__ __forceinline__ bool finish(const KParams &P, Ctx &c, const Ins &in) 
                 }
             }
         }
-        if (nch == 1 || !elect_last(P, c, in.merge)) return true;
+        if (nch == 1 || !elect_last(P, c, in)) return true;
+        if (in.tr && lane == 0) in.tr[TR_ELECT] = wall_clock64();
         // the last chunk to finish merges all chunks, in chunk order
         if (!tgather_range(
                 c, rp, 0, nch * G * ATTN_PART, [&](int i, float v) { c.part[i] = v; }, in.pc))
             return false;
+        if (in.tr && lane == 0) in.tr[TR_GATHER] = wall_clock64();
         for (int h = 0; h < G; ++h) {
             float o, m, l;
             merge_parts(nullptr, c.part + h * ATTN_PART, nch, G * ATTN_PART, lane, &o, &m, &l);
@@ -806,11 +875,13 @@ __device__ __forceinline__ bool finish(const KParams &P, Ctx &c, const Ins &in) 
             tput(rl, (uint32_t)((in.slot * P.B + lane) * 2), bv, tag);
             tput(rl, (uint32_t)((in.slot * P.B + lane) * 2 + 1), __int_as_float(bi), tag);
         }
-        if (!elect_last(P, c, in.merge)) return true;
+        if (!elect_last(P, c, in)) return true;
+        if (in.tr && lane == 0) in.tr[TR_ELECT] = wall_clock64();
         // the argmax is a maximum under a total order: any combination order gives the same token
         if (!tgather_range(
                 c, rl, 0, in.nslot * P.B * 2, [&](int i, float v) { c.act[i] = v; }, in.pc))
             return false;
+        if (in.tr && lane == 0) in.tr[TR_GATHER] = wall_clock64();
         if (lane < P.B) {
             float bv = -INFINITY;
             int bi = 0x7fffffff;
@@ -823,13 +894,13 @@ __device__ __forceinline__ bool finish(const KParams &P, Ctx &c, const Ins &in) 
                 }
             }
             P.tokens_out[lane] = bi;
-            if (P.kv_lens_out) P.kv_lens_out[lane] = sload(P.kv_lens, lane) + 1;
+            if (P.kv_lens_out) P.kv_lens_out[lane] = (int32_t)c.misc[M_KVLEN + lane] + 1;
         }
         return true;
     }
     if ((in.flags & F_STEP_FINAL) && in.merge >= 0) {  // last layer's down projection without an LM head
-        if (elect_last(P, c, in.merge) && P.kv_lens_out && lane < P.B)
-            P.kv_lens_out[lane] = sload(P.kv_lens, lane) + 1;
+        if (elect_last(P, c, in) && P.kv_lens_out && lane < P.B)
+            P.kv_lens_out[lane] = (int32_t)c.misc[M_KVLEN + lane] + 1;
     }
     return true;
 }
@@ -852,10 +923,12 @@ __device__ __forceinline__ bool leave(const KParams &P, Ctx &c, const Ins &in, A
     uint32_t old = 0;
     if (lane == 0) old = lds_add(c.misc + M_FIN, 1u);
     old = __builtin_amdgcn_readfirstlane(__shfl(old, 0, 64));
+    if (in.tr && lane == 0 && old == (uint32_t)NC * in.pc) in.tr[TR_FIRST] = wall_clock64();
     if (old != (uint32_t)NC * (in.pc + 1) - 1) return true;
+    if (in.tr && lane == 0) in.tr[TR_LAST] = wall_clock64();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if (!finish<G>(P, c, in)) return false;
-    if (in.tr && lane == 0) in.tr[2] = wall_clock64();
+    if (in.tr && lane == 0) in.tr[TR_END] = wall_clock64();
     if (lane == 0) lds_add(c.misc + M_DONE, 1u);
     return true;
 }
@@ -914,7 +987,7 @@ __device__ __forceinline__ void run(const KParams &P, Ctx &c) {
             const bool empty = cc.u >= cc.nu;
             if (!empty) {
                 if (cc.op == OP_ATTN) consume_attn<G>(P, c, cc, in, buf, at);
-                else consume_mv<NB>(P, c, cc, in, buf, acc);
+                else consume_mv<NB, G>(P, c, cc, in, buf, acc, at);
             }
             const bool last = empty || (cc.s == cc.sp - 1 && cc.u + NC >= cc.nu);
             issue_any(slot, P, ic, c.lane);
@@ -940,6 +1013,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(BLOCK_THREADS, BLOCK_THREA
     MK_LDS char *lds = (MK_LDS char *)lds_raw;
     Ctx c;
     c.misc = (MK_LDS uint32_t *)lds;
+    c.q = (const MK_LDS int32_t *)(lds + P.queue_off);
     c.xrow = (MK_LDS float *)(lds + P.xrow_off);
     c.part = (MK_LDS float *)(lds + P.part_off);
     c.act = (MK_LDS float *)(lds + P.act_off);
@@ -952,6 +1026,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(BLOCK_THREADS, BLOCK_THREA
     c.err = P.err;
     c.host_err = P.host_err;
     for (int i = threadIdx.x; i < MISC_BYTES / 4; i += BLOCK_THREADS) c.misc[i] = 0;
+    __syncthreads();
+    // the CU's queue and the request lengths are read once, here: scalar
+    // reads of them later in the step would miss in caches that the weight
+    // stream has long since flushed
+    {
+        MK_LDS int32_t *q = (MK_LDS int32_t *)(lds + P.queue_off);
+        const int32_t *src = P.queue + (int64_t)c.cu * P.Q * INSTR_WORDS;
+        for (int i = threadIdx.x; i < P.Q * LDS_INSTR_WORDS; i += BLOCK_THREADS)
+            q[i] = src[(i / LDS_INSTR_WORDS) * INSTR_WORDS + i % LDS_INSTR_WORDS];
+        if (threadIdx.x < (unsigned)P.B) c.misc[M_KVLEN + threadIdx.x] = (uint32_t)P.kv_lens[threadIdx.x];
+    }
     __syncthreads();
     run<NB, G>(P, c);
 }

@@ -46,7 +46,14 @@ enum : int {
     W_SLOT = 10,   // this instruction's slot among the merge's partials
     W_NSLOT = 11,  // slots of the merge
     W_SEQ = 12,    // position in the global topological order
-    INSTR_WORDS = 32
+    W_MCTR = 13,   // counter of the merge event (-1: none)
+    W_MNEED = 14,  // finishers the merge event waits for
+    // operand addresses, bound when the schedule is built (64-bit, low word first):
+    W_WA = 16,     // matvec: first weight matrix (UPGATE: gate); LM head: embedding
+    W_WB = 18,     // UPGATE: up matrix; else = W_WA
+    W_WN = 20,     // norm weight of the op's input (QKV, UPGATE, LM head); else 0
+    INSTR_WORDS = 32,
+    LDS_INSTR_WORDS = 24  // words of each instruction the interpreter copies into LDS
 };
 
 enum : int32_t {
@@ -71,6 +78,11 @@ constexpr int PREFETCH_SLICES = 4;     // slices each wave keeps in flight
 constexpr int ATTN_PART = 64 + 2;      // o[d], m, l of one head
 constexpr int ATTN_WAVE_PART = 68;     // floats per head of a wave's attention state in LDS
 constexpr int MAX_B = 8;
+// device-clock stamps per instruction in a traced step: start, inputs staged,
+// end (merges included), first wave done with its slices, last wave done,
+// merge finisher elected, merge inputs gathered, unused
+constexpr int TRACE_WORDS = 8;  // MK_TRACE_WORDS of mk.h
+enum : int { TR_START = 0, TR_READY = 1, TR_END = 2, TR_FIRST = 3, TR_LAST = 4, TR_ELECT = 5, TR_GATHER = 6 };
 constexpr int MAX_G = 8;
 
 // device error word: code << 28 | cu << 16 | pc

@@ -278,6 +278,8 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
             w[W_SLOT] = t.slot;
             w[W_NSLOT] = t.nslot;
             w[W_SEQ] = id;
+            w[W_MCTR] = t.merge;  // the merge event's counter is its index
+            w[W_MNEED] = t.merge >= 0 ? ev_need[t.merge] : 0;
             bytes += t.bytes;
             if (t.op == OP_OPROJ || t.op == OP_DOWN) max_rows_x = std::max(max_rows_x, t.r1 - t.r0);
         }
@@ -304,7 +306,8 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     const int64_t act_floats = std::max<int64_t>({(int64_t)NBP * P.act_stride, (int64_t)G * 64 + 64,
                                                   (int64_t)P.n_lm_slots * B * 2});
     auto up256 = [](int64_t x) { return (x + 255) / 256 * 256; };
-    const int64_t xrow_off = MISC_BYTES;
+    const int64_t queue_off = MISC_BYTES;  // the CU's queue, LDS_INSTR_WORDS words per instruction
+    const int64_t xrow_off = queue_off + up256((int64_t)Q * LDS_INSTR_WORDS * 4);
     const int64_t part_off = xrow_off + up256((int64_t)NBP * P.xrow_stride * 4);
     const int64_t act_off = part_off + up256(part_floats * 4);
     const int64_t lds = act_off + up256(act_floats * 4);
@@ -313,6 +316,7 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
                                            " bytes of LDS (limit " + std::to_string(LDS_LIMIT) +
                                            "): the activation area holds " + std::to_string(NBP) + " x " +
                                            std::to_string(P.act_stride) + " floats");
+    P.queue_off = (int)queue_off;
     P.xrow_off = (int)xrow_off;
     P.part_off = (int)part_off;
     P.act_off = (int)act_off;
