@@ -220,28 +220,55 @@ __device__ __forceinline__ void attn_lane_block(AttnLaneT<G> &st, const MK_LDS f
     }
 }
 
-// Merges the eight lane groups' states (in a fixed butterfly order) and
-// writes the wave's state as partials [G][ATTN_WAVE_PART] (o[64], m, l).
+// Exchanges with lane ^ 8, lane ^ 16 and lane ^ 32, all in the VALU: a DPP
+// rotate by 8 within each 16-lane row, and the gfx950 row swaps
+// (v_permlane16_swap / v_permlane32_swap), which hand each lane its partner
+// in one of their two outputs. Which output that is gets settled once per
+// wave by swapping the lane indices themselves.
+struct XorPick {
+    bool x16, x32;  // the partner of the 16- / 32-lane swap is in output 0
+};
+__device__ __forceinline__ XorPick xor_pick_init(int lane) {
+    const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)lane, (uint32_t)lane, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap((uint32_t)lane, (uint32_t)lane, false, false);
+    return XorPick{a[0] == (uint32_t)(lane ^ 16), b[0] == (uint32_t)(lane ^ 32)};
+}
+__device__ __forceinline__ float xor8(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));  // row_ror:8
+}
+__device__ __forceinline__ float xor16(float v, XorPick x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(x.x16 ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32(float v, XorPick x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(x.x32 ? r[0] : r[1]);
+}
+
+// Merges the eight lane groups' states (a butterfly over lane ^ 8, ^ 16,
+// ^ 32: every lane ends with the same sums) and writes the wave's state as
+// partials [G][ATTN_WAVE_PART] (o[64], m, l).
 template <int G>
 __device__ __forceinline__ void attn_lane_store(AttnLaneT<G> &st, MK_LDS float *part, int lane) {
+    const XorPick xp = xor_pick_init(lane);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         float M = st.m[h];
-        M = fmaxf(M, __shfl_xor(M, 8, 64));
-        M = fmaxf(M, __shfl_xor(M, 16, 64));
-        M = fmaxf(M, __shfl_xor(M, 32, 64));
+        M = fmaxf(M, xor8(M));
+        M = fmaxf(M, xor16(M, xp));
+        M = fmaxf(M, xor32(M, xp));
         const float f = __expf(st.m[h] - M);
         float l = st.l[h] * f;
-        l += __shfl_xor(l, 8, 64);
-        l += __shfl_xor(l, 16, 64);
-        l += __shfl_xor(l, 32, 64);
+        l += xor8(l);
+        l += xor16(l, xp);
+        l += xor32(l, xp);
         float o[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             o[e] = st.o[h][e] * f;
-            o[e] += __shfl_xor(o[e], 8, 64);
-            o[e] += __shfl_xor(o[e], 16, 64);
-            o[e] += __shfl_xor(o[e], 32, 64);
+            o[e] += xor8(o[e]);
+            o[e] += xor16(o[e], xp);
+            o[e] += xor32(o[e], xp);
         }
         if (lane < 8) {
             MK_LDS float *ph = part + h * ATTN_WAVE_PART + lane * 8;
@@ -255,28 +282,38 @@ __device__ __forceinline__ void attn_lane_store(AttnLaneT<G> &st, MK_LDS float *
     }
 }
 
-// Merge partial softmax states (o, m, l) of `n` sources in source order;
-// lanes are dims. Sources are global (gsrc) or LDS (lsrc), `stride` floats
-// apart, laid out [o 0..63, m, l].
-__device__ __forceinline__ void merge_parts(const float *gsrc, const MK_LDS float *lsrc, int n, int stride, int lane,
-                                            float *o, float *m, float *l) {
-    float M = -1e30f;
-    for (int i = 0; i < n; ++i) {
-        const float mi = gsrc ? gsrc[i * stride + 64] : lsrc[i * stride + 64];
-        M = fmaxf(M, mi);
+// Softmax-state merge, one source at a time in a fixed order: (O, M, L)
+// absorbs (o, m, l). Every merge of attention states (the waves of a tile,
+// the chunks of a kv head) goes through this step, in source order.
+__device__ __forceinline__ void merge_step(float &O, float &M, float &L, float o, float m, float l) {
+    const float mn = fmaxf(M, m);
+    const float a = __expf(M - mn), b = __expf(m - mn);
+    O = fmaf(O, a, o * b);
+    L = fmaf(L, a, l * b);
+    M = mn;
+}
+__device__ __forceinline__ void merge_init(float &O, float &M, float &L) {
+    O = 0.0f;
+    M = -1e30f;
+    L = 0.0f;
+}
+
+// Merges the NW wave states of head h (LDS, [NW][G][ATTN_WAVE_PART]) in
+// wave order; lane = dim. All reads are issued before the merge.
+template <int G, int NW>
+__device__ __forceinline__ void merge_wave_states(const MK_LDS float *part, int h, int lane, float &O, float &M,
+                                                  float &L) {
+    float o[NW], m[NW], l[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const MK_LDS float *ph = part + (w * G + h) * ATTN_WAVE_PART;
+        o[w] = ph[lane];
+        m[w] = ph[64];
+        l[w] = ph[65];
     }
-    float L = 0.0f, O = 0.0f;
-    for (int i = 0; i < n; ++i) {
-        const float mi = gsrc ? gsrc[i * stride + 64] : lsrc[i * stride + 64];
-        const float li = gsrc ? gsrc[i * stride + 65] : lsrc[i * stride + 65];
-        const float oi = gsrc ? gsrc[i * stride + lane] : lsrc[i * stride + lane];
-        const float f = expf(mi - M);
-        L = fmaf(li, f, L);
-        O = fmaf(oi, f, O);
-    }
-    *o = O;
-    *m = M;
-    *l = L;
+    merge_init(O, M, L);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) merge_step(O, M, L, o[w], m[w], l[w]);
 }
 
 // (value, index) order of the greedy pick: larger value, then lower index

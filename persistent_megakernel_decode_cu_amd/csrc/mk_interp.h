@@ -134,24 +134,56 @@ __device__ __forceinline__ void chunk_blocks(int p, int c, int nch, int *lo, int
 // loads are issued before any tag is checked. False on abort or timeout.
 template <int N, typename IDX, typename PUT>
 __device__ __forceinline__ bool tgather(Ctx &c, __amdgpu_buffer_rsrc_t r, int n, IDX idx, PUT put, int pc) {
-    static_assert(N >= 1 && N <= 16, "gather width");
+    static_assert(N >= 1 && N <= 48, "gather width");
     const uint32_t tag = c.tag;
-    uint32_t pend = n <= 0 ? 0u : (n >= N ? ((1u << N) - 1u) : ((1u << n) - 1u));
+    uint64_t pend = n <= 0 ? 0ull : (n >= N ? ((1ull << N) - 1ull) : ((1ull << n) - 1ull));
     int64_t spins = 0;
     for (;;) {
         v2u wv[N];
 #pragma unroll
         for (int k = 0; k < N; ++k)
-            if (pend & (1u << k)) wv[k] = tget(r, idx(k));
+            if (pend & (1ull << k)) wv[k] = tget(r, idx(k));
 #pragma unroll
         for (int k = 0; k < N; ++k)
-            if ((pend & (1u << k)) && wv[k].y == tag) {
+            if ((pend & (1ull << k)) && wv[k].y == tag) {
                 put(k, __uint_as_float(wv[k].x));
-                pend &= ~(1u << k);
+                pend &= ~(1ull << k);
             }
         if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) return true;
         if (lds_ld(c.misc + M_ABORT)) return false;
         // a producer on another unit may have failed: then this data never comes
+        if ((++spins & 63) == 0 &&
+            __builtin_amdgcn_readfirstlane(__hip_atomic_load(c.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+            lds_st(c.misc + M_ABORT, 1u);
+            return false;
+        }
+        if (spins > c.watchdog) {
+            raise_err(c, ERR_TIMEOUT, pc);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// Like tgather, but every poll reloads all n words and the wait ends when
+// they all carry the step's tag; the values are then in v[k] (k < n). Needs
+// no second copy of the words, at the cost of re-reading words that had
+// already arrived while others are still pending.
+template <int N, typename IDX>
+__device__ __forceinline__ bool tgather_all(Ctx &c, __amdgpu_buffer_rsrc_t r, IDX idx, float (&v)[N], int pc) {
+    static_assert(N >= 1 && N <= 48, "gather width");
+    const uint32_t tag = c.tag;
+    int64_t spins = 0;
+    for (;;) {
+        bool miss = false;
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            const v2u w = tget(r, idx(k));
+            v[k] = __uint_as_float(w.x);
+            miss |= w.y != tag;
+        }
+        if (__builtin_amdgcn_ballot_w64(miss) == 0) return true;
+        if (lds_ld(c.misc + M_ABORT)) return false;
         if ((++spins & 63) == 0 &&
             __builtin_amdgcn_readfirstlane(__hip_atomic_load(c.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
             lds_st(c.misc + M_ABORT, 1u);
@@ -268,10 +300,10 @@ template <>
 __device__ __forceinline__ void slot_loads<0>(uint32_t o, v4u ra, v4u rb) {
     asm volatile(
         "s_nop 4\n\t"
-        "buffer_load_dwordx4 v[168:171], %0, %1, 0 offen ; slot_load\n\t"
-        "buffer_load_dwordx4 v[172:175], %0, %1, 0 offen offset:1024 ; slot_load\n\t"
-        "buffer_load_dwordx4 v[176:179], %0, %2, 0 offen ; slot_load\n\t"
-        "buffer_load_dwordx4 v[180:183], %0, %2, 0 offen offset:1024 ; slot_load"
+        "buffer_load_dwordx4 v[168:171], %0, %1, 0 offen nt ; slot_load\n\t"
+        "buffer_load_dwordx4 v[172:175], %0, %1, 0 offen offset:1024 nt ; slot_load\n\t"
+        "buffer_load_dwordx4 v[176:179], %0, %2, 0 offen nt ; slot_load\n\t"
+        "buffer_load_dwordx4 v[180:183], %0, %2, 0 offen offset:1024 nt ; slot_load"
         :
         : "v"(o), "s"(ra), "s"(rb)
         : "memory", "v168", "v169", "v170", "v171", "v172", "v173", "v174", "v175", "v176", "v177", "v178", "v179", "v180", "v181", "v182", "v183");
@@ -280,10 +312,10 @@ template <>
 __device__ __forceinline__ void slot_loads<1>(uint32_t o, v4u ra, v4u rb) {
     asm volatile(
         "s_nop 4\n\t"
-        "buffer_load_dwordx4 v[184:187], %0, %1, 0 offen ; slot_load\n\t"
-        "buffer_load_dwordx4 v[188:191], %0, %1, 0 offen offset:1024 ; slot_load\n\t"
-        "buffer_load_dwordx4 v[192:195], %0, %2, 0 offen ; slot_load\n\t"
-        "buffer_load_dwordx4 v[196:199], %0, %2, 0 offen offset:1024 ; slot_load"
+        "buffer_load_dwordx4 v[184:187], %0, %1, 0 offen nt ; slot_load\n\t"
+        "buffer_load_dwordx4 v[188:191], %0, %1, 0 offen offset:1024 nt ; slot_load\n\t"
+        "buffer_load_dwordx4 v[192:195], %0, %2, 0 offen nt ; slot_load\n\t"
+        "buffer_load_dwordx4 v[196:199], %0, %2, 0 offen offset:1024 nt ; slot_load"
         :
         : "v"(o), "s"(ra), "s"(rb)
         : "memory", "v184", "v185", "v186", "v187", "v188", "v189", "v190", "v191", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199");
@@ -292,10 +324,10 @@ template <>
 __device__ __forceinline__ void slot_loads<2>(uint32_t o, v4u ra, v4u rb) {
     asm volatile(
         "s_nop 4\n\t"
-        "buffer_load_dwordx4 v[200:203], %0, %1, 0 offen ; slot_load\n\t"
-        "buffer_load_dwordx4 v[204:207], %0, %1, 0 offen offset:1024 ; slot_load\n\t"
-        "buffer_load_dwordx4 v[208:211], %0, %2, 0 offen ; slot_load\n\t"
-        "buffer_load_dwordx4 v[212:215], %0, %2, 0 offen offset:1024 ; slot_load"
+        "buffer_load_dwordx4 v[200:203], %0, %1, 0 offen nt ; slot_load\n\t"
+        "buffer_load_dwordx4 v[204:207], %0, %1, 0 offen offset:1024 nt ; slot_load\n\t"
+        "buffer_load_dwordx4 v[208:211], %0, %2, 0 offen nt ; slot_load\n\t"
+        "buffer_load_dwordx4 v[212:215], %0, %2, 0 offen offset:1024 nt ; slot_load"
         :
         : "v"(o), "s"(ra), "s"(rb)
         : "memory", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215");
@@ -304,10 +336,10 @@ template <>
 __device__ __forceinline__ void slot_loads<3>(uint32_t o, v4u ra, v4u rb) {
     asm volatile(
         "s_nop 4\n\t"
-        "buffer_load_dwordx4 v[216:219], %0, %1, 0 offen ; slot_load\n\t"
-        "buffer_load_dwordx4 v[220:223], %0, %1, 0 offen offset:1024 ; slot_load\n\t"
-        "buffer_load_dwordx4 v[224:227], %0, %2, 0 offen ; slot_load\n\t"
-        "buffer_load_dwordx4 v[228:231], %0, %2, 0 offen offset:1024 ; slot_load"
+        "buffer_load_dwordx4 v[216:219], %0, %1, 0 offen nt ; slot_load\n\t"
+        "buffer_load_dwordx4 v[220:223], %0, %1, 0 offen offset:1024 nt ; slot_load\n\t"
+        "buffer_load_dwordx4 v[224:227], %0, %2, 0 offen nt ; slot_load\n\t"
+        "buffer_load_dwordx4 v[228:231], %0, %2, 0 offen offset:1024 nt ; slot_load"
         :
         : "v"(o), "s"(ra), "s"(rb)
         : "memory", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231");
@@ -556,6 +588,75 @@ __device__ __forceinline__ bool stage_copy(const KParams &P, Ctx &c, const Ins &
 // Attention staging: the group's queries rotated (fp32, act[0, G*64)), and
 // the new K/V entry rotated and rounded to bf16 (act + G*64 as uint16 [2][64]);
 // the last chunk also appends that entry to the cache.
+// act[b] <- o of every query head (the O projection's input): the attention
+// tiles of the layer publish one softmax state (o, m, l) per chunk and head,
+// and the O projection merges them here, in chunk order, so that attention
+// needs no merging tile and no second exchange. Wave w takes heads w + 8 j
+// (j < HPW, HPW a power of two); a round gathers, per lane, the o words of
+// up to 32 / HPW chunks of each of its heads plus one of the round's 64 m/l
+// words, which the merge then reads back with v_readlane.
+constexpr int GW = 16;  // o words per lane and round of the O projection's merge gather
+
+template <int G, int HPW>
+__device__ __forceinline__ bool stage_attn_merge_h(const KParams &P, Ctx &c, const Ins &in) {
+    constexpr int LG = HPW == 1 ? 0 : HPW == 2 ? 1 : HPW == 4 ? 2 : 3;
+    constexpr int CPR = GW / HPW;  // chunks per round
+    const int lane = c.lane, nch = P.attn_chunks, nq = P.nq;
+    for (int b = 0; b < P.B; ++b) {
+        const size_t pb = ((size_t)in.layer * P.B + b) * P.nkv * nch * G * ATTN_PART;
+        const __amdgpu_buffer_rsrc_t r = tres(P.tpart + pb, (uint32_t)(P.nkv * nch * G * ATTN_PART));
+        // word of (head hq, chunk cc, element e)
+        auto word = [&](int hq, int cc, int e) {
+            return (uint32_t)((((hq / G) * nch + cc) * G + hq % G) * ATTN_PART + e);
+        };
+        float O[HPW], M[HPW], L[HPW];
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) merge_init(O[j], M[j], L[j]);
+        for (int c0 = 0; c0 < nch; c0 += CPR) {
+            float ov[GW + 1];  // o words of (head j, chunk c0 + (k >> LG)), k = (chunk - c0) HPW + j; [GW]: m/l word
+            // m/l word of this lane: t = ((cc - c0) << (LG + 1)) | (j << 1) | which
+            const int tj = (lane >> 1) & (HPW - 1), tc = c0 + (lane >> (LG + 1));
+            const int thq = c.w + 8 * tj;
+            const bool tok = tc < nch && thq < nq;
+            // words outside the heads or chunks read word 0, which this step writes too
+            if (!tgather_all<GW + 1>(
+                    c, r,
+                    [&](int k) {
+                        if (k == GW) return tok ? word(thq, tc, 64 + (lane & 1)) : 0u;
+                        const int j = k & (HPW - 1), cc = c0 + (k >> LG), hq = c.w + 8 * j;
+                        return (cc < nch && hq < nq) ? word(hq, cc, lane) : 0u;
+                    },
+                    ov, in.pc))
+                return false;
+            const float ml = ov[GW];
+#pragma unroll
+            for (int k = 0; k < GW; ++k) {
+                const int j = k & (HPW - 1), cc = c0 + (k >> LG);
+                if (cc < nch) {
+                    const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml), (k << 1)));
+                    const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml), (k << 1) + 1));
+                    merge_step(O[j], M[j], L[j], ov[k], m, l);
+                }
+            }
+        }
+        MK_LDS float *a = c.act + b * P.act_stride;
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+            const int hq = c.w + 8 * j;
+            if (hq < nq) a[act_index(hq * 64 + lane)] = O[j] / L[j];
+        }
+    }
+    return true;
+}
+template <int G>
+__device__ __forceinline__ bool stage_attn_merge(const KParams &P, Ctx &c, const Ins &in) {
+    const int hpw = (P.nq + NC - 1) / NC;
+    if (hpw <= 1) return stage_attn_merge_h<G, 1>(P, c, in);
+    if (hpw <= 2) return stage_attn_merge_h<G, 2>(P, c, in);
+    if (hpw <= 4) return stage_attn_merge_h<G, 4>(P, c, in);
+    return stage_attn_merge_h<G, 8>(P, c, in);
+}
+
 template <int G>
 __device__ __forceinline__ bool stage_attn(const KParams &P, Ctx &c, const Ins &in) {
     const int lane = c.lane;
@@ -629,7 +730,7 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
         case OP_LMHEAD: ok = stage_norm(P, c, in, (const uint16_t *)(uintptr_t)in.wn, 2 * P.L); break;
         case OP_OPROJ:
             ok = stage_rows(P, c, in, (in.flags & F_X_FROM_INPUT) ? 0 : 2 * in.layer) &&
-                 stage_copy(P, c, in, P.to + (size_t)in.layer * P.B * P.nq * P.d, P.nq * P.d) && cbar(c, pc);
+                 stage_attn_merge<G>(P, c, in) && cbar(c, pc);
             break;
         case OP_DOWN:
             ok = stage_rows(P, c, in, 2 * in.layer + 1) &&
@@ -824,37 +925,18 @@ template <int G>
 __device__ __forceinline__ bool finish(const KParams &P, Ctx &c, const Ins &in) {
     const int lane = c.lane;
     const uint32_t tag = P.tag;
-    if (in.op == OP_ATTN) {
-        const int QD = P.nq * P.d;
-        const int b = in.b, g = in.g, nch = in.nch;
-        const __amdgpu_buffer_rsrc_t ro = tres(P.to + ((size_t)in.layer * P.B + b) * QD, (uint32_t)QD);
-        const size_t pbase = (((size_t)in.layer * P.B + b) * P.nkv + g) * nch * G * ATTN_PART;
-        const __amdgpu_buffer_rsrc_t rp = tres(P.tpart + pbase, (uint32_t)(nch * G * ATTN_PART));
+    if (in.op == OP_ATTN) {  // the chunk's state of each head, merged over the waves
+        const size_t pbase = ((((size_t)in.layer * P.B + in.b) * P.nkv + in.g) * in.nch + in.c) * G * ATTN_PART;
+        const __amdgpu_buffer_rsrc_t rp = tres(P.tpart + pbase, (uint32_t)(G * ATTN_PART));
+#pragma unroll 1
         for (int h = 0; h < G; ++h) {
-            float o, m, l;
-            merge_parts(nullptr, c.part + h * ATTN_WAVE_PART, NC, G * ATTN_WAVE_PART, lane, &o, &m, &l);
-            if (nch == 1) {
-                tput(ro, (uint32_t)((g * G + h) * 64 + lane), o / l, tag);
-            } else {
-                const uint32_t e = (uint32_t)((in.c * G + h) * ATTN_PART);
-                tput(rp, e + lane, o, tag);
-                if (lane == 0) {
-                    tput(rp, e + 64, m, tag);
-                    tput(rp, e + 65, l, tag);
-                }
+            float O, M, L;
+            merge_wave_states<G, NC>(c.part, h, lane, O, M, L);
+            tput(rp, (uint32_t)(h * ATTN_PART + lane), O, tag);
+            if (lane == 0) {
+                tput(rp, (uint32_t)(h * ATTN_PART + 64), M, tag);
+                tput(rp, (uint32_t)(h * ATTN_PART + 65), L, tag);
             }
-        }
-        if (nch == 1 || !elect_last(P, c, in)) return true;
-        if (in.tr && lane == 0) in.tr[TR_ELECT] = wall_clock64();
-        // the last chunk to finish merges all chunks, in chunk order
-        if (!tgather_range(
-                c, rp, 0, nch * G * ATTN_PART, [&](int i, float v) { c.part[i] = v; }, in.pc))
-            return false;
-        if (in.tr && lane == 0) in.tr[TR_GATHER] = wall_clock64();
-        for (int h = 0; h < G; ++h) {
-            float o, m, l;
-            merge_parts(nullptr, c.part + h * ATTN_PART, nch, G * ATTN_PART, lane, &o, &m, &l);
-            tput(ro, (uint32_t)((g * G + h) * 64 + lane), o / l, tag);
         }
         return true;
     }

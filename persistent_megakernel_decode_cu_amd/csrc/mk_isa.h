@@ -84,6 +84,9 @@ constexpr int MAX_B = 8;
 constexpr int TRACE_WORDS = 8;  // MK_TRACE_WORDS of mk.h
 enum : int { TR_START = 0, TR_READY = 1, TR_END = 2, TR_FIRST = 3, TR_LAST = 4, TR_ELECT = 5, TR_GATHER = 6 };
 constexpr int MAX_G = 8;
+// K/V chunks per (request, kv head): the O projection merges the chunks'
+// softmax states while it stages its input, which bounds their number
+constexpr int MAX_ATTN_CHUNKS = 16;
 
 // device error word: code << 28 | cu << 16 | pc
 enum : int32_t { ERR_TIMEOUT = 1, ERR_OPCODE = 2, ERR_RANGE = 3, ERR_NAN = 4 };

@@ -37,7 +37,6 @@ struct KParams {
     // high: tag), each written once per step
     uint64_t *tx;      // [2L][B][H]: x_1 .. x_{2L} (x_v at index v - 1)
     uint64_t *tqkv;    // [L][B][(nq + 2 nkv) d]
-    uint64_t *to;      // [L][B][nq d]
     uint64_t *tact;    // [L][B][F]
     uint64_t *tpart;   // [L][B][nkv][chunks][G][ATTN_PART] attention chunk partials
     uint64_t *tlm;     // [lm slots][B][2] argmax partials (value, index)

@@ -147,8 +147,12 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     const int nb_max = (maxlen + 1 + T - 1) / T;
     // enough chunks that one chunk's K/V blocks fit in its workgroup's
     // prefetch window (N_COMPUTE_WAVES waves x PREFETCH_SLICES blocks)
+    if (desc.attn_chunks > MAX_ATTN_CHUNKS)
+        return set_error(MK_EINVAL, "attn_chunks above " + std::to_string(MAX_ATTN_CHUNKS));
+    // about one K/V block per wave: attention is short arithmetic on few
+    // units, so it is spread as wide as the merge in the O projection allows
     int C = desc.attn_chunks > 0 ? desc.attn_chunks
-                                 : std::max(1, ceil_div(nb_max, N_COMPUTE_WAVES * PREFETCH_SLICES));
+                                 : std::min(MAX_ATTN_CHUNKS, std::max(1, ceil_div(nb_max, N_COMPUTE_WAVES)));
     C = std::min(C, nb_max);
     P.attn_chunks = C;
     P.n_cus = S;
@@ -199,11 +203,10 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     for (int l = 0; l < L; ++l) {
         const int first = l == 0 ? F_X_FROM_INPUT : 0;
         matvec_op(OP_QKV, l, QKV, (int64_t)H * 2, first);
-        // attention chunks; with several chunks the last of each (b, g) to
-        // finish merges them
+        // attention chunks; each publishes its softmax state, which the O
+        // projection tiles merge
         for (int b = 0; b < B; ++b)
             for (int g = 0; g < nkv; ++g) {
-                const int ev = C > 1 ? new_merge(C) : -1;
                 for (int c = 0; c < C; ++c) {
                     Tile t;
                     t.op = OP_ATTN;
@@ -212,7 +215,7 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
                     t.g = g;
                     t.c = c;
                     t.nch = C;
-                    t.merge = ev;
+                    t.merge = -1;
                     t.slot = c;
                     t.nslot = C;
                     int lo, hi;
@@ -301,8 +304,7 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     const int kmax = std::max(H, std::max(F, QD));
     P.act_stride = (kmax + 511) / 512 * 512;
     P.xrow_stride = (max_rows_x + 3) / 4 * 4;
-    const int64_t part_floats = std::max<int64_t>((int64_t)N_COMPUTE_WAVES * G * ATTN_WAVE_PART,
-                                                  (int64_t)C * G * ATTN_PART);
+    const int64_t part_floats = (int64_t)N_COMPUTE_WAVES * G * ATTN_WAVE_PART;
     const int64_t act_floats = std::max<int64_t>({(int64_t)NBP * P.act_stride, (int64_t)G * 64 + 64,
                                                   (int64_t)P.n_lm_slots * B * 2});
     auto up256 = [](int64_t x) { return (x + 255) / 256 * 256; };

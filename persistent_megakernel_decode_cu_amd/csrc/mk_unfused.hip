@@ -190,27 +190,30 @@ __global__ __launch_bounds__(UF_ATTN_THREADS) void uf_attn(KParams P, int layer,
     __syncthreads();
     if (wave == 0) {
         for (int hq = 0; hq < G; ++hq) {
-            float o, m, l;
-            merge_parts(nullptr, (const MK_LDS float *)(part + hq * ATTN_WAVE_PART), NW, G * ATTN_WAVE_PART, lane, &o,
-                        &m, &l);
+            float O, M, Ls;
+            merge_wave_states<G, NW>((const MK_LDS float *)part, hq, lane, O, M, Ls);
             float *dst = P.attn_part + ((((int64_t)b * P.nkv + g) * nch + c) * G + hq) * ATTN_PART_STRIDE;
-            dst[lane] = o;
+            dst[lane] = O;
             if (lane == 0) {
-                dst[64] = m;
-                dst[65] = l;
+                dst[64] = M;
+                dst[65] = Ls;
             }
         }
     }
 }
 
+// Chunk states of each head merged in chunk order, then o = O / L.
 __global__ __launch_bounds__(64) void uf_attn_merge(KParams P, int nch) {
     const int g = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
     const int G = P.nq / P.nkv;
     for (int hq = 0; hq < G; ++hq) {
-        const float *src = P.attn_part + (((int64_t)b * P.nkv + g) * nch * G + hq) * ATTN_PART_STRIDE;
-        float o, m, l;
-        merge_parts(src, nullptr, nch, G * ATTN_PART_STRIDE, lane, &o, &m, &l);
-        P.o[(int64_t)b * P.nq * P.d + (g * G + hq) * 64 + lane] = o / l;
+        float O, M, L;
+        merge_init(O, M, L);
+        for (int c = 0; c < nch; ++c) {
+            const float *src = P.attn_part + ((((int64_t)b * P.nkv + g) * nch + c) * G + hq) * ATTN_PART_STRIDE;
+            merge_step(O, M, L, src[lane], src[64], src[65]);
+        }
+        P.o[(int64_t)b * P.nq * P.d + (g * G + hq) * 64 + lane] = O / L;
     }
 }
 

@@ -128,13 +128,15 @@ def dependencies(shape, batch: int, ins):
                 writers[("act", i.layer)].append((b * F + i.r0, b * F + i.r1, node))
             elif i.op == I["OP_DOWN"]:
                 writers[("x", 2 * i.layer + 2)].append((b * H + i.r0, b * H + i.r1, node))
-        if i.op == I["OP_ATTN"]:
-            onode = ("m", i.merge) if i.nch > 1 else node
-            if i.nch == 1 or i.c == 0:
-                lo = i.b * QD + i.g * G * d
-                writers[("o", i.layer)].append((lo, lo + G * d, onode))
+        if i.op == I["OP_ATTN"]:  # one softmax state per (request, kv head, chunk)
+            lo = (i.b * nkv + i.g) * i.nch + i.c
+            writers[("opart", i.layer)].append((lo, lo + 1, node))
     for k in writers:
         writers[k].sort()
+    n_chunks = defaultdict(int)
+    for i in ins:
+        if i.op == I["OP_ATTN"]:
+            n_chunks[i.layer] = i.nch
 
     def producers(buf, lo, hi):
         out = set()
@@ -162,8 +164,9 @@ def dependencies(shape, batch: int, ins):
                 g = i.g
                 for lo, n in ((g * G * d, G * d), (QD + g * d, d), (QD + nkv * d + g * d, d)):
                     need |= producers(("qkv", i.layer), b * QKV + lo, b * QKV + lo + n)
-            elif i.op == I["OP_OPROJ"]:
-                need |= producers(("o", i.layer), b * QD, (b + 1) * QD)
+            elif i.op == I["OP_OPROJ"]:  # merges every chunk state of the request
+                nch = n_chunks[i.layer]
+                need |= producers(("opart", i.layer), b * nkv * nch, (b + 1) * nkv * nch)
                 if not first:
                     need |= producers(("x", 2 * i.layer), b * H + i.r0, b * H + i.r1)
             elif i.op == I["OP_UPGATE"]:
@@ -220,13 +223,12 @@ def validate(shape, batch: int, queue: np.ndarray, events: np.ndarray, attn_chun
         _req(sorted(m.slot for m in mem) == list(range(need)), f"merge event {e}: slots not 0..n-1")
         ops = {m.op for m in mem}
         _req(len(ops) == 1, f"merge event {e} mixes ops")
-        if I["OP_ATTN"] in ops:
-            keys = {(m.layer, m.b, m.g) for m in mem}
-            _req(len(keys) == 1, f"merge event {e} mixes attention heads")
+        _req(I["OP_ATTN"] not in ops, f"merge event {e} on attention tiles (the O projection merges chunks)")
     for i in ins:
         _req(i.merge < ne, "merge of an unknown event")
         if i.op == I["OP_ATTN"]:
-            _req((i.merge >= 0) == (i.nch > 1), "split attention needs a merge event, whole attention none")
+            _req(i.merge < 0, "attention tiles publish chunk states without a merge event")
+            _req(1 <= i.nch <= ISA["MAX_ATTN_CHUNKS"], "attention chunk count out of range")
         if i.op == I["OP_LMHEAD"]:
             _req(i.merge >= 0, "LM-head tiles need the argmax merge")
     # every input is produced earlier in the global order

@@ -60,12 +60,20 @@ def test_streamed_bytes_match_the_byte_model():
     assert p.info.stream_bytes_max_cu <= 1.02 * p.info.stream_bytes_total / 256
 
 
-def test_auto_chunks_fit_the_prefetch_window():
-    # one chunk's K/V blocks fit the waves' register slots (8 waves x 4)
-    for name in ("1b-kv1024", "1b-kv8192"):
+def test_auto_chunks_about_one_block_per_wave():
+    # attention is spread so that each of a tile's 8 waves takes about one
+    # 16-position K/V block, up to the chunk limit of the O projection's merge
+    for name in ("tiny-2l", "1b-kv1024", "1b-kv8192"):
         w, B, maxlen, p = plan_for(name, 256)
         nb = (maxlen + 1 + 15) // 16
-        assert -(-nb // p.info.attn_chunks) <= 8 * p.info.prefetch_slices
+        want = min(nb, sched_check.ISA["MAX_ATTN_CHUNKS"], max(1, -(-nb // 8)))
+        assert p.info.attn_chunks == want, (name, p.info.attn_chunks, want)
+
+
+def test_attention_chunks_above_the_limit_are_rejected():
+    with pytest.raises(_mk.MkError) as ex:
+        plan_for("1b-kv1024", 256, chunks=sched_check.ISA["MAX_ATTN_CHUNKS"] + 1)
+    assert ex.value.code == _mk.MK_EINVAL
 
 
 @pytest.mark.parametrize("name,n_cus,steps", [("tiny-2l", 8, 2000), ("tiny-2l", 256, 50),
@@ -81,11 +89,10 @@ def test_simulator_reports_injected_deadlocks():
     w, B, maxlen, p = plan_for("tiny-2l", 8, chunks=2)
     ins = sched_check.decode(p.queue)
     I = sched_check.ISA
-    # a merge that can never complete: its output is never written
-    merged = next(i for i in ins if i.op == I["OP_ATTN"])
-    need = int(p.events[merged.merge, I["EV_NEED"]])
+    # an attention chunk whose softmax state never arrives: the O projection waits on it
+    chunk = next(i for i in ins if i.op == I["OP_ATTN"] and i.layer == 0)
     with pytest.raises(sched_check.Deadlock) as ex:
-        sched_check.simulate(w, B, p.queue, p.events, 3, need_override={merged.merge: need + 1})
+        sched_check.simulate(w, B, p.queue, p.events, 3, drop=chunk.seq)
     assert "blocked" in str(ex.value)
     # a producer whose rows never arrive
     producer = next(i for i in ins if i.op == I["OP_UPGATE"])
