@@ -80,6 +80,11 @@ def main():
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", default="megakernel", choices=["megakernel", "unfused"])
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after timing, run the plain copy kernel three times over this many bytes "
+                         "(the reference for the rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU oracle sample: consecutive decode steps until this much time has passed")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the decode step is measured on one MI355X); got --gpus {args.gpus}",
@@ -121,6 +126,24 @@ def main():
     lens_timed = [int(st0.kv_lens[0]) + args.warmup + s for s in range(args.steps)]
     bytes_avg = float(np.mean([algorithmic_bytes(cfg, [n]) for n in lens_timed]))
     achieved = bytes_avg / (ms * 1e-3) / 1e9
+    if args.copy_bytes > 0:
+        from persistent_megakernel_decode_cu_amd import _mk
+        n = args.copy_bytes // 16 * 16
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            _mk.mk_debug_copy_probe(src.data_ptr(), dst.data_ptr(), n, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert torch.equal(src, dst)
+        del src, dst
+    # HBM traffic per launch, measured with rocprofv3 counters (see the summary
+    # file); reported only while the kernel sources are the ones it was taken on
+    traffic = None
+    if args.mode == "megakernel":
+        from persistent_megakernel_decode_cu_amd import profile_summary
+        rec = profile_summary.read_traffic(os.path.join(ROOT, "profiles", f"traffic_megakernel_{cfg.name}.txt"))
+        if rec is not None and rec[1] == profile_summary.digest():
+            traffic = int(rec[0])
     out = {
         "metric": "us/decode-step and achieved HBM GB/s (% of peak), 1B-shape batch 1",
         "value": round(ms * 1000.0, 2),
@@ -139,7 +162,7 @@ def main():
                    "mode": args.mode, "n_cus": info["n_cus"], "launches_per_step": info["launches_per_step"]},
         "hbm_gbps": round(achieved, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
                      "bytes_per_launch": int(bytes_avg)},
     }
     if "unfused" in result_modes and args.mode != "unfused":
@@ -148,16 +171,25 @@ def main():
                           "hbm_gbps": round(bytes_avg / (ums * 1e-3) / 1e9, 1),
                           "speedup_of_megakernel": round(ums / ms, 3)}
     if not args.no_cpu_baseline:
+        # the oracle as it stands (single-threaded fp64 C), on consecutive greedy
+        # steps of the same workload until the sample time has passed
         from oracle import Oracle
         ora = Oracle("f64")
         ost = st0.copy()
-        t = time.time()
-        r = ora.decode_step(model, ost)
-        dt = time.time() - t
-        assert r["rc"] == 0
-        out["cpu_baseline"] = {"value": round(dt * 1e6, 1), "unit": "us/step", "cores": 1, "kind": "oracle",
-                               "sample": f"one full decode step of {cfg.name} (same weights, K/V length "
-                                         f"{int(st0.kv_lens[0])}), single-threaded fp64 C oracle"}
+        n, t = 0, time.time()
+        while True:
+            r = ora.decode_step(model, ost)
+            assert r["rc"] == 0
+            ost.tokens[:] = r["tokens"]
+            ost.kv_lens += 1
+            n += 1
+            dt = time.time() - t
+            if dt >= args.cpu_seconds or n >= 64:
+                break
+        out["cpu_baseline"] = {"value": round(dt / n * 1e6, 1), "unit": "us/step", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} consecutive greedy decode steps of {cfg.name} from K/V length "
+                                         f"{int(st0.kv_lens[0])} (same weights and cache), single-threaded fp64 C "
+                                         f"oracle, {dt:.1f} s"}
     dec.close()
     print(json.dumps(out), flush=True)
 

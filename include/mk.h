@@ -227,6 +227,13 @@ int mk_debug_ring_probe(const void *src, size_t src_bytes, int n_granules, int r
  * bandwidth. Asynchronous on the null stream. Errors: MK_EINVAL, MK_EHIP. */
 int mk_debug_stream_probe(const void *src, size_t bytes, int blocks, void *out_dev);
 
+/* Plain device copy of `bytes` (a multiple of 16) from src_dev to dst_dev on
+ * `stream` (a hipStream_t, NULL: the null stream), each byte read and written
+ * once: the reference whose HBM traffic counters (FETCH_SIZE, WRITE_SIZE)
+ * scale those measured for the decode kernels. Asynchronous. Errors:
+ * MK_EINVAL (null pointer, size not a positive multiple of 16), MK_EHIP. */
+int mk_debug_copy_probe(const void *src_dev, void *dst_dev, size_t bytes, void *stream);
+
 /* Cross-XCD message-passing litmus: `pairs` writer/reader workgroup pairs
  * (co-resident, cooperative launch) run `rounds` rounds over `n_words` int32
  * words each (data_dev: pairs * n_words int32; flags_dev: pairs * 64 int32,

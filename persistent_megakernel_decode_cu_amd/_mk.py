@@ -83,6 +83,7 @@ _SIGS = {
     "mk_debug_dma_probe": (i32, [vp, vp, i32, i32]),
     "mk_debug_ring_probe": (i32, [vp, ctypes.c_size_t, i32, i32, i32, i32, vp, i32, vp]),
     "mk_debug_stream_probe": (i32, [vp, ctypes.c_size_t, i32, vp]),
+    "mk_debug_copy_probe": (i32, [vp, vp, ctypes.c_size_t, vp]),
     "mk_debug_litmus": (i32, [i32, i32, i32, i32, vp, vp, vp]),
     "mk_debug_hop_probe": (i32, [vp, ctypes.c_size_t, vp, ctypes.c_size_t, i32, i32, i32, vp]),
     "mk_debug_ll_probe": (i32, [vp, ctypes.c_size_t, i32, i32, i32, i32, vp]),
@@ -166,6 +167,10 @@ def mk_debug_copy_scratch(handle: int, which: str, n_floats: int) -> np.ndarray:
     out = np.zeros(n_floats, dtype=np.float32)
     _check(lib().mk_debug_copy_scratch(handle, SCRATCH[which], out.ctypes.data, out.nbytes))
     return out
+
+
+def mk_debug_copy_probe(src_ptr: int, dst_ptr: int, nbytes: int, stream: int = 0) -> None:
+    _check(lib().mk_debug_copy_probe(src_ptr, dst_ptr, nbytes, stream))
 
 
 def mk_debug_dma_probe(src_ptr: int, dst_ptr: int, n_kib: int, lds_offset_kib: int = 0) -> None:

@@ -487,6 +487,12 @@ int mk_debug_stream_probe(const void *src, size_t bytes, int blocks, void *out_d
     return MK_OK;
 }
 
+int mk_debug_copy_probe(const void *src_dev, void *dst_dev, size_t bytes, void *stream) {
+    if (!src_dev || !dst_dev || bytes < 16 || bytes % 16) return set_error(MK_EINVAL, "bad copy arguments");
+    MK_HIP(mk::copy_probe(src_dev, dst_dev, bytes, (hipStream_t)stream));
+    return MK_OK;
+}
+
 int mk_debug_litmus(int pairs, int n_words, int rounds, int mode, int32_t *data_dev, int32_t *flags_dev,
                     int32_t *res_dev) {
     if (pairs < 1 || pairs > 128 || n_words < 1 || rounds < 1 || mode < 0 || mode > 1 || !data_dev || !flags_dev ||

@@ -64,6 +64,7 @@ hipError_t launch_unfused(const KParams &p, float *u_scratch, float *qrot, hipSt
 hipError_t dma_probe(const void *src, void *dst, int n_kib, int off_kib);
 hipError_t ring_probe(const void *src, int n, int ring, int depth, int variant, int32_t *errs, int blocks);
 hipError_t stream_probe(const void *src, size_t bytes, int blocks, uint32_t *out);
+hipError_t copy_probe(const void *src, void *dst, size_t bytes, hipStream_t s);
 hipError_t litmus(int pairs, int n, int rounds, int mode, int32_t *data, int32_t *flags, int32_t *res);
 hipError_t hop_probe(int32_t *ctr, float *xbuf, int n_cus, int rounds, int variant, int32_t *res);
 hipError_t ll_probe(uint64_t *buf, int n_cus, int per, int copies, int rounds, int32_t *res);

@@ -700,4 +700,16 @@ hipError_t stream_probe(const void *src, size_t bytes, int blocks, uint32_t *out
     return hipGetLastError();
 }
 
+// Plain device copy of n16 16-byte words: each word is read once and written
+// once, so its traffic counters calibrate those of the other kernels.
+__global__ __launch_bounds__(256) void mk_copy_probe(const v4u *src, v4u *dst, size_t n16) {
+    const size_t stride = (size_t)gridDim.x * 256;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+hipError_t copy_probe(const void *src, void *dst, size_t bytes, hipStream_t s) {
+    hipLaunchKernelGGL(mk_copy_probe, dim3(2048), dim3(256), 0, s, (const v4u *)src, (v4u *)dst, bytes / 16);
+    return hipGetLastError();
+}
+
 }  // namespace mk
