@@ -87,6 +87,8 @@ constexpr int MAX_G = 8;
 // K/V chunks per (request, kv head): the O projection merges the chunks'
 // softmax states while it stages its input, which bounds their number
 constexpr int MAX_ATTN_CHUNKS = 16;
+// chunks the automatic choice stops at: one gather round of the O projection's merge
+constexpr int AUTO_ATTN_CHUNKS = 8;
 
 // device error word: code << 28 | cu << 16 | pc
 enum : int32_t { ERR_TIMEOUT = 1, ERR_OPCODE = 2, ERR_RANGE = 3, ERR_NAN = 4 };

@@ -152,7 +152,7 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     // about one K/V block per wave: attention is short arithmetic on few
     // units, so it is spread as wide as the merge in the O projection allows
     int C = desc.attn_chunks > 0 ? desc.attn_chunks
-                                 : std::min(MAX_ATTN_CHUNKS, std::max(1, ceil_div(nb_max, N_COMPUTE_WAVES)));
+                                 : std::min(AUTO_ATTN_CHUNKS, std::max(1, ceil_div(nb_max, N_COMPUTE_WAVES)));
     C = std::min(C, nb_max);
     P.attn_chunks = C;
     P.n_cus = S;

@@ -62,11 +62,12 @@ def test_streamed_bytes_match_the_byte_model():
 
 def test_auto_chunks_about_one_block_per_wave():
     # attention is spread so that each of a tile's 8 waves takes about one
-    # 16-position K/V block, up to the chunk limit of the O projection's merge
+    # 16-position K/V block, up to the chunks one gather round of the O
+    # projection's merge covers
     for name in ("tiny-2l", "1b-kv1024", "1b-kv8192"):
         w, B, maxlen, p = plan_for(name, 256)
         nb = (maxlen + 1 + 15) // 16
-        want = min(nb, sched_check.ISA["MAX_ATTN_CHUNKS"], max(1, -(-nb // 8)))
+        want = min(nb, sched_check.ISA["AUTO_ATTN_CHUNKS"], max(1, -(-nb // 8)))
         assert p.info.attn_chunks == want, (name, p.info.attn_chunks, want)
 
 
