@@ -12,7 +12,12 @@ code must satisfy, and this check proves on the assembly of every kernel:
 2. every `slot_take` copy is preceded, on every path from the loads, by a
    `slot_wait` (an s_waitcnt vmcnt) -- checked locally: each run of copies
    follows a wait in the same basic block with no label in between;
-3. the kernel descriptor allocates the slot registers.
+3. the kernel descriptor allocates the slot registers;
+4. the slice loop (the innermost loop around the first slot_wait, found by
+   the compiler's loop annotations) holds no compiler-inserted vmcnt wait:
+   the compiler does not see the slice loads, so any wait it places there
+   for its own loads (a spill reload, say) is a vmcnt(0) that drains every
+   slice in flight.
 
 Usage: python -m persistent_megakernel_decode_cu_amd.check_isa file.s ...
 """
@@ -56,6 +61,7 @@ def check_kernel(body):
     waited = False   # a slot_wait seen in this basic block
     n_load = n_take = 0
     max_compiler = -1
+    top_slot = -1
     for i, l in enumerate(body):
         code, _, comment = l.partition(";")
         code = code.strip()
@@ -70,6 +76,7 @@ def check_kernel(body):
             continue
         if "slot_load" in comment:
             n_load += 1
+            top_slot = max([top_slot] + list(_regs(code.split(",")[0])))
             if not code.startswith("buffer_load_dwordx4") or min(_regs(code.split(",")[0])) < SLOT_VGPR0:
                 problems.append(f"line {i}: malformed slot load '{code}'")
             continue
@@ -86,7 +93,40 @@ def check_kernel(body):
             if hi >= SLOT_VGPR0:
                 problems.append(f"line {i}: compiler instruction names a slot register: '{code}'")
             max_compiler = max(max_compiler, hi)
-    return problems, n_load, n_take, max_compiler
+    return problems, n_load, n_take, max_compiler, top_slot
+
+
+def slice_loop_waits(body):
+    """(loop header, lines in the loop, [compiler vmcnt waits in it])."""
+    first = next((i for i, l in enumerate(body) if "slot_wait" in l), None)
+    if first is None:
+        return None, 0, []
+    hdr = None
+    for i in range(first, -1, -1):
+        m = re.search(r"Loop: Header=(BB\S+) Depth=\d+", body[i])
+        if m:
+            hdr = m.group(1)
+            break
+        m = re.match(r"^\.L(BB\S+):.*Loop Header: Depth=\d+", body[i])
+        if m:
+            hdr = m.group(1)
+            break
+    if hdr is None:
+        return None, 0, []
+    inloop, n, bad = False, 0, []
+    for i, l in enumerate(body):
+        m = re.match(r"^\.L(BB\S+):(.*)$", l)
+        if m:
+            inloop = m.group(1) == hdr or f"Header={hdr} " in m.group(2)
+            continue
+        if re.match(r"^; %bb\.\d+:", l):
+            inloop = f"Header={hdr} " in l
+            continue
+        if inloop:
+            n += 1
+            if "s_waitcnt" in l and "vmcnt" in l and "slot_wait" not in l:
+                bad.append(f"line {i}: compiler vmcnt wait in the slice loop: '{l.strip()}'")
+    return hdr, n, bad
 
 
 def main(paths):
@@ -97,12 +137,13 @@ def main(paths):
         counts = {m.group(1): int(m.group(2))
                   for m in re.finditer(r"\.name:\s+(\S+)[\s\S]*?\.vgpr_count:\s+(\d+)", txt)}
         for name, body in _kernels(lines):
-            pr, n_load, n_take, mx = check_kernel(body)
+            pr, n_load, n_take, mx, top = check_kernel(body)
+            _, _, loop_waits = slice_loop_waits(body)
             vg = counts.get(name)
-            if n_load and (vg is None or vg < SLOT_VGPR0 + 64):
-                pr.append(f"kernel allocates {vg} VGPRs, below the slot registers")
+            if n_load and (vg is None or vg <= top):
+                pr.append(f"kernel allocates {vg} VGPRs, not covering slot register v{top}")
             print(f"{p}: {name}: {n_load} slot loads, {n_take} slot copies, compiler VGPRs <= v{mx}, "
-                  f"{vg} allocated: {len(pr)} problems")
+                  f"{vg} allocated: {len(pr)} problems, {len(loop_waits)} slice-loop waits")
             for x in pr[:10]:
                 print("   ", x)
             bad += len(pr)

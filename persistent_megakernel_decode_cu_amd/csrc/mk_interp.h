@@ -916,7 +916,7 @@ __device__ __forceinline__ bool elect_last(const KParams &P, Ctx &c, const Ins &
     if (c.lane == 0)
         old = __hip_atomic_fetch_add(P.counters + (int64_t)in.mctr * CTR_STRIDE, 1, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
-    old = __builtin_amdgcn_readfirstlane(__shfl(old, 0, 64));
+    old = __builtin_amdgcn_readfirstlane(old);  // lane 0's: every lane is active here
     return old + 1 == need;
 }
 
@@ -1004,7 +1004,7 @@ __device__ __forceinline__ bool leave(const KParams &P, Ctx &c, const Ins &in, A
     }
     uint32_t old = 0;
     if (lane == 0) old = lds_add(c.misc + M_FIN, 1u);
-    old = __builtin_amdgcn_readfirstlane(__shfl(old, 0, 64));
+    old = __builtin_amdgcn_readfirstlane(old);  // lane 0's: every lane is active here
     if (in.tr && lane == 0 && old == (uint32_t)NC * in.pc) in.tr[TR_FIRST] = wall_clock64();
     if (old != (uint32_t)NC * (in.pc + 1) - 1) return true;
     if (in.tr && lane == 0) in.tr[TR_LAST] = wall_clock64();
