@@ -202,27 +202,40 @@ __global__ __launch_bounds__(UF_ATTN_THREADS) void uf_attn(KParams P, int layer,
     }
 }
 
-// Chunk states of each head merged in chunk order, then o = O / L.
-__global__ __launch_bounds__(64) void uf_attn_merge(KParams P, int nch) {
-    const int g = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+// Chunk states of each head merged in chunk order, then o = O / L: one wave
+// per query head of the kv group, every chunk's state loaded before the merge.
+__global__ __launch_bounds__(64 * MAX_G) void uf_attn_merge(KParams P, int nch) {
+    const int g = blockIdx.x, b = blockIdx.y, lane = threadIdx.x & 63, hq = threadIdx.x >> 6;
     const int G = P.nq / P.nkv;
-    for (int hq = 0; hq < G; ++hq) {
-        float O, M, L;
-        merge_init(O, M, L);
-        for (int c = 0; c < nch; ++c) {
+    if (hq >= G) return;
+    float o[MAX_ATTN_CHUNKS], m[MAX_ATTN_CHUNKS], l[MAX_ATTN_CHUNKS];
+#pragma unroll
+    for (int c = 0; c < MAX_ATTN_CHUNKS; ++c)
+        if (c < nch) {
             const float *src = P.attn_part + ((((int64_t)b * P.nkv + g) * nch + c) * G + hq) * ATTN_PART_STRIDE;
-            merge_step(O, M, L, src[lane], src[64], src[65]);
+            o[c] = src[lane];
+            m[c] = src[64];
+            l[c] = src[65];
         }
-        P.o[(int64_t)b * P.nq * P.d + (g * G + hq) * 64 + lane] = O / L;
-    }
+    float O, M, L;
+    merge_init(O, M, L);
+#pragma unroll
+    for (int c = 0; c < MAX_ATTN_CHUNKS; ++c)
+        if (c < nch) merge_step(O, M, L, o[c], m[c], l[c]);
+    P.o[(int64_t)b * P.nq * P.d + (g * G + hq) * 64 + lane] = O / L;
 }
 
-// greedy token per request over the LM-head blocks' partials
-__global__ __launch_bounds__(64) void uf_argmax(KParams P, int nslot) {
-    const int b = blockIdx.x, lane = threadIdx.x;
+// greedy token per request over the LM-head blocks' partials: 1024 threads
+// take the partials round-robin, then the waves and the workgroup reduce
+// (the pick is a maximum under a total order, so the order does not matter)
+constexpr int UF_AMAX_THREADS = 1024;
+__global__ __launch_bounds__(UF_AMAX_THREADS) void uf_argmax(KParams P, int nslot) {
+    __shared__ float sv[UF_AMAX_THREADS / 64];
+    __shared__ int si[UF_AMAX_THREADS / 64];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int t = lane; t < nslot; t += 64) {
+    for (int t = tid; t < nslot; t += UF_AMAX_THREADS) {
         const float v = P.lm_part[((int64_t)t * P.B + b) * 2];
         const int i = ((const int32_t *)P.lm_part)[((int64_t)t * P.B + b) * 2 + 1];
         if (amax_better(v, i, bv, bi)) {
@@ -239,9 +252,20 @@ __global__ __launch_bounds__(64) void uf_argmax(KParams P, int nslot) {
         }
     }
     if (lane == 0) {
+        sv[wave] = bv;
+        si[wave] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        for (int w = 1; w < UF_AMAX_THREADS / 64; ++w)
+            if (amax_better(sv[w], si[w], bv, bi)) {
+                bv = sv[w];
+                bi = si[w];
+            }
         if (P.has_embed) P.tokens_out[b] = bi;
         if (P.kv_lens_out) P.kv_lens_out[b] = P.kv_lens[b] + 1;
     }
+}
 }
 
 __global__ void k_rope_table(float2 *t, int capacity, int d, double theta) {
@@ -306,7 +330,7 @@ hipError_t launch_unfused(const KParams &p, float *u, float *qrot, hipStream_t s
             }
         }
         MK_TRY(hipGetLastError());
-        hipLaunchKernelGGL(uf_attn_merge, dim3(p.nkv, p.B), dim3(64), 0, s, p, nch);
+        hipLaunchKernelGGL(uf_attn_merge, dim3(p.nkv, p.B), dim3(64 * (p.nq / p.nkv)), 0, s, p, nch);
         MK_TRY(hipGetLastError());
         MK_TRY(uf_mv_any(p, OP_OPROJ, l, first, p.o, s));
         hipLaunchKernelGGL(uf_norm, dim3(p.B), dim3(UF_THREADS), 0, s, p, l, 3, 0, u);
@@ -319,7 +343,7 @@ hipError_t launch_unfused(const KParams &p, float *u, float *qrot, hipStream_t s
         MK_TRY(hipGetLastError());
         MK_TRY(uf_mv_any(p, OP_LMHEAD, p.L, 0, u, s));
     }
-    hipLaunchKernelGGL(uf_argmax, dim3(p.B), dim3(64), 0, s, p,
+    hipLaunchKernelGGL(uf_argmax, dim3(p.B), dim3(UF_AMAX_THREADS), 0, s, p,
                        p.has_embed ? (p.V + UF_WAVES - 1) / UF_WAVES : 0);
     MK_TRY(hipGetLastError());
     return hipSuccess;
