@@ -131,12 +131,31 @@ __device__ __forceinline__ float dot8(v4u w, v4f a0, v4f a1) {
     return s;
 }
 
+// dot8 with the weights already converted to fp32 (the same arithmetic)
+__device__ __forceinline__ float dot8f(const float (&w)[8], v4f a0, v4f a1) {
+    float s = w[0] * a0.x;
+    s = fmaf(w[1], a0.y, s);
+    s = fmaf(w[2], a0.z, s);
+    s = fmaf(w[3], a0.w, s);
+    s = fmaf(w[4], a1.x, s);
+    s = fmaf(w[5], a1.y, s);
+    s = fmaf(w[6], a1.z, s);
+    s = fmaf(w[7], a1.w, s);
+    return s;
+}
+
 // Activation layout in LDS for a matvec input of length K: element i of
 // 16-byte weight chunk ci = i / 8 sits where lane ci % 64 of pass ci / 64
 // reads it with two conflict-free 16-byte LDS reads.
 __device__ __forceinline__ int act_index(int i) {
     const int ci = i >> 3, e8 = i & 7;
     return ((((ci >> 6) << 1) + (e8 >> 2)) << 8) + ((ci & 63) << 2) + (e8 & 3);
+}
+// bf16 form of the same layout (16-bit elements): chunk ci's 8 values are one
+// 16-byte LDS read of lane ci % 64 in pass ci / 64
+__device__ __forceinline__ int act16_index(int i) {
+    const int ci = i >> 3;
+    return ((ci >> 6) << 9) + ((ci & 63) << 3) + (i & 7);
 }
 
 // Rotate-half RoPE of element i (lane) of a 64-wide head: x_i cos - x_{i+32}

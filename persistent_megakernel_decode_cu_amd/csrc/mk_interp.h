@@ -51,6 +51,9 @@ enum : int {
 };
 
 constexpr int NC = N_COMPUTE_WAVES;
+// at a padded batch of 8 the down projection's input is staged in LDS as bf16
+template <int NB>
+constexpr bool ACT16_DOWN = NB == 8;
 constexpr int D = PREFETCH_SLICES;
 
 // Every lane reads the same LDS word; readfirstlane makes that visible to the
@@ -572,14 +575,22 @@ __device__ __forceinline__ bool stage_rows(const KParams &P, Ctx &c, const Ins &
     return true;
 }
 
-// act[b] <- src[b][0, K) in the matvec layout; src: tagged [B][K]
+// act[b] <- src[b][0, K) in the matvec layout (A16: rounded to bf16, in the
+// 16-bit layout); src: tagged [B][K]
+template <bool A16>
 __device__ __forceinline__ bool stage_copy(const KParams &P, Ctx &c, const Ins &in, const uint64_t *src, int K) {
     const int per = K / NC;
     for (int b = 0; b < P.B; ++b) {
         MK_LDS float *a = c.act + b * P.act_stride;
+        MK_LDS uint16_t *a16 = (MK_LDS uint16_t *)c.act + b * 2 * P.act_stride;
         const __amdgpu_buffer_rsrc_t r = tres(src + (size_t)b * K, (uint32_t)K);
         if (!tgather_range(
-                c, r, c.w * per, (c.w + 1) * per, [&](int i, float v) { a[act_index(i)] = v; }, in.pc))
+                c, r, c.w * per, (c.w + 1) * per,
+                [&](int i, float v) {
+                    if (A16) a16[act16_index(i)] = f2bf(v);
+                    else a[act_index(i)] = v;
+                },
+                in.pc))
             return false;
     }
     return true;
@@ -734,7 +745,7 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
             break;
         case OP_DOWN:
             ok = stage_rows(P, c, in, 2 * in.layer + 1) &&
-                 stage_copy(P, c, in, P.tact + (size_t)in.layer * P.B * P.F, P.F) && cbar(c, pc);
+                 stage_copy<ACT16_DOWN<NB>>(P, c, in, P.tact + (size_t)in.layer * P.B * P.F, P.F) && cbar(c, pc);
             break;
         case OP_ATTN: {
             const int p = in.b >= 0 && in.b < P.B ? (int)lds_ld(c.misc + M_KVLEN + in.b) : -1;
@@ -808,9 +819,11 @@ __device__ __forceinline__ void emit_row(const KParams &P, Ctx &c, const Ins &in
 // the unit's dot product (m: gate or up matrix of UPGATE). Three forms with
 // the same arithmetic: at batch 1 with K = 2048 the activations sit in
 // registers, loaded once per instruction into the attention state's output
-// registers (xr.o[j], free during a matvec); a full slice reads them from
-// LDS with every read issued before the products; a slice past the end of a
-// short row guards each chunk.
+// registers (xr.o[j], free during a matvec); a full slice converts its
+// weights once and reads each request's activations from LDS right before
+// that request's products (at a padded batch of 8 the down projection's
+// input is staged as bf16, the only way 8 requests' 8192-wide inputs fit in
+// LDS); a slice past the end of a short row guards each chunk.
 template <int NB, int G>
 __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &k, const Ins &in, const v4u (&r)[4],
                                            Acc<NB> &acc, const AttnLaneT<G> &xr) {
@@ -825,26 +838,40 @@ __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &
         acc.a0[0] = m ? acc.a0[0] : a;
         acc.a1[0] = m ? a : acc.a1[0];
     } else if (k.K >= (part + 1) * 2048) {
-        v4f x0[4][NB], x1[4][NB];
+        // the slice's weights as fp32 once; then each request's activations
+        // are read right before its products, so that few are live at once
+        float wf[4][8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const MK_LDS float *ab = c.act + b * P.act_stride + part * 2048 + j * 512 + lane * 4;
-                x0[j][b] = *(const MK_LDS v4f *)ab;
-                x1[j][b] = *(const MK_LDS v4f *)(ab + 256);
-            }
-        float a[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) a[b] = m ? acc.a1[b] : acc.a0[b];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) a[b] += dot8(r[j], x0[j][b], x1[j][b]);
+        for (int j = 0; j < 4; ++j) {
+            wf[j][0] = bf_lo(r[j].x);
+            wf[j][1] = bf_hi(r[j].x);
+            wf[j][2] = bf_lo(r[j].y);
+            wf[j][3] = bf_hi(r[j].y);
+            wf[j][4] = bf_lo(r[j].z);
+            wf[j][5] = bf_hi(r[j].z);
+            wf[j][6] = bf_lo(r[j].w);
+            wf[j][7] = bf_hi(r[j].w);
+        }
+        const bool act16 = ACT16_DOWN<NB> && in.op == OP_DOWN;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            acc.a0[b] = m ? acc.a0[b] : a[b];
-            acc.a1[b] = m ? a[b] : acc.a1[b];
+            float a = m ? acc.a1[b] : acc.a0[b];
+            if (act16) {
+                const MK_LDS uint16_t *ab = (const MK_LDS uint16_t *)c.act + b * 2 * P.act_stride + part * 2048 + lane * 8;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const v4u x = *(const MK_LDS v4u *)(ab + j * 512);
+                    a += dot8f(wf[j], v4f{bf_lo(x.x), bf_hi(x.x), bf_lo(x.y), bf_hi(x.y)},
+                               v4f{bf_lo(x.z), bf_hi(x.z), bf_lo(x.w), bf_hi(x.w)});
+                }
+            } else {
+                const MK_LDS float *ab = c.act + b * P.act_stride + part * 2048 + lane * 4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    a += dot8f(wf[j], *(const MK_LDS v4f *)(ab + j * 512), *(const MK_LDS v4f *)(ab + j * 512 + 256));
+            }
+            acc.a0[b] = m ? acc.a0[b] : a;
+            acc.a1[b] = m ? a : acc.a1[b];
         }
     } else {
         const int nchunk = k.K >> 3;

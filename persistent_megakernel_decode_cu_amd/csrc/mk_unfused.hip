@@ -266,7 +266,6 @@ __global__ __launch_bounds__(UF_AMAX_THREADS) void uf_argmax(KParams P, int nslo
         if (P.kv_lens_out) P.kv_lens_out[b] = P.kv_lens[b] + 1;
     }
 }
-}
 
 __global__ void k_rope_table(float2 *t, int capacity, int d, double theta) {
     const int half = d / 2;
