@@ -2,6 +2,7 @@
 // one-kernel-per-op baseline (bf16 unpacking, wave reductions, the
 // activation layout, the attention block update and the op epilogues).
 #pragma once
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -79,6 +80,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t plain_rsrc(const void *base, u
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+// binary16 halves of a 32-bit word, and binary32 -> binary16 (round to nearest even)
+__device__ __forceinline__ float h_lo(uint32_t w) { return __half2float(__ushort_as_half((unsigned short)(w & 0xffffu))); }
+__device__ __forceinline__ float h_hi(uint32_t w) { return __half2float(__ushort_as_half((unsigned short)(w >> 16))); }
+__device__ __forceinline__ uint16_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
 
 // binary32 -> bf16, round to nearest even (NaN kept quiet).
 __device__ __forceinline__ uint16_t f2bf(float f) {
@@ -151,8 +156,8 @@ __device__ __forceinline__ int act_index(int i) {
     const int ci = i >> 3, e8 = i & 7;
     return ((((ci >> 6) << 1) + (e8 >> 2)) << 8) + ((ci & 63) << 2) + (e8 & 3);
 }
-// bf16 form of the same layout (16-bit elements): chunk ci's 8 values are one
-// 16-byte LDS read of lane ci % 64 in pass ci / 64
+// 16-bit form of the same layout: chunk ci's 8 values are one 16-byte LDS
+// read of lane ci % 64 in pass ci / 64
 __device__ __forceinline__ int act16_index(int i) {
     const int ci = i >> 3;
     return ((ci >> 6) << 9) + ((ci & 63) << 3) + (i & 7);

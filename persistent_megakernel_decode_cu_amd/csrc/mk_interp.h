@@ -51,7 +51,8 @@ enum : int {
 };
 
 constexpr int NC = N_COMPUTE_WAVES;
-// at a padded batch of 8 the down projection's input is staged in LDS as bf16
+// at a padded batch of 8 the down projection's input is staged in LDS as
+// binary16 (8 requests' fp32 inputs of 8192 do not fit)
 template <int NB>
 constexpr bool ACT16_DOWN = NB == 8;
 constexpr int D = PREFETCH_SLICES;
@@ -575,8 +576,8 @@ __device__ __forceinline__ bool stage_rows(const KParams &P, Ctx &c, const Ins &
     return true;
 }
 
-// act[b] <- src[b][0, K) in the matvec layout (A16: rounded to bf16, in the
-// 16-bit layout); src: tagged [B][K]
+// act[b] <- src[b][0, K) in the matvec layout (A16: rounded to binary16, in
+// the 16-bit layout); src: tagged [B][K]
 template <bool A16>
 __device__ __forceinline__ bool stage_copy(const KParams &P, Ctx &c, const Ins &in, const uint64_t *src, int K) {
     const int per = K / NC;
@@ -587,7 +588,7 @@ __device__ __forceinline__ bool stage_copy(const KParams &P, Ctx &c, const Ins &
         if (!tgather_range(
                 c, r, c.w * per, (c.w + 1) * per,
                 [&](int i, float v) {
-                    if (A16) a16[act16_index(i)] = f2bf(v);
+                    if (A16) a16[act16_index(i)] = f2h(v);
                     else a[act_index(i)] = v;
                 },
                 in.pc))
@@ -822,8 +823,8 @@ __device__ __forceinline__ void emit_row(const KParams &P, Ctx &c, const Ins &in
 // registers (xr.o[j], free during a matvec); a full slice converts its
 // weights once and reads each request's activations from LDS right before
 // that request's products (at a padded batch of 8 the down projection's
-// input is staged as bf16, the only way 8 requests' 8192-wide inputs fit in
-// LDS); a slice past the end of a short row guards each chunk.
+// input is staged as binary16, the only way 8 requests' 8192-wide inputs fit
+// in LDS); a slice past the end of a short row guards each chunk.
 template <int NB, int G>
 __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &k, const Ins &in, const v4u (&r)[4],
                                            Acc<NB> &acc, const AttnLaneT<G> &xr) {
@@ -861,8 +862,8 @@ __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const v4u x = *(const MK_LDS v4u *)(ab + j * 512);
-                    a += dot8f(wf[j], v4f{bf_lo(x.x), bf_hi(x.x), bf_lo(x.y), bf_hi(x.y)},
-                               v4f{bf_lo(x.z), bf_hi(x.z), bf_lo(x.w), bf_hi(x.w)});
+                    a += dot8f(wf[j], v4f{h_lo(x.x), h_hi(x.x), h_lo(x.y), h_hi(x.y)},
+                               v4f{h_lo(x.z), h_hi(x.z), h_lo(x.w), h_hi(x.w)});
                 }
             } else {
                 const MK_LDS float *ab = c.act + b * P.act_stride + part * 2048 + lane * 4;

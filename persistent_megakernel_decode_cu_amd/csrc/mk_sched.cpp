@@ -301,8 +301,8 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
 
     // LDS layout (capacity obligation: everything a tile stages must fit)
     const int NBP = B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8;  // requests the interpreter is compiled for
-    // at a padded batch of 8 the down projection's input is staged as bf16
-    // (half the bytes); every other matvec input is fp32
+    // at a padded batch of 8 the down projection's input is staged as
+    // binary16 (half the bytes); every other matvec input is fp32
     const int kmax = NBP == 8 ? std::max({H, QD, (F + 1) / 2}) : std::max(H, std::max(F, QD));
     P.act_stride = (kmax + 511) / 512 * 512;
     P.xrow_stride = (max_rows_x + 3) / 4 * 4;

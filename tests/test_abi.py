@@ -1,6 +1,7 @@
 """The C-ABI library loads, exports every call declared in include/*.h, and
 its argument checks and host-only planning work without a GPU."""
 import ctypes
+import dataclasses
 import glob
 import os
 import re
@@ -69,11 +70,14 @@ def test_capacity_checks():
         _mk.Plan(cfg_of(w, max_batch=2), _mk.MkScheduleDesc(3, 8, 0, 0, 0, 0, 0, 0, 0))  # batch > max_batch
     assert e.value.code == _mk.MK_EINVAL
     big = synthetic.workload("1b-b8-paged")
-    with pytest.raises(_mk.MkError) as e:   # 8 activation rows of 8192 fp32 do not fit in the LDS
-        _mk.Plan(cfg_of(big, max_batch=8, pages=258), _mk.MkScheduleDesc(8, 256, 0, 0, 0, 0, 0, 0, 0))
+    # batch 8 of the 1B shape fits (the down projection's input is staged as binary16)
+    _mk.Plan(cfg_of(big, max_batch=8, pages=258), _mk.MkScheduleDesc(8, 256, 0, 0, 0, 0, 0, 0, 0))
+    wide = dataclasses.replace(big, ffn=32768)
+    with pytest.raises(_mk.MkError) as e:   # 8 activation rows of 32768 do not fit in the LDS
+        _mk.Plan(cfg_of(wide, max_batch=8, pages=258), _mk.MkScheduleDesc(8, 256, 0, 0, 0, 0, 0, 0, 0))
     assert e.value.code == _mk.MK_ECAPACITY
     # the one-kernel-per-op mode has no such limit
-    _mk.Plan(cfg_of(big, max_batch=8, pages=258), _mk.MkScheduleDesc(8, 256, 1, 0, 0, 0, 0, 0, 0))
+    _mk.Plan(cfg_of(wide, max_batch=8, pages=258), _mk.MkScheduleDesc(8, 256, 1, 0, 0, 0, 0, 0, 0))
     with pytest.raises(_mk.MkError) as e:   # reserved fields
         _mk.Plan(cfg_of(w), _mk.MkScheduleDesc(1, 8, 0, 0, 0, 0, 0, 1, 0))
     assert e.value.code == _mk.MK_EINVAL

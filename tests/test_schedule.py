@@ -43,12 +43,12 @@ def test_tiny_batched_plans_validate(batch, n_cus, chunks):
     sched_check.validate(w, batch, p.queue, p.events, p.info.attn_chunks, maxlen)
 
 
-def test_1b_batch4_fits_and_batch8_reports_capacity():
-    w, B, maxlen, p = plan_for("1b-kv1024", 256, batch=4)
-    sched_check.validate(w, 4, p.queue, p.events, p.info.attn_chunks, maxlen)
-    with pytest.raises(_mk.MkError) as ex:
-        plan_for("1b-kv1024", 256, batch=8)
-    assert ex.value.code == _mk.MK_ECAPACITY and "LDS" in str(ex.value)
+def test_1b_batch4_and_batch8_fit():
+    # at a padded batch of 8 the down projection's input is staged as binary16
+    for batch in (4, 8):
+        w, B, maxlen, p = plan_for("1b-kv1024", 256, batch=batch)
+        sched_check.validate(w, batch, p.queue, p.events, p.info.attn_chunks, maxlen)
+        assert p.info.lds_bytes <= 160 * 1024
 
 
 def test_streamed_bytes_match_the_byte_model():
