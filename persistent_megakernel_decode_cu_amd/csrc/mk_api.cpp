@@ -316,7 +316,7 @@ int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream) {
         const mk::Plan &P = h->plan;
         // epoch-based counters: re-zero before the int32 counts could wrap
         if ((h->epoch + 1) * (int64_t)h->max_need >= ((int64_t)1 << 30)) {
-            MK_HIP(hipMemsetAsync(h->counters, 0, (size_t)std::max(P.n_counters, 1) * mk::CTR_STRIDE * 4, st));
+            MK_HIP(mk::fill_u32((uint32_t *)h->counters, (size_t)std::max(P.n_counters, 1) * mk::CTR_STRIDE, 0u, st));
             h->epoch = 0;
         }
         h->epoch++;

@@ -112,17 +112,6 @@ __device__ __forceinline__ float wave_sum(float v) {
     v += dpp_shift0<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
-__device__ __forceinline__ float group16_sum(float v) {
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-__device__ __forceinline__ float group16_max(float v) {
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
-}
-
 // 8 bf16 weights (one 16-byte chunk) times 8 activations
 __device__ __forceinline__ float dot8(v4u w, v4f a0, v4f a1) {
     float s = bf_lo(w.x) * a0.x;

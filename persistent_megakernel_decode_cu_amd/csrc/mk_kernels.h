@@ -57,6 +57,7 @@ constexpr int ATTN_PART_STRIDE = 68;
 
 // The resident interpreter exists for B in 1..8 and G = nq / nkv in {1, 2, 4, 8}.
 bool megakernel_supports(int B, int G);
+hipError_t fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t s);
 hipError_t launch_megakernel(const KParams &p, int lds_bytes, hipStream_t s);
 hipError_t setup_megakernel(int B, int G, int lds_bytes);
 hipError_t megakernel_occupancy(int B, int G, int lds_bytes, int *blocks_per_cu);

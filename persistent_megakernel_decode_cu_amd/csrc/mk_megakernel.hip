@@ -2,6 +2,8 @@
 // kernel variant (padded batch, q heads per kv head), sets its LDS size,
 // checks co-residency and launches it cooperatively. The device code is in
 // mk_interp.h, instantiated by mk_interp_b{1,2,4,8}.hip.
+#include <algorithm>
+
 #include "mk_device.h"
 
 namespace mk {
@@ -34,6 +36,18 @@ hipError_t megakernel_occupancy(int B, int G, int lds_bytes, int *blocks_per_cu)
     const void *k = kernel_for(B, G);
     if (!k) return hipErrorInvalidValue;
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, k, BLOCK_THREADS, lds_bytes);
+}
+
+// Plain fill kernel: clears device words on a stream without hipMemsetAsync,
+// whose nodes have given wrong results on graph replays after the first.
+__global__ __launch_bounds__(256) void mk_fill_u32(uint32_t *p, size_t n, uint32_t v) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = v;
+}
+
+hipError_t fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t s) {
+    const unsigned blocks = (unsigned)std::min<size_t>(1024, (n + 255) / 256);
+    hipLaunchKernelGGL(mk_fill_u32, dim3(blocks ? blocks : 1), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
 }
 
 hipError_t launch_megakernel(const KParams &p, int lds_bytes, hipStream_t s) {
