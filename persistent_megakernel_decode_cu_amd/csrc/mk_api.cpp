@@ -60,7 +60,7 @@ struct mk_handle {
     int32_t *queue = nullptr, *events = nullptr, *counters = nullptr;
     float *x = nullptr, *qkv = nullptr, *o = nullptr, *act = nullptr, *attn_part = nullptr, *lm_part = nullptr;
     float *u = nullptr, *qrot = nullptr;
-    uint64_t *tx = nullptr, *tqkv = nullptr, *tact = nullptr, *tpart = nullptr, *tlm = nullptr;
+    uint64_t *tx = nullptr, *tqkv = nullptr, *to = nullptr, *tact = nullptr, *tpart = nullptr, *tlm = nullptr;
     uint32_t tag = 0;  // tag of the last step's activations (never 0 on the device)
     int64_t *trace = nullptr;
     int64_t epoch = 0;
@@ -90,6 +90,7 @@ void free_schedule(mk_handle *h) {
     dfree(h->qrot);
     dfree(h->tx);
     dfree(h->tqkv);
+    dfree(h->to);
     dfree(h->tact);
     dfree(h->tpart);
     dfree(h->tlm);
@@ -265,6 +266,7 @@ int mk_build_schedule(mk_handle *h, const mk_schedule_desc *s) {
             const size_t L = (size_t)c.n_layers;
             if (!rc) rc = dalloc(h->tx, 2 * L * B * c.hidden);
             if (!rc) rc = dalloc(h->tqkv, L * B * QKV);
+            if (!rc) rc = dalloc(h->to, L * B * QD);
             if (!rc) rc = dalloc(h->tact, L * B * c.ffn);
             if (!rc) rc = dalloc(h->tpart, L * B * c.n_kv_heads * plan.attn_chunks * G * mk::ATTN_PART);
             if (!rc) rc = dalloc(h->tlm, (size_t)std::max(plan.n_lm_slots, 1) * B * 2);
@@ -371,6 +373,7 @@ int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream) {
         k.lm_part = h->lm_part;
         k.tx = h->tx;
         k.tqkv = h->tqkv;
+        k.to = h->to;
         k.tact = h->tact;
         k.tpart = h->tpart;
         k.tlm = h->tlm;

@@ -169,38 +169,6 @@ __device__ __forceinline__ bool tgather(Ctx &c, __amdgpu_buffer_rsrc_t r, int n,
     }
 }
 
-// Like tgather, but every poll reloads all n words and the wait ends when
-// they all carry the step's tag; the values are then in v[k] (k < n). Needs
-// no second copy of the words, at the cost of re-reading words that had
-// already arrived while others are still pending.
-template <int N, typename IDX>
-__device__ __forceinline__ bool tgather_all(Ctx &c, __amdgpu_buffer_rsrc_t r, IDX idx, float (&v)[N], int pc) {
-    static_assert(N >= 1 && N <= 48, "gather width");
-    const uint32_t tag = c.tag;
-    int64_t spins = 0;
-    for (;;) {
-        bool miss = false;
-#pragma unroll
-        for (int k = 0; k < N; ++k) {
-            const v2u w = tget(r, idx(k));
-            v[k] = __uint_as_float(w.x);
-            miss |= w.y != tag;
-        }
-        if (__builtin_amdgcn_ballot_w64(miss) == 0) return true;
-        if (lds_ld(c.misc + M_ABORT)) return false;
-        if ((++spins & 63) == 0 &&
-            __builtin_amdgcn_readfirstlane(__hip_atomic_load(c.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
-            lds_st(c.misc + M_ABORT, 1u);
-            return false;
-        }
-        if (spins > c.watchdog) {
-            raise_err(c, ERR_TIMEOUT, pc);
-            return false;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-}
-
 // Gathers words [lo, hi) of a tagged vector into fn(i, v), the lane taking
 // i = lo + lane + 64 k, in rounds of up to 16 words per lane.
 template <typename FN>
@@ -253,6 +221,8 @@ __device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k,
         chunk_blocks(p, iw(c, pc, W_C), iw(c, pc, W_NCH), &lo, &hi);
         k.blo = lo;
         k.nu = hi - lo;
+    } else if (k.op == OP_AMERGE) {
+        k.nu = 0;  // streams nothing: one empty slice
     } else if (k.op > OP_END && k.op < OP_COUNT) {
         k.K = op_k(P, k.op);
         k.rowb = (uint32_t)k.K * 2;
@@ -597,78 +567,49 @@ __device__ __forceinline__ bool stage_copy(const KParams &P, Ctx &c, const Ins &
     return true;
 }
 
-// Attention staging: the group's queries rotated (fp32, act[0, G*64)), and
-// the new K/V entry rotated and rounded to bf16 (act + G*64 as uint16 [2][64]);
-// the last chunk also appends that entry to the cache.
-// act[b] <- o of every query head (the O projection's input): the attention
-// tiles of the layer publish one softmax state (o, m, l) per chunk and head,
-// and the O projection merges them here, in chunk order, so that attention
-// needs no merging tile and no second exchange. Wave w takes heads w + 8 j
-// (j < HPW, HPW a power of two); a round gathers, per lane, the o words of
-// up to 32 / HPW chunks of each of its heads plus one of the round's 64 m/l
-// words, which the merge then reads back with v_readlane.
-constexpr int GW = 16;  // o words per lane and round of the O projection's merge gather
-
-template <int G, int HPW>
-__device__ __forceinline__ bool stage_attn_merge_h(const KParams &P, Ctx &c, const Ins &in) {
-    constexpr int LG = HPW == 1 ? 0 : HPW == 2 ? 1 : HPW == 4 ? 2 : 3;
-    constexpr int CPR = GW / HPW;  // chunks per round
-    const int lane = c.lane, nch = P.attn_chunks, nq = P.nq;
-    for (int b = 0; b < P.B; ++b) {
-        const size_t pb = ((size_t)in.layer * P.B + b) * P.nkv * nch * G * ATTN_PART;
-        const __amdgpu_buffer_rsrc_t r = tres(P.tpart + pb, (uint32_t)(P.nkv * nch * G * ATTN_PART));
-        // word of (head hq, chunk cc, element e)
-        auto word = [&](int hq, int cc, int e) {
-            return (uint32_t)((((hq / G) * nch + cc) * G + hq % G) * ATTN_PART + e);
-        };
-        float O[HPW], M[HPW], L[HPW];
+// AMERGE: the chunk states (o, m, l) that the attention tiles of request b
+// and kv head g published are gathered into LDS (the activation area, which
+// no other part of a merge uses) by all waves, then merged in
+// chunk order, one wave per query head of the group (lane = dim), and
+// o = O / L is published for the O projection: one gather round per merge,
+// and the O projection reads only the merged outputs.
+template <int G>
+__device__ __forceinline__ bool stage_amerge(const KParams &P, Ctx &c, const Ins &in) {
+    const int nch = in.nch, lane = c.lane;
+    const int n = nch * G * ATTN_PART;
+    const size_t pbase = (((size_t)in.layer * P.B + in.b) * P.nkv + in.g) * nch * G * ATTN_PART;
+    const __amdgpu_buffer_rsrc_t rp = tres(P.tpart + pbase, (uint32_t)n);
+    const int per = (n + NC - 1) / NC;
+    if (!tgather_range(
+            c, rp, c.w * per, min(n, (c.w + 1) * per), [&](int i, float v) { c.act[i] = v; }, in.pc))
+        return false;
+    if (!cbar(c, in.pc)) return false;
+    if (c.w < G && nch <= MAX_ATTN_CHUNKS) {
+        const int h = c.w;
+        float o[MAX_ATTN_CHUNKS], m[MAX_ATTN_CHUNKS], l[MAX_ATTN_CHUNKS];
 #pragma unroll
-        for (int j = 0; j < HPW; ++j) merge_init(O[j], M[j], L[j]);
-        for (int c0 = 0; c0 < nch; c0 += CPR) {
-            float ov[GW + 1];  // o words of (head j, chunk c0 + (k >> LG)), k = (chunk - c0) HPW + j; [GW]: m/l word
-            // m/l word of this lane: t = ((cc - c0) << (LG + 1)) | (j << 1) | which
-            const int tj = (lane >> 1) & (HPW - 1), tc = c0 + (lane >> (LG + 1));
-            const int thq = c.w + 8 * tj;
-            const bool tok = tc < nch && thq < nq;
-            // words outside the heads or chunks read word 0, which this step writes too
-            if (!tgather_all<GW + 1>(
-                    c, r,
-                    [&](int k) {
-                        if (k == GW) return tok ? word(thq, tc, 64 + (lane & 1)) : 0u;
-                        const int j = k & (HPW - 1), cc = c0 + (k >> LG), hq = c.w + 8 * j;
-                        return (cc < nch && hq < nq) ? word(hq, cc, lane) : 0u;
-                    },
-                    ov, in.pc))
-                return false;
-            const float ml = ov[GW];
-#pragma unroll
-            for (int k = 0; k < GW; ++k) {
-                const int j = k & (HPW - 1), cc = c0 + (k >> LG);
-                if (cc < nch) {
-                    const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml), (k << 1)));
-                    const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml), (k << 1) + 1));
-                    merge_step(O[j], M[j], L[j], ov[k], m, l);
-                }
+        for (int cc = 0; cc < MAX_ATTN_CHUNKS; ++cc)
+            if (cc < nch) {
+                const MK_LDS float *src = c.act + (cc * G + h) * ATTN_PART;
+                o[cc] = src[lane];
+                m[cc] = src[64];
+                l[cc] = src[65];
             }
-        }
-        MK_LDS float *a = c.act + b * P.act_stride;
+        float O, M, L;
+        merge_init(O, M, L);
 #pragma unroll
-        for (int j = 0; j < HPW; ++j) {
-            const int hq = c.w + 8 * j;
-            if (hq < nq) a[act_index(hq * 64 + lane)] = O[j] / L[j];
-        }
+        for (int cc = 0; cc < MAX_ATTN_CHUNKS; ++cc)
+            if (cc < nch) merge_step(O, M, L, o[cc], m[cc], l[cc]);
+        const int QD = P.nq * P.d;
+        tput(tres(P.to + ((size_t)in.layer * P.B + in.b) * QD, (uint32_t)QD), (uint32_t)((in.g * G + h) * 64 + lane),
+             O / L, c.tag);
     }
     return true;
 }
-template <int G>
-__device__ __forceinline__ bool stage_attn_merge(const KParams &P, Ctx &c, const Ins &in) {
-    const int hpw = (P.nq + NC - 1) / NC;
-    if (hpw <= 1) return stage_attn_merge_h<G, 1>(P, c, in);
-    if (hpw <= 2) return stage_attn_merge_h<G, 2>(P, c, in);
-    if (hpw <= 4) return stage_attn_merge_h<G, 4>(P, c, in);
-    return stage_attn_merge_h<G, 8>(P, c, in);
-}
 
+// Attention staging: the group's queries rotated (fp32, act[0, G*64)), and
+// the new K/V entry rotated and rounded to bf16 (act + G*64 as uint16 [2][64]);
+// the last chunk also appends that entry to the cache.
 template <int G>
 __device__ __forceinline__ bool stage_attn(const KParams &P, Ctx &c, const Ins &in) {
     const int lane = c.lane;
@@ -742,7 +683,7 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
         case OP_LMHEAD: ok = stage_norm(P, c, in, (const uint16_t *)(uintptr_t)in.wn, 2 * P.L); break;
         case OP_OPROJ:
             ok = stage_rows(P, c, in, (in.flags & F_X_FROM_INPUT) ? 0 : 2 * in.layer) &&
-                 stage_attn_merge<G>(P, c, in) && cbar(c, pc);
+                 stage_copy<false>(P, c, in, P.to + (size_t)in.layer * P.B * P.nq * P.d, P.nq * P.d) && cbar(c, pc);
             break;
         case OP_DOWN:
             ok = stage_rows(P, c, in, 2 * in.layer + 1) &&
@@ -758,6 +699,7 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
             ok = stage_attn<G>(P, c, in);
             break;
         }
+        case OP_AMERGE: ok = stage_amerge<G>(P, c, in); break;
         default:
             if (c.lane == 0) raise_err(c, ERR_OPCODE, pc);
             return false;

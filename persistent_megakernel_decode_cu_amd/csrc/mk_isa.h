@@ -28,7 +28,8 @@ enum Op : int32_t {
     OP_UPGATE = 4,  // rows [r0,r1) of Wgate, Wup . rmsnorm(x_{2l+1}), SiLU -> act_l
     OP_DOWN = 5,    // rows [r0,r1) of Wdown . act_l, plus residual x_{2l+1} -> x_{2l+2}
     OP_LMHEAD = 6,  // rows [r0,r1) of E . rmsnorm_final(x_{2L}), argmax   -> logits, token
-    OP_COUNT = 7
+    OP_AMERGE = 7,  // request b, kv head g: merge the chunks' softmax states -> o_l
+    OP_COUNT = 8
 };
 
 // instruction words
@@ -84,11 +85,10 @@ constexpr int MAX_B = 8;
 constexpr int TRACE_WORDS = 8;  // MK_TRACE_WORDS of mk.h
 enum : int { TR_START = 0, TR_READY = 1, TR_END = 2, TR_FIRST = 3, TR_LAST = 4, TR_ELECT = 5, TR_GATHER = 6 };
 constexpr int MAX_G = 8;
-// K/V chunks per (request, kv head): the O projection merges the chunks'
-// softmax states while it stages its input, which bounds their number
+// K/V chunks per (request, kv head), merged by one AMERGE instruction
 constexpr int MAX_ATTN_CHUNKS = 16;
-// chunks the automatic choice stops at: one gather round of the O projection's merge
-constexpr int AUTO_ATTN_CHUNKS = 8;
+// chunks the automatic choice stops at
+constexpr int AUTO_ATTN_CHUNKS = 16;
 
 // device error word: code << 28 | cu << 16 | pc
 enum : int32_t { ERR_TIMEOUT = 1, ERR_OPCODE = 2, ERR_RANGE = 3, ERR_NAN = 4 };

@@ -39,6 +39,7 @@ struct KParams {
     uint64_t *tqkv;    // [L][B][(nq + 2 nkv) d]
     uint64_t *tact;    // [L][B][F]
     uint64_t *tpart;   // [L][B][nkv][chunks][G][ATTN_PART] attention chunk partials
+    uint64_t *to;      // [L][B][nq d] merged attention outputs
     uint64_t *tlm;     // [lm slots][B][2] argmax partials (value, index)
     int32_t attn_chunks;
     // one-kernel-per-op baseline scratch (fp32, overwritten in place)

@@ -203,8 +203,8 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     for (int l = 0; l < L; ++l) {
         const int first = l == 0 ? F_X_FROM_INPUT : 0;
         matvec_op(OP_QKV, l, QKV, (int64_t)H * 2, first);
-        // attention chunks; each publishes its softmax state, which the O
-        // projection tiles merge
+        // attention chunks, each publishing its softmax state; then one
+        // merge per (request, kv head), on the least-loaded unit
         for (int b = 0; b < B; ++b)
             for (int g = 0; g < nkv; ++g) {
                 for (int c = 0; c < C; ++c) {
@@ -225,6 +225,20 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
                     cum[t.cu] += t.bytes;
                     tiles.push_back(t);
                 }
+            }
+        for (int b = 0; b < B; ++b)
+            for (int g = 0; g < nkv; ++g) {
+                Tile t;
+                t.op = OP_AMERGE;
+                t.layer = l;
+                t.b = b;
+                t.g = g;
+                t.nch = C;
+                t.merge = -1;
+                t.bytes = 0;  // streams nothing; charged below at the chunk states it gathers, to spread the merges
+                t.cu = pick_least(cum);
+                cum[t.cu] += (int64_t)C * G * ATTN_PART * 8;
+                tiles.push_back(t);
             }
         matvec_op(OP_OPROJ, l, H, (int64_t)QD * 2, first);
         matvec_op(OP_UPGATE, l, F, (int64_t)H * 4, 0);
@@ -306,9 +320,10 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     const int kmax = NBP == 8 ? std::max({H, QD, (F + 1) / 2}) : std::max(H, std::max(F, QD));
     P.act_stride = (kmax + 511) / 512 * 512;
     P.xrow_stride = (max_rows_x + 3) / 4 * 4;
-    const int64_t part_floats = (int64_t)N_COMPUTE_WAVES * G * ATTN_WAVE_PART;
+    const int64_t part_floats = (int64_t)N_COMPUTE_WAVES * G * ATTN_WAVE_PART;  // per-wave attention states
+    // matvec inputs; attention staging; an AMERGE's chunk states; LM-head partials
     const int64_t act_floats = std::max<int64_t>({(int64_t)NBP * P.act_stride, (int64_t)G * 64 + 64,
-                                                  (int64_t)P.n_lm_slots * B * 2});
+                                                  (int64_t)C * G * ATTN_PART, (int64_t)P.n_lm_slots * B * 2});
     auto up256 = [](int64_t x) { return (x + 255) / 256 * 256; };
     const int64_t queue_off = MISC_BYTES;  // the CU's queue, LDS_INSTR_WORDS words per instruction
     const int64_t xrow_off = queue_off + up256((int64_t)Q * LDS_INSTR_WORDS * 4);

@@ -131,6 +131,9 @@ def dependencies(shape, batch: int, ins):
         if i.op == I["OP_ATTN"]:  # one softmax state per (request, kv head, chunk)
             lo = (i.b * nkv + i.g) * i.nch + i.c
             writers[("opart", i.layer)].append((lo, lo + 1, node))
+        if i.op == I["OP_AMERGE"]:  # the merged outputs of (request, kv head)
+            lo = i.b * QD + i.g * G * d
+            writers[("o", i.layer)].append((lo, lo + G * d, node))
     for k in writers:
         writers[k].sort()
     n_chunks = defaultdict(int)
@@ -164,9 +167,13 @@ def dependencies(shape, batch: int, ins):
                 g = i.g
                 for lo, n in ((g * G * d, G * d), (QD + g * d, d), (QD + nkv * d + g * d, d)):
                     need |= producers(("qkv", i.layer), b * QKV + lo, b * QKV + lo + n)
-            elif i.op == I["OP_OPROJ"]:  # merges every chunk state of the request
-                nch = n_chunks[i.layer]
-                need |= producers(("opart", i.layer), b * nkv * nch, (b + 1) * nkv * nch)
+            elif i.op == I["OP_AMERGE"]:  # every chunk state of its (request, kv head)
+                if b != i.b:
+                    continue
+                lo = (i.b * nkv + i.g) * i.nch
+                need |= producers(("opart", i.layer), lo, lo + i.nch)
+            elif i.op == I["OP_OPROJ"]:  # the merged outputs of the request
+                need |= producers(("o", i.layer), b * QD, (b + 1) * QD)
                 if not first:
                     need |= producers(("x", 2 * i.layer), b * H + i.r0, b * H + i.r1)
             elif i.op == I["OP_UPGATE"]:
@@ -196,10 +203,14 @@ def validate(shape, batch: int, queue: np.ndarray, events: np.ndarray, attn_chun
     L, H, F, nq, nkv, d, G, QD, QKV = _shape(shape)
     rows = defaultdict(list)
     attn = defaultdict(list)
+    merges = defaultdict(list)
     for i in ins:
         if i.op == I["OP_ATTN"]:
             attn[i.layer].append((i.b, i.g, i.c))
             _req(i.nch == attn_chunks, "ATTN instruction with a different chunk count")
+        elif i.op == I["OP_AMERGE"]:
+            merges[i.layer].append((i.b, i.g))
+            _req(i.nch == attn_chunks, "AMERGE instruction with a different chunk count")
         else:
             rows[(i.op, i.layer)].append((i.r0, i.r1))
     for l in range(L):
@@ -209,6 +220,8 @@ def validate(shape, batch: int, queue: np.ndarray, events: np.ndarray, attn_chun
         _cover(rows[(I["OP_DOWN"], l)], H, f"DOWN layer {l}")
         want = sorted((b, g, c) for b in range(batch) for g in range(nkv) for c in range(attn_chunks))
         _req(sorted(attn[l]) == want, f"attention tiles of layer {l} incomplete or duplicated")
+        want_m = sorted((b, g) for b in range(batch) for g in range(nkv))
+        _req(sorted(merges[l]) == want_m, f"attention merges of layer {l} incomplete or duplicated")
     if shape.has_embed:
         _cover(rows[(I["OP_LMHEAD"], L)], shape.vocab, "LMHEAD")
     # merge events
