@@ -184,6 +184,34 @@ __device__ __forceinline__ bool tgather_range(Ctx &c, __amdgpu_buffer_rsrc_t r, 
     return true;
 }
 
+// Gathers the flattened tagged vector src[0, B K) (B requests of K words)
+// with every wave of the workgroup, 16 words per lane and round, handing
+// word (b, i) to put(b, i, v): the gathers of all requests share their
+// rounds, where one gather per request would pay one round trip each.
+template <typename PUT>
+__device__ __forceinline__ bool tgather_batch(Ctx &c, const uint64_t *src, int B, int K, PUT put, int pc) {
+    const int total = B * K;
+    const __amdgpu_buffer_rsrc_t r = tres(src, (uint32_t)total);
+    const float invK = 1.0f / (float)K;
+    constexpr int STRIDE = NC * 64;
+    for (int base = 0; base < total; base += STRIDE * 16) {
+        const int first = base + c.w * 64 + c.lane;
+        const int n = first < total ? min(16, (total - first + STRIDE - 1) / STRIDE) : 0;
+        if (!tgather<16>(
+                c, r, n, [&](int k) { return (uint32_t)(first + STRIDE * k); },
+                [&](int k, float v) {
+                    const int j = first + STRIDE * k;
+                    int b = (int)((float)j * invK);  // j < 2^24: off by at most one
+                    if (b * K > j) --b;
+                    if ((b + 1) * K <= j) ++b;
+                    put(b, j - b * K, v);
+                },
+                pc))
+            return false;
+    }
+    return true;
+}
+
 // ------------------------------------------------------------ slice stream
 
 // A wave's position in its stream of slices: instruction pc, unit u (a row,
@@ -465,6 +493,7 @@ __device__ __forceinline__ int token_of(const KParams &P, Ctx &c, int b, int pc)
 // input). Waves 0..3 each gather the elements i = 64 w + lane + 256 k and
 // sum their squares in that order, which is the reduction of the
 // one-kernel-per-op baseline's norm, so both paths agree bit for bit.
+template <int NB>
 __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &in, const uint16_t *wn, int xv) {
     const int H = P.H, lane = c.lane, w = c.w;
     MK_LDS float *norm = (MK_LDS float *)(c.misc + M_NORM);
@@ -474,12 +503,29 @@ __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &
     // The norm weights of the lane's first 16 elements are loaded with the
     // inputs: a load issued later would wait behind the weight slices in flight.
     float wv[16];
-    if (w < 4) {
+    // several requests: every wave gathers, all requests in shared rounds
+    const bool batched = NB > 1 && xv != 0;
+    if (batched) {
+        if (w < 4) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) wv[k] = k < n ? bf2f(wn[first + 256 * k]) : 0.0f;
+            for (int k = 0; k < 16; ++k) wv[k] = k < n ? bf2f(wn[first + 256 * k]) : 0.0f;
+        }
+        if (!tgather_batch(
+                c, P.tx + (size_t)(xv - 1) * P.B * H, P.B, H,
+                [&](int b, int i, float v) { c.act[b * P.act_stride + act_index(i)] = v; }, in.pc))
+            return false;
+        if (!cbar(c, in.pc)) return false;
+    }
+    if (w < 4) {
+        if (!batched) {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) wv[k] = k < n ? bf2f(wn[first + 256 * k]) : 0.0f;
+        }
         for (int b = 0; b < P.B; ++b) {
             MK_LDS float *a = c.act + b * P.act_stride;
-            if (xv == 0) {
+            if (batched) {
+                // gathered above
+            } else if (xv == 0) {
                 const int tok = P.has_embed ? token_of(P, c, b, in.pc) : 0;
                 for (int i = first; i < H; i += 256) a[act_index(i)] = x_input(P, b, i, true, tok);
             } else {
@@ -525,8 +571,17 @@ __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &
 }
 
 // xrow[b][j] <- x_v[b][r0 + j] for the instruction's rows (x_0: the input)
+template <int NB>
 __device__ __forceinline__ bool stage_rows(const KParams &P, Ctx &c, const Ins &in, int xv) {
     const int nr = in.r1 - in.r0;
+    if (NB > 1 && xv != 0 && P.B * nr <= NC * 64) {  // every (request, row) word in one round
+        const __amdgpu_buffer_rsrc_t r = tres(P.tx + (size_t)(xv - 1) * P.B * P.H, (uint32_t)(P.B * P.H));
+        const int L = c.w * 64 + c.lane;
+        const int b = nr > 0 ? L / nr : 0, j = L - b * nr;
+        return tgather<1>(
+            c, r, L < P.B * nr ? 1 : 0, [&](int) { return (uint32_t)(b * P.H + in.r0 + j); },
+            [&](int, float v) { c.xrow[b * P.xrow_stride + j] = v; }, in.pc);
+    }
     for (int b = 0; b < P.B; ++b) {
         MK_LDS float *xr = c.xrow + b * P.xrow_stride;
         if (xv == 0) {
@@ -548,8 +603,16 @@ __device__ __forceinline__ bool stage_rows(const KParams &P, Ctx &c, const Ins &
 
 // act[b] <- src[b][0, K) in the matvec layout (A16: rounded to binary16, in
 // the 16-bit layout); src: tagged [B][K]
-template <bool A16>
+template <bool A16, int NB>
 __device__ __forceinline__ bool stage_copy(const KParams &P, Ctx &c, const Ins &in, const uint64_t *src, int K) {
+    if (NB > 1)
+        return tgather_batch(
+            c, src, P.B, K,
+            [&](int b, int i, float v) {
+                if (A16) ((MK_LDS uint16_t *)c.act + b * 2 * P.act_stride)[act16_index(i)] = f2h(v);
+                else c.act[b * P.act_stride + act_index(i)] = v;
+            },
+            in.pc);
     const int per = K / NC;
     for (int b = 0; b < P.B; ++b) {
         MK_LDS float *a = c.act + b * P.act_stride;
@@ -677,17 +740,17 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
     bool ok = true;
     switch (in.op) {
         case OP_QKV:
-            ok = stage_norm(P, c, in, (const uint16_t *)(uintptr_t)in.wn, (in.flags & F_X_FROM_INPUT) ? 0 : 2 * in.layer);
+            ok = stage_norm<NB>(P, c, in, (const uint16_t *)(uintptr_t)in.wn, (in.flags & F_X_FROM_INPUT) ? 0 : 2 * in.layer);
             break;
-        case OP_UPGATE: ok = stage_norm(P, c, in, (const uint16_t *)(uintptr_t)in.wn, 2 * in.layer + 1); break;
-        case OP_LMHEAD: ok = stage_norm(P, c, in, (const uint16_t *)(uintptr_t)in.wn, 2 * P.L); break;
+        case OP_UPGATE: ok = stage_norm<NB>(P, c, in, (const uint16_t *)(uintptr_t)in.wn, 2 * in.layer + 1); break;
+        case OP_LMHEAD: ok = stage_norm<NB>(P, c, in, (const uint16_t *)(uintptr_t)in.wn, 2 * P.L); break;
         case OP_OPROJ:
-            ok = stage_rows(P, c, in, (in.flags & F_X_FROM_INPUT) ? 0 : 2 * in.layer) &&
-                 stage_copy<false>(P, c, in, P.to + (size_t)in.layer * P.B * P.nq * P.d, P.nq * P.d) && cbar(c, pc);
+            ok = stage_rows<NB>(P, c, in, (in.flags & F_X_FROM_INPUT) ? 0 : 2 * in.layer) &&
+                 stage_copy<false, NB>(P, c, in, P.to + (size_t)in.layer * P.B * P.nq * P.d, P.nq * P.d) && cbar(c, pc);
             break;
         case OP_DOWN:
-            ok = stage_rows(P, c, in, 2 * in.layer + 1) &&
-                 stage_copy<ACT16_DOWN<NB>>(P, c, in, P.tact + (size_t)in.layer * P.B * P.F, P.F) && cbar(c, pc);
+            ok = stage_rows<NB>(P, c, in, 2 * in.layer + 1) &&
+                 stage_copy<ACT16_DOWN<NB>, NB>(P, c, in, P.tact + (size_t)in.layer * P.B * P.F, P.F) && cbar(c, pc);
             break;
         case OP_ATTN: {
             const int p = in.b >= 0 && in.b < P.B ? (int)lds_ld(c.misc + M_KVLEN + in.b) : -1;

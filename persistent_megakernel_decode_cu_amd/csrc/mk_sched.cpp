@@ -150,9 +150,11 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     if (desc.attn_chunks > MAX_ATTN_CHUNKS)
         return set_error(MK_EINVAL, "attn_chunks above " + std::to_string(MAX_ATTN_CHUNKS));
     // about one K/V block per wave: attention is short arithmetic on few
-    // units, so it is spread as wide as the merge in the O projection allows
+    // units, so it is spread wide; with more requests there are more tiles
+    // already, and half the chunk cap
     int C = desc.attn_chunks > 0 ? desc.attn_chunks
-                                 : std::min(AUTO_ATTN_CHUNKS, std::max(1, ceil_div(nb_max, N_COMPUTE_WAVES)));
+                                 : std::min(B <= 2 ? AUTO_ATTN_CHUNKS : AUTO_ATTN_CHUNKS / 2,
+                                            std::max(1, ceil_div(nb_max, N_COMPUTE_WAVES)));
     C = std::min(C, nb_max);
     P.attn_chunks = C;
     P.n_cus = S;
