@@ -13,8 +13,8 @@ code must satisfy, and this check proves on the assembly of every kernel:
    `slot_wait` (an s_waitcnt vmcnt) -- checked locally: each run of copies
    follows a wait in the same basic block with no label in between;
 3. the kernel descriptor allocates the slot registers;
-4. the slice loop (the innermost loop around the first slot_wait, found by
-   the compiler's loop annotations) holds no compiler-inserted vmcnt wait:
+4. the slice loops (the innermost loops around each slot_wait, found by the
+   compiler's loop annotations) hold no compiler-inserted vmcnt wait:
    the compiler does not see the slice loads, so any wait it places there
    for its own loads (a spill reload, say) is a vmcnt(0) that drains every
    slice in flight.
@@ -96,37 +96,38 @@ def check_kernel(body):
     return problems, n_load, n_take, max_compiler, top_slot
 
 
+def _innermost_header(body, i):
+    for j in range(i, -1, -1):
+        m = re.search(r"Loop: Header=(BB\S+) Depth=\d+", body[j])
+        if m:
+            return m.group(1)
+        m = re.match(r"^\.L(BB\S+):.*Loop Header: Depth=\d+", body[j])
+        if m:
+            return m.group(1)
+    return None
+
+
 def slice_loop_waits(body):
-    """(loop header, lines in the loop, [compiler vmcnt waits in it])."""
-    first = next((i for i, l in enumerate(body) if "slot_wait" in l), None)
-    if first is None:
-        return None, 0, []
-    hdr = None
-    for i in range(first, -1, -1):
-        m = re.search(r"Loop: Header=(BB\S+) Depth=\d+", body[i])
-        if m:
-            hdr = m.group(1)
-            break
-        m = re.match(r"^\.L(BB\S+):.*Loop Header: Depth=\d+", body[i])
-        if m:
-            hdr = m.group(1)
-            break
-    if hdr is None:
+    """(loop headers, lines in those loops, [compiler vmcnt waits in them]) for
+    every innermost loop that holds a slot_wait (the slice loops)."""
+    hdrs = {_innermost_header(body, i) for i, l in enumerate(body) if "slot_wait" in l}
+    hdrs.discard(None)
+    if not hdrs:
         return None, 0, []
     inloop, n, bad = False, 0, []
     for i, l in enumerate(body):
         m = re.match(r"^\.L(BB\S+):(.*)$", l)
         if m:
-            inloop = m.group(1) == hdr or f"Header={hdr} " in m.group(2)
+            inloop = m.group(1) in hdrs or any(f"Header={h} " in m.group(2) for h in hdrs)
             continue
         if re.match(r"^; %bb\.\d+:", l):
-            inloop = f"Header={hdr} " in l
+            inloop = any(f"Header={h} " in l for h in hdrs)
             continue
         if inloop:
             n += 1
             if "s_waitcnt" in l and "vmcnt" in l and "slot_wait" not in l:
-                bad.append(f"line {i}: compiler vmcnt wait in the slice loop: '{l.strip()}'")
-    return hdr, n, bad
+                bad.append(f"line {i}: compiler vmcnt wait in a slice loop: '{l.strip()}'")
+    return sorted(hdrs), n, bad
 
 
 def main(paths):

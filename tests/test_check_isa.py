@@ -51,5 +51,5 @@ def test_malformed_slot_load_is_reported():
 
 def test_compiler_wait_inside_the_slice_loop_is_counted():
     bad = CLEAN.replace("\tv_fma_f32 v5, v10, v11, v5", "\ts_waitcnt vmcnt(0)\n\tv_fma_f32 v5, v10, v11, v5")
-    hdr, n, waits = check_isa.slice_loop_waits(lines(bad))
-    assert hdr == "BB0_1" and len(waits) == 1
+    hdrs, n, waits = check_isa.slice_loop_waits(lines(bad))
+    assert hdrs == ["BB0_1"] and len(waits) == 1
