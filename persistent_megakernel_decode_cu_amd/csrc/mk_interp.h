@@ -351,7 +351,7 @@ __device__ __forceinline__ void slot_take<0>(v2u (&x)[8], int n_wait) {
     if (n_wait == 0)  // a constant at every call site
         asm volatile("s_waitcnt vmcnt(0) ; slot_wait" ::: "memory");
     else
-        asm volatile("s_waitcnt vmcnt(12) ; slot_wait" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0) ; slot_wait" ::"i"(4 * (D - 1)) : "memory");
     asm volatile(
         "v_mov_b64 %0, v[168:169] ; slot_take\n\t"
         "v_mov_b64 %1, v[170:171] ; slot_take\n\t"
@@ -370,7 +370,7 @@ __device__ __forceinline__ void slot_take<1>(v2u (&x)[8], int n_wait) {
     if (n_wait == 0)  // a constant at every call site
         asm volatile("s_waitcnt vmcnt(0) ; slot_wait" ::: "memory");
     else
-        asm volatile("s_waitcnt vmcnt(12) ; slot_wait" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0) ; slot_wait" ::"i"(4 * (D - 1)) : "memory");
     asm volatile(
         "v_mov_b64 %0, v[184:185] ; slot_take\n\t"
         "v_mov_b64 %1, v[186:187] ; slot_take\n\t"
@@ -389,7 +389,7 @@ __device__ __forceinline__ void slot_take<2>(v2u (&x)[8], int n_wait) {
     if (n_wait == 0)  // a constant at every call site
         asm volatile("s_waitcnt vmcnt(0) ; slot_wait" ::: "memory");
     else
-        asm volatile("s_waitcnt vmcnt(12) ; slot_wait" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0) ; slot_wait" ::"i"(4 * (D - 1)) : "memory");
     asm volatile(
         "v_mov_b64 %0, v[200:201] ; slot_take\n\t"
         "v_mov_b64 %1, v[202:203] ; slot_take\n\t"
@@ -408,7 +408,7 @@ __device__ __forceinline__ void slot_take<3>(v2u (&x)[8], int n_wait) {
     if (n_wait == 0)  // a constant at every call site
         asm volatile("s_waitcnt vmcnt(0) ; slot_wait" ::: "memory");
     else
-        asm volatile("s_waitcnt vmcnt(12) ; slot_wait" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0) ; slot_wait" ::"i"(4 * (D - 1)) : "memory");
     asm volatile(
         "v_mov_b64 %0, v[216:217] ; slot_take\n\t"
         "v_mov_b64 %1, v[218:219] ; slot_take\n\t"
@@ -489,6 +489,21 @@ __device__ __forceinline__ int token_of(const KParams &P, Ctx &c, int b, int pc)
     return t;
 }
 
+// wv[k] <- wn[first + 256 k] for k < n, else 0 (k < NW_FAST). The loads are
+// unconditional, with the index clamped into the vector, so they issue back
+// to back under one wait: a load guarded per element compiles to a load and
+// a wait each, and every one of those waits also drains all the weight
+// slices in flight. Elements k >= NW_FAST (H above 2048) are read later, one
+// by one.
+constexpr int NW_FAST = 8;
+__device__ __forceinline__ void load_norm_w(const uint16_t *wn, int H, int first, int n, float (&wv)[NW_FAST]) {
+    uint16_t raw[NW_FAST];
+#pragma unroll
+    for (int k = 0; k < NW_FAST; ++k) raw[k] = wn[min(first + 256 * k, H - 1)];
+#pragma unroll
+    for (int k = 0; k < NW_FAST; ++k) wv[k] = k < n ? bf2f(raw[k]) : 0.0f;
+}
+
 // act[b] <- rmsnorm(x_v[b]) * wn in the matvec layout (x_0: the layer-0
 // input). Waves 0..3 each gather the elements i = 64 w + lane + 256 k and
 // sum their squares in that order, which is the reduction of the
@@ -500,16 +515,9 @@ __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &
     const int first = w * 64 + lane;
     const int n = first < H ? (H - first + 255) / 256 : 0;  // this lane's elements
     const int nmax = (H - w * 64 + 255) / 256;               // lane 0's: the most
-    // The norm weights of the lane's first 16 elements are loaded with the
-    // inputs: a load issued later would wait behind the weight slices in flight.
-    float wv[16];
     // several requests: every wave gathers, all requests in shared rounds
     const bool batched = NB > 1 && xv != 0;
     if (batched) {
-        if (w < 4) {
-#pragma unroll
-            for (int k = 0; k < 16; ++k) wv[k] = k < n ? bf2f(wn[first + 256 * k]) : 0.0f;
-        }
         if (!tgather_batch(
                 c, P.tx + (size_t)(xv - 1) * P.B * H, P.B, H,
                 [&](int b, int i, float v) { c.act[b * P.act_stride + act_index(i)] = v; }, in.pc))
@@ -517,10 +525,6 @@ __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &
         if (!cbar(c, in.pc)) return false;
     }
     if (w < 4) {
-        if (!batched) {
-#pragma unroll
-            for (int k = 0; k < 16; ++k) wv[k] = k < n ? bf2f(wn[first + 256 * k]) : 0.0f;
-        }
         for (int b = 0; b < P.B; ++b) {
             MK_LDS float *a = c.act + b * P.act_stride;
             if (batched) {
@@ -550,18 +554,23 @@ __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &
     }
     if (!cbar(c, in.pc)) return false;
     if (w < 4) {
+        // the norm weights are read once the inputs are in: by then no weight
+        // slice is in flight ahead of these loads, and no register holds them
+        // across the polls
+        float wv[NW_FAST];
+        load_norm_w(wn, H, first, n, wv);
         for (int b = 0; b < P.B; ++b) {
             float tot = 0.0f;
             for (int v = 0; v < 4; ++v) tot += norm[v * MAX_B + b];
             const float inv = 1.0f / sqrtf(tot / (float)H + P.eps);
             MK_LDS float *a = c.act + b * P.act_stride;
 #pragma unroll
-            for (int k = 0; k < 16; ++k)
+            for (int k = 0; k < NW_FAST; ++k)
                 if (k < n) {
                     const int ai = act_index(first + 256 * k);
                     a[ai] = a[ai] * inv * wv[k];
                 }
-            for (int k = 16; k < n; ++k) {
+            for (int k = NW_FAST; k < n; ++k) {
                 const int i = first + 256 * k;
                 a[act_index(i)] = a[act_index(i)] * inv * bf2f(wn[i]);
             }
@@ -1068,13 +1077,13 @@ __device__ __forceinline__ void issue_any(int k, const KParams &P, const Cur &cu
 }
 
 // The wave's main loop. Slices are consumed in the order they were issued,
-// so the slot being consumed always has the other three slots issued after
-// it, and a wait for all but the 12 newest loads is a wait for exactly this
-// slot. At an instruction boundary the wave leaves the previous instruction
+// so the slot being consumed always has the other D - 1 slots issued after
+// it, and a wait for all but the 4 (D - 1) newest loads is a wait for
+// exactly this slot. At an instruction boundary the wave leaves the previous instruction
 // and enters the next one while the slices already issued stay in flight.
 template <int NB, int G>
 __device__ __forceinline__ void run(const KParams &P, Ctx &c) {
-    static_assert(D == 4, "four slots");
+    static_assert(D >= 2 && D <= 4, "two to four slots");
     Cur ic, cc;
     cur_load(P, c, ic, 0);
     cur_load(P, c, cc, 0);
@@ -1082,10 +1091,14 @@ __device__ __forceinline__ void run(const KParams &P, Ctx &c) {
     cur_next(P, c, ic);
     issue<1>(P, ic, c.lane);
     cur_next(P, c, ic);
-    issue<2>(P, ic, c.lane);
-    cur_next(P, c, ic);
-    issue<3>(P, ic, c.lane);
-    cur_next(P, c, ic);
+    if constexpr (D > 2) {
+        issue<2>(P, ic, c.lane);
+        cur_next(P, c, ic);
+    }
+    if constexpr (D > 3) {
+        issue<3>(P, ic, c.lane);
+        cur_next(P, c, ic);
+    }
     Ins in{};
     Acc<NB> acc;
     AttnLaneT<G> at;
@@ -1108,7 +1121,7 @@ __device__ __forceinline__ void run(const KParams &P, Ctx &c) {
             issue_any(slot, P, ic, c.lane);
             cur_next(P, c, ic);
             cur_next(P, c, cc);
-            slot = (slot + 1) & 3;
+            slot = slot + 1 == D ? 0 : slot + 1;
             if (uni(last)) break;
         }
     }
