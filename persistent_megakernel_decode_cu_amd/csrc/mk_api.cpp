@@ -335,6 +335,7 @@ int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream) {
         k.xrow_off = P.xrow_off;
         k.part_off = P.part_off;
         k.act_off = P.act_off;
+        k.nw_off = P.nw_off;
         k.act_stride = P.act_stride;
         k.xrow_stride = P.xrow_stride;
         k.watchdog = P.desc.watchdog_spins;

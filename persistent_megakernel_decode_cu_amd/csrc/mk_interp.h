@@ -489,19 +489,20 @@ __device__ __forceinline__ int token_of(const KParams &P, Ctx &c, int b, int pc)
     return t;
 }
 
-// wv[k] <- wn[first + 256 k] for k < n, else 0 (k < NW_FAST). The loads are
-// unconditional, with the index clamped into the vector, so they issue back
-// to back under one wait: a load guarded per element compiles to a load and
-// a wait each, and every one of those waits also drains all the weight
-// slices in flight. Elements k >= NW_FAST (H above 2048) are read later, one
-// by one.
-constexpr int NW_FAST = 8;
-__device__ __forceinline__ void load_norm_w(const uint16_t *wn, int H, int first, int n, float (&wv)[NW_FAST]) {
-    uint16_t raw[NW_FAST];
-#pragma unroll
-    for (int k = 0; k < NW_FAST; ++k) raw[k] = wn[min(first + 256 * k, H - 1)];
-#pragma unroll
-    for (int k = 0; k < NW_FAST; ++k) wv[k] = k < n ? bf2f(raw[k]) : 0.0f;
+// Copies the norm weights wn[0, H) (bf16) into the LDS area at nw_off with
+// 1 KiB wave loads that write LDS directly (no registers held, no wait of
+// their own): issued before the input polls, they land under the same waits.
+// Wave w < 4 copies KiB w, w + 4, ...; lanes past the vector re-read its last
+// 16 bytes into the area's padding.
+__device__ __forceinline__ void prefetch_norm_w(const KParams &P, const Ctx &c, const uint16_t *wn) {
+    if (c.w >= 4) return;
+    const int bytes = P.H * 2;
+    MK_LDS char *dst = (MK_LDS char *)c.misc + P.nw_off;
+    for (int kib = c.w; kib * 1024 < bytes; kib += 4) {
+        const int off = min(kib * 1024 + c.lane * 16, bytes - 16);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)((const char *)wn + off),
+                                         (__attribute__((address_space(3))) void *)(dst + kib * 1024), 16, 0, 0);
+    }
 }
 
 // act[b] <- rmsnorm(x_v[b]) * wn in the matvec layout (x_0: the layer-0
@@ -515,6 +516,7 @@ __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &
     const int first = w * 64 + lane;
     const int n = first < H ? (H - first + 255) / 256 : 0;  // this lane's elements
     const int nmax = (H - w * 64 + 255) / 256;               // lane 0's: the most
+    prefetch_norm_w(P, c, wn);
     // several requests: every wave gathers, all requests in shared rounds
     const bool batched = NB > 1 && xv != 0;
     if (batched) {
@@ -552,28 +554,18 @@ __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &
             if (lane == 0) norm[w * MAX_B + b] = ss;
         }
     }
+    // the norm-weight copies have landed (the polls waited for every load
+    // issued before them; the embedding path has no polls)
+    if (w < 4) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (!cbar(c, in.pc)) return false;
     if (w < 4) {
-        // the norm weights are read once the inputs are in: by then no weight
-        // slice is in flight ahead of these loads, and no register holds them
-        // across the polls
-        float wv[NW_FAST];
-        load_norm_w(wn, H, first, n, wv);
+        const MK_LDS uint16_t *nw = (const MK_LDS uint16_t *)((MK_LDS char *)c.misc + P.nw_off);
         for (int b = 0; b < P.B; ++b) {
             float tot = 0.0f;
             for (int v = 0; v < 4; ++v) tot += norm[v * MAX_B + b];
             const float inv = 1.0f / sqrtf(tot / (float)H + P.eps);
             MK_LDS float *a = c.act + b * P.act_stride;
-#pragma unroll
-            for (int k = 0; k < NW_FAST; ++k)
-                if (k < n) {
-                    const int ai = act_index(first + 256 * k);
-                    a[ai] = a[ai] * inv * wv[k];
-                }
-            for (int k = NW_FAST; k < n; ++k) {
-                const int i = first + 256 * k;
-                a[act_index(i)] = a[act_index(i)] * inv * bf2f(wn[i]);
-            }
+            for (int i = first; i < H; i += 256) a[act_index(i)] = a[act_index(i)] * inv * bf2f(nw[i]);
         }
     }
     return cbar(c, in.pc);

@@ -13,7 +13,7 @@ struct KParams {
     int32_t *counters;        // [n_counters * CTR_STRIDE]
     int32_t Q, epoch, n_cus;
     uint32_t tag;             // this step's tag on every exchanged activation (never 0)
-    int32_t queue_off, xrow_off, part_off, act_off;  // LDS byte offsets
+    int32_t queue_off, xrow_off, part_off, act_off, nw_off;  // LDS byte offsets
     int32_t act_stride;       // floats per request in the activation area
     int32_t xrow_stride;      // floats per request in the residual-row area
     int64_t watchdog;

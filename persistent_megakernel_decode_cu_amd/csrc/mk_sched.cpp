@@ -331,7 +331,9 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     const int64_t xrow_off = queue_off + up256((int64_t)Q * LDS_INSTR_WORDS * 4);
     const int64_t part_off = xrow_off + up256((int64_t)NBP * P.xrow_stride * 4);
     const int64_t act_off = part_off + up256(part_floats * 4);
-    const int64_t lds = act_off + up256(act_floats * 4);
+    // the norm weights of a staged RMSNorm, copied in whole 1 KiB wave loads
+    const int64_t nw_off = act_off + up256(act_floats * 4);
+    const int64_t lds = nw_off + ((int64_t)H * 2 + 1023) / 1024 * 1024;
     if (lds > LDS_LIMIT)
         return set_error(MK_ECAPACITY, "a tile's on-chip staging needs " + std::to_string(lds) +
                                            " bytes of LDS (limit " + std::to_string(LDS_LIMIT) +
@@ -341,6 +343,7 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     P.xrow_off = (int)xrow_off;
     P.part_off = (int)part_off;
     P.act_off = (int)act_off;
+    P.nw_off = (int)nw_off;
     P.lds_bytes = (int)lds;
     return MK_OK;
 }
