@@ -45,6 +45,7 @@ enum : int {
     M_ARRIVE = 1,  // compute-wave barrier arrivals
     M_FIN = 2,     // waves finished with an instruction's slices
     M_DONE = 3,    // instructions fully finished (incl. their merges)
+    M_AFIN = 4,    // attention heads merged over the waves (G per instruction)
     M_KVLEN = 8,   // [MAX_B] lengths of the requests (read once at start)
     M_NORM = 16,   // [4][MAX_B] sums of squares
     M_AMAX = 64,   // [NC][MAX_B][2] per-wave argmax (value, index)
@@ -959,21 +960,6 @@ template <int G>
 __device__ __forceinline__ bool finish(const KParams &P, Ctx &c, const Ins &in) {
     const int lane = c.lane;
     const uint32_t tag = P.tag;
-    if (in.op == OP_ATTN) {  // the chunk's state of each head, merged over the waves
-        const size_t pbase = ((((size_t)in.layer * P.B + in.b) * P.nkv + in.g) * in.nch + in.c) * G * ATTN_PART;
-        const __amdgpu_buffer_rsrc_t rp = tres(P.tpart + pbase, (uint32_t)(G * ATTN_PART));
-#pragma unroll 1
-        for (int h = 0; h < G; ++h) {
-            float O, M, L;
-            merge_wave_states<G, NC>(c.part, h, lane, O, M, L);
-            tput(rp, (uint32_t)(h * ATTN_PART + lane), O, tag);
-            if (lane == 0) {
-                tput(rp, (uint32_t)(h * ATTN_PART + 64), M, tag);
-                tput(rp, (uint32_t)(h * ATTN_PART + 65), L, tag);
-            }
-        }
-        return true;
-    }
     if (in.op == OP_LMHEAD) {
         const MK_LDS float *am = (const MK_LDS float *)(c.misc + M_AMAX);
         const __amdgpu_buffer_rsrc_t rl = tres(P.tlm, (uint32_t)(in.nslot * P.B * 2));
@@ -1040,8 +1026,36 @@ __device__ __forceinline__ bool leave(const KParams &P, Ctx &c, const Ins &in, A
     if (lane == 0) old = lds_add(c.misc + M_FIN, 1u);
     old = __builtin_amdgcn_readfirstlane(old);  // lane 0's: every lane is active here
     if (in.tr && lane == 0 && old == (uint32_t)NC * in.pc) in.tr[TR_FIRST] = wall_clock64();
+    if (in.tr && lane == 0 && old == (uint32_t)NC * (in.pc + 1) - 1) in.tr[TR_LAST] = wall_clock64();
+    if (in.op == OP_ATTN) {
+        // Once every wave has stored its state, wave h < G merges head h over
+        // the waves (in wave order) and publishes the chunk's (o, m, l) of
+        // that head; the last head merged ends the instruction. The other
+        // waves go on to the next instruction, whose staging waits for that.
+        if (c.w >= G) return true;
+        if (!lds_wait_ge(c, c.misc + M_FIN, (uint32_t)NC * (in.pc + 1), in.pc)) return false;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        const int h = c.w;
+        const size_t pbase = ((((size_t)in.layer * P.B + in.b) * P.nkv + in.g) * in.nch + in.c) * G * ATTN_PART;
+        const __amdgpu_buffer_rsrc_t rp = tres(P.tpart + pbase, (uint32_t)(G * ATTN_PART));
+        float O, M, L;
+        merge_wave_states<G, NC>(c.part, h, lane, O, M, L);
+        tput(rp, (uint32_t)(h * ATTN_PART + lane), O, P.tag);
+        if (lane == 0) {
+            tput(rp, (uint32_t)(h * ATTN_PART + 64), M, P.tag);
+            tput(rp, (uint32_t)(h * ATTN_PART + 65), L, P.tag);
+        }
+        uint32_t m = 0;
+        if (lane == 0) m = lds_add(c.misc + M_AFIN, 1u);
+        m = __builtin_amdgcn_readfirstlane(m);
+        // an instruction's merges all end before the next one's begin, so
+        // the count reaches a multiple of G exactly at its last merge
+        if ((m + 1) % G != 0) return true;
+        if (in.tr && lane == 0) in.tr[TR_END] = wall_clock64();
+        if (lane == 0) lds_add(c.misc + M_DONE, 1u);
+        return true;
+    }
     if (old != (uint32_t)NC * (in.pc + 1) - 1) return true;
-    if (in.tr && lane == 0) in.tr[TR_LAST] = wall_clock64();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if (!finish<G>(P, c, in)) return false;
     if (in.tr && lane == 0) in.tr[TR_END] = wall_clock64();
