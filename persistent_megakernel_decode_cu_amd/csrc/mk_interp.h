@@ -559,6 +559,11 @@ __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &
     // issued before them; the embedding path has no polls)
     if (w < 4) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (!cbar(c, in.pc)) return false;
+    // batch 1 with H = 2048: every wave applies the norm as it loads its
+    // register activations (norm_scale, at entry to the slices), so the
+    // inputs stay unscaled here and neither a scaling pass nor a second
+    // barrier is needed
+    if (NB == 1 && H == 2048) return true;
     if (w < 4) {
         const MK_LDS uint16_t *nw = (const MK_LDS uint16_t *)((MK_LDS char *)c.misc + P.nw_off);
         for (int b = 0; b < P.B; ++b) {
@@ -781,12 +786,29 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
     acc.nan = false;
     attn_lane_init(at);
     if (NB == 1 && in.op != OP_ATTN && k.K == 2048) {
+        // the lane's activations: chunk 64 j + lane, elements 8 (64 j + lane) + e
+        const bool normed = in.op == OP_QKV || in.op == OP_UPGATE || in.op == OP_LMHEAD;
+        float inv = 1.0f;
+        if (normed) {  // the same sum and order as a staged norm's scaling pass
+            const MK_LDS float *norm = (const MK_LDS float *)(c.misc + M_NORM);
+            float tot = 0.0f;
+            for (int v = 0; v < 4; ++v) tot += norm[v * MAX_B];
+            inv = 1.0f / sqrtf(tot / (float)P.H + P.eps);
+        }
+        const MK_LDS uint16_t *nw = (const MK_LDS uint16_t *)((MK_LDS char *)c.misc + P.nw_off);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const v4f a = *(const MK_LDS v4f *)(c.act + j * 512 + c.lane * 4);
             const v4f b = *(const MK_LDS v4f *)(c.act + j * 512 + 256 + c.lane * 4);
             at.o[j][0] = a.x; at.o[j][1] = a.y; at.o[j][2] = a.z; at.o[j][3] = a.w;
             at.o[j][4] = b.x; at.o[j][5] = b.y; at.o[j][6] = b.z; at.o[j][7] = b.w;
+            if (normed) {
+                const v4u wq = *(const MK_LDS v4u *)(nw + (j * 64 + c.lane) * 8);
+                const float wf[8] = {bf_lo(wq.x), bf_hi(wq.x), bf_lo(wq.y), bf_hi(wq.y),
+                                     bf_lo(wq.z), bf_hi(wq.z), bf_lo(wq.w), bf_hi(wq.w)};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) at.o[j][e] = at.o[j][e] * inv * wf[e];
+            }
         }
     }
     return true;

@@ -149,12 +149,13 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     // prefetch window (N_COMPUTE_WAVES waves x PREFETCH_SLICES blocks)
     if (desc.attn_chunks > MAX_ATTN_CHUNKS)
         return set_error(MK_EINVAL, "attn_chunks above " + std::to_string(MAX_ATTN_CHUNKS));
-    // about one K/V block per wave: attention is short arithmetic on few
-    // units, so it is spread wide; with more requests there are more tiles
-    // already, and half the chunk cap
+    // about one K/V block per wave on half the waves (one wave per SIMD,
+    // which then has the vector unit to itself): attention is short
+    // arithmetic on few units, so it is spread wide; with more requests there
+    // are more tiles already, and half the chunk cap
     int C = desc.attn_chunks > 0 ? desc.attn_chunks
                                  : std::min(B <= 2 ? AUTO_ATTN_CHUNKS : AUTO_ATTN_CHUNKS / 2,
-                                            std::max(1, ceil_div(nb_max, N_COMPUTE_WAVES)));
+                                            std::max(1, ceil_div(nb_max, N_COMPUTE_WAVES / 2)));
     C = std::min(C, nb_max);
     P.attn_chunks = C;
     P.n_cus = S;
