@@ -128,6 +128,23 @@ __device__ __forceinline__ uint64_t iw64(const Ctx &c, int pc, int w) {
     return (uint64_t)(uint32_t)iw(c, pc, w) | ((uint64_t)(uint32_t)iw(c, pc, w + 1) << 32);
 }
 
+// Words [w0, w0 + 4) of instruction pc as one 16-byte LDS read (every lane
+// the same address): the reads of a record issue together and wait once,
+// where a read per word would wait a full LDS round trip each.
+typedef int32_t iv4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ iv4 iw4(const Ctx &c, int pc, int w0) {
+    return *(const MK_LDS iv4 *)(c.q + pc * LDS_INSTR_WORDS + w0);
+}
+__device__ __forceinline__ int32_t rfl(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t rfl64(int32_t lo, int32_t hi) {
+    return (uint64_t)(uint32_t)rfl(lo) | ((uint64_t)(uint32_t)rfl(hi) << 32);
+}
+static_assert(W_OP == 0 && W_LAYER == 1 && W_R0 == 2 && W_R1 == 3 && W_B == 4 && W_G == 5 && W_C == 6 &&
+                  W_NCH == 7 && W_FLAGS == 8 && W_MERGE == 9 && W_SLOT == 10 && W_NSLOT == 11 && W_MCTR == 13 &&
+                  W_MNEED == 14 && W_WA == 16 && W_WB == 18 && W_WN == 20 && LDS_INSTR_WORDS % 4 == 0 &&
+                  W_WN + 4 <= LDS_INSTR_WORDS,
+              "instruction record layout read by iw4");
+
 __device__ __forceinline__ void chunk_blocks(int p, int c, int nch, int *lo, int *hi) {
     const int nb = (p + 1 + 15) >> 4;
     *lo = (int)((int64_t)c * nb / nch);
@@ -228,7 +245,7 @@ struct Cur {
 
 __device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k, int pc) {
     k.pc = pc;
-    k.op = pc < P.Q ? iw(c, pc, W_OP) : OP_END;
+    k.op = OP_END;
     k.u = c.w;
     k.s = 0;
     k.nu = 0;
@@ -237,17 +254,20 @@ __device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k,
     k.K = 0;
     k.rowb = 0;
     k.wa = k.wb = (uint64_t)(uintptr_t)P.wtab;
+    if (pc >= P.Q) return;
+    const iv4 a = iw4(c, pc, W_OP), bw = iw4(c, pc, W_B), wq = iw4(c, pc, W_WA);
+    k.op = rfl(a[0]);
     if (k.op == OP_END) return;
-    k.layer = iw(c, pc, W_LAYER);
-    k.r0 = iw(c, pc, W_R0);
+    k.layer = rfl(a[1]);
+    k.r0 = rfl(a[2]);
     if (k.op == OP_ATTN) {
-        k.b = iw(c, pc, W_B);
-        k.g = iw(c, pc, W_G);
+        k.b = rfl(bw[0]);
+        k.g = rfl(bw[1]);
         int p = (int)lds_ld(c.misc + M_KVLEN + (k.b & (MAX_B - 1)));
         if (p < 0 || p >= P.T * P.max_pages) p = 0;  // the staging raises the error
         k.p = p;
         int lo, hi;
-        chunk_blocks(p, iw(c, pc, W_C), iw(c, pc, W_NCH), &lo, &hi);
+        chunk_blocks(p, rfl(bw[2]), rfl(bw[3]), &lo, &hi);
         k.blo = lo;
         k.nu = hi - lo;
     } else if (k.op == OP_AMERGE) {
@@ -257,9 +277,9 @@ __device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k,
         k.rowb = (uint32_t)k.K * 2;
         k.spm = (int)((k.rowb + SLICE_BYTES - 1) / SLICE_BYTES);
         k.sp = (k.op == OP_UPGATE ? 2 : 1) * k.spm;
-        k.nu = iw(c, pc, W_R1) - k.r0;
-        k.wa = iw64(c, pc, W_WA);
-        k.wb = iw64(c, pc, W_WB);
+        k.nu = rfl(a[3]) - k.r0;
+        k.wa = rfl64(wq[0], wq[1]);
+        k.wb = rfl64(wq[2], wq[3]);
     }
     // an unknown opcode yields one empty slice; its staging raises the error
 }
@@ -724,21 +744,23 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
                                       AttnLaneT<G> &at) {
     const int pc = k.pc;
     in.pc = pc;
-    in.op = iw(c, pc, W_OP);
-    in.layer = iw(c, pc, W_LAYER);
-    in.r0 = iw(c, pc, W_R0);
-    in.r1 = iw(c, pc, W_R1);
-    in.flags = iw(c, pc, W_FLAGS);
-    in.b = iw(c, pc, W_B);
-    in.g = iw(c, pc, W_G);
-    in.c = iw(c, pc, W_C);
-    in.nch = iw(c, pc, W_NCH);
-    in.merge = iw(c, pc, W_MERGE);
-    in.slot = iw(c, pc, W_SLOT);
-    in.nslot = iw(c, pc, W_NSLOT);
-    in.mctr = iw(c, pc, W_MCTR);
-    in.mneed = iw(c, pc, W_MNEED);
-    in.wn = iw64(c, pc, W_WN);
+    const iv4 a = iw4(c, pc, W_OP), bw = iw4(c, pc, W_B), fw = iw4(c, pc, W_FLAGS), mw = iw4(c, pc, 12),
+              nw = iw4(c, pc, W_WN);
+    in.op = rfl(a[0]);
+    in.layer = rfl(a[1]);
+    in.r0 = rfl(a[2]);
+    in.r1 = rfl(a[3]);
+    in.b = rfl(bw[0]);
+    in.g = rfl(bw[1]);
+    in.c = rfl(bw[2]);
+    in.nch = rfl(bw[3]);
+    in.flags = rfl(fw[0]);
+    in.merge = rfl(fw[1]);
+    in.slot = rfl(fw[2]);
+    in.nslot = rfl(fw[3]);
+    in.mctr = rfl(mw[W_MCTR - 12]);
+    in.mneed = rfl(mw[W_MNEED - 12]);
+    in.wn = rfl64(nw[0], nw[1]);
     in.tr = P.trace ? P.trace + ((int64_t)c.cu * P.Q + pc) * TRACE_WORDS : nullptr;
     const bool tracer = in.tr && c.w == 0 && c.lane == 0;
     if (tracer) in.tr[TR_START] = wall_clock64();
