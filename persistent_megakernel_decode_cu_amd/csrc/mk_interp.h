@@ -1028,19 +1028,32 @@ __device__ __forceinline__ bool finish(const KParams &P, Ctx &c, const Ins &in) 
                 c, rl, 0, in.nslot * P.B * 2, [&](int i, float v) { c.act[i] = v; }, in.pc))
             return false;
         if (in.tr && lane == 0) in.tr[TR_GATHER] = wall_clock64();
-        if (lane < P.B) {
+        // per request: each lane takes slots lane, lane + 64, ..., then an
+        // xor butterfly over the wave leaves every lane with the maximum
+        for (int b = 0; b < P.B; ++b) {
             float bv = -INFINITY;
             int bi = 0x7fffffff;
-            for (int t = 0; t < in.nslot; ++t) {
-                const float v = c.act[(t * P.B + lane) * 2];
-                const int i = __float_as_int(c.act[(t * P.B + lane) * 2 + 1]);
+            for (int t = lane; t < in.nslot; t += 64) {
+                const float v = c.act[(t * P.B + b) * 2];
+                const int i = __float_as_int(c.act[(t * P.B + b) * 2 + 1]);
                 if (amax_better(v, i, bv, bi)) {
                     bv = v;
                     bi = i;
                 }
             }
-            P.tokens_out[lane] = bi;
-            if (P.kv_lens_out) P.kv_lens_out[lane] = (int32_t)c.misc[M_KVLEN + lane] + 1;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const float ov = __shfl_xor(bv, o, 64);
+                const int oi = __shfl_xor(bi, o, 64);
+                if (amax_better(ov, oi, bv, bi)) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            if (lane == 0) {
+                P.tokens_out[b] = bi;
+                if (P.kv_lens_out) P.kv_lens_out[b] = (int32_t)c.misc[M_KVLEN + b] + 1;
+            }
         }
         return true;
     }
