@@ -17,9 +17,10 @@
 // What this file does, in order:
 //   1. cut every op of every layer into tiles: a contiguous row range per
 //      compute unit for each matvec (rows handed out by a least-loaded-first
-//      fill over streamed bytes, so compute units that also carry attention
-//      chunks get fewer rows of the next op), and one tile per (request, kv
-//      head, K/V chunk) for attention;
+//      fill over streamed bytes, restarted at each op that follows a hop;
+//      the O projection's fill counts the layer's QKV and attention bytes,
+//      so compute units that also carry attention chunks get fewer of its
+//      rows), and one tile per (request, kv head, K/V chunk) for attention;
 //   2. create the merge events: last-finisher counters for the attention
 //      chunks of each (layer, request, kv head), the LM-head argmax, and the
 //      end of a step without an LM head. The data edges need no event: every
@@ -205,6 +206,11 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
 
     for (int l = 0; l < L; ++l) {
         const int first = l == 0 ? F_X_FROM_INPUT : 0;
+        // Every unit starts an op that follows a hop at about the same time,
+        // so the fill starts afresh there (QKV, UPGATE, DOWN, LM head); the
+        // O projection continues from the QKV and attention bytes, so that
+        // units carrying attention chunks get fewer of its rows.
+        std::fill(cum.begin(), cum.end(), 0);
         matvec_op(OP_QKV, l, QKV, (int64_t)H * 2, first);
         // attention chunks, each publishing its softmax state; then one
         // merge per (request, kv head), on the least-loaded unit
@@ -244,7 +250,9 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
                 tiles.push_back(t);
             }
         matvec_op(OP_OPROJ, l, H, (int64_t)QD * 2, first);
+        std::fill(cum.begin(), cum.end(), 0);
         matvec_op(OP_UPGATE, l, F, (int64_t)H * 4, 0);
+        std::fill(cum.begin(), cum.end(), 0);
         const bool last = l == L - 1;
         std::vector<int> down_ids = matvec_op(OP_DOWN, l, H, (int64_t)F * 2, last ? F_WRITE_HIDDEN : 0);
         if (last && !cfg.has_embed) {  // the last down-projection tile to finish ends the step
@@ -259,6 +267,7 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
         }
     }
     if (cfg.has_embed) {
+        std::fill(cum.begin(), cum.end(), 0);
         std::vector<int> lm_ids = matvec_op(OP_LMHEAD, L, cfg.vocab, (int64_t)H * 2, F_STEP_FINAL);
         const int ev = new_merge((int)lm_ids.size());
         for (size_t i = 0; i < lm_ids.size(); ++i) {
