@@ -85,6 +85,9 @@ def main():
                          "(the reference for the rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle sample: consecutive decode steps until this much time has passed")
+    ap.add_argument("--trace-layer", type=int, default=-1,
+                    help="after timing, run three untimed steps of a traced megakernel schedule and print the "
+                         "per-op timeline of this layer to stderr")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the decode step is measured on one MI355X); got --gpus {args.gpus}",
@@ -170,6 +173,20 @@ def main():
         out["unfused"] = {"us_per_step": round(ums * 1000.0, 2), "launches_per_step": uinfo["launches_per_step"],
                           "hbm_gbps": round(bytes_avg / (ums * 1e-3) / 1e9, 1),
                           "speedup_of_megakernel": round(ums / ms, 3)}
+    if args.trace_layer >= 0:
+        # a separate traced schedule, outside the timed region
+        from persistent_megakernel_decode_cu_amd import _mk, trace_summary
+        from tests import sched_check
+        tinfo = dec.build_schedule(1, mode="megakernel", max_kv_len=max_len, trace=True)
+        ds.kv_lens.copy_(torch.from_numpy(st0.kv_lens))
+        ds.tokens.copy_(torch.from_numpy(st0.tokens))
+        for _ in range(3):
+            gu.run_step(dec, ds, cfg, want_logits=False)
+        plan = _mk.Plan(dec.cfg, _mk.MkScheduleDesc(1, tinfo["n_cus"], 0, max_len, 0, 1, 0, 0, 0))
+        names = {v: k[3:] for k, v in sched_check.ISA.items() if k.startswith("OP_") and k not in ("OP_END", "OP_COUNT")}
+        text = trace_summary.timeline(dec.trace(), sched_check.decode(plan.queue), names, args.trace_layer)
+        for line in text.splitlines():
+            print(f"# {line}", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         # the oracle as it stands (single-threaded fp64 C), on consecutive greedy
         # steps of the same workload until the sample time has passed

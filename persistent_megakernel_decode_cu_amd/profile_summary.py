@@ -7,6 +7,7 @@ mk_copy_probe of a known size.
     python -m persistent_megakernel_decode_cu_amd.profile_summary stats DB --command "..."
     python -m persistent_megakernel_decode_cu_amd.profile_summary traffic --fetch DB --write DB \\
         --kernel mk_megakernel --copy-bytes N --command "..." --command "..."
+    python -m persistent_megakernel_decode_cu_amd.profile_summary counters DB [DB ...] --command "..."
 
 `digest()` fingerprints the kernel sources; a traffic summary records it, so
 that a reader can tell whether the kernels changed after the counters were
@@ -107,6 +108,27 @@ def traffic_text(fetch_db: str, write_db: str, kernel: str, copy_kernel: str, co
     return "\n".join(lines) + "\n"
 
 
+def counters_text(dbs, kernel: str, commands, skip: int) -> str:
+    """Per-dispatch averages (summed over counter instances) of every counter
+    in the --pmc databases `dbs`, for the kernels whose name holds `kernel`;
+    one line per counter, the first `skip` dispatches left out."""
+    lines = [f"command: {c}" for c in commands] + ["", f"kernel: {kernel} (first {skip} dispatches skipped)",
+                                                   f"{'counter':28s} {'dispatches':>10s} {'per dispatch':>16s}"]
+    for db in dbs:
+        per = pmc_per_dispatch(db)
+        vals = collections.defaultdict(list)
+        for name, lst in per.items():
+            if kernel not in name:
+                continue
+            for _, v in lst[skip:]:
+                for cn, cv in v.items():
+                    vals[cn].append(cv)
+        for cn in sorted(vals):
+            lines.append(f"{cn:28s} {len(vals[cn]):10d} {statistics.mean(vals[cn]):16.6g}")
+    lines.append(f"source_digest: {digest()}")
+    return "\n".join(lines) + "\n"
+
+
 def read_traffic(path: str):
     """(traffic bytes per launch, source digest) of a traffic summary, or None."""
     if not os.path.exists(path):
@@ -135,6 +157,11 @@ def main(argv=None):
     b.add_argument("--copy-bytes", type=int, required=True)
     b.add_argument("--skip", type=int, default=1, help="leading dispatches of the kernel to leave out (warm-up)")
     b.add_argument("--command", action="append", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dbs", nargs="+")
+    c.add_argument("--kernel", default="mk_megakernel")
+    c.add_argument("--skip", type=int, default=1)
+    c.add_argument("--command", action="append", required=True)
     sub.add_parser("digest")
     args = ap.parse_args(argv)
     if args.what == "stats":
@@ -144,6 +171,8 @@ def main(argv=None):
             ap.error("give --command twice: the FETCH_SIZE run, then the WRITE_SIZE run")
         sys.stdout.write(traffic_text(args.fetch, args.write, args.kernel, args.copy_kernel, args.copy_bytes,
                                       args.command, args.skip))
+    elif args.what == "counters":
+        sys.stdout.write(counters_text(args.dbs, args.kernel, args.command, args.skip))
     else:
         print(digest())
 
