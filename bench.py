@@ -11,9 +11,17 @@ next on the device, with no host synchronisation inside the timed region.
 
 Prints one JSON line. `value` is microseconds per decode step (lower is
 better); `roofline` gives the achieved algorithmic HBM bandwidth of the
-megakernel launch against the 8 TB/s peak; `cpu_baseline` times the CPU
-oracle on one full step of the same workload; `unfused` times the
-one-kernel-per-op baseline on the same chain.
+megakernel launch against the 8 TB/s peak; `step_us` the 10th, 50th and 90th
+percentiles of single steps within the chain; `read_probe` the read rate
+the interpreter's streaming shape reaches on a plain buffer, a second,
+achievable peak; `cpu_baseline` times the CPU oracle on consecutive steps of
+the same workload; `unfused` times the one-kernel-per-op baseline on the
+same chain.
+
+`--workload 1b-layer-kv512` times one 1B-shaped layer instead (hidden
+vector in and out): single steps, each after a write that evicts the
+memory-side cache the layer's weights would otherwise sit in, with hot-cache
+figures beside them.
 """
 from __future__ import annotations
 
@@ -45,9 +53,11 @@ def algorithmic_bytes(cfg, kv_lens) -> int:
     return total
 
 
-def time_chain(dec, ds, cfg, steps, warmup, torch):
+def time_chain(dec, ds, cfg, steps, warmup, torch, per_step=None):
     """Runs warmup + steps chained greedy steps; returns ms per timed step
-    (device events around the timed region on the launch stream)."""
+    (device events around the timed region on the launch stream). With a
+    list `per_step`, also records an event between consecutive steps and
+    appends each step's ms to it (no host synchronisation in between)."""
     stream = torch.cuda.current_stream()
     tokens = ds.tokens
     kv = ds.kv_lens
@@ -62,13 +72,106 @@ def time_chain(dec, ds, cfg, steps, warmup, torch):
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps - 1)] if per_step is not None else []
     t0.record(stream)
-    for _ in range(steps):
+    for k in range(steps):
         one()
+        if marks and k < steps - 1:
+            marks[k].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     dec.sync(stream.cuda_stream)
+    if per_step is not None:
+        bounds = [t0] + marks + [t1]
+        per_step.extend(bounds[k].elapsed_time(bounds[k + 1]) for k in range(steps))
     return t0.elapsed_time(t1) / steps
+
+
+def read_probe_gbps(torch, nbytes: int) -> float:
+    """Best of three passes of the register-slice read probe (one workgroup
+    of 8 waves per compute unit, 4 slices of 4 KiB in flight per wave: the
+    interpreter's own streaming shape) over `nbytes` of device memory."""
+    from persistent_megakernel_decode_cu_amd import _mk
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    best = 0.0
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        _mk.mk_debug_regstream_probe(src.data_ptr(), nbytes, n_cus, 512, 4, sink.data_ptr())
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, sink
+    return best
+
+
+def pct(v, q):
+    import numpy as np
+    return round(float(np.percentile(np.asarray(v), q)) * 1000.0, 2)
+
+
+def bench_layer(args, cfg, torch, np, gu, synthetic):
+    """One 1B-shaped layer (hidden vector in, hidden vector out, no embedding
+    or LM head): repeated single steps, each timed alone with device events.
+    Its 123 MB fit in the 256 MB memory-side cache, so before every cold
+    iteration a 512 MB scratch write evicts it; hot iterations (no flush)
+    are reported beside them."""
+    model = synthetic.make_model(cfg)
+    st0 = synthetic.make_state(cfg)
+    wdev = gu.upload_model(model)
+    ds = gu.DevState(st0)
+    dec = gu.make_decoder(model, st0, wdev)
+    info = dec.build_schedule(1, mode=args.mode, max_kv_len=int(st0.kv_lens.max()) + 1)
+    stream = torch.cuda.current_stream()
+    hidden = torch.empty((1, cfg.hidden), dtype=torch.float32, device="cuda")
+    kv_out = torch.empty_like(ds.kv_lens)
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+
+    def one():
+        dec.step(kv_lens=ds.kv_lens, k_pool=ds.k_pool, v_pool=ds.v_pool, page_table=ds.page_table,
+                 hidden_in=ds.hidden_in, hidden_out=hidden, kv_lens_out=kv_out, stream=stream.cuda_stream)
+
+    times = {"cold": [], "hot": []}
+    for _ in range(args.warmup):
+        one()
+    for kind in ("cold", "hot"):
+        for _ in range(args.steps):
+            if kind == "cold":
+                flush.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            one()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[kind].append(e0.elapsed_time(e1))
+    dec.sync(stream.cuda_stream)
+    dec.close()
+    nbytes = algorithmic_bytes(cfg, [int(st0.kv_lens[0])])
+    cold_us = pct(times["cold"], 50)
+    achieved = nbytes / (cold_us * 1e-6) / 1e9
+    out = {
+        "metric": "us/decode-step and achieved HBM GB/s (% of peak), 1B-shape batch 1",
+        "value": cold_us, "unit": "us/step", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(cold_us / 1000.0, 5), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 weights, fp32 compute",
+        "data": "synthetic (seeded random-init weights, K/V cache and input vector)",
+        "config": {"workload": f"{cfg.name}: one Llama-3.2-1B-shaped layer (H 2048, 32q/8kv x 64, F 8192), "
+                               f"batch 1, K/V length {int(st0.kv_lens[0])}, no embedding or LM head; median of "
+                               f"{args.steps} single steps, each after a 512 MB cache-evicting write",
+                   "mode": args.mode, "n_cus": info["n_cus"], "launches_per_step": info["launches_per_step"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None, "bytes_per_launch": int(nbytes)},
+        "step_us": {"p10": pct(times["cold"], 10), "p50": cold_us, "p90": pct(times["cold"], 90)},
+        "hot_cache_step_us": {"p10": pct(times["hot"], 10), "p50": pct(times["hot"], 50),
+                              "p90": pct(times["hot"], 90)},
+    }
+    print(json.dumps(out), flush=True)
 
 
 def main():
@@ -85,6 +188,8 @@ def main():
                          "(the reference for the rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle sample: consecutive decode steps until this much time has passed")
+    ap.add_argument("--probe-bytes", type=int, default=2 << 30,
+                    help="bytes the register-slice read probe streams for the achievable-read-rate figure (0: skip)")
     ap.add_argument("--trace-layer", type=int, default=-1,
                     help="after timing, run three untimed steps of a traced megakernel schedule and print the "
                          "per-op timeline of this layer to stderr")
@@ -101,6 +206,9 @@ def main():
     from tests import gpu_util as gu
 
     cfg = synthetic.workload(args.workload)
+    if cfg.batch == 1 and not cfg.has_embed:
+        bench_layer(args, cfg, torch, np, gu, synthetic)
+        return
     chain = args.steps + args.warmup
     if cfg.batch != 1 or chain > cfg.steps:
         print(f"workload {cfg.name}: batch {cfg.batch}, {cfg.steps}-step chain; need batch 1 and "
@@ -121,11 +229,12 @@ def main():
         info = dec.build_schedule(1, mode=mode, max_kv_len=max_len)
         ds.kv_lens.copy_(torch.from_numpy(st0.kv_lens))
         ds.tokens.copy_(torch.from_numpy(st0.tokens))
-        ms = time_chain(dec, ds, cfg, args.steps, args.warmup, torch)
-        result_modes[mode] = (ms, info)
+        per_step = []
+        ms = time_chain(dec, ds, cfg, args.steps, args.warmup, torch, per_step)
+        result_modes[mode] = (ms, info, per_step)
         print(f"# {mode}: {ms * 1000:.1f} us/step", file=sys.stderr, flush=True)
 
-    ms, info = result_modes[args.mode]
+    ms, info, per_step = result_modes[args.mode]
     lens_timed = [int(st0.kv_lens[0]) + args.warmup + s for s in range(args.steps)]
     bytes_avg = float(np.mean([algorithmic_bytes(cfg, [n]) for n in lens_timed]))
     achieved = bytes_avg / (ms * 1e-3) / 1e9
@@ -167,9 +276,17 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
                      "bytes_per_launch": int(bytes_avg)},
+        "step_us": {"p10": pct(per_step, 10), "p50": pct(per_step, 50), "p90": pct(per_step, 90)},
     }
+    if args.probe_bytes > 0:
+        # the achievable read rate of the interpreter's streaming shape, a
+        # second denominator beside the nominal peak
+        pg = read_probe_gbps(torch, args.probe_bytes // 4096 * 4096)
+        out["read_probe"] = {"gbps": round(pg, 1), "bytes": args.probe_bytes,
+                             "frac_of_probe": round(achieved / pg, 4),
+                             "shape": "1 workgroup x 8 waves per CU, 4 slices of 4 KiB in flight per wave"}
     if "unfused" in result_modes and args.mode != "unfused":
-        ums, uinfo = result_modes["unfused"]
+        ums, uinfo, _ = result_modes["unfused"]
         out["unfused"] = {"us_per_step": round(ums * 1000.0, 2), "launches_per_step": uinfo["launches_per_step"],
                           "hbm_gbps": round(bytes_avg / (ums * 1e-3) / 1e9, 1),
                           "speedup_of_megakernel": round(ums / ms, 3)}

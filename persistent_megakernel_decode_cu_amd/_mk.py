@@ -173,6 +173,10 @@ def mk_debug_copy_probe(src_ptr: int, dst_ptr: int, nbytes: int, stream: int = 0
     _check(lib().mk_debug_copy_probe(src_ptr, dst_ptr, nbytes, stream))
 
 
+def mk_debug_regstream_probe(src_ptr: int, nbytes: int, blocks: int, threads: int, depth: int, out_ptr: int) -> None:
+    _check(lib().mk_debug_regstream_probe(src_ptr, nbytes, blocks, threads, depth, out_ptr))
+
+
 def mk_debug_dma_probe(src_ptr: int, dst_ptr: int, n_kib: int, lds_offset_kib: int = 0) -> None:
     _check(lib().mk_debug_dma_probe(src_ptr, dst_ptr, n_kib, lds_offset_kib))
 
