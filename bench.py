@@ -16,7 +16,8 @@ percentiles of single steps within the chain; `read_probe` the read rate
 the interpreter's streaming shape reaches on a plain buffer, a second,
 achievable peak; `cpu_baseline` times the CPU oracle on consecutive steps of
 the same workload; `unfused` times the one-kernel-per-op baseline on the
-same chain.
+same chain, and `unfused_graph` that baseline with one step captured in a
+HIP graph and replayed per step.
 
 `--workload 1b-layer-kv512` times one 1B-shaped layer instead (hidden
 vector in and out): single steps, each after a write that evicts the
@@ -84,6 +85,33 @@ def time_chain(dec, ds, cfg, steps, warmup, torch, per_step=None):
     if per_step is not None:
         bounds = [t0] + marks + [t1]
         per_step.extend(bounds[k].elapsed_time(bounds[k + 1]) for k in range(steps))
+    return t0.elapsed_time(t1) / steps
+
+
+def time_graph_chain(dec, ds, cfg, steps, warmup, torch):
+    """The same greedy chain with one step captured in a HIP graph and the
+    graph replayed per step (the schedule must be the one-kernel-per-op
+    baseline: its launches have fixed arguments, and every step's inputs and
+    outputs are the same device buffers). Returns ms per timed step."""
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        dec.step(kv_lens=ds.kv_lens, k_pool=ds.k_pool, v_pool=ds.v_pool, page_table=ds.page_table,
+                 tokens_in=ds.tokens, tokens_out=ds.tokens, kv_lens_out=ds.kv_lens, stream=side.cuda_stream)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    dec.sync()
+    del graph
     return t0.elapsed_time(t1) / steps
 
 
@@ -188,6 +216,8 @@ def main():
                          "(the reference for the rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle sample: consecutive decode steps until this much time has passed")
+    ap.add_argument("--no-graph-baseline", action="store_true",
+                    help="skip the one-kernel-per-op chain replayed from a captured HIP graph")
     ap.add_argument("--probe-bytes", type=int, default=2 << 30,
                     help="bytes the register-slice read probe streams for the achievable-read-rate figure (0: skip)")
     ap.add_argument("--trace-layer", type=int, default=-1,
@@ -234,6 +264,13 @@ def main():
         result_modes[mode] = (ms, info, per_step)
         print(f"# {mode}: {ms * 1000:.1f} us/step", file=sys.stderr, flush=True)
 
+    graph_ms = None
+    if "unfused" in result_modes and not args.no_graph_baseline:
+        dec.build_schedule(1, mode="unfused", max_kv_len=max_len)
+        ds.kv_lens.copy_(torch.from_numpy(st0.kv_lens))
+        ds.tokens.copy_(torch.from_numpy(st0.tokens))
+        graph_ms = time_graph_chain(dec, ds, cfg, args.steps, args.warmup, torch)
+        print(f"# unfused, graph-captured: {graph_ms * 1000:.1f} us/step", file=sys.stderr, flush=True)
     ms, info, per_step = result_modes[args.mode]
     lens_timed = [int(st0.kv_lens[0]) + args.warmup + s for s in range(args.steps)]
     bytes_avg = float(np.mean([algorithmic_bytes(cfg, [n]) for n in lens_timed]))
@@ -290,6 +327,10 @@ def main():
         out["unfused"] = {"us_per_step": round(ums * 1000.0, 2), "launches_per_step": uinfo["launches_per_step"],
                           "hbm_gbps": round(bytes_avg / (ums * 1e-3) / 1e9, 1),
                           "speedup_of_megakernel": round(ums / ms, 3)}
+        if graph_ms is not None:
+            out["unfused_graph"] = {"us_per_step": round(graph_ms * 1000.0, 2),
+                                    "hbm_gbps": round(bytes_avg / (graph_ms * 1e-3) / 1e9, 1),
+                                    "speedup_of_megakernel": round(graph_ms / ms, 3)}
     if args.trace_layer >= 0:
         # a separate traced schedule, outside the timed region
         from persistent_megakernel_decode_cu_amd import _mk, trace_summary

@@ -10,6 +10,8 @@
   same sequence.
 - The per-instruction trace: every instruction of a traced step is stamped,
   and its stamps are ordered (start <= inputs staged <= end).
+- The baseline captured in a HIP graph: replays of one captured step form
+  the same greedy chain as eager steps.
 """
 import numpy as np
 import pytest
@@ -82,3 +84,55 @@ def test_trace_stamps_every_instruction_in_order():
         start, ready, end = (int(x) for x in tr[i.cu, i.pc, :3])
         assert 0 < start <= ready <= end, (i.cu, i.pc, i.op, start, ready, end)
     dec.close()
+
+
+def test_graph_captured_baseline_replays_match_eager():
+    """The one-kernel-per-op baseline, one step captured in a HIP graph on a
+    side stream and replayed as a greedy chain (tokens and lengths updated in
+    place on the device): every replay must give the token and length of the
+    eager chain's step, with eager device work and synchronisations between
+    the replays."""
+    n = 6
+    cfg = synthetic.workload("tiny-2l")
+    m = synthetic.make_model(cfg)
+    st = synthetic.make_state(cfg, extra_positions=n + 1)
+    wdev = gu.upload_model(m)
+
+    def fresh():
+        ds = gu.DevState(st)
+        dec = gu.make_decoder(m, st, wdev)
+        dec.build_schedule(1, mode="unfused", max_kv_len=int(st.kv_lens.max()) + n)
+        return ds, dec
+
+    def step(dec, ds, stream):
+        dec.step(kv_lens=ds.kv_lens, k_pool=ds.k_pool, v_pool=ds.v_pool, page_table=ds.page_table,
+                 tokens_in=ds.tokens, tokens_out=ds.tokens, kv_lens_out=ds.kv_lens, stream=stream)
+
+    ds, dec = fresh()
+    eager = []
+    for _ in range(n):
+        step(dec, ds, torch.cuda.current_stream().cuda_stream)
+        dec.sync()
+        eager.append((int(ds.tokens.cpu()[0]), int(ds.kv_lens.cpu()[0])))
+    dec.close()
+
+    ds, dec = fresh()
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        step(dec, ds, side.cuda_stream)
+    replayed = []
+    scratch = torch.zeros(1 << 20, device="cuda")
+    for k in range(n):
+        graph.replay()
+        torch.cuda.synchronize()
+        replayed.append((int(ds.tokens.cpu()[0]), int(ds.kv_lens.cpu()[0])))
+        scratch.add_(float(k))  # eager work between replays
+        torch.cuda.synchronize()
+    dec.sync()
+    del graph
+    dec.close()
+    print(f"eager {eager}; replayed {replayed}", flush=True)
+    assert replayed == eager
+    assert eager[-1][1] == int(st.kv_lens[0]) + n
