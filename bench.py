@@ -240,13 +240,11 @@ def main():
         bench_layer(args, cfg, torch, np, gu, synthetic)
         return
     chain = args.steps + args.warmup
-    if cfg.batch != 1 or chain > cfg.steps:
-        print(f"workload {cfg.name}: batch {cfg.batch}, {cfg.steps}-step chain; need batch 1 and "
-              f"warmup + steps <= {cfg.steps}", file=sys.stderr)
-        sys.exit(2)
+    B = cfg.batch
     t = time.time()
     model = synthetic.make_model(cfg)
-    st0 = synthetic.make_state(cfg)
+    # every request gets cache pages for the whole chain
+    st0 = synthetic.make_state(cfg, extra_positions=max(cfg.steps, chain + 1))
     print(f"# inputs generated in {time.time() - t:.1f} s", file=sys.stderr, flush=True)
     wdev = gu.upload_model(model)
     ds = gu.DevState(st0)
@@ -256,7 +254,7 @@ def main():
     result_modes = {}
     modes = [args.mode] + ([] if args.no_unfused or args.mode == "unfused" else ["unfused"])
     for mode in modes:
-        info = dec.build_schedule(1, mode=mode, max_kv_len=max_len)
+        info = dec.build_schedule(B, mode=mode, max_kv_len=max_len)
         ds.kv_lens.copy_(torch.from_numpy(st0.kv_lens))
         ds.tokens.copy_(torch.from_numpy(st0.tokens))
         per_step = []
@@ -266,14 +264,14 @@ def main():
 
     graph_ms = None
     if "unfused" in result_modes and not args.no_graph_baseline:
-        dec.build_schedule(1, mode="unfused", max_kv_len=max_len)
+        dec.build_schedule(B, mode="unfused", max_kv_len=max_len)
         ds.kv_lens.copy_(torch.from_numpy(st0.kv_lens))
         ds.tokens.copy_(torch.from_numpy(st0.tokens))
         graph_ms = time_graph_chain(dec, ds, cfg, args.steps, args.warmup, torch)
         print(f"# unfused, graph-captured: {graph_ms * 1000:.1f} us/step", file=sys.stderr, flush=True)
     ms, info, per_step = result_modes[args.mode]
-    lens_timed = [int(st0.kv_lens[0]) + args.warmup + s for s in range(args.steps)]
-    bytes_avg = float(np.mean([algorithmic_bytes(cfg, [n]) for n in lens_timed]))
+    bytes_avg = float(np.mean([algorithmic_bytes(cfg, [int(n) + args.warmup + s for n in st0.kv_lens])
+                               for s in range(args.steps)]))
     achieved = bytes_avg / (ms * 1e-3) / 1e9
     if args.copy_bytes > 0:
         from persistent_megakernel_decode_cu_amd import _mk
@@ -306,8 +304,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16 weights, fp32 compute",
         "data": "synthetic (seeded random-init weights and K/V cache)",
-        "config": {"workload": f"{cfg.name}: 16-layer Llama-3.2-1B shape (H 2048, 32q/8kv x 64, F 8192, "
-                               f"V 128256, tied), batch 1, K/V length {int(st0.kv_lens[0])}, greedy chain",
+        "config": {"workload": f"{cfg.name}: {cfg.n_layers}-layer Llama-3.2-1B shape (H {cfg.hidden}, "
+                               f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}, F {cfg.ffn}, V {cfg.vocab}, "
+                               f"tied), batch {B}, K/V length "
+                               + (f"{int(st0.kv_lens[0])}" if B == 1 else
+                                  f"{int(st0.kv_lens.min())}-{int(st0.kv_lens.max())} (paged)")
+                               + ", greedy chain",
                    "mode": args.mode, "n_cus": info["n_cus"], "launches_per_step": info["launches_per_step"]},
         "hbm_gbps": round(achieved, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -335,12 +337,12 @@ def main():
         # a separate traced schedule, outside the timed region
         from persistent_megakernel_decode_cu_amd import _mk, trace_summary
         from tests import sched_check
-        tinfo = dec.build_schedule(1, mode="megakernel", max_kv_len=max_len, trace=True)
+        tinfo = dec.build_schedule(B, mode="megakernel", max_kv_len=max_len, trace=True)
         ds.kv_lens.copy_(torch.from_numpy(st0.kv_lens))
         ds.tokens.copy_(torch.from_numpy(st0.tokens))
         for _ in range(3):
             gu.run_step(dec, ds, cfg, want_logits=False)
-        plan = _mk.Plan(dec.cfg, _mk.MkScheduleDesc(1, tinfo["n_cus"], 0, max_len, 0, 1, 0, 0, 0))
+        plan = _mk.Plan(dec.cfg, _mk.MkScheduleDesc(B, tinfo["n_cus"], 0, max_len, 0, 1, 0, 0, 0))
         names = {v: k[3:] for k, v in sched_check.ISA.items() if k.startswith("OP_") and k not in ("OP_END", "OP_COUNT")}
         text = trace_summary.timeline(dec.trace(), sched_check.decode(plan.queue), names, args.trace_layer)
         for line in text.splitlines():
