@@ -805,6 +805,16 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
         acc.bv[b] = -INFINITY;
         acc.bi[b] = 0x7fffffff;
     }
+    if constexpr (NB > 1) {
+        // batched kernels keep the LM head's running best of request b in the
+        // wave's LDS slot (lane b reads and writes it), not in registers the
+        // slice loop would have to spill
+        if (in.op == OP_LMHEAD && c.lane < P.B) {
+            MK_LDS float *am = (MK_LDS float *)(c.misc + M_AMAX);
+            am[(c.w * MAX_B + c.lane) * 2] = -INFINITY;
+            ((MK_LDS int32_t *)am)[(c.w * MAX_B + c.lane) * 2 + 1] = 0x7fffffff;
+        }
+    }
     acc.nan = false;
     attn_lane_init(at);
     if (NB == 1 && in.op != OP_ATTN && k.K == 2048) {
@@ -955,9 +965,19 @@ __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &
             if (lane == b) emit_row(P, c, in, row, b, v0, v1);
             if (in.op == OP_LMHEAD) {
                 if (v0 != v0) acc.nan = true;
-                if (v0 > acc.bv[b]) {  // a wave's rows rise, so ties keep the lowest index
-                    acc.bv[b] = v0;
-                    acc.bi[b] = row;
+                // a wave's rows rise, so ties keep the lowest index
+                if constexpr (NB == 1) {
+                    if (v0 > acc.bv[b]) {
+                        acc.bv[b] = v0;
+                        acc.bi[b] = row;
+                    }
+                } else if (lane == b) {
+                    MK_LDS float *am = (MK_LDS float *)(c.misc + M_AMAX);
+                    const int at = (c.w * MAX_B + b) * 2;
+                    if (v0 > am[at]) {
+                        am[at] = v0;
+                        ((MK_LDS int32_t *)am)[at + 1] = row;
+                    }
                 }
             }
         }
@@ -1068,13 +1088,13 @@ template <int NB, int G>
 __device__ __forceinline__ bool leave(const KParams &P, Ctx &c, const Ins &in, Acc<NB> &acc, AttnLaneT<G> &at) {
     const int lane = c.lane;
     if (in.op == OP_LMHEAD) {
-        MK_LDS float *am = (MK_LDS float *)(c.misc + M_AMAX);
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-            if (lane == b && b < P.B) {
-                am[(c.w * MAX_B + b) * 2] = acc.bv[b];
-                ((MK_LDS int32_t *)am)[(c.w * MAX_B + b) * 2 + 1] = acc.bi[b];
+        if constexpr (NB == 1) {  // batched kernels kept the running best there already
+            MK_LDS float *am = (MK_LDS float *)(c.misc + M_AMAX);
+            if (lane == 0 && P.B > 0) {
+                am[(c.w * MAX_B) * 2] = acc.bv[0];
+                ((MK_LDS int32_t *)am)[(c.w * MAX_B) * 2 + 1] = acc.bi[0];
             }
+        }
         if (acc.nan && lane == 0) raise_err(c, ERR_NAN, in.pc);
     } else if (in.op == OP_ATTN) {
         attn_lane_store(at, c.part + c.w * G * ATTN_WAVE_PART, lane);
