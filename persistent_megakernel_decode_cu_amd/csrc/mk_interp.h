@@ -498,8 +498,17 @@ struct Acc {
     float a0[NB], a1[NB];  // dot products of the current unit (gate/up for UPGATE)
     float bv[NB];          // LM head: best value and index so far
     int bi[NB];
+    float g;               // batched UPGATE: lane b holds request b's finished gate product
     bool nan;
 };
+
+// Batched kernels accumulate an UPGATE unit's gate and up products in one
+// register per request: when the gate half of the unit ends, its reduced
+// product is parked in lane b (Acc::g) and the register starts the up half.
+// The sums and their order are unchanged; the slice loop carries NB fewer
+// live values, which it would otherwise spill.
+template <int NB>
+constexpr bool ONE_ACC = NB > 1;
 
 __device__ __forceinline__ int token_of(const KParams &P, Ctx &c, int b, int pc) {
     int t = sload(P.tokens_in, b);
@@ -917,7 +926,7 @@ __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &
         const bool act16 = ACT16_DOWN<NB> && in.op == OP_DOWN;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            float a = m ? acc.a1[b] : acc.a0[b];
+            float a = ONE_ACC<NB> ? acc.a0[b] : (m ? acc.a1[b] : acc.a0[b]);
             if (act16) {
                 const MK_LDS uint16_t *ab = (const MK_LDS uint16_t *)c.act + b * 2 * P.act_stride + part * 2048 + lane * 8;
 #pragma unroll
@@ -932,8 +941,12 @@ __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &
                 for (int j = 0; j < 4; ++j)
                     a += dot8f(wf[j], *(const MK_LDS v4f *)(ab + j * 512), *(const MK_LDS v4f *)(ab + j * 512 + 256));
             }
-            acc.a0[b] = m ? acc.a0[b] : a;
-            acc.a1[b] = m ? a : acc.a1[b];
+            if constexpr (ONE_ACC<NB>) {
+                acc.a0[b] = a;
+            } else {
+                acc.a0[b] = m ? acc.a0[b] : a;
+                acc.a1[b] = m ? a : acc.a1[b];
+            }
         }
     } else {
         const int nchunk = k.K >> 3;
@@ -946,10 +959,21 @@ __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &
                 for (int b = 0; b < NB; ++b) {
                     const MK_LDS float *a = c.act + b * P.act_stride + base;
                     const float d = dot8(r[j], *(const MK_LDS v4f *)a, *(const MK_LDS v4f *)(a + 256));
-                    if (m == 0) acc.a0[b] += d;
+                    if (ONE_ACC<NB> || m == 0) acc.a0[b] += d;
                     else acc.a1[b] += d;
                 }
             }
+        }
+    }
+    if constexpr (ONE_ACC<NB>) {
+        if (in.op == OP_UPGATE && k.s == k.spm - 1) {  // the unit's gate half is complete
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const float gsum = wave_sum(acc.a0[b]);
+                if (lane == b) acc.g = gsum;
+                acc.a0[b] = 0.0f;
+            }
+            return;
         }
     }
     if (k.s != k.sp - 1) return;
@@ -957,8 +981,14 @@ __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &
     const int row = k.r0 + k.u;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        const float v0 = wave_sum(acc.a0[b]);
-        const float v1 = in.op == OP_UPGATE ? wave_sum(acc.a1[b]) : 0.0f;
+        float v0, v1;
+        if (ONE_ACC<NB> && in.op == OP_UPGATE) {
+            v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc.g), b));
+            v1 = wave_sum(acc.a0[b]);
+        } else {
+            v0 = wave_sum(acc.a0[b]);
+            v1 = in.op == OP_UPGATE ? wave_sum(acc.a1[b]) : 0.0f;
+        }
         acc.a0[b] = 0.0f;
         acc.a1[b] = 0.0f;
         if (b < P.B) {
