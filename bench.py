@@ -310,7 +310,8 @@ def main():
                                + (f"{int(st0.kv_lens[0])}" if B == 1 else
                                   f"{int(st0.kv_lens.min())}-{int(st0.kv_lens.max())} (paged)")
                                + ", greedy chain",
-                   "mode": args.mode, "n_cus": info["n_cus"], "launches_per_step": info["launches_per_step"]},
+                   "mode": args.mode, "n_cus": info["n_cus"], "launches_per_step": info["launches_per_step"],
+                   "lds_bytes_per_workgroup": info["lds_bytes"]},
         "hbm_gbps": round(achieved, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,

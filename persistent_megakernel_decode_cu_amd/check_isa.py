@@ -130,6 +130,19 @@ def slice_loop_waits(body):
     return sorted(hdrs), n, bad
 
 
+def _usage(txt):
+    """{kernel name: {metadata key: int}} from the code object metadata of an
+    assembly file (SGPR count, scratch bytes per lane, ...)."""
+    out = {}
+    for block in re.split(r"\n\s+- \.", txt):
+        m = re.search(r"\.name:\s+(\S+)", block)
+        if not m:
+            continue
+        vals = {k: int(v) for k, v in re.findall(r"\.(\w+):\s+(\d+)\s*$", block, re.M)}
+        out[m.group(1)] = vals
+    return out
+
+
 def main(paths):
     bad = 0
     for p in paths:
@@ -137,14 +150,19 @@ def main(paths):
         lines = txt.split("\n")
         counts = {m.group(1): int(m.group(2))
                   for m in re.finditer(r"\.name:\s+(\S+)[\s\S]*?\.vgpr_count:\s+(\d+)", txt)}
+        usage = _usage(txt)
         for name, body in _kernels(lines):
             pr, n_load, n_take, mx, top = check_kernel(body)
             _, _, loop_waits = slice_loop_waits(body)
             vg = counts.get(name)
             if n_load and (vg is None or vg <= top):
                 pr.append(f"kernel allocates {vg} VGPRs, not covering slot register v{top}")
+            u = usage.get(name, {})
+            n_spill = sum(1 for l in body if re.match(r"^\s+scratch_(load|store)", l))
             print(f"{p}: {name}: {n_load} slot loads, {n_take} slot copies, compiler VGPRs <= v{mx}, "
-                  f"{vg} allocated: {len(pr)} problems, {len(loop_waits)} slice-loop waits")
+                  f"{vg} allocated: {len(pr)} problems, {len(loop_waits)} slice-loop waits; "
+                  f"{u.get('sgpr_count', '?')} SGPRs, {u.get('private_segment_fixed_size', '?')} bytes of scratch "
+                  f"per lane, {n_spill} spill instructions")
             for x in pr[:10]:
                 print("   ", x)
             bad += len(pr)
