@@ -138,6 +138,49 @@ def read_probe_gbps(torch, nbytes: int) -> float:
     return best
 
 
+def gpu_env(device: int = 0) -> dict | None:
+    """Socket power, clocks, temperatures and throttle state of the GPU from
+    `amd-smi metric --json` (None where the tool is missing or fails)."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", str(device), "--json"], capture_output=True, text=True,
+                           timeout=60)
+        d = json.loads(r.stdout)
+    except Exception:
+        return None
+    g = d["gpu_data"][0] if isinstance(d, dict) and "gpu_data" in d else (d[0] if isinstance(d, list) else d)
+
+    def val(x):
+        return x.get("value") if isinstance(x, dict) else None
+
+    clk = g.get("clock", {})
+    gfx = [val(v.get("clk")) for k, v in clk.items() if k.startswith("gfx_") and isinstance(v, dict)]
+    gfx = [c for c in gfx if isinstance(c, (int, float))]
+    first_gfx = next((v for k, v in clk.items() if k.startswith("gfx_") and isinstance(v, dict)), {})
+    temp, power = g.get("temperature", {}), g.get("power", {})
+    return {"socket_power_w": val(power.get("socket_power")),
+            "gfx_clk_mhz_mean": round(sum(gfx) / len(gfx), 1) if gfx else None,
+            "gfx_clk_max_mhz": val(first_gfx.get("max_clk")),
+            "gfx_clk_locked": first_gfx.get("clk_locked"),
+            "mem_clk_mhz": val(clk.get("mem_0", {}).get("clk")) if isinstance(clk.get("mem_0"), dict) else None,
+            "hotspot_c": val(temp.get("hotspot")), "mem_c": val(temp.get("mem")),
+            "throttle_status": power.get("throttle_status")}
+
+
+def host_cpu() -> dict:
+    """CPU model of the host and the cores this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
 def pct(v, q):
     import numpy as np
     return round(float(np.percentile(np.asarray(v), q)) * 1000.0, 2)
@@ -233,7 +276,7 @@ def main():
     import torch
 
     import synthetic
-    from tests import gpu_util as gu
+    from persistent_megakernel_decode_cu_amd import devio as gu
 
     cfg = synthetic.workload(args.workload)
     if cfg.batch == 1 and not cfg.has_embed:
@@ -252,13 +295,18 @@ def main():
     dec = gu.make_decoder(model, st0, wdev)
 
     result_modes = {}
+    env = {}
     modes = [args.mode] + ([] if args.no_unfused or args.mode == "unfused" else ["unfused"])
     for mode in modes:
         info = dec.build_schedule(B, mode=mode, max_kv_len=max_len)
         ds.kv_lens.copy_(torch.from_numpy(st0.kv_lens))
         ds.tokens.copy_(torch.from_numpy(st0.tokens))
         per_step = []
+        if mode == args.mode:
+            env["before"] = gpu_env()
         ms = time_chain(dec, ds, cfg, args.steps, args.warmup, torch, per_step)
+        if mode == args.mode:
+            env["after"] = gpu_env()
         result_modes[mode] = (ms, info, per_step)
         print(f"# {mode}: {ms * 1000:.1f} us/step", file=sys.stderr, flush=True)
 
@@ -337,38 +385,54 @@ def main():
     if args.trace_layer >= 0:
         # a separate traced schedule, outside the timed region
         from persistent_megakernel_decode_cu_amd import _mk, trace_summary
-        from tests import sched_check
         tinfo = dec.build_schedule(B, mode="megakernel", max_kv_len=max_len, trace=True)
         ds.kv_lens.copy_(torch.from_numpy(st0.kv_lens))
         ds.tokens.copy_(torch.from_numpy(st0.tokens))
         for _ in range(3):
             gu.run_step(dec, ds, cfg, want_logits=False)
         plan = _mk.Plan(dec.cfg, _mk.MkScheduleDesc(B, tinfo["n_cus"], 0, max_len, 0, 1, 0, 0, 0))
-        names = {v: k[3:] for k, v in sched_check.ISA.items() if k.startswith("OP_") and k not in ("OP_END", "OP_COUNT")}
-        text = trace_summary.timeline(dec.trace(), sched_check.decode(plan.queue), names, args.trace_layer)
+        text = trace_summary.timeline(dec.trace(), trace_summary.decode_queue(plan.queue), args.trace_layer)
         for line in text.splitlines():
             print(f"# {line}", file=sys.stderr, flush=True)
-    if not args.no_cpu_baseline:
-        # the oracle as it stands (single-threaded fp64 C), on consecutive greedy
-        # steps of the same workload until the sample time has passed
-        from oracle import Oracle
-        ora = Oracle("f64")
-        ost = st0.copy()
-        n, t = 0, time.time()
-        while True:
-            r = ora.decode_step(model, ost)
-            assert r["rc"] == 0
-            ost.tokens[:] = r["tokens"]
-            ost.kv_lens += 1
-            n += 1
-            dt = time.time() - t
-            if dt >= args.cpu_seconds or n >= 64:
-                break
-        out["cpu_baseline"] = {"value": round(dt / n * 1e6, 1), "unit": "us/step", "cores": 1, "kind": "oracle",
-                               "sample": f"{n} consecutive greedy decode steps of {cfg.name} from K/V length "
-                                         f"{int(st0.kv_lens[0])} (same weights and cache), single-threaded fp64 C "
-                                         f"oracle, {dt:.1f} s"}
+    out["gpu_env"] = env
+    out["host_cpu"] = host_cpu()
+    # release the device objects in order while the runtime is intact: the
+    # decoder's handle (its schedule buffers and pinned error word), then the
+    # tensors it borrowed, then torch's cached blocks
     dec.close()
+    del dec, ds, wdev
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        # the oracle as it stands (single-threaded fp32 C) on one pinned core,
+        # on consecutive greedy steps of the same workload until the sample
+        # time has passed
+        from oracle import Oracle
+        ora = Oracle("f32")
+        ost = st0.copy()
+        saved = os.sched_getaffinity(0)
+        core = min(saved)
+        os.sched_setaffinity(0, {core})
+        try:
+            n, t = 0, time.time()
+            while True:
+                r = ora.decode_step(model, ost)
+                assert r["rc"] == 0
+                ost.tokens[:] = r["tokens"]
+                ost.kv_lens += 1
+                n += 1
+                dt = time.time() - t
+                if dt >= args.cpu_seconds or n >= 64:
+                    break
+        finally:
+            os.sched_setaffinity(0, saved)
+        hc = out["host_cpu"]
+        out["cpu_baseline"] = {"value": round(dt / n * 1e6, 1), "unit": "us/step", "cores": 1, "kind": "oracle",
+                               "cpu": hc["model"], "host_cpus": hc["cpu_count"], "pinned_core": core,
+                               "sample": f"{n} consecutive greedy decode steps of {cfg.name} from K/V length "
+                                         f"{int(st0.kv_lens[0])} (same weights and cache), single-threaded fp32 C "
+                                         f"oracle pinned to core {core} of {hc['cpu_count']} ({hc['model']}), "
+                                         f"{dt:.1f} s"}
     print(json.dumps(out), flush=True)
 
 

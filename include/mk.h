@@ -115,8 +115,10 @@ typedef struct mk_schedule_desc {
 
 /* Buffers of one step. All device pointers; the caller owns them. The new
  * K/V entry of request b is written at position kv_lens[b]. tokens_out may
- * alias tokens_in and kv_lens_out may alias kv_lens (the step writes them
- * after its last read). */
+ * alias tokens_in (every read of the tokens feeds the layer-0 activations,
+ * which the LM head depends on) and kv_lens_out may alias kv_lens (the
+ * resident grid writes them only after every workgroup has counted itself
+ * started, which it does once it holds its copy of the lengths). */
 typedef struct mk_step_io {
     const int32_t *tokens_in;   /* [B] (has_embed == 1) */
     const float *hidden_in;     /* [B, H] fp32 (has_embed == 0) */
@@ -160,12 +162,21 @@ int mk_build_schedule(mk_handle *h, const mk_schedule_desc *s);
  * needs mk_build_schedule before the next step. */
 int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream);
 
-/* Frees everything the handle owns; never touches borrowed buffers. NULL is
- * a no-op. */
+/* Ends the lifetimes the object table of the "principle, schedule and
+ * dataflow" section gives to what a binding owns: the queue and counters
+ * (the resident kernel's and the dependency intervals' objects) and the
+ * per-instance scratch. Waits for the handle's device work, then frees
+ * everything the handle allocated; never touches borrowed buffers (weights,
+ * K/V pools, step io). NULL is a no-op. No error is reported. */
 void mk_destroy(mk_handle *h);
 
-/* Thread-local text of the last error, valid until the next call on the
- * same thread. Never NULL. */
+/* The text behind the last non-MK_OK status on the calling thread: the
+ * capacity and resource obligations of the "unified framework" section are
+ * checked before any launch and reported here with the quantity that failed,
+ * and a device wait that hit its watchdog or a device-side range/NaN check
+ * (the progress and visibility obligations) is reported with the failing
+ * compute unit and instruction. Thread-local; valid until the next call on
+ * the same thread; never NULL ("no error" before any failure). */
 const char *mk_last_error(void);
 
 /* Waits for the handle's device work on `stream` and returns the sticky
@@ -195,37 +206,14 @@ int mk_read_trace(mk_handle *h, int64_t *out, size_t cap, size_t *n);
 
 /* ---- debugging aids ---- */
 
-/* Copies the handle's scratch buffer `which` (0: residual stream x [B, H],
- * 1: qkv [B, (nq + 2 nkv) d], 2: attention output o [B, nq d], 3: gated MLP
- * activation [B, F]) into the host buffer `out` of `bytes` bytes, after
- * synchronising the device. Errors: MK_EINVAL, MK_ENOSCHED, MK_EHIP. */
+/* Copies the last layer's activation `which` of the previous step (0:
+ * residual stream x after the last layer [B, H], 1: qkv [B, (nq + 2 nkv) d],
+ * 2: attention output o [B, nq d], 3: gated MLP activation [B, F]) as fp32
+ * into the host buffer `out` of `bytes` bytes, after synchronising the
+ * device. In MK_MODE_UNFUSED these are the baseline's scratch buffers; in
+ * MK_MODE_MEGAKERNEL the value halves of the last layer's tagged exchange
+ * words. Errors: MK_EINVAL, MK_ENOSCHED, MK_EHIP. */
 int mk_debug_copy_scratch(mk_handle *h, int which, void *out, size_t bytes);
-
-/* Runs the weight loader's HBM -> LDS transfer on one wave: copies `n_kib`
- * KiB from device `src` into LDS at byte offset 1024 * lds_offset_kib with
- * the 16-byte-per-lane DMA the resident loop uses (workgroup LDS of 160
- * KiB), then writes those LDS bytes back to device `dst`. Synchronous.
- * Errors: MK_EINVAL (n_kib + lds_offset_kib > 160), MK_EHIP. */
-int mk_debug_dma_probe(const void *src, void *dst, int n_kib, int lds_offset_kib);
-
-/* Streams `n_granules` KiB per workgroup (`blocks` workgroups, 1..256,
- * workgroup b reading from src + b * n_granules KiB; the request must fit in
- * the `src_bytes` of the source buffer, else MK_EINVAL) through an LDS ring of
- * `ring_granules` (2..150) KiB with the resident loop's loader protocol
- * (`depth` transfers in flight: 0, 8, 40 or 56) while the compute waves check
- * every word they read against `src`; `variant` 2 or 3 makes another wave
- * issue agent-scope acquire or release fences meanwhile, `variant` 4 consumes
- * without checking (for timing). Adds the number of mismatching words to
- * errs_dev[0], granules checked to errs_dev[1] and timed-out waits to
- * errs_dev[2] (device int32[4]). Asynchronous on the null stream. Errors:
- * MK_EINVAL, MK_EHIP. */
-int mk_debug_ring_probe(const void *src, size_t src_bytes, int n_granules, int ring_granules, int depth,
-                        int variant, int32_t *errs_dev, int blocks, void *stream);
-
-/* Plain HBM streaming read of `bytes` from device `src` by `blocks`
- * workgroups of 256 threads (16-byte loads), for the achievable read
- * bandwidth. Asynchronous on the null stream. Errors: MK_EINVAL, MK_EHIP. */
-int mk_debug_stream_probe(const void *src, size_t bytes, int blocks, void *out_dev);
 
 /* Plain device copy of `bytes` (a multiple of 16) from src_dev to dst_dev on
  * `stream` (a hipStream_t, NULL: the null stream), each byte read and written

@@ -80,9 +80,6 @@ _SIGS = {
     "mk_get_schedule_info": (i32, [vp, ctypes.POINTER(MkScheduleInfo)]),
     "mk_read_trace": (i32, [vp, ctypes.POINTER(ctypes.c_int64), ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]),
     "mk_debug_copy_scratch": (i32, [vp, i32, vp, ctypes.c_size_t]),
-    "mk_debug_dma_probe": (i32, [vp, vp, i32, i32]),
-    "mk_debug_ring_probe": (i32, [vp, ctypes.c_size_t, i32, i32, i32, i32, vp, i32, vp]),
-    "mk_debug_stream_probe": (i32, [vp, ctypes.c_size_t, i32, vp]),
     "mk_debug_copy_probe": (i32, [vp, vp, ctypes.c_size_t, vp]),
     "mk_debug_litmus": (i32, [i32, i32, i32, i32, vp, vp, vp]),
     "mk_debug_hop_probe": (i32, [vp, ctypes.c_size_t, vp, ctypes.c_size_t, i32, i32, i32, vp]),
@@ -175,10 +172,6 @@ def mk_debug_copy_probe(src_ptr: int, dst_ptr: int, nbytes: int, stream: int = 0
 
 def mk_debug_regstream_probe(src_ptr: int, nbytes: int, blocks: int, threads: int, depth: int, out_ptr: int) -> None:
     _check(lib().mk_debug_regstream_probe(src_ptr, nbytes, blocks, threads, depth, out_ptr))
-
-
-def mk_debug_dma_probe(src_ptr: int, dst_ptr: int, n_kib: int, lds_offset_kib: int = 0) -> None:
-    _check(lib().mk_debug_dma_probe(src_ptr, dst_ptr, n_kib, lds_offset_kib))
 
 
 class Plan:

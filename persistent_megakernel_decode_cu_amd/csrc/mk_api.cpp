@@ -253,16 +253,19 @@ int mk_build_schedule(mk_handle *h, const mk_schedule_desc *s) {
         int rc = MK_OK;
         if (!rc) rc = dalloc(h->queue, std::max<size_t>(plan.queue.size(), 32));
         if (!rc) rc = dalloc(h->events, std::max<size_t>(plan.events.size(), 16));
-        if (!rc) rc = dalloc(h->counters, (size_t)std::max(plan.n_counters, 1) * mk::CTR_STRIDE);
-        if (!rc) rc = dalloc(h->x, (size_t)B * c.hidden);
-        if (!rc) rc = dalloc(h->qkv, (size_t)B * QKV);
-        if (!rc) rc = dalloc(h->o, (size_t)B * QD);
-        if (!rc) rc = dalloc(h->act, (size_t)B * c.ffn);
-        if (!rc) rc = dalloc(h->attn_part, (size_t)B * c.n_kv_heads * plan.attn_chunks * G * mk::ATTN_PART_STRIDE);
-        if (!rc) rc = dalloc(h->lm_part, lm_slots * B * 2);
-        if (!rc) rc = dalloc(h->u, (size_t)B * kmax);
-        if (!rc) rc = dalloc(h->qrot, (size_t)B * QD);
-        if (d.mode == MK_MODE_MEGAKERNEL) {  // tagged activations, each written once per step
+        // the merge events' counters, then the start counter
+        if (!rc) rc = dalloc(h->counters, (size_t)(plan.n_counters + 1) * mk::CTR_STRIDE);
+        if (d.mode == MK_MODE_UNFUSED) {  // the baseline's scratch, overwritten in place by its kernels
+            if (!rc) rc = dalloc(h->x, (size_t)B * c.hidden);
+            if (!rc) rc = dalloc(h->qkv, (size_t)B * QKV);
+            if (!rc) rc = dalloc(h->o, (size_t)B * QD);
+            if (!rc) rc = dalloc(h->act, (size_t)B * c.ffn);
+            if (!rc)
+                rc = dalloc(h->attn_part, (size_t)B * c.n_kv_heads * plan.attn_chunks * G * mk::ATTN_PART_STRIDE);
+            if (!rc) rc = dalloc(h->lm_part, lm_slots * B * 2);
+            if (!rc) rc = dalloc(h->u, (size_t)B * kmax);
+            if (!rc) rc = dalloc(h->qrot, (size_t)B * QD);
+        } else {  // tagged activations, each written once per step
             const size_t L = (size_t)c.n_layers;
             if (!rc) rc = dalloc(h->tx, 2 * L * B * c.hidden);
             if (!rc) rc = dalloc(h->tqkv, L * B * QKV);
@@ -281,7 +284,7 @@ int mk_build_schedule(mk_handle *h, const mk_schedule_desc *s) {
             MK_HIP(hipMemcpy(h->queue, h->plan.queue.data(), h->plan.queue.size() * 4, hipMemcpyHostToDevice));
         if (!plan.events.empty())
             MK_HIP(hipMemcpy(h->events, plan.events.data(), plan.events.size() * 4, hipMemcpyHostToDevice));
-        h->max_need = 1;
+        h->max_need = std::max(1, plan.n_cus);  // the start counter counts every workgroup
         for (int e = 0; e < plan.n_events; ++e)
             h->max_need = std::max(h->max_need, plan.events[(size_t)e * mk::EV_WORDS + mk::EV_NEED]);
         MK_HIP(hipMemset(h->err, 0, 4));
@@ -318,22 +321,22 @@ int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream) {
         const mk::Plan &P = h->plan;
         // epoch-based counters: re-zero before the int32 counts could wrap
         if ((h->epoch + 1) * (int64_t)h->max_need >= ((int64_t)1 << 30)) {
-            MK_HIP(mk::fill_u32((uint32_t *)h->counters, (size_t)std::max(P.n_counters, 1) * mk::CTR_STRIDE, 0u, st));
+            MK_HIP(mk::fill_u32((uint32_t *)h->counters, (size_t)(P.n_counters + 1) * mk::CTR_STRIDE, 0u, st));
             h->epoch = 0;
         }
         h->epoch++;
         if (++h->tag == 0) h->tag = 1;  // the buffers start at tag 0, which no step uses
         mk::KParams k{};
+        k.epoch = (int32_t)h->epoch;
+        k.tag = h->tag;
         k.queue = h->queue;
         k.events = h->events;
         k.counters = h->counters;
+        k.start_ctr = P.n_counters;
         k.Q = P.Q;
-        k.epoch = (int32_t)h->epoch;
         k.n_cus = P.n_cus;
-        k.tag = h->tag;
         k.queue_off = P.queue_off;
         k.xrow_off = P.xrow_off;
-        k.part_off = P.part_off;
         k.act_off = P.act_off;
         k.nw_off = P.nw_off;
         k.act_stride = P.act_stride;
@@ -445,49 +448,30 @@ int mk_debug_copy_scratch(mk_handle *h, int which, void *out, size_t bytes) {
     if (!h || !out) return set_error(MK_EINVAL, "null argument");
     if (!h->built) return set_error(MK_ENOSCHED, "no schedule");
     const mk_config &c = h->cfg;
-    const size_t B = (size_t)h->plan.desc.batch;
-    const float *src = nullptr;
+    const size_t B = (size_t)h->plan.desc.batch, L = (size_t)c.n_layers;
+    const size_t QKV = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim, QD = (size_t)c.n_q_heads * c.head_dim;
+    const bool mega = h->plan.desc.mode == MK_MODE_MEGAKERNEL;
     size_t n = 0;
+    const void *src = nullptr;
     switch (which) {
-        case 0: src = h->x; n = B * c.hidden; break;
-        case 1: src = h->qkv; n = B * (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim; break;
-        case 2: src = h->o; n = B * c.n_q_heads * c.head_dim; break;
-        case 3: src = h->act; n = B * c.ffn; break;
+        case 0: n = B * c.hidden; src = mega ? (const void *)(h->tx + (2 * L - 1) * n) : h->x; break;
+        case 1: n = B * QKV; src = mega ? (const void *)(h->tqkv + (L - 1) * n) : h->qkv; break;
+        case 2: n = B * QD; src = mega ? (const void *)(h->to + (L - 1) * n) : h->o; break;
+        case 3: n = B * c.ffn; src = mega ? (const void *)(h->tact + (L - 1) * n) : h->act; break;
         default: return set_error(MK_EINVAL, "unknown scratch buffer");
     }
     if (bytes < n * 4) return set_error(MK_EINVAL, "buffer too small");
     MK_HIP(hipSetDevice(c.device));
     MK_HIP(hipDeviceSynchronize());
-    MK_HIP(hipMemcpy(out, src, n * 4, hipMemcpyDeviceToHost));
-    return MK_OK;
-}
-
-int mk_debug_dma_probe(const void *src, void *dst, int n_kib, int lds_offset_kib) {
-    if (n_kib == -1 && src && dst && lds_offset_kib >= 0 && lds_offset_kib + 2 <= mk::LDS_LIMIT / 1024) {
-        MK_HIP(mk::dma_probe(src, dst, -1, lds_offset_kib));
+    if (!mega) {
+        MK_HIP(hipMemcpy(out, src, n * 4, hipMemcpyDeviceToHost));
         return MK_OK;
     }
-    if (!src || !dst || n_kib < 1 || lds_offset_kib < 0 || n_kib + lds_offset_kib > mk::LDS_LIMIT / 1024)
-        return set_error(MK_EINVAL, "bad probe arguments");
-    MK_HIP(mk::dma_probe(src, dst, n_kib, lds_offset_kib));
-    return MK_OK;
-}
-
-int mk_debug_ring_probe(const void *src, size_t src_bytes, int n_granules, int ring_granules, int depth,
-                        int variant, int32_t *errs_dev, int blocks, void *stream) {
-    if (!src || !errs_dev || n_granules < 1 || ring_granules < 2 || ring_granules > 150 || depth < 0 || blocks < 1 ||
-        blocks > 256)
-        return set_error(MK_EINVAL, "bad probe arguments");
-    if ((size_t)blocks * (size_t)n_granules * 1024 > src_bytes)
-        return set_error(MK_EINVAL, "blocks * n_granules KiB exceeds the source buffer");
-    (void)stream;
-    MK_HIP(mk::ring_probe(src, n_granules, ring_granules, depth, variant, errs_dev, blocks));
-    return MK_OK;
-}
-
-int mk_debug_stream_probe(const void *src, size_t bytes, int blocks, void *out_dev) {
-    if (!src || !out_dev || blocks < 1 || bytes < 16) return set_error(MK_EINVAL, "bad probe arguments");
-    MK_HIP(mk::stream_probe(src, bytes, blocks, (uint32_t *)out_dev));
+    // tagged words: fp32 bits in the low half, the step tag in the high half
+    std::vector<uint64_t> words(n);
+    MK_HIP(hipMemcpy(words.data(), src, n * 8, hipMemcpyDeviceToHost));
+    uint32_t *o32 = (uint32_t *)out;
+    for (size_t i = 0; i < n; ++i) o32[i] = (uint32_t)words[i];
     return MK_OK;
 }
 

@@ -161,31 +161,11 @@ __device__ __forceinline__ float rope_rotate(float xi, float xp, float2 cs, bool
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// Online-softmax state of one lane for the G query heads of one kv group. A
-// 16-position K/V block (page) is spread over the wave as 16-byte chunks:
-// lane l holds dims 8 (l % 8) .. 8 (l % 8) + 7 of positions l / 8 (t0) and
-// 8 + l / 8 (t1), for K and for V. A score is summed over the 8 lanes that
-// share a position (DPP within the lane group), and each lane group keeps its
-// own running max m, sum l and output share o[h] (dims 8 (l % 8) .. +7) over
-// its positions, so a block needs no exchange between lane groups; the eight
-// group states are merged once, when the wave's state is stored.
-// (o has room for at least four heads: the interpreter keeps a matvec's
-// register activations there while no attention state is live)
-template <int G>
-struct AttnLaneT {
-    float m[G], l[G], o[G < 4 ? 4 : G][8];
+// A matvec's activations held in registers at batch 1 with K = 2048: lane
+// l's 32 inputs, chunk 64 j + l, elements 8 (64 j + l) + e.
+struct RegAct {
+    float o[4][8];
 };
-
-template <int G>
-__device__ __forceinline__ void attn_lane_init(AttnLaneT<G> &s) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        s.m[h] = -1e30f;
-        s.l[h] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s.o[h][e] = 0.0f;
-    }
-}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
@@ -201,98 +181,103 @@ __device__ __forceinline__ float sum8lanes(float v) {
     return v;
 }
 
-// One block: k0/v0 are this lane's K/V chunks of position t0, k1/v1 of t1;
-// ok0/ok1 say whether those positions exist (<= the new position). q: the
-// group's rotated queries, [G][64] fp32 in LDS.
+// Maximum over the 64 lanes of a wave, returned to every lane: the row
+// shifts and row broadcasts of wave_sum, with -inf where a lane has no
+// source (max is exact, so the combination order does not matter).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max_src(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_max_src<0x111, 0xf>(v));
+    v = fmaxf(v, dpp_max_src<0x112, 0xf>(v));
+    v = fmaxf(v, dpp_max_src<0x114, 0xf>(v));
+    v = fmaxf(v, dpp_max_src<0x118, 0xf>(v));
+    v = fmaxf(v, dpp_max_src<0x142, 0xa>(v));
+    v = fmaxf(v, dpp_max_src<0x143, 0xc>(v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Attention over one tile's K/V blocks (16 positions of one kv head each),
+// in rounds of up to N_COMPUTE_WAVES blocks, one block per wave:
+//  1. each wave holding a block writes, for the G query heads of the group,
+//     the 16 scaled scores q_h . K_t / sqrt(64) into S[h][16 w + t] (-inf at
+//     positions past the new one) and the block's values into V[16 w + t][64]
+//     (bf16, zero past the new position: a missing position may hold any bit
+//     pattern);
+//  2. after a barrier, wave h < G folds the round into its running state of
+//     head h, lane = dim: M = max(M, max_t S), every state scaled by
+//     exp(M_old - M), L += sum_t exp(S - M), O += sum_t exp(S - M) V[t]
+//     (positions in ascending order).
+// The tile's (O, M, L) is the chunk's softmax state (O unnormalised). The
+// lane layout of a block follows the K/V page: lane l holds the 16-byte chunk
+// l of K and of V, i.e. dims 8 (l % 8) .. + 7 of positions l / 8 (t0) and
+// 8 + l / 8 (t1); a score is summed over the 8 lanes sharing a position.
+// (ATTN_ROUND_POS and the area's size attn_round_floats are in mk_isa.h)
+
+struct AttnRun {
+    float O, M, L;  // head wave: running state of its head (lane = dim)
+    int rounds;     // rounds of the current tile this wave has gone through
+};
+
+__device__ __forceinline__ void attn_run_init(AttnRun &r) {
+    r.O = 0.0f;
+    r.M = -1e30f;
+    r.L = 0.0f;
+    r.rounds = 0;
+}
+
+// Step 1 for the block of wave slot `ws` of a round; q: the group's rotated
+// queries [G][64] fp32; area: the round's LDS area.
 template <int G>
-__device__ __forceinline__ void attn_lane_block(AttnLaneT<G> &st, const MK_LDS float *q, int lane, v4u k0, v4u k1,
-                                                v4u v0, v4u v1, bool ok0, bool ok1) {
-    const int dd = (lane & 7) * 8;
-    if (!ok0) v0 = v4u{0u, 0u, 0u, 0u};  // a missing position may hold any bit pattern
-    if (!ok1) v1 = v4u{0u, 0u, 0u, 0u};
-    const float va[8] = {bf_lo(v0.x), bf_hi(v0.x), bf_lo(v0.y), bf_hi(v0.y),
-                         bf_lo(v0.z), bf_hi(v0.z), bf_lo(v0.w), bf_hi(v0.w)};
-    const float vb[8] = {bf_lo(v1.x), bf_hi(v1.x), bf_lo(v1.y), bf_hi(v1.y),
-                         bf_lo(v1.z), bf_hi(v1.z), bf_lo(v1.w), bf_hi(v1.w)};
+__device__ __forceinline__ void attn_block_write(const MK_LDS float *q, MK_LDS float *area, int ws, int lane, v4u k0,
+                                                 v4u k1, v4u v0, v4u v1, bool ok0, bool ok1) {
+    const int dd = (lane & 7) * 8, t0 = lane >> 3;
+    MK_LDS float *S = area;
+    MK_LDS uint16_t *V = (MK_LDS uint16_t *)(area + G * ATTN_ROUND_POS);
+    const int j0 = ws * 16 + t0;
+    *(MK_LDS v4u *)(V + j0 * 64 + dd) = ok0 ? v0 : v4u{0u, 0u, 0u, 0u};
+    *(MK_LDS v4u *)(V + (j0 + 8) * 64 + dd) = ok1 ? v1 : v4u{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         const v4f qa = *(const MK_LDS v4f *)(q + h * 64 + dd);
         const v4f qb = *(const MK_LDS v4f *)(q + h * 64 + dd + 4);
-        float s0 = sum8lanes(dot8(k0, qa, qb)) * 0.125f;  // 1 / sqrt(64)
-        float s1 = sum8lanes(dot8(k1, qa, qb)) * 0.125f;
-        if (!ok0) s0 = -INFINITY;
-        if (!ok1) s1 = -INFINITY;
-        const float mnew = fmaxf(st.m[h], fmaxf(s0, s1));
-        const float alpha = __expf(st.m[h] - mnew);
-        const float p0 = ok0 ? __expf(s0 - mnew) : 0.0f;
-        const float p1 = ok1 ? __expf(s1 - mnew) : 0.0f;
-        st.l[h] = st.l[h] * alpha + (p0 + p1);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st.o[h][e] = fmaf(p1, vb[e], fmaf(p0, va[e], st.o[h][e] * alpha));
-        st.m[h] = mnew;
+        const float s0 = sum8lanes(dot8(k0, qa, qb)) * 0.125f;  // 1 / sqrt(64)
+        const float s1 = sum8lanes(dot8(k1, qa, qb)) * 0.125f;
+        if ((lane & 7) == (h & 7)) {
+            S[h * ATTN_ROUND_POS + j0] = ok0 ? s0 : -INFINITY;
+            S[h * ATTN_ROUND_POS + j0 + 8] = ok1 ? s1 : -INFINITY;
+        }
     }
 }
 
-// Exchanges with lane ^ 8, lane ^ 16 and lane ^ 32, all in the VALU: a DPP
-// rotate by 8 within each 16-lane row, and the gfx950 row swaps
-// (v_permlane16_swap / v_permlane32_swap), which hand each lane its partner
-// in one of their two outputs. Which output that is gets settled once per
-// wave by swapping the lane indices themselves.
-struct XorPick {
-    bool x16, x32;  // the partner of the 16- / 32-lane swap is in output 0
-};
-__device__ __forceinline__ XorPick xor_pick_init(int lane) {
-    const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)lane, (uint32_t)lane, false, false);
-    const auto b = __builtin_amdgcn_permlane32_swap((uint32_t)lane, (uint32_t)lane, false, false);
-    return XorPick{a[0] == (uint32_t)(lane ^ 16), b[0] == (uint32_t)(lane ^ 32)};
-}
-__device__ __forceinline__ float xor8(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));  // row_ror:8
-}
-__device__ __forceinline__ float xor16(float v, XorPick x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(x.x16 ? r[0] : r[1]);
-}
-__device__ __forceinline__ float xor32(float v, XorPick x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(x.x32 ? r[0] : r[1]);
-}
-
-// Merges the eight lane groups' states (a butterfly over lane ^ 8, ^ 16,
-// ^ 32: every lane ends with the same sums) and writes the wave's state as
-// partials [G][ATTN_WAVE_PART] (o[64], m, l).
-template <int G>
-__device__ __forceinline__ void attn_lane_store(AttnLaneT<G> &st, MK_LDS float *part, int lane) {
-    const XorPick xp = xor_pick_init(lane);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        float M = st.m[h];
-        M = fmaxf(M, xor8(M));
-        M = fmaxf(M, xor16(M, xp));
-        M = fmaxf(M, xor32(M, xp));
-        const float f = __expf(st.m[h] - M);
-        float l = st.l[h] * f;
-        l += xor8(l);
-        l += xor16(l, xp);
-        l += xor32(l, xp);
-        float o[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            o[e] = st.o[h][e] * f;
-            o[e] += xor8(o[e]);
-            o[e] += xor16(o[e], xp);
-            o[e] += xor32(o[e], xp);
-        }
-        if (lane < 8) {
-            MK_LDS float *ph = part + h * ATTN_WAVE_PART + lane * 8;
-            *(MK_LDS v4f *)ph = v4f{o[0], o[1], o[2], o[3]};
-            *(MK_LDS v4f *)(ph + 4) = v4f{o[4], o[5], o[6], o[7]};
-        }
-        if (lane == 0) {
-            part[h * ATTN_WAVE_PART + 64] = M;
-            part[h * ATTN_WAVE_PART + 65] = l;
-        }
+// Step 2 for head h over the round's first npos positions (a multiple of
+// 16): each lane turns its positions' scores into weights exp(S - M) in
+// place, and the weights are then read back by every lane.
+__device__ __forceinline__ void attn_round_fold(MK_LDS float *S_h, const MK_LDS uint16_t *V, int npos, int lane,
+                                                AttnRun &r) {
+    float mx = -INFINITY;
+    for (int j = lane; j < npos; j += 64) mx = fmaxf(mx, S_h[j]);
+    const float Mn = fmaxf(r.M, wave_max(mx));
+    const float scale = __expf(r.M - Mn);
+    float ls = 0.0f;
+    for (int j = lane; j < npos; j += 64) {
+        const float e = __expf(S_h[j] - Mn);
+        S_h[j] = e;
+        ls += e;
     }
+    float o = r.O * scale;
+    for (int j = 0; j < npos; j += 4) {
+        const v4f p4 = *(const MK_LDS v4f *)(S_h + j);
+        o = fmaf(p4.x, bf2f(V[(j + 0) * 64 + lane]), o);
+        o = fmaf(p4.y, bf2f(V[(j + 1) * 64 + lane]), o);
+        o = fmaf(p4.z, bf2f(V[(j + 2) * 64 + lane]), o);
+        o = fmaf(p4.w, bf2f(V[(j + 3) * 64 + lane]), o);
+    }
+    r.L = fmaf(r.L, scale, wave_sum(ls));
+    r.O = o;
+    r.M = Mn;
 }
 
 // Softmax-state merge, one source at a time in a fixed order: (O, M, L)
@@ -309,24 +294,6 @@ __device__ __forceinline__ void merge_init(float &O, float &M, float &L) {
     O = 0.0f;
     M = -1e30f;
     L = 0.0f;
-}
-
-// Merges the NW wave states of head h (LDS, [NW][G][ATTN_WAVE_PART]) in
-// wave order; lane = dim. All reads are issued before the merge.
-template <int G, int NW>
-__device__ __forceinline__ void merge_wave_states(const MK_LDS float *part, int h, int lane, float &O, float &M,
-                                                  float &L) {
-    float o[NW], m[NW], l[NW];
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const MK_LDS float *ph = part + (w * G + h) * ATTN_WAVE_PART;
-        o[w] = ph[lane];
-        m[w] = ph[64];
-        l[w] = ph[65];
-    }
-    merge_init(O, M, L);
-#pragma unroll
-    for (int w = 0; w < NW; ++w) merge_step(O, M, L, o[w], m[w], l[w]);
 }
 
 // (value, index) order of the greedy pick: larger value, then lower index

@@ -64,6 +64,12 @@ constexpr int D = PREFETCH_SLICES;
 __device__ __forceinline__ uint32_t lds_ld(MK_LDS uint32_t *p) {
     return __builtin_amdgcn_readfirstlane(__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
 }
+// A word written once before the workgroup's first barrier (the request
+// lengths): a plain read, made visibly uniform. An acquire load here would
+// wait for the wave's outstanding global loads, the weight slices in flight.
+__device__ __forceinline__ uint32_t lds_ld_const(const MK_LDS uint32_t *p) {
+    return __builtin_amdgcn_readfirstlane(*p);
+}
 __device__ __forceinline__ void lds_st(MK_LDS uint32_t *p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -76,13 +82,13 @@ struct Ctx {
     const MK_LDS int32_t *q;  // this CU's queue, LDS_INSTR_WORDS words per instruction
     MK_LDS float *act;   // matvec inputs of all requests, or the attention staging
     MK_LDS float *xrow;  // residual rows of the instruction (O projection, down projection)
-    MK_LDS float *part;  // per-wave attention states; merge staging
     int cu, lane, w;
     uint32_t nbar;
     uint32_t tag;        // copies of kernel arguments the helpers need: taking
     int64_t watchdog;    // the argument block's address would move it to
     int32_t *err;        // private memory
     int32_t *host_err;
+    int pending_timeout; // instruction whose LDS-only barrier timed out (-1: none), raised on exit
 };
 
 __device__ __forceinline__ void raise_err(Ctx &c, int code, int pc) {
@@ -100,6 +106,10 @@ __device__ __forceinline__ bool uni(bool b) { return __builtin_amdgcn_readfirstl
 // Wait until *p >= v; false (after raising an error on timeout) if the
 // workgroup aborts.
 __device__ __forceinline__ bool lds_wait_ge(Ctx &c, MK_LDS uint32_t *p, uint32_t v, int pc) {
+    // a target every lane agrees on, made visibly uniform: otherwise the
+    // loop's exit is taken for divergent, and so is every value that flows
+    // through a barrier in a loop
+    v = __builtin_amdgcn_readfirstlane(v);
     if (lds_ld(p) >= v) return true;
     int64_t spins = 0;
     while (lds_ld(p) < v) {
@@ -118,6 +128,42 @@ __device__ __forceinline__ bool cbar(Ctx &c, int pc) {
     c.nbar++;
     if (c.lane == 0) lds_add(c.misc + M_ARRIVE, 1u);
     return lds_wait_ge(c, c.misc + M_ARRIVE, (uint32_t)NC * c.nbar, pc);
+}
+
+// Barrier of the workgroup's waves (the same arrival count as cbar) that
+// orders only their LDS accesses, with LDS-only fences: a full release would
+// first wait for the wave's outstanding global loads, which are the weight
+// slices in flight. On a timeout it raises the abort flag and leaves the
+// error to be recorded once the wave has left its loops (so that no global
+// atomic sits in them).
+__device__ __forceinline__ bool lbar(Ctx &c, int pc) {
+    c.nbar++;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    if (c.lane == 0)
+        __hip_atomic_fetch_add(c.misc + M_ARRIVE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t target = __builtin_amdgcn_readfirstlane((uint32_t)NC * c.nbar);
+    int64_t spins = 0;
+    while (__builtin_amdgcn_readfirstlane(
+               __hip_atomic_load(c.misc + M_ARRIVE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < target) {
+        if (__builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(c.misc + M_ABORT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)))
+            return false;
+        if (++spins > c.watchdog) {
+            c.pending_timeout = pc;
+            __hip_atomic_store(c.misc + M_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    return true;
+}
+
+// LDS counter increment that publishes the wave's earlier LDS accesses only
+// (see lbar); returns the old value, read by lane 0
+__device__ __forceinline__ uint32_t lds_add_local(MK_LDS uint32_t *p, uint32_t v) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // word `w` of instruction pc, from the LDS copy of the queue
@@ -263,7 +309,7 @@ __device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k,
     if (k.op == OP_ATTN) {
         k.b = rfl(bw[0]);
         k.g = rfl(bw[1]);
-        int p = (int)lds_ld(c.misc + M_KVLEN + (k.b & (MAX_B - 1)));
+        int p = (int)lds_ld_const(c.misc + M_KVLEN + (k.b & (MAX_B - 1)));
         if (p < 0 || p >= P.T * P.max_pages) p = 0;  // the staging raises the error
         k.p = p;
         int lo, hi;
@@ -489,6 +535,7 @@ __device__ __forceinline__ void take_slot(v4u (&r)[4]) {
 
 struct Ins {
     int pc, op, layer, r0, r1, flags, b, g, c, nch, p, merge, slot, nslot, mctr, mneed;
+    int nblk;     // attention: K/V blocks of the tile
     uint64_t wn;  // norm weight of the op's input
     int64_t *tr;
 };
@@ -749,8 +796,7 @@ __device__ __forceinline__ bool stage_attn(const KParams &P, Ctx &c, const Ins &
 }
 
 template <int NB, int G>
-__device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, Ins &in, Acc<NB> &acc,
-                                      AttnLaneT<G> &at) {
+__device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, Ins &in, Acc<NB> &acc, RegAct &ra) {
     const int pc = k.pc;
     in.pc = pc;
     const iv4 a = iw4(c, pc, W_OP), bw = iw4(c, pc, W_B), fw = iw4(c, pc, W_FLAGS), mw = iw4(c, pc, 12),
@@ -791,12 +837,13 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
                  stage_copy<ACT16_DOWN<NB>, NB>(P, c, in, P.tact + (size_t)in.layer * P.B * P.F, P.F) && cbar(c, pc);
             break;
         case OP_ATTN: {
-            const int p = in.b >= 0 && in.b < P.B ? (int)lds_ld(c.misc + M_KVLEN + in.b) : -1;
+            const int p = in.b >= 0 && in.b < P.B ? (int)lds_ld_const(c.misc + M_KVLEN + in.b) : -1;
             if (p < 0 || p >= P.T * P.max_pages) {
                 if (c.lane == 0) raise_err(c, ERR_RANGE, pc);
                 return false;
             }
             in.p = p;
+            in.nblk = k.nu;  // the cursor's blocks of this tile at this length
             ok = stage_attn<G>(P, c, in);
             break;
         }
@@ -825,7 +872,6 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
         }
     }
     acc.nan = false;
-    attn_lane_init(at);
     if (NB == 1 && in.op != OP_ATTN && k.K == 2048) {
         // the lane's activations: chunk 64 j + lane, elements 8 (64 j + lane) + e
         const bool normed = in.op == OP_QKV || in.op == OP_UPGATE || in.op == OP_LMHEAD;
@@ -841,14 +887,14 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
         for (int j = 0; j < 4; ++j) {
             const v4f a = *(const MK_LDS v4f *)(c.act + j * 512 + c.lane * 4);
             const v4f b = *(const MK_LDS v4f *)(c.act + j * 512 + 256 + c.lane * 4);
-            at.o[j][0] = a.x; at.o[j][1] = a.y; at.o[j][2] = a.z; at.o[j][3] = a.w;
-            at.o[j][4] = b.x; at.o[j][5] = b.y; at.o[j][6] = b.z; at.o[j][7] = b.w;
+            ra.o[j][0] = a.x; ra.o[j][1] = a.y; ra.o[j][2] = a.z; ra.o[j][3] = a.w;
+            ra.o[j][4] = b.x; ra.o[j][5] = b.y; ra.o[j][6] = b.z; ra.o[j][7] = b.w;
             if (normed) {
                 const v4u wq = *(const MK_LDS v4u *)(nw + (j * 64 + c.lane) * 8);
                 const float wf[8] = {bf_lo(wq.x), bf_hi(wq.x), bf_lo(wq.y), bf_hi(wq.y),
                                      bf_lo(wq.z), bf_hi(wq.z), bf_lo(wq.w), bf_hi(wq.w)};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) at.o[j][e] = at.o[j][e] * inv * wf[e];
+                for (int e = 0; e < 8; ++e) ra.o[j][e] = ra.o[j][e] * inv * wf[e];
             }
         }
     }
@@ -895,9 +941,9 @@ __device__ __forceinline__ void emit_row(const KParams &P, Ctx &c, const Ins &in
 // that request's products (at a padded batch of 8 the down projection's
 // input is staged as binary16, the only way 8 requests' 8192-wide inputs fit
 // in LDS); a slice past the end of a short row guards each chunk.
-template <int NB, int G>
+template <int NB>
 __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &k, const Ins &in, const v4u (&r)[4],
-                                           Acc<NB> &acc, const AttnLaneT<G> &xr) {
+                                           Acc<NB> &acc, const RegAct &xr) {
     const int lane = c.lane;
     const int m = k.s >= k.spm ? 1 : 0, part = k.s - m * k.spm;
     if (NB == 1 && k.K == 2048) {
@@ -1014,14 +1060,40 @@ __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &
     }
 }
 
+// The attention tile's LDS area of a round: after the staged queries
+// ([G][64] fp32) and the new K/V entry (bf16 [2][64], 64 floats' room).
 template <int G>
-__device__ __forceinline__ void consume_attn(const KParams &P, Ctx &c, const Cur &k, const Ins &in, const v4u (&r)[4],
-                                             AttnLaneT<G> &at) {
+__device__ __forceinline__ MK_LDS float *attn_area(const Ctx &c) {
+    return c.act + G * 64 + 64;
+}
+
+// Ends round run.rounds of an attention tile for this wave: a barrier (every
+// wave holding a block of the round has written it), the fold of the round
+// by the head waves, and between rounds a second barrier (the fold has read
+// the round before the next one overwrites it). Every wave goes through
+// every round of the tile, with a block or without. False on abort.
+template <int G>
+__device__ __forceinline__ bool attn_round_sync(Ctx &c, const Ins &in, AttnRun &run) {
+    const int nround = (in.nblk + NC - 1) / NC;
+    if (!uni(lbar(c, in.pc))) return false;
+    MK_LDS float *area = attn_area<G>(c);
+    if (c.w < G)
+        attn_round_fold(area + c.w * ATTN_ROUND_POS, (const MK_LDS uint16_t *)(area + G * ATTN_ROUND_POS),
+                        16 * min(NC, in.nblk - run.rounds * NC), c.lane, run);
+    run.rounds++;
+    return run.rounds >= nround || uni(lbar(c, in.pc));
+}
+
+// One K/V block of an attention tile (the wave's block of its round): the
+// new entry replaces whatever the cache slot held, then the block's scores
+// and values go to the round area.
+template <int G>
+__device__ __forceinline__ void attn_write_block(Ctx &c, const Cur &k, const Ins &in, const v4u (&r)[4]) {
     const int lane = c.lane;
     const int blk = k.blo + k.u;
     v4u k0 = r[0], k1 = r[1], v0 = r[2], v1 = r[3];
     const int t0 = lane >> 3;
-    if (blk == (in.p >> 4)) {  // the new entry replaces whatever the cache slot held
+    if (blk == (in.p >> 4)) {
         const int j = in.p & 15, dd = (lane & 7) * 8;
         const MK_LDS uint16_t *kvn = (const MK_LDS uint16_t *)(c.act + G * 64);
         const v4u nk = *(const MK_LDS v4u *)(kvn + dd), nv = *(const MK_LDS v4u *)(kvn + 64 + dd);
@@ -1035,7 +1107,7 @@ __device__ __forceinline__ void consume_attn(const KParams &P, Ctx &c, const Cur
         }
     }
     const int pos0 = blk * 16 + t0;
-    attn_lane_block(at, c.act, lane, k0, k1, v0, v1, pos0 <= in.p, pos0 + 8 <= in.p);
+    attn_block_write<G>(c.act, attn_area<G>(c), c.w, lane, k0, k1, v0, v1, pos0 <= in.p, pos0 + 8 <= in.p);
 }
 
 // Elects the last of the instruction's merge-event finishers (one per step).
@@ -1047,6 +1119,29 @@ __device__ __forceinline__ bool elect_last(const KParams &P, Ctx &c, const Ins &
                                      __HIP_MEMORY_SCOPE_AGENT);
     old = __builtin_amdgcn_readfirstlane(old);  // lane 0's: every lane is active here
     return old + 1 == need;
+}
+
+// The start counter: every workgroup bumps it once it has read kv_lens, so
+// a step that writes kv_lens_out (which may alias kv_lens) first checks that
+// every workgroup of the grid has taken its copy. `first` is a value read
+// earlier; by the end of a step the count is normally complete already.
+__device__ __forceinline__ int32_t started_count(const KParams &P) {
+    return __hip_atomic_load(P.counters + (int64_t)P.start_ctr * CTR_STRIDE, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool wait_all_started(const KParams &P, Ctx &c, int32_t first, int pc) {
+    const int32_t need = (int32_t)((int64_t)P.epoch * P.n_cus);
+    int32_t v = __builtin_amdgcn_readfirstlane(first);
+    int64_t spins = 0;
+    while (v < need) {
+        if (++spins > c.watchdog) {
+            raise_err(c, ERR_TIMEOUT, pc);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        v = __builtin_amdgcn_readfirstlane(started_count(P));
+    }
+    return true;
 }
 
 // Run by the last wave to finish an instruction's slices.
@@ -1073,6 +1168,7 @@ __device__ __forceinline__ bool finish(const KParams &P, Ctx &c, const Ins &in) 
         }
         if (!elect_last(P, c, in)) return true;
         if (in.tr && lane == 0) in.tr[TR_ELECT] = wall_clock64();
+        const int32_t started = P.kv_lens_out ? started_count(P) : 0;  // read now, checked before the write
         // the argmax is a maximum under a total order: any combination order gives the same token
         if (!tgather_range(
                 c, rl, 0, in.nslot * P.B * 2, [&](int i, float v) { c.act[i] = v; }, in.pc))
@@ -1100,22 +1196,25 @@ __device__ __forceinline__ bool finish(const KParams &P, Ctx &c, const Ins &in) 
                     bi = oi;
                 }
             }
-            if (lane == 0) {
-                P.tokens_out[b] = bi;
-                if (P.kv_lens_out) P.kv_lens_out[b] = (int32_t)c.misc[M_KVLEN + b] + 1;
-            }
+            if (lane == 0) P.tokens_out[b] = bi;
+        }
+        if (P.kv_lens_out) {
+            if (!wait_all_started(P, c, started, in.pc)) return false;
+            if (lane < P.B) P.kv_lens_out[lane] = (int32_t)c.misc[M_KVLEN + lane] + 1;
         }
         return true;
     }
     if ((in.flags & F_STEP_FINAL) && in.merge >= 0) {  // last layer's down projection without an LM head
-        if (elect_last(P, c, in) && P.kv_lens_out && lane < P.B)
-            P.kv_lens_out[lane] = (int32_t)c.misc[M_KVLEN + lane] + 1;
+        if (elect_last(P, c, in) && P.kv_lens_out) {
+            if (!wait_all_started(P, c, started_count(P), in.pc)) return false;
+            if (lane < P.B) P.kv_lens_out[lane] = (int32_t)c.misc[M_KVLEN + lane] + 1;
+        }
     }
     return true;
 }
 
 template <int NB, int G>
-__device__ __forceinline__ bool leave(const KParams &P, Ctx &c, const Ins &in, Acc<NB> &acc, AttnLaneT<G> &at) {
+__device__ __forceinline__ bool leave(const KParams &P, Ctx &c, const Ins &in, Acc<NB> &acc) {
     const int lane = c.lane;
     if (in.op == OP_LMHEAD) {
         if constexpr (NB == 1) {  // batched kernels kept the running best there already
@@ -1126,42 +1225,13 @@ __device__ __forceinline__ bool leave(const KParams &P, Ctx &c, const Ins &in, A
             }
         }
         if (acc.nan && lane == 0) raise_err(c, ERR_NAN, in.pc);
-    } else if (in.op == OP_ATTN) {
-        attn_lane_store(at, c.part + c.w * G * ATTN_WAVE_PART, lane);
     }
     uint32_t old = 0;
     if (lane == 0) old = lds_add(c.misc + M_FIN, 1u);
     old = __builtin_amdgcn_readfirstlane(old);  // lane 0's: every lane is active here
     if (in.tr && lane == 0 && old == (uint32_t)NC * in.pc) in.tr[TR_FIRST] = wall_clock64();
     if (in.tr && lane == 0 && old == (uint32_t)NC * (in.pc + 1) - 1) in.tr[TR_LAST] = wall_clock64();
-    if (in.op == OP_ATTN) {
-        // Once every wave has stored its state, wave h < G merges head h over
-        // the waves (in wave order) and publishes the chunk's (o, m, l) of
-        // that head; the last head merged ends the instruction. The other
-        // waves go on to the next instruction, whose staging waits for that.
-        if (c.w >= G) return true;
-        if (!lds_wait_ge(c, c.misc + M_FIN, (uint32_t)NC * (in.pc + 1), in.pc)) return false;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        const int h = c.w;
-        const size_t pbase = ((((size_t)in.layer * P.B + in.b) * P.nkv + in.g) * in.nch + in.c) * G * ATTN_PART;
-        const __amdgpu_buffer_rsrc_t rp = tres(P.tpart + pbase, (uint32_t)(G * ATTN_PART));
-        float O, M, L;
-        merge_wave_states<G, NC>(c.part, h, lane, O, M, L);
-        tput(rp, (uint32_t)(h * ATTN_PART + lane), O, P.tag);
-        if (lane == 0) {
-            tput(rp, (uint32_t)(h * ATTN_PART + 64), M, P.tag);
-            tput(rp, (uint32_t)(h * ATTN_PART + 65), L, P.tag);
-        }
-        uint32_t m = 0;
-        if (lane == 0) m = lds_add(c.misc + M_AFIN, 1u);
-        m = __builtin_amdgcn_readfirstlane(m);
-        // an instruction's merges all end before the next one's begin, so
-        // the count reaches a multiple of G exactly at its last merge
-        if ((m + 1) % G != 0) return true;
-        if (in.tr && lane == 0) in.tr[TR_END] = wall_clock64();
-        if (lane == 0) lds_add(c.misc + M_DONE, 1u);
-        return true;
-    }
+    if (in.op == OP_ATTN) return true;  // the attention loop published the tile and ended it
     if (old != (uint32_t)NC * (in.pc + 1) - 1) return true;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if (!finish<G>(P, c, in)) return false;
@@ -1189,6 +1259,55 @@ __device__ __forceinline__ void issue_any(int k, const KParams &P, const Cur &cu
     }
 }
 
+// An attention tile, outside the matvec slice loop (its barriers and head
+// state would otherwise share that loop's registers): the wave takes its
+// blocks (units w, w + NC, ...: one per round) from the slice stream in
+// order, keeping the stream D slices ahead, and goes through every round of
+// the tile, with a block or without; a wave without any block consumes its
+// one empty slice. After the last round wave h < G publishes head h's
+// softmax state as the chunk's (o, m, l); the last head published ends the
+// instruction. False on abort.
+template <int G>
+__device__ __forceinline__ bool attn_tile(const KParams &P, Ctx &c, Cur &ic, Cur &cc, const Ins &in, int &slot) {
+    AttnRun run;
+    attn_run_init(run);
+    const int nround = (in.nblk + NC - 1) / NC;
+    const int pc = in.pc;
+    bool took = false;
+    for (int r = 0; uni(r < nround || !took); ++r) {
+        // this wave's block of round r, or the tile's one empty slice
+        if (uni(cc.pc == pc && cc.op == OP_ATTN && (cc.u >= cc.nu ? !took : cc.u == c.w + r * NC))) {
+            v4u buf[4];
+            take_any(slot, buf);
+            if (cc.u < cc.nu) attn_write_block<G>(c, cc, in, buf);
+            took = true;
+            issue_any(slot, P, ic, c.lane);
+            cur_next(P, c, ic);
+            cur_next(P, c, cc);
+            slot = slot + 1 == D ? 0 : slot + 1;
+        }
+        if (r < nround && !uni(attn_round_sync<G>(c, in, run))) return false;
+    }
+    if (c.w >= G) return true;
+    const int h = c.w, lane = c.lane;
+    const size_t pbase = ((((size_t)in.layer * P.B + in.b) * P.nkv + in.g) * in.nch + in.c) * G * ATTN_PART;
+    const __amdgpu_buffer_rsrc_t rp = tres(P.tpart + pbase, (uint32_t)(G * ATTN_PART));
+    tput(rp, (uint32_t)(h * ATTN_PART + lane), run.O, P.tag);
+    if (lane == 0) {
+        tput(rp, (uint32_t)(h * ATTN_PART + 64), run.M, P.tag);
+        tput(rp, (uint32_t)(h * ATTN_PART + 65), run.L, P.tag);
+    }
+    uint32_t m = 0;
+    if (lane == 0) m = lds_add_local(c.misc + M_AFIN, 1u);
+    m = __builtin_amdgcn_readfirstlane(m);
+    // a tile's publishes all end before the next tile's begin, so the count
+    // reaches a multiple of G exactly at its last publish
+    if ((m + 1) % G != 0) return true;
+    if (in.tr && lane == 0) in.tr[TR_END] = wall_clock64();
+    if (lane == 0) lds_add_local(c.misc + M_DONE, 1u);
+    return true;
+}
+
 // The wave's main loop. Slices are consumed in the order they were issued,
 // so the slot being consumed always has the other D - 1 slots issued after
 // it, and a wait for all but the 4 (D - 1) newest loads is a wait for
@@ -1214,22 +1333,23 @@ __device__ __forceinline__ void run(const KParams &P, Ctx &c) {
     }
     Ins in{};
     Acc<NB> acc;
-    AttnLaneT<G> at;
+    RegAct ra;
     bool first = true;
     int slot = 0;
     for (;;) {
-        if (!first && !uni(leave<NB, G>(P, c, in, acc, at))) break;
+        if (!first && !uni(leave<NB, G>(P, c, in, acc))) break;
         first = false;
         if (cc.op == OP_END) break;
-        if (!uni(enter<NB, G>(P, c, cc, in, acc, at))) break;
+        if (!uni(enter<NB, G>(P, c, cc, in, acc, ra))) break;
+        if (cc.op == OP_ATTN) {
+            if (!uni(attn_tile<G>(P, c, ic, cc, in, slot))) break;
+            continue;
+        }
         for (;;) {
             v4u buf[4];
             take_any(slot, buf);
             const bool empty = cc.u >= cc.nu;
-            if (!empty) {
-                if (cc.op == OP_ATTN) consume_attn<G>(P, c, cc, in, buf, at);
-                else consume_mv<NB, G>(P, c, cc, in, buf, acc, at);
-            }
+            if (!empty) consume_mv<NB>(P, c, cc, in, buf, acc, ra);
             const bool last = empty || (cc.s == cc.sp - 1 && cc.u + NC >= cc.nu);
             issue_any(slot, P, ic, c.lane);
             cur_next(P, c, ic);
@@ -1240,6 +1360,7 @@ __device__ __forceinline__ void run(const KParams &P, Ctx &c) {
     }
     // no load may still be writing a slot register when the wave ends
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (c.pending_timeout >= 0) raise_err(c, ERR_TIMEOUT, c.pending_timeout);
 }
 
 }  // namespace
@@ -1256,7 +1377,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(BLOCK_THREADS, BLOCK_THREA
     c.misc = (MK_LDS uint32_t *)lds;
     c.q = (const MK_LDS int32_t *)(lds + P.queue_off);
     c.xrow = (MK_LDS float *)(lds + P.xrow_off);
-    c.part = (MK_LDS float *)(lds + P.part_off);
     c.act = (MK_LDS float *)(lds + P.act_off);
     c.cu = blockIdx.x;
     c.lane = threadIdx.x & 63;
@@ -1266,6 +1386,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(BLOCK_THREADS, BLOCK_THREA
     c.watchdog = P.watchdog;
     c.err = P.err;
     c.host_err = P.host_err;
+    c.pending_timeout = -1;
     for (int i = threadIdx.x; i < MISC_BYTES / 4; i += BLOCK_THREADS) c.misc[i] = 0;
     __syncthreads();
     // the CU's queue and the request lengths are read once, here: scalar
@@ -1279,6 +1400,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(BLOCK_THREADS, BLOCK_THREA
         if (threadIdx.x < (unsigned)P.B) c.misc[M_KVLEN + threadIdx.x] = (uint32_t)P.kv_lens[threadIdx.x];
     }
     __syncthreads();
+    // the lengths are in LDS (their loads have returned): count this
+    // workgroup as started
+    if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(P.counters + (int64_t)P.start_ctr * CTR_STRIDE, 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     run<NB, G>(P, c);
 }
 

@@ -77,7 +77,11 @@ constexpr int MISC_BYTES = 4096;
 constexpr int SLICE_BYTES = 4096;      // weight bytes one wave holds per register slice
 constexpr int PREFETCH_SLICES = 4;     // slices each wave keeps in flight
 constexpr int ATTN_PART = 64 + 2;      // o[d], m, l of one head
-constexpr int ATTN_WAVE_PART = 68;     // floats per head of a wave's attention state in LDS
+// an attention tile works in rounds of one 16-position K/V block per wave;
+// a round's LDS area for G query heads holds its scores [G][ATTN_ROUND_POS]
+// fp32, then its values [ATTN_ROUND_POS][64] bf16
+constexpr int ATTN_ROUND_POS = N_COMPUTE_WAVES * 16;
+constexpr int attn_round_floats(int G) { return G * ATTN_ROUND_POS + ATTN_ROUND_POS * 32; }
 constexpr int MAX_B = 8;
 // device-clock stamps per instruction in a traced step: start, inputs staged,
 // end (merges included), first wave done with its slices, last wave done,

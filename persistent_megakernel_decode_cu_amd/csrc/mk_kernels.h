@@ -12,8 +12,9 @@ struct KParams {
     const int32_t *events;    // [n_events, EV_WORDS] merge events
     int32_t *counters;        // [n_counters * CTR_STRIDE]
     int32_t Q, epoch, n_cus;
+    int32_t start_ctr;        // counter every workgroup bumps once it has read kv_lens
     uint32_t tag;             // this step's tag on every exchanged activation (never 0)
-    int32_t queue_off, xrow_off, part_off, act_off, nw_off;  // LDS byte offsets
+    int32_t queue_off, xrow_off, act_off, nw_off;  // LDS byte offsets
     int32_t act_stride;       // floats per request in the activation area
     int32_t xrow_stride;      // floats per request in the residual-row area
     int64_t watchdog;
@@ -63,9 +64,6 @@ hipError_t launch_megakernel(const KParams &p, int lds_bytes, hipStream_t s);
 hipError_t setup_megakernel(int B, int G, int lds_bytes);
 hipError_t megakernel_occupancy(int B, int G, int lds_bytes, int *blocks_per_cu);
 hipError_t launch_unfused(const KParams &p, float *u_scratch, float *qrot, hipStream_t s);
-hipError_t dma_probe(const void *src, void *dst, int n_kib, int off_kib);
-hipError_t ring_probe(const void *src, int n, int ring, int depth, int variant, int32_t *errs, int blocks);
-hipError_t stream_probe(const void *src, size_t bytes, int blocks, uint32_t *out);
 hipError_t copy_probe(const void *src, void *dst, size_t bytes, hipStream_t s);
 hipError_t litmus(int pairs, int n, int rounds, int mode, int32_t *data, int32_t *flags, int32_t *res);
 hipError_t hop_probe(int32_t *ctr, float *xbuf, int n_cus, int rounds, int variant, int32_t *res);

@@ -1,41 +1,17 @@
 // mk_probes.hip - measurement kernels behind the mk_debug_* exports: the
-// latency of one dependency hop between workgroups, and the read bandwidth of
-// one resident workgroup per compute unit streaming through registers.
+// latency of one dependency hop between workgroups (fenced counters and
+// tagged words), a cross-XCD visibility litmus of the tagged-word protocol,
+// the read bandwidth of one resident workgroup per compute unit streaming
+// through registers, and a plain copy of known size that calibrates the
+// traffic counters.
 #include "mk_device.h"
 
 namespace mk {
 
 namespace {
 
-enum : int { PM_LANDED = 1, PM_ABORT = 2, PM_WPOS = 16 };
-// shape of the ring probe: one loader wave, PNC consumer waves, 1 KiB granules
-constexpr int PNC = 8;
-constexpr int P_WAVES = PNC + 2;
-constexpr int P_THREADS = P_WAVES * 64;
-constexpr int P_GRANULE = 1024;
-constexpr int P_MISC = 4096;
-
-__device__ __forceinline__ uint32_t lds_ld(MK_LDS uint32_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ __forceinline__ void lds_st(MK_LDS uint32_t *p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-// HBM -> LDS, 16 bytes per active lane at lds_addr + 16 * lane. Issued from
-// inline assembly so that the compiler does not conservatively wait for the
-// transfer before unrelated LDS accesses; the loader tracks completion with
-// its own vmcnt waits. m0 carries the LDS base; nothing else in this kernel
-// uses m0.
-__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_addr) {
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "s_nop 1\n\t"
-        "global_load_lds_dwordx4 %1, off"
-        :
-        : "s"(lds_addr), "v"(gptr)
-        : "memory");
-}
+// launch bound of the register-stream probe (launched with up to 512 threads)
+constexpr int P_THREADS = 640;
 
 }  // namespace
 
@@ -322,382 +298,6 @@ hipError_t litmus(int pairs, int n, int rounds, int mode, int32_t *data, int32_t
     hipError_t e = hipLaunchCooperativeKernel((const void *)mk_litmus, dim3(2 * pairs), dim3(256), args, 0, nullptr);
     if (e != hipSuccess) return e;
     return hipDeviceSynchronize();
-}
-
-// One wave: DMA n granules into LDS at byte offset `off` exactly as the
-// loader does, wait, then copy those LDS bytes out with ordinary loads.
-__global__ __launch_bounds__(64) void mk_dma_probe(const char *src, char *dst, int n, int off) {
-    extern __shared__ char lds_raw[];
-    MK_LDS char *lds = (MK_LDS char *)lds_raw;
-    const int lane = threadIdx.x;
-    for (int i = lane; i < LDS_LIMIT / 4; i += 64) ((MK_LDS uint32_t *)lds)[i] = 0u;
-    __syncthreads();
-    const uint32_t base = (uint32_t)(uintptr_t)lds + (uint32_t)off;
-    if (n < 0) {
-        // two transfers, one m0 value, the second with instruction offset 1024
-        const char *g = src + lane * 16;
-        asm volatile(
-            "s_mov_b32 m0, %0\n\t"
-            "s_nop 1\n\t"
-            "global_load_lds_dwordx4 %1, off\n\t"
-            "global_load_lds_dwordx4 %1, off offset:1024"
-            :
-            : "s"(base), "v"(g)
-            : "memory");
-        n = 2;
-    } else {
-        for (int k = 0; k < n; ++k)
-            dma16(src + (size_t)k * P_GRANULE + lane * 16, __builtin_amdgcn_readfirstlane(base + k * P_GRANULE));
-    }
-    wait_vmcnt<0>();
-    for (int k = 0; k < n; ++k) {
-        const v4u v = *(const MK_LDS v4u *)(lds + off + k * P_GRANULE + lane * 16);
-        *(v4u *)(dst + (size_t)k * P_GRANULE + lane * 16) = v;
-    }
-}
-
-hipError_t dma_probe(const void *src, void *dst, int n_kib, int off_kib) {
-    hipError_t e = hipFuncSetAttribute((const void *)mk_dma_probe, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       LDS_LIMIT);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mk_dma_probe, dim3(1), dim3(64), LDS_LIMIT, 0, (const char *)src, (char *)dst, n_kib,
-                       off_kib * P_GRANULE);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return hipDeviceSynchronize();
-}
-
-// Ring protocol probe: wave 0 streams n granules of a known pattern through
-// a ring of `ring` granules exactly as the loader does (issue, keep `depth`
-// in flight, publish landed); PNC consumer waves take granules round-robin,
-// wait for them to land, check every word and release them. `variant` 1
-// makes the loader read back one word of the newest landed granule before
-// publishing. Counts mismatching words into errs[0] and granules checked
-// into errs[1].
-__global__ __launch_bounds__(P_THREADS, 1) void mk_ring_probe(const uint32_t *src, int n, int ring, int depth,
-                                                                   int variant, int64_t watchdog, int32_t *errs) {
-    extern __shared__ char lds_raw[];
-    MK_LDS char *lds = (MK_LDS char *)lds_raw;
-    MK_LDS uint32_t *misc = (MK_LDS uint32_t *)lds;
-    MK_LDS char *rb = lds + P_MISC;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    src += (size_t)blockIdx.x * n * 256;
-    for (int i = threadIdx.x; i < P_MISC / 4; i += P_THREADS) misc[i] = 0;
-    __syncthreads();
-    const int nl = (variant >> 8) & 15;
-    const int gb = ((variant >> 12) & 15) ? ((variant >> 12) & 15) : 1;  // granules per DMA batch: 1 or 4
-    const bool regs = (variant >> 16) & 1;                                // register-staged loaders
-    const bool inter = (variant >> 17) & 1;  // batch t of workgroup b at (t * gridDim.x + b) * 4 KiB
-    const bool plain = (variant >> 18) & 1;  // ordinary loads instead of non-temporal ones
-    variant &= 255;
-    if (inter) src -= (size_t)blockIdx.x * n * 256;  // undo the per-block slice
-    if (regs && nl >= 1) {
-        // nl loader waves; batch t = 4 granules issued by loader t % nl with
-        // ordinary 16-byte loads into registers, 4 batches in flight, then
-        // written into the ring once its slots are free
-        const int ncons = P_WAVES - nl;
-        const int nbatch = n / 4;
-        if (wave < nl) {
-            uint32_t mine = 0, lim = ring;
-            v4u ra[4], rbuf[4], rc[4], rd[4];
-            auto issue = [&](v4u (&r)[4], int t) {
-                if (t < nbatch) {
-                    const size_t bt = inter ? (size_t)t * gridDim.x + blockIdx.x : (size_t)t;
-                    const v4u *g = (const v4u *)(src + bt * 4 * 256) + lane;
-                    if (plain) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) r[i] = g[i * 64];
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) r[i] = __builtin_nontemporal_load(g + i * 64);
-                    }
-                }
-            };
-            auto commit = [&](v4u (&r)[4], int t) -> bool {
-                if (t >= nbatch) return true;
-                const uint32_t k = (uint32_t)t * 4;
-                if (k + 4 > lim) {
-                    int64_t spins = 0;
-                    for (;;) {
-                        uint32_t mn = lds_ld(misc + PM_WPOS);
-                        for (int w = 1; w < ncons; ++w) mn = min(mn, lds_ld(misc + PM_WPOS + w));
-                        lim = __builtin_amdgcn_readfirstlane(mn + ring);
-                        if (k + 4 <= lim) break;
-                        if (++spins > watchdog) {
-                            lds_st(misc + PM_ABORT, 1u);
-                            return false;
-                        }
-                        __builtin_amdgcn_s_sleep(1);
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) *(MK_LDS v4u *)(rb + ((k + i) % ring) * P_GRANULE + lane * 16) = r[i];
-                mine += 4;
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                __hip_atomic_store(misc + PM_LANDED + 32 + wave, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                return true;
-            };
-            const int step = nl;
-            int t = wave;
-            issue(ra, t);
-            issue(rbuf, t + step);
-            issue(rc, t + 2 * step);
-            issue(rd, t + 3 * step);
-            for (; t < nbatch; t += 4 * step) {
-                if (!commit(ra, t)) return;
-                issue(ra, t + 4 * step);
-                if (!commit(rbuf, t + step)) return;
-                issue(rbuf, t + 5 * step);
-                if (!commit(rc, t + 2 * step)) return;
-                issue(rc, t + 6 * step);
-                if (!commit(rd, t + 3 * step)) return;
-                issue(rd, t + 7 * step);
-            }
-        } else {
-            const int w = wave - nl;
-            int bad = 0, seen = 0;
-            for (int g = w; g < nbatch * 4; g += ncons) {
-                const int tb = g / 4;
-                const int j = tb % nl;
-                const uint32_t need = (uint32_t)((tb / nl + 1) * 4);
-                int64_t spins = 0;
-                while (lds_ld(misc + PM_LANDED + 32 + j) < need) {
-                    if (lds_ld(misc + PM_ABORT) == 1u || ++spins > watchdog) {
-                        if (lane == 0) atomicAdd(errs + 2, 1);
-                        return;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                const v4u v = *(const MK_LDS v4u *)(rb + (g % ring) * P_GRANULE + lane * 16);
-                const uint32_t e = (uint32_t)g * 256u + lane * 4u;
-                if (variant == 4)
-                    bad += (v.x ^ v.y ^ v.z ^ v.w) == 0x12345678u;
-                else
-                    bad += (v.x != src[e]) + (v.y != src[e + 1]) + (v.z != src[e + 2]) + (v.w != src[e + 3]);
-                ++seen;
-                const int gn = g + ncons;
-                if (lane == 0) lds_st(misc + PM_WPOS + w, (uint32_t)(gn < nbatch * 4 ? gn : nbatch * 4));
-            }
-            if (lane == 0) lds_st(misc + PM_WPOS + w, (uint32_t)(nbatch * 4));
-            bad = (int)wave_sum((float)bad);
-            if (lane == 0) {
-                atomicAdd(errs, bad);
-                atomicAdd(errs + 1, seen);
-            }
-        }
-        return;
-    }
-    if (nl >= 1) {
-        // nl loader waves; batch t (granules [t*gb, t*gb+gb)) is issued by
-        // loader t % nl with one m0 write; consumers are waves nl .. P_WAVES-1
-        // and wait on the issuing loader's own landed count (in granules)
-        const int ncons = P_WAVES - nl;
-        const int nbatch = n / gb;
-        if (wave < nl) {
-            const uint32_t ring_lds = (uint32_t)(uintptr_t)rb;
-            uint32_t mine = 0, pub = 0, lim = ring;
-            for (int t = wave; t < nbatch; t += nl) {
-                const uint32_t k = (uint32_t)t * gb;  // first granule of the batch
-                if (k + gb > lim) {
-                    int64_t spins = 0;
-                    for (;;) {
-                        wait_vmcnt<0>();
-                        pub = mine;
-                        lds_st(misc + PM_LANDED + 32 + wave, mine);
-                        uint32_t mn = lds_ld(misc + PM_WPOS);
-                        for (int w = 1; w < ncons; ++w) mn = min(mn, lds_ld(misc + PM_WPOS + w));
-                        lim = __builtin_amdgcn_readfirstlane(mn + ring);
-                        if (k + gb <= lim) break;
-                        if (++spins > watchdog) {
-                            lds_st(misc + PM_ABORT, 1u);
-                            return;
-                        }
-                        __builtin_amdgcn_s_sleep(1);
-                    }
-                }
-                const size_t kk = inter ? ((size_t)t * gridDim.x + blockIdx.x) * gb : (size_t)k;
-                const char *g = (const char *)(src + kk * 256 + lane * 4);
-                const uint32_t l = __builtin_amdgcn_readfirstlane(ring_lds + (k % ring) * P_GRANULE);
-                if (gb == 4) {
-                    asm volatile(
-                        "s_mov_b32 m0, %0\n\t"
-                        "s_nop 1\n\t"
-                        "global_load_lds_dwordx4 %1, off\n\t"
-                        "global_load_lds_dwordx4 %1, off offset:1024\n\t"
-                        "global_load_lds_dwordx4 %1, off offset:2048\n\t"
-                        "global_load_lds_dwordx4 %1, off offset:3072"
-                        :
-                        : "s"(l), "v"(g)
-                        : "memory");
-                } else {
-                    dma16(g, l);
-                }
-                mine += gb;
-                uint32_t dd;
-                switch (depth) {
-                    case 8: wait_vmcnt<8>(); dd = 8; break;
-                    case 32: wait_vmcnt<32>(); dd = 32; break;
-                    case 48: wait_vmcnt<48>(); dd = 48; break;
-                    case 56: wait_vmcnt<56>(); dd = 56; break;
-                    default: wait_vmcnt<16>(); dd = 16; break;
-                }
-                if (mine > dd && mine - dd > pub) {
-                    pub = mine - dd;
-                    lds_st(misc + PM_LANDED + 32 + wave, pub);
-                }
-            }
-            wait_vmcnt<0>();
-            lds_st(misc + PM_LANDED + 32 + wave, mine);
-        } else {
-            const int w = wave - nl;
-            int bad = 0, seen = 0;
-            for (int g = w; g < nbatch * gb; g += ncons) {
-                const int t = g / gb;
-                const int j = t % nl;
-                const uint32_t need = (uint32_t)((t / nl + 1) * gb);
-                int64_t spins = 0;
-                while (lds_ld(misc + PM_LANDED + 32 + j) < need) {
-                    if (lds_ld(misc + PM_ABORT) == 1u || ++spins > watchdog) {
-                        if (lane == 0) atomicAdd(errs + 2, 1);
-                        return;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                const v4u v = *(const MK_LDS v4u *)(rb + (g % ring) * P_GRANULE + lane * 16);
-                const uint32_t e = (uint32_t)g * 256u + lane * 4u;
-                if (variant == 4)
-                    bad += (v.x ^ v.y ^ v.z ^ v.w) == 0x12345678u;
-                else
-                    bad += (v.x != src[e]) + (v.y != src[e + 1]) + (v.z != src[e + 2]) + (v.w != src[e + 3]);
-                ++seen;
-                const int gn = g + ncons;
-                if (lane == 0) lds_st(misc + PM_WPOS + w, (uint32_t)(gn < nbatch * gb ? gn : nbatch * gb));
-            }
-            if (lane == 0) lds_st(misc + PM_WPOS + w, (uint32_t)(nbatch * gb));
-            bad = (int)wave_sum((float)bad);
-            if (lane == 0) {
-                atomicAdd(errs, bad);
-                atomicAdd(errs + 1, seen);
-            }
-        }
-        return;
-    }
-    if (wave == 0) {
-        const uint32_t ring_lds = (uint32_t)(uintptr_t)rb;
-        uint32_t issued = 0, slot = 0, lim = ring, pub = 0;
-        for (int k = 0; k < n; ++k) {
-            if (issued >= lim) {
-                int64_t spins = 0;
-                for (;;) {
-                    wait_vmcnt<0>();
-                    pub = issued;
-                    lds_st(misc + PM_LANDED, issued);
-                    uint32_t mn = lds_ld(misc + PM_WPOS);
-                    for (int w = 1; w < PNC; ++w) mn = min(mn, lds_ld(misc + PM_WPOS + w));
-                    lim = __builtin_amdgcn_readfirstlane(mn + ring);
-                    if (issued < lim) break;
-                    if (++spins > watchdog) {
-                        lds_st(misc + PM_ABORT, 1u);
-                        return;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-            }
-            dma16(src + (size_t)k * 256 + lane * 4, __builtin_amdgcn_readfirstlane(ring_lds + slot * P_GRANULE));
-            ++issued;
-            slot = (slot + 1 == (uint32_t)ring) ? 0 : slot + 1;
-            switch (depth) {
-                case 0: wait_vmcnt<0>(); break;
-                case 8: wait_vmcnt<8>(); break;
-                case 40: wait_vmcnt<40>(); break;
-                default: wait_vmcnt<56>(); break;
-            }
-            if (issued > (uint32_t)depth && issued - depth > pub) {
-                pub = issued - depth;
-                if (variant == 1) {
-                    const uint32_t s2 = (pub - 1) % ring;
-                    const uint32_t v = *(volatile MK_LDS uint32_t *)(rb + s2 * P_GRANULE + lane * 16);
-                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-                    if (v == 0xdeadbeefu) misc[PM_ABORT] = 2;
-                }
-                lds_st(misc + PM_LANDED, pub);
-            }
-        }
-        wait_vmcnt<0>();
-        lds_st(misc + PM_LANDED, issued);
-    } else if (wave == 1) {
-        // variant 2: agent-scope acquire fences, variant 3: release fences,
-        // issued by a second wave while the loader streams
-        if (variant >= 2) {
-            int64_t spins = 0;
-            while (lds_ld(misc + PM_LANDED) < (uint32_t)n && lds_ld(misc + PM_ABORT) != 1u && ++spins < watchdog) {
-                (void)__hip_atomic_load(errs + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (variant == 2) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                else __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-                __builtin_amdgcn_s_sleep(2);
-            }
-        }
-    } else if (wave >= 2) {
-        const int w = wave - 2;
-        int bad = 0, seen = 0;
-        for (int g = w; g < n; g += PNC) {
-            int64_t spins = 0;
-            while (lds_ld(misc + PM_LANDED) < (uint32_t)(g + 1)) {
-                if (lds_ld(misc + PM_ABORT) == 1u || ++spins > watchdog) {
-                    if (lane == 0) atomicAdd(errs + 2, 1);
-                    return;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-            const v4u v = *(const MK_LDS v4u *)(rb + (g % ring) * P_GRANULE + lane * 16);
-            const uint32_t e = (uint32_t)g * 256u + lane * 4u;
-            if (variant == 4)
-                bad += (v.x ^ v.y ^ v.z ^ v.w) == 0x12345678u;
-            else
-                bad += (v.x != src[e]) + (v.y != src[e + 1]) + (v.z != src[e + 2]) + (v.w != src[e + 3]);
-            ++seen;
-            const int gn = g + PNC;
-            if (lane == 0) lds_st(misc + PM_WPOS + w, (uint32_t)(gn < n ? gn : n));
-        }
-        if (lane == 0) lds_st(misc + PM_WPOS + w, (uint32_t)n);
-        bad = (int)wave_sum((float)bad);
-        if (lane == 0) {
-            atomicAdd(errs, bad);
-            atomicAdd(errs + 1, seen);
-        }
-    }
-}
-
-hipError_t ring_probe(const void *src, int n, int ring, int depth, int variant, int32_t *errs, int blocks) {
-    const int lds = P_MISC + ring * P_GRANULE;
-    hipError_t e = hipFuncSetAttribute((const void *)mk_ring_probe, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mk_ring_probe, dim3(blocks), dim3(P_THREADS), lds, 0, (const uint32_t *)src, n, ring,
-                       depth, variant, (int64_t)1 << 22, errs);
-    return hipGetLastError();
-}
-
-// Plain HBM streaming read: every thread sums 16-byte loads; the achievable
-// read bandwidth of the chip.
-__global__ __launch_bounds__(256) void mk_stream_probe(const v4u *src, size_t n16, uint32_t *out) {
-    uint32_t acc = 0;
-    const size_t stride = (size_t)gridDim.x * 256;
-    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const v4u a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
-    }
-    for (; i < n16; i += stride) {
-        const v4u a = src[i];
-        acc ^= a.x ^ a.y ^ a.z ^ a.w;
-    }
-    if (acc == 0x9e3779b9u) out[0] = acc;
-}
-
-hipError_t stream_probe(const void *src, size_t bytes, int blocks, uint32_t *out) {
-    hipLaunchKernelGGL(mk_stream_probe, dim3(blocks), dim3(256), 0, 0, (const v4u *)src, bytes / 16, out);
-    return hipGetLastError();
 }
 
 // Plain device copy of n16 16-byte words: each word is read once and written

@@ -31,7 +31,7 @@
 //      which makes every queue consistent with one order and so rules out
 //      deadlock while all workgroups are co-resident (progress obligation);
 //   4. encode each queue as [Q, 32] int32 words (mk_isa.h) and lay out the
-//      LDS of a workgroup (residual rows, attention states, activations).
+//      LDS of a workgroup (residual rows, activations, attention rounds).
 #include "mk_sched.h"
 
 #include <algorithm>
@@ -332,15 +332,15 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     const int kmax = NBP == 8 ? std::max({H, QD, (F + 1) / 2}) : std::max(H, std::max(F, QD));
     P.act_stride = (kmax + 511) / 512 * 512;
     P.xrow_stride = (max_rows_x + 3) / 4 * 4;
-    const int64_t part_floats = (int64_t)N_COMPUTE_WAVES * G * ATTN_WAVE_PART;  // per-wave attention states
-    // matvec inputs; attention staging; an AMERGE's chunk states; LM-head partials
-    const int64_t act_floats = std::max<int64_t>({(int64_t)NBP * P.act_stride, (int64_t)G * 64 + 64,
-                                                  (int64_t)C * G * ATTN_PART, (int64_t)P.n_lm_slots * B * 2});
+    // matvec inputs; attention staging (queries, new K/V entry) and one
+    // round's scores and values; an AMERGE's chunk states; LM-head partials
+    const int64_t act_floats =
+        std::max<int64_t>({(int64_t)NBP * P.act_stride, (int64_t)G * 64 + 64 + attn_round_floats(G),
+                           (int64_t)C * G * ATTN_PART, (int64_t)P.n_lm_slots * B * 2});
     auto up256 = [](int64_t x) { return (x + 255) / 256 * 256; };
     const int64_t queue_off = MISC_BYTES;  // the CU's queue, LDS_INSTR_WORDS words per instruction
     const int64_t xrow_off = queue_off + up256((int64_t)Q * LDS_INSTR_WORDS * 4);
-    const int64_t part_off = xrow_off + up256((int64_t)NBP * P.xrow_stride * 4);
-    const int64_t act_off = part_off + up256(part_floats * 4);
+    const int64_t act_off = xrow_off + up256((int64_t)NBP * P.xrow_stride * 4);
     // the norm weights of a staged RMSNorm, copied in whole 1 KiB wave loads
     const int64_t nw_off = act_off + up256(act_floats * 4);
     const int64_t lds = nw_off + ((int64_t)H * 2 + 1023) / 1024 * 1024;
@@ -351,7 +351,6 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
                                            std::to_string(P.act_stride) + " floats");
     P.queue_off = (int)queue_off;
     P.xrow_off = (int)xrow_off;
-    P.part_off = (int)part_off;
     P.act_off = (int)act_off;
     P.nw_off = (int)nw_off;
     P.lds_bytes = (int)lds;

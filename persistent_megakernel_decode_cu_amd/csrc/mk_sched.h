@@ -19,8 +19,9 @@ struct Plan {
     int attn_chunks = 0;
     int max_kv_len = 0;
     // LDS layout of a resident workgroup (bytes): misc | instruction queue |
-    // residual rows | attention states / merge staging | activation area
-    int queue_off = 0, xrow_off = 0, part_off = 0, act_off = 0, nw_off = 0, lds_bytes = 0;
+    // residual rows | activation area (matvec inputs, attention staging and
+    // rounds, merge staging) | norm weights
+    int queue_off = 0, xrow_off = 0, act_off = 0, nw_off = 0, lds_bytes = 0;
     int xrow_stride = 0, act_stride = 0;  // floats per request
     int n_lm_slots = 0;        // LM-head tiles (partial argmax slots)
     std::vector<int32_t> queue;   // [n_cus, Q, INSTR_WORDS]

@@ -163,7 +163,7 @@ template <int G>
 __global__ __launch_bounds__(UF_ATTN_THREADS) void uf_attn(KParams P, int layer, const float *qrot) {
     constexpr int NW = N_COMPUTE_WAVES;
     __shared__ float q[MAX_G * 64];
-    __shared__ float part[NW * MAX_G * ATTN_WAVE_PART];
+    __shared__ float area[attn_round_floats(MAX_G)];
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, nch = gridDim.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int p = P.kv_lens[b];
@@ -173,31 +173,36 @@ __global__ __launch_bounds__(UF_ATTN_THREADS) void uf_attn(KParams P, int layer,
     const int nb = (p + 1 + 15) >> 4;
     const int blo = (int)((int64_t)c * nb / nch), bhi = (int)((int64_t)(c + 1) * nb / nch);
     const size_t layer_pool = (size_t)P.n_pages * P.nkv * 16 * 64;
-    AttnLaneT<G> st;
-    attn_lane_init(st);
+    MK_LDS float *ar = (MK_LDS float *)area;
+    AttnRun run;
+    attn_run_init(run);
     const int t0 = lane >> 3;
-    for (int blk = blo + wave; blk < bhi; blk += NW) {
-        int page = P.page_table[(int64_t)b * P.max_pages + blk];
-        if (page < 0 || page >= P.n_pages) page = 0;
-        const size_t off = (size_t)layer * layer_pool + ((size_t)page * P.nkv + g) * 1024;
-        const v4u *kb = (const v4u *)(P.k_pool + off);
-        const v4u *vb = (const v4u *)(P.v_pool + off);
-        const int pos0 = blk * 16 + t0;
-        attn_lane_block(st, (const MK_LDS float *)q, lane, kb[lane], kb[64 + lane], vb[lane], vb[64 + lane],
-                        pos0 <= p, pos0 + 8 <= p);
+    // rounds of NW blocks, block blo + NW r + w on wave w, as the resident
+    // interpreter hands them out
+    for (int r0 = blo; r0 < bhi; r0 += NW) {
+        const int blk = r0 + wave;
+        if (blk < bhi) {
+            int page = P.page_table[(int64_t)b * P.max_pages + blk];
+            if (page < 0 || page >= P.n_pages) page = 0;
+            const size_t off = (size_t)layer * layer_pool + ((size_t)page * P.nkv + g) * 1024;
+            const v4u *kb = (const v4u *)(P.k_pool + off);
+            const v4u *vb = (const v4u *)(P.v_pool + off);
+            const int pos0 = blk * 16 + t0;
+            attn_block_write<G>((const MK_LDS float *)q, ar, wave, lane, kb[lane], kb[64 + lane], vb[lane],
+                                vb[64 + lane], pos0 <= p, pos0 + 8 <= p);
+        }
+        __syncthreads();
+        if (wave < G)
+            attn_round_fold(ar + wave * ATTN_ROUND_POS, (const MK_LDS uint16_t *)(ar + G * ATTN_ROUND_POS),
+                            16 * min(NW, bhi - r0), lane, run);
+        __syncthreads();
     }
-    attn_lane_store(st, (MK_LDS float *)(part + wave * G * ATTN_WAVE_PART), lane);
-    __syncthreads();
-    if (wave == 0) {
-        for (int hq = 0; hq < G; ++hq) {
-            float O, M, Ls;
-            merge_wave_states<G, NW>((const MK_LDS float *)part, hq, lane, O, M, Ls);
-            float *dst = P.attn_part + ((((int64_t)b * P.nkv + g) * nch + c) * G + hq) * ATTN_PART_STRIDE;
-            dst[lane] = O;
-            if (lane == 0) {
-                dst[64] = M;
-                dst[65] = Ls;
-            }
+    if (wave < G) {
+        float *dst = P.attn_part + ((((int64_t)b * P.nkv + g) * nch + c) * G + wave) * ATTN_PART_STRIDE;
+        dst[lane] = run.O;
+        if (lane == 0) {
+            dst[64] = run.M;
+            dst[65] = run.L;
         }
     }
 }

@@ -10,13 +10,39 @@ the last compute unit to finish the step.
 """
 from __future__ import annotations
 
+from typing import NamedTuple
+
 import numpy as np
 
 CLOCK_MHZ = 100.0  # wall_clock64 ticks per microsecond
 TR_START, TR_READY, TR_END, TR_FIRST, TR_LAST = 0, 1, 2, 3, 4
+# queue encoding of csrc/mk_isa.h: the words a timeline needs, and the op names
+W_OP, W_LAYER = 0, 1
+OP_END = 0
+OP_NAMES = {1: "QKV", 2: "ATTN", 3: "OPROJ", 4: "UPGATE", 5: "DOWN", 6: "LMHEAD", 7: "AMERGE"}
 
 
-def timeline(trace: np.ndarray, instrs, op_names: dict, layer: int) -> str:
+class Instr(NamedTuple):
+    cu: int
+    pc: int
+    op: int
+    layer: int
+
+
+def decode_queue(queue: np.ndarray) -> list:
+    """Instructions of encoded queues [n_cus, Q, 32] int32, up to each
+    queue's END word."""
+    out = []
+    for cu in range(queue.shape[0]):
+        for pc in range(queue.shape[1]):
+            op = int(queue[cu, pc, W_OP])
+            if op == OP_END:
+                break
+            out.append(Instr(cu, pc, op, int(queue[cu, pc, W_LAYER])))
+    return out
+
+
+def timeline(trace: np.ndarray, instrs, layer: int, op_names: dict = OP_NAMES) -> str:
     """trace: int64 [n_cus, Q, words]; instrs: decoded instructions (cu, pc,
     op, layer); op_names: opcode -> name."""
     rows = {}

@@ -1,56 +1,15 @@
-"""Helpers shared by the GPU tests: upload seeded inputs as torch device
-tensors, run one step through the C ABI, and compare with the oracle."""
+"""Helpers shared by the GPU tests: the comparison bar against the oracle.
+Device upload and the step runner live in the package (devio) and are
+re-exported here for the tests."""
 from __future__ import annotations
 
 import numpy as np
-import torch
 
-from persistent_megakernel_decode_cu_amd import Decoder
+from persistent_megakernel_decode_cu_amd.devio import (DevState, make_decoder, run_step, u16_to_dev,  # noqa: F401
+                                                       upload_model)
 
 LOGIT_TOL = 5e-2       # max |logit difference| allowed against the oracle
 TOP2_GAP = 1e-2        # greedy tokens must match where the oracle's top-2 gap exceeds this
-
-
-def u16_to_dev(a: np.ndarray) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
-
-
-def upload_model(model):
-    w = {}
-    for k, v in model.weights.items():
-        w[k] = None if v is None else u16_to_dev(v)
-    return w
-
-
-class DevState:
-    def __init__(self, st):
-        self.kv_lens = torch.from_numpy(st.kv_lens.copy()).cuda()
-        self.k_pool = u16_to_dev(st.k_pool)
-        self.v_pool = u16_to_dev(st.v_pool)
-        self.page_table = torch.from_numpy(st.page_table.copy()).cuda()
-        self.tokens = torch.from_numpy(st.tokens.copy()).cuda()
-        self.hidden_in = None if st.hidden_in is None else torch.from_numpy(st.hidden_in.copy()).cuda()
-
-
-def make_decoder(model, st, wdev, max_batch=None):
-    cfg = model.cfg
-    return Decoder(cfg, wdev, max_batch=max_batch or st.batch, max_pages_per_req=st.page_table.shape[1])
-
-
-def run_step(dec: Decoder, ds: DevState, cfg, want_logits=True, want_hidden=False):
-    B = ds.kv_lens.shape[0]
-    out = {"tokens": torch.full((B,), -1, dtype=torch.int32, device="cuda"),
-           "kv_lens": torch.zeros(B, dtype=torch.int32, device="cuda")}
-    if want_logits and cfg.has_embed:
-        out["logits"] = torch.full((B, cfg.vocab), float("nan"), dtype=torch.float32, device="cuda")
-    if want_hidden or not cfg.has_embed:
-        out["hidden"] = torch.full((B, cfg.hidden), float("nan"), dtype=torch.float32, device="cuda")
-    dec.step(kv_lens=ds.kv_lens, k_pool=ds.k_pool, v_pool=ds.v_pool, page_table=ds.page_table,
-             tokens_in=ds.tokens if cfg.has_embed else None, hidden_in=ds.hidden_in,
-             tokens_out=out["tokens"] if cfg.has_embed else None, kv_lens_out=out["kv_lens"],
-             logits_out=out.get("logits"), hidden_out=out.get("hidden"))
-    dec.sync()
-    return {k: v.cpu().numpy() for k, v in out.items()}
 
 
 def top2_gap(logits_row: np.ndarray) -> float:

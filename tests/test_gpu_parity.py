@@ -5,8 +5,8 @@ Bar: max |logit difference| <= 5e-2 and the greedy token equal wherever the
 oracle's top-2 gap exceeds 1e-2; the hidden output of the headless one-layer
 block within the same 5e-2 (with an LM head, the final residual stream only
 gets a relative sanity bound of 1e-2); appended K/V entries within one bf16
-step of the oracle's (both round the same binary32 value to nearest even,
-from differently ordered sums).
+spacing plus 1e-4 of the oracle's (both round a binary32 sum to bf16; the
+sums differ only by their order), the rest of the pools untouched.
 """
 import numpy as np
 import pytest
@@ -25,7 +25,8 @@ def inputs(name_or_cfg):
     key = cfg.name + str(cfg.cid)
     if key not in _cache:
         _cache.clear()
-        _cache[key] = (synthetic.make_model(cfg), synthetic.make_state(cfg))
+        # cache pages for a few more positions than the workload's own steps
+        _cache[key] = (synthetic.make_model(cfg), synthetic.make_state(cfg, extra_positions=max(cfg.steps, 4)))
     m, st = _cache[key]
     return cfg, m, st
 
@@ -36,18 +37,53 @@ def need_gpu():
         pytest.skip("no GPU")
 
 
-def run_compare(cfg, m, st, oracle64, mode, steps=1, check_kv=True):
+def bf16_values(u16):
+    return (u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_appended(ds, ost, cfg, before, kv_rel=0.0):
+    """The step's K/V append against the oracle's: the slot at position
+    kv_lens[b] of every layer and kv head within one bf16 spacing of the
+    oracle's entry plus 1e-4 (both round a binary32 sum to bf16, and the two
+    sums, ordered differently, differ by about 1e-6; near zero that is
+    several bf16 steps, against entries of order 1), and every other entry
+    of the device pools bit for bit what it was before the step (`before`:
+    host copies of both pools, updated here to the pools after the step).
+    `ost` is the oracle's state after its step, lengths not yet advanced.
+    kv_rel adds kv_rel times the largest oracle entry of the slot, for a path
+    whose residual stream carries a documented staging error (the relative
+    hidden-state bound, 1e-2)."""
+    T = cfg.page_tokens
+    for name, ora_pool in (("k", ost.k_pool), ("v", ost.v_pool)):
+        g = (ds.k_pool if name == "k" else ds.v_pool).cpu().numpy().view(np.uint16)
+        want_rest = before[name].copy()
+        for b in range(ost.batch):
+            p = int(ost.kv_lens[b])
+            page, slot = int(ost.page_table[b, p // T]), p % T
+            got, want = g[:, page, :, slot, :], ora_pool[:, page, :, slot, :]
+            a, w = bf16_values(got), bf16_values(want)
+            excess = np.abs(a - w) - (2.0 ** -7 * np.maximum(np.abs(a), np.abs(w)) + 1e-4 +
+                                      kv_rel * float(np.max(np.abs(w))))
+            assert np.all(excess <= 0), (f"{name} entry of request {b} at position {p}: off by "
+                                         f"{float(np.max(np.abs(a - w))):.3g} from the oracle's")
+            want_rest[:, page, :, slot, :] = got
+        assert np.array_equal(g, want_rest), f"{name} pool changed outside the appended slots"
+        before[name] = g.copy()
+
+
+def run_compare(cfg, m, st, oracle32, mode, steps=1, check_kv=True, kv_rel=0.0):
     wdev = gu.upload_model(m)
     ds = gu.DevState(st)
     dec = gu.make_decoder(m, st, wdev)
     maxlen = int(st.kv_lens.max()) + steps - 1
     dec.build_schedule(st.batch, mode=mode, max_kv_len=maxlen)
     ost = st.copy()
+    before = {"k": st.k_pool.copy(), "v": st.v_pool.copy()}
     worst = 0.0
     for s in range(steps):
         print(f"[{cfg.name} {mode}] step {s}", flush=True)
         g = gu.run_step(dec, ds, cfg, want_hidden=True)
-        o = oracle64.decode_step(m, ost, want_hidden=True)
+        o = oracle32.decode_step(m, ost, want_hidden=True)
         assert o["rc"] == 0
         if cfg.has_embed:
             diff, _ = gu.check_logits(g["logits"], o["logits"], g["tokens"], o["tokens"])
@@ -63,10 +99,7 @@ def run_compare(cfg, m, st, oracle64, mode, steps=1, check_kv=True):
             assert hd <= gu.LOGIT_TOL, f"hidden diff {hd}"
         assert np.array_equal(g["kv_lens"], ost.kv_lens + 1)
         if check_kv:
-            kp = ds.k_pool.cpu().numpy().view(np.uint16)
-            vp = ds.v_pool.cpu().numpy().view(np.uint16)
-            assert gu.bf16_ulp_diff(kp, ost.k_pool) <= 1
-            assert gu.bf16_ulp_diff(vp, ost.v_pool) <= 1
+            check_appended(ds, ost, cfg, before, kv_rel)
         # next step: the oracle's token (teacher-forced), lengths + 1
         ost.kv_lens = ost.kv_lens + 1
         if cfg.has_embed:
@@ -78,57 +111,59 @@ def run_compare(cfg, m, st, oracle64, mode, steps=1, check_kv=True):
 
 
 @pytest.mark.parametrize("mode", ["unfused", "megakernel"])
-def test_tiny_step(mode, oracle64):
+def test_tiny_step(mode, oracle32):
     cfg, m, st = inputs("tiny-2l")
-    diff = run_compare(cfg, m, st, oracle64, mode, steps=3)
+    diff = run_compare(cfg, m, st, oracle32, mode, steps=3)
     print(f"tiny {mode}: max |dlogit| = {diff:.3g}")
     assert diff < 1e-3
 
 
 @pytest.mark.parametrize("mode", ["unfused", "megakernel"])
-def test_tiny_batched_paged(mode, oracle64):
+def test_tiny_batched_paged(mode, oracle32):
     cfg = synthetic.Workload(11, "tiny-b4-paged", n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2,
                              head_dim=64, ffn=1024, vocab=4096, has_embed=True, batch=4,
                              kv_len_range=(1, 300), steps=2, paged_random=True)
     cfg, m, st = inputs(cfg)
-    run_compare(cfg, m, st, oracle64, mode, steps=2)
+    run_compare(cfg, m, st, oracle32, mode, steps=2)
 
 
 @pytest.mark.parametrize("mode", ["unfused", "megakernel"])
-def test_tiny_gqa8_first_position(mode, oracle64):
+def test_tiny_gqa8_first_position(mode, oracle32):
     """Eight query heads per kv head (two attention passes) and an empty cache
     (the new token attends to itself only)."""
     cfg = synthetic.Workload(12, "tiny-g8", n_layers=1, hidden=512, n_q_heads=8, n_kv_heads=1, head_dim=64,
                              ffn=512, vocab=1000, has_embed=True, batch=2, kv_len=0, steps=1)
     cfg, m, st = inputs(cfg)
-    run_compare(cfg, m, st, oracle64, mode)
+    run_compare(cfg, m, st, oracle32, mode)
 
 
 @pytest.mark.parametrize("mode", ["unfused", "megakernel"])
-def test_one_1b_layer(mode, oracle64):
+def test_one_1b_layer(mode, oracle32):
     cfg, m, st = inputs("1b-layer-kv512")
-    run_compare(cfg, m, st, oracle64, mode)
+    run_compare(cfg, m, st, oracle32, mode)
 
 
 @pytest.mark.parametrize("mode", ["unfused", "megakernel"])
-def test_1b_kv1024(mode, oracle64):
+def test_1b_kv1024(mode, oracle32):
     cfg, m, st = inputs("1b-kv1024")
-    diff = run_compare(cfg, m, st, oracle64, mode, steps=2, check_kv=False)
+    diff = run_compare(cfg, m, st, oracle32, mode, steps=2)
     print(f"1b-kv1024 {mode}: max |dlogit| = {diff:.3g}")
 
 
 @pytest.mark.parametrize("mode", ["unfused", "megakernel"])
-def test_1b_kv8192(mode, oracle64):
+def test_1b_kv8192(mode, oracle32):
     cfg, m, st = inputs("1b-kv8192")
-    run_compare(cfg, m, st, oracle64, mode, check_kv=False)
+    run_compare(cfg, m, st, oracle32, mode)
 
 
 @pytest.mark.parametrize("mode", ["unfused", "megakernel"])
-def test_1b_batch8_paged(mode, oracle64):
+def test_1b_batch8_paged(mode, oracle32):
     # eight requests of lengths 128-4096 in shuffled 16-token pages; the
     # megakernel stages the down projection's input as binary16 at this batch
     cfg, m, st = inputs("1b-b8-paged")
-    diff = run_compare(cfg, m, st, oracle64, mode, check_kv=False)
+    # the binary16 staging of the down input at batch 8 perturbs every later
+    # layer's residual stream (relative ~1e-3), and with it the appended K/V
+    diff = run_compare(cfg, m, st, oracle32, mode, steps=2, kv_rel=1e-2 if mode == "megakernel" else 0.0)
     print(f"1b batch 8 {mode}: max |dlogit| = {diff:.3g}")
 
 
@@ -171,3 +206,45 @@ def test_megakernel_equals_unfused_bitwise_1b_layer():
     k = _outputs(cfg, m, st, wdev, "megakernel")
     for key in ("kv_lens", "hidden", "k_pool", "v_pool"):
         assert np.array_equal(u[key].view(np.uint8), k[key].view(np.uint8)), key
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+@pytest.mark.parametrize("mode", ["unfused", "megakernel"])
+def test_argmax_ties_take_the_lowest_index(mode, batch, oracle32):
+    """Exact ties in the LM head. With Wo = Wdown = 0 the residual stream
+    stays the token's embedding row E[t], so row t has the largest logit
+    (|E_t|^2 / rms(E_t) against roughly N(0, 0.3) elsewhere), and copies of
+    row t placed below and above it score bit for bit the same (each row's
+    dot product runs the same operations in the same order). The greedy
+    token must be the lowest index of the tied rows, as the oracle picks it;
+    the copies sit on different compute units and waves of the LM head."""
+    cfg = synthetic.Workload(13, "tiny-ties", n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                             ffn=1024, vocab=4096, has_embed=True, batch=batch, kv_len_range=(3, 90), steps=1,
+                             paged_random=True)
+    m = synthetic.make_model(cfg)
+    st = synthetic.make_state(cfg, extra_positions=2)
+    m.weights["wo"][:] = 0
+    m.weights["w_down"][:] = 0
+    E = m.weights["embed"]
+    toks = [int(t) for t in st.tokens]
+    expect = []
+    for b, t in enumerate(toks):
+        rows = [r for r in (5 + b, 1031 + 17 * b, 2600 + b, 4090 + b) if r not in toks]
+        for r in rows:
+            E[r] = E[t]
+        expect.append(min(rows + [t]))
+    wdev = gu.upload_model(m)
+    ds = gu.DevState(st)
+    dec = gu.make_decoder(m, st, wdev)
+    dec.build_schedule(batch, mode=mode, max_kv_len=int(st.kv_lens.max()))
+    g = gu.run_step(dec, ds, cfg)
+    dec.close()
+    o = oracle32.decode_step(m, st.copy())
+    assert o["rc"] == 0
+    assert [int(x) for x in o["tokens"]] == expect
+    for b in range(batch):
+        tied = [r for r in range(cfg.vocab) if np.array_equal(E[r], E[toks[b]])]
+        vals = g["logits"][b, tied]
+        assert np.all(vals.view(np.uint32) == vals[0:1].view(np.uint32)), f"tied logits differ: {vals}"
+        assert float(vals[0]) == float(np.max(g["logits"][b]))
+    assert [int(x) for x in g["tokens"]] == expect, (g["tokens"], expect)

@@ -405,6 +405,155 @@ def test_mlp_block_closed_form(oracle64):
     assert np.allclose(r["hidden"][0], ref, rtol=1e-12, atol=1e-12)
 
 
+def _complex_rope(v, pos, theta):
+    """Rotate-half RoPE written as complex multiplication: element i < d/2
+    pairs with i + d/2 as the complex number v_i + 1j v_(i+d/2), turned by
+    the angle pos * theta^(-2i/d). v: [heads, d] float64."""
+    d = v.shape[-1]
+    half = d // 2
+    z = v[..., :half] + 1j * v[..., half:]
+    ang = pos * theta ** (-2.0 * np.arange(half) / d)
+    z = z * np.exp(1j * ang)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def _pool_rows(st, l, b, g, n, T):
+    """K and V rows 0..n-1 of request b, kv head g, layer l, read through the
+    page table, as float64 [n, d]."""
+    pr = st.page_table[b]
+    K = np.stack([bf16_to_f64(st.k_pool[l, pr[j // T], g, j % T]) for j in range(n)])
+    V = np.stack([bf16_to_f64(st.v_pool[l, pr[j // T], g, j % T]) for j in range(n)])
+    return K, V
+
+
+def _attention_block_ref(m, st_after, l, x, p, cfg):
+    """x + Wo . attention for layer l at position p, in float64, from the
+    cache as it stands after the step (the new entry included): scores of
+    R(p) q_h against the stored keys, softmax over positions 0..p (library
+    routine), weights times the stored values."""
+    H, nq, nkv, d = cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    G = nq // nkv
+    wn = bf16_to_f64(m.weights["attn_norm"][l])
+    u = x / math.sqrt(np.mean(x * x) + cfg.rms_eps) * wn
+    qkv = bf16_to_f64(m.weights["wqkv"][l]) @ u
+    q = _complex_rope(qkv[:nq * d].reshape(nq, d), p, cfg.rope_theta)
+    o = np.empty((nq, d))
+    for h in range(nq):
+        K, V = _pool_rows(st_after, l, 0, h // G, p + 1, cfg.page_tokens)
+        o[h] = scipy.special.softmax(K @ q[h] / math.sqrt(d)) @ V
+    return x + bf16_to_f64(m.weights["wo"][l]) @ o.reshape(-1), qkv
+
+
+def _mlp_block_ref(m, l, x, cfg):
+    wn = bf16_to_f64(m.weights["mlp_norm"][l])
+    u = x / math.sqrt(np.mean(x * x) + cfg.rms_eps) * wn
+    g = bf16_to_f64(m.weights["w_gate"][l]) @ u
+    up = bf16_to_f64(m.weights["w_up"][l]) @ u
+    return x + bf16_to_f64(m.weights["w_down"][l]) @ (g * scipy.special.expit(g) * up)
+
+
+def _appended_ok(got_u16, want_f64, prec):
+    """The appended bf16 entry against bf16-RNE of the float64 reference:
+    exact for the double build; within one bf16 step for the single build,
+    whose own rounding of the sum may land on the other side of a halfway
+    point."""
+    want = torch_bf16_rne(want_f64.astype(np.float32))
+    if prec == "f64":
+        return np.array_equal(got_u16, want)
+    k = lambda a: np.where(a.astype(np.int32) & 0x8000, -(a.astype(np.int32) & 0x7fff), a.astype(np.int32))
+    return int(np.max(np.abs(k(got_u16) - k(want)))) <= 1
+
+
+def _randomise_norms(m, seed):
+    """Distinct norm weights per layer (bf16 in [0.5, 1.5)), so that a layer
+    reading another layer's norm weight gives another result."""
+    rng = np.random.default_rng(seed)
+    for key in ("attn_norm", "mlp_norm"):
+        w = m.weights[key]
+        w[:] = torch_bf16_rne(rng.uniform(0.5, 1.5, size=w.shape).astype(np.float32))
+
+
+@pytest.mark.parametrize("prec", ["f64", "f32"])
+def test_step_rope_at_later_position(prec, oracle64, oracle32):
+    """At position p > 0 inside a full step: the appended key is
+    bf16(R(p) Wk u) and the value bf16(Wv u), with R(p) written as complex
+    rotations; with Wdown = 0 the layer's output is x + Wo . softmax(R(p) q .
+    K^T / 8) V over the stored cache, all in float64. Rotating q or k at the
+    wrong position, or storing an unrotated key, fails it."""
+    ora = oracle64 if prec == "f64" else oracle32
+    cfg = small_cfg(has_embed=False, vocab=0, kv_len=37, n_layers=1, head_dim=16, hidden=64,
+                    page_tokens=4, cid=105, paged_random=True)
+    m, st = _fresh(cfg)
+    m.weights["w_down"][:] = 0
+    _randomise_norms(m, 5)
+    p = int(st.kv_lens[0])
+    x = st.hidden_in[0].astype(np.float64)
+    r = ora.decode_step(m, st, want_hidden=True)
+    assert r["rc"] == 0
+    ref, qkv = _attention_block_ref(m, st, 0, x, p, cfg)
+    nq, nkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    k_new = _complex_rope(qkv[nq * d:(nq + nkv) * d].reshape(nkv, d), p, cfg.rope_theta).reshape(-1)
+    v_new = qkv[(nq + nkv) * d:]
+    pr = st.page_table[0]
+    got_k = st.k_pool[0, pr[p // 4], :, p % 4, :].reshape(-1)
+    got_v = st.v_pool[0, pr[p // 4], :, p % 4, :].reshape(-1)
+    assert _appended_ok(got_k, k_new, prec)
+    assert _appended_ok(got_v, v_new, prec)
+    tol = 1e-12 if prec == "f64" else 2e-5
+    assert np.allclose(r["hidden"][0], ref, rtol=tol, atol=tol)
+
+
+@pytest.mark.parametrize("prec", ["f64", "f32"])
+def test_two_layers_each_read_their_own_weights_and_cache(prec, oracle64, oracle32):
+    """Two layers with distinct weights, norm weights and cache contents.
+    Layer 0 keeps only its attention block's cache append (Wo = Wdown = 0),
+    layer 1 only its attention block (Wdown = 0): the output is
+    x + Wo1 . attention1(x) with layer 1's weights over layer 1's cache, and
+    both layers' appended entries are checked. A step that reads layer 0's
+    weights or pool for layer 1 fails it."""
+    ora = oracle64 if prec == "f64" else oracle32
+    cfg = small_cfg(has_embed=False, vocab=0, kv_len=22, n_layers=2, head_dim=16, hidden=64,
+                    page_tokens=4, cid=106, paged_random=True)
+    m, st = _fresh(cfg)
+    m.weights["wo"][0] = 0
+    m.weights["w_down"][:] = 0
+    _randomise_norms(m, 6)
+    p = int(st.kv_lens[0])
+    x = st.hidden_in[0].astype(np.float64)
+    r = ora.decode_step(m, st, want_hidden=True)
+    assert r["rc"] == 0
+    ref, qkv1 = _attention_block_ref(m, st, 1, x, p, cfg)
+    nq, nkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    pr = st.page_table[0]
+    for l in range(2):
+        wn = bf16_to_f64(m.weights["attn_norm"][l])
+        u = x / math.sqrt(np.mean(x * x) + cfg.rms_eps) * wn
+        qkv = bf16_to_f64(m.weights["wqkv"][l]) @ u
+        k_new = _complex_rope(qkv[nq * d:(nq + nkv) * d].reshape(nkv, d), p, cfg.rope_theta).reshape(-1)
+        assert _appended_ok(st.k_pool[l, pr[p // 4], :, p % 4, :].reshape(-1), k_new, prec), l
+        assert _appended_ok(st.v_pool[l, pr[p // 4], :, p % 4, :].reshape(-1), qkv[(nq + nkv) * d:], prec), l
+    tol = 1e-12 if prec == "f64" else 2e-5
+    assert np.allclose(r["hidden"][0], ref, rtol=tol, atol=tol)
+
+
+@pytest.mark.parametrize("prec", ["f64", "f32"])
+def test_two_layer_mlp_chain_closed_form(prec, oracle64, oracle32):
+    """With Wo = 0 in both layers, two layers are two MLP blocks in a row,
+    each with its own norm weight and matrices: x2 = m1(m0(x)), m_l(x) =
+    x + Wdown_l (silu(Wgate_l u) * (Wup_l u)), u = rmsnorm(x) * w_l."""
+    ora = oracle64 if prec == "f64" else oracle32
+    cfg = small_cfg(has_embed=False, vocab=0, kv_len=9, n_layers=2, cid=107)
+    m, st = _fresh(cfg)
+    m.weights["wo"][:] = 0
+    _randomise_norms(m, 7)
+    x = st.hidden_in[0].astype(np.float64)
+    r = ora.decode_step(m, st, want_hidden=True)
+    assert r["rc"] == 0
+    ref = _mlp_block_ref(m, 1, _mlp_block_ref(m, 0, x, cfg), cfg)
+    tol = 1e-12 if prec == "f64" else 2e-5
+    assert np.allclose(r["hidden"][0], ref, rtol=tol, atol=tol)
+
+
 def test_batch_requests_are_independent(oracle64):
     cfg = small_cfg(batch=3, kv_len_range=(2, 11), paged_random=True, n_layers=2, cid=102)
     m, st = _fresh(cfg)

@@ -126,3 +126,13 @@ def test_validator_catches_a_coverage_gap():
                     sched_check.validate(w, B, q, p.events, p.info.attn_chunks, maxlen)
                 return
     pytest.fail("no DOWN instruction with two rows")
+
+
+def test_trace_decoder_follows_the_queue_encoding():
+    """The package's queue decoder (used by the benchmark's trace timeline)
+    reads the words and opcodes mk_isa.h defines."""
+    from persistent_megakernel_decode_cu_amd import trace_summary as ts
+    from tests.sched_check import ISA
+    assert (ts.W_OP, ts.W_LAYER, ts.OP_END) == (ISA["W_OP"], ISA["W_LAYER"], ISA["OP_END"])
+    ops = {v: k[3:] for k, v in ISA.items() if k.startswith("OP_") and k not in ("OP_END", "OP_COUNT")}
+    assert ts.OP_NAMES == ops
