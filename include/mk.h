@@ -162,6 +162,25 @@ int mk_build_schedule(mk_handle *h, const mk_schedule_desc *s);
  * needs mk_build_schedule before the next step. */
 int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream);
 
+/* mk_decode_step for callers that cannot allocate device memory at the call
+ * or around it (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). It runs the same resident interpreter, but the
+ * step's exchange words and counters live in a file-scope device array of
+ * MK_STATIC_SCRATCH_BYTES (64 MiB) per device, which the library sets up in
+ * mk_create and holds until the process ends; the call itself allocates and
+ * frees nothing. Every call on a device shares that array and keeps the last
+ * call's contents: each call first clears the part its schedule uses (on
+ * `stream`, with a fill kernel), so calls that overlap on one device race
+ * and must be ordered by the caller (one stream, or events). The handle's
+ * own exchange buffers and step tag are untouched, so the handle also stays
+ * valid for mk_decode_step. Arguments, layouts and sticky errors as
+ * mk_decode_step. Errors: MK_ENOSCHED; MK_EINVAL (also: the schedule is not
+ * MK_MODE_MEGAKERNEL); MK_ECAPACITY when the schedule's exchange buffers
+ * exceed MK_STATIC_SCRATCH_BYTES (the 16-layer 1B shape needs about 4.4 MB
+ * at batch 1 and 35 MB at batch 8); MK_EHIP. */
+#define MK_STATIC_SCRATCH_BYTES (64u << 20)
+int mk_decode_step_static(mk_handle *h, const mk_step_io *io, void *stream);
+
 /* Ends the lifetimes the object table of the "principle, schedule and
  * dataflow" section gives to what a binding owns: the queue and counters
  * (the resident kernel's and the dependency intervals' objects) and the

@@ -16,6 +16,7 @@ from typing import Mapping, Optional
 from . import _mk
 from ._mk import (MK_MODE_MEGAKERNEL, MK_MODE_UNFUSED, MkConfig, MkError, MkLayerWeights,  # noqa: F401
                   MkScheduleDesc, MkStepIO, MkWeights, Plan, mk_build_schedule, mk_create, mk_decode_step,
+                  mk_decode_step_static,
                   mk_destroy, mk_get_schedule_info, mk_last_error, mk_read_trace, mk_sync_status)
 
 _MODES = {"megakernel": MK_MODE_MEGAKERNEL, "unfused": MK_MODE_UNFUSED}
@@ -92,7 +93,10 @@ class Decoder:
         return self.info()
 
     def step(self, *, kv_lens, k_pool, v_pool, page_table, tokens_in=None, hidden_in=None, tokens_out=None,
-             kv_lens_out=None, logits_out=None, hidden_out=None, stream: Optional[int] = None) -> None:
+             kv_lens_out=None, logits_out=None, hidden_out=None, stream: Optional[int] = None,
+             static_scratch: bool = False) -> None:
+        """One step (mk_decode_step), or with ``static_scratch`` the
+        allocation-free mk_decode_step_static."""
         import torch
         s = self.shape
         B = self.batch
@@ -106,7 +110,7 @@ class Decoder:
             _ptr(logits_out, "logits_out", 4, (B, s.vocab)), _ptr(hidden_out, "hidden_out", 4, (B, s.hidden)))
         if stream is None:
             stream = torch.cuda.current_stream().cuda_stream
-        mk_decode_step(self.handle, io, stream)
+        (mk_decode_step_static if static_scratch else mk_decode_step)(self.handle, io, stream)
 
     def sync(self, stream: Optional[int] = None) -> None:
         import torch

@@ -74,6 +74,7 @@ _SIGS = {
     "mk_create": (i32, [ctypes.POINTER(MkConfig), ctypes.POINTER(MkWeights), ctypes.POINTER(vp)]),
     "mk_build_schedule": (i32, [vp, ctypes.POINTER(MkScheduleDesc)]),
     "mk_decode_step": (i32, [vp, ctypes.POINTER(MkStepIO), vp]),
+    "mk_decode_step_static": (i32, [vp, ctypes.POINTER(MkStepIO), vp]),
     "mk_destroy": (None, [vp]),
     "mk_last_error": (ctypes.c_char_p, []),
     "mk_sync_status": (i32, [vp, vp]),
@@ -130,6 +131,10 @@ def mk_build_schedule(handle: int, desc: MkScheduleDesc) -> None:
 
 def mk_decode_step(handle: int, io: MkStepIO, stream: int = 0) -> None:
     _check(lib().mk_decode_step(handle, ctypes.byref(io), stream))
+
+
+def mk_decode_step_static(handle: int, io: MkStepIO, stream: int = 0) -> None:
+    _check(lib().mk_decode_step_static(handle, ctypes.byref(io), stream))
 
 
 def mk_destroy(handle: int) -> None:

@@ -155,6 +155,43 @@ static void bind_operands(const mk_handle *h, mk::Plan &plan) {
     }
 }
 
+// Where mk_decode_step_static puts a schedule's exchange words and counters
+// inside the device's static scratch: the same buffers mk_build_schedule
+// allocates for the resident interpreter, each 256-byte aligned.
+struct StaticLayout {
+    char *base;
+    size_t bytes;  // used, from base
+    uint64_t *tx, *tqkv, *to, *tact, *tpart, *tlm;
+    int32_t *counters;
+};
+
+static int static_layout(const mk_handle *h, char *base, StaticLayout *sl) {
+    const mk_config &c = h->cfg;
+    const mk::Plan &P = h->plan;
+    const size_t B = (size_t)P.desc.batch, L = (size_t)c.n_layers, G = (size_t)(c.n_q_heads / c.n_kv_heads);
+    const size_t QKV = (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim, QD = (size_t)c.n_q_heads * c.head_dim;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char *p = base + off;
+        off += (bytes + 255) / 256 * 256;
+        return p;
+    };
+    sl->base = base;
+    sl->tx = (uint64_t *)take(2 * L * B * c.hidden * 8);
+    sl->tqkv = (uint64_t *)take(L * B * QKV * 8);
+    sl->to = (uint64_t *)take(L * B * QD * 8);
+    sl->tact = (uint64_t *)take(L * B * c.ffn * 8);
+    sl->tpart = (uint64_t *)take(L * B * c.n_kv_heads * P.attn_chunks * G * mk::ATTN_PART * 8);
+    sl->tlm = (uint64_t *)take((size_t)std::max(P.n_lm_slots, 1) * B * 2 * 8);
+    sl->counters = (int32_t *)take((size_t)(P.n_counters + 1) * mk::CTR_STRIDE * 4);
+    sl->bytes = off;
+    if (off > mk::STATIC_SCRATCH_BYTES)
+        return set_error(MK_ECAPACITY, "this schedule's exchange buffers need " + std::to_string(off) +
+                                           " bytes; the static scratch holds " +
+                                           std::to_string(mk::STATIC_SCRATCH_BYTES));
+    return MK_OK;
+}
+
 extern "C" {
 
 const char *mk_last_error(void) { return mk::g_last_error.c_str(); }
@@ -179,6 +216,9 @@ int mk_create(const mk_config *cfg, const mk_weights *w, mk_handle **out) {
         MK_HIP(hipGetDeviceProperties(&prop, cfg->device));
         if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
             return set_error(MK_EINVAL, std::string("built for gfx950, device is ") + prop.gcnArchName);
+        // the device's static scratch (mk_decode_step_static): its address,
+        // looked up once per device with the device current
+        MK_HIP(mk::static_scratch_setup(cfg->device));
 
         mk_handle *h = new (std::nothrow) mk_handle();
         if (!h) return set_error(MK_EINVAL, "out of host memory");
@@ -300,7 +340,7 @@ int mk_build_schedule(mk_handle *h, const mk_schedule_desc *s) {
     }
 }
 
-int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream) {
+static int decode_step(mk_handle *h, const mk_step_io *io, void *stream, const StaticLayout *sl) {
     try {
         if (!h || !io) return set_error(MK_EINVAL, "null argument");
         if (!h->built) return set_error(MK_ENOSCHED, "mk_decode_step before mk_build_schedule");
@@ -319,19 +359,29 @@ int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream) {
         if (io->n_pages < 1) return set_error(MK_EINVAL, "n_pages must be positive");
         hipStream_t st = (hipStream_t)stream;
         const mk::Plan &P = h->plan;
-        // epoch-based counters: re-zero before the int32 counts could wrap
-        if ((h->epoch + 1) * (int64_t)h->max_need >= ((int64_t)1 << 30)) {
-            MK_HIP(mk::fill_u32((uint32_t *)h->counters, (size_t)(P.n_counters + 1) * mk::CTR_STRIDE, 0u, st));
-            h->epoch = 0;
-        }
-        h->epoch++;
-        if (++h->tag == 0) h->tag = 1;  // the buffers start at tag 0, which no step uses
         mk::KParams k{};
-        k.epoch = (int32_t)h->epoch;
-        k.tag = h->tag;
+        if (sl) {
+            // the static scratch keeps whatever the last call on this device
+            // left there: clear the part this schedule uses (a fill kernel,
+            // which a captured graph replays correctly), then run as the first
+            // step on cleared buffers
+            MK_HIP(mk::fill_u32((uint32_t *)sl->base, sl->bytes / 4, 0u, st));
+            k.epoch = 1;
+            k.tag = 1;
+        } else {
+            // epoch-based counters: re-zero before the int32 counts could wrap
+            if ((h->epoch + 1) * (int64_t)h->max_need >= ((int64_t)1 << 30)) {
+                MK_HIP(mk::fill_u32((uint32_t *)h->counters, (size_t)(P.n_counters + 1) * mk::CTR_STRIDE, 0u, st));
+                h->epoch = 0;
+            }
+            h->epoch++;
+            if (++h->tag == 0) h->tag = 1;  // the buffers start at tag 0, which no step uses
+            k.epoch = (int32_t)h->epoch;
+            k.tag = h->tag;
+        }
         k.queue = h->queue;
         k.events = h->events;
-        k.counters = h->counters;
+        k.counters = sl ? sl->counters : h->counters;
         k.start_ctr = P.n_counters;
         k.Q = P.Q;
         k.n_cus = P.n_cus;
@@ -375,12 +425,12 @@ int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream) {
         k.act = h->act;
         k.attn_part = h->attn_part;
         k.lm_part = h->lm_part;
-        k.tx = h->tx;
-        k.tqkv = h->tqkv;
-        k.to = h->to;
-        k.tact = h->tact;
-        k.tpart = h->tpart;
-        k.tlm = h->tlm;
+        k.tx = sl ? sl->tx : h->tx;
+        k.tqkv = sl ? sl->tqkv : h->tqkv;
+        k.to = sl ? sl->to : h->to;
+        k.tact = sl ? sl->tact : h->tact;
+        k.tpart = sl ? sl->tpart : h->tpart;
+        k.tlm = sl ? sl->tlm : h->tlm;
         k.attn_chunks = P.attn_chunks;
         k.err = h->err;
         k.host_err = h->host_err_dev;
@@ -394,7 +444,26 @@ int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream) {
         if (e != hipSuccess) return set_error(MK_EHIP, std::string("launch failed: ") + hipGetErrorString(e));
         return MK_OK;
     } catch (...) {
-        return set_error(MK_EINVAL, "internal error in mk_decode_step");
+        return set_error(MK_EINVAL, "internal error in a decode step");
+    }
+}
+
+int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream) { return decode_step(h, io, stream, nullptr); }
+
+int mk_decode_step_static(mk_handle *h, const mk_step_io *io, void *stream) {
+    try {
+        if (!h || !io) return set_error(MK_EINVAL, "null argument");
+        if (!h->built) return set_error(MK_ENOSCHED, "mk_decode_step_static before mk_build_schedule");
+        if (h->plan.desc.mode != MK_MODE_MEGAKERNEL)
+            return set_error(MK_EINVAL, "mk_decode_step_static runs the resident interpreter: build the schedule "
+                                        "in MK_MODE_MEGAKERNEL");
+        void *base = mk::static_scratch(h->cfg.device);
+        if (!base) return set_error(MK_EHIP, "the static scratch of this device was not set up by mk_create");
+        StaticLayout sl{};
+        if (int rc = static_layout(h, (char *)base, &sl)) return rc;
+        return decode_step(h, io, stream, &sl);
+    } catch (...) {
+        return set_error(MK_EINVAL, "internal error in mk_decode_step_static");
     }
 }
 

@@ -61,6 +61,10 @@ constexpr int ATTN_PART_STRIDE = 68;
 bool megakernel_supports(int B, int G);
 hipError_t fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t s);
 hipError_t launch_megakernel(const KParams &p, int lds_bytes, hipStream_t s);
+// The file-scope device array behind mk_decode_step_static, one per device.
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)64 << 20;  // MK_STATIC_SCRATCH_BYTES of mk.h
+hipError_t static_scratch_setup(int device);  // with `device` current; once per device
+void *static_scratch(int device);             // its device address, or null before set-up
 hipError_t setup_megakernel(int B, int G, int lds_bytes);
 hipError_t megakernel_occupancy(int B, int G, int lds_bytes, int *blocks_per_cu);
 hipError_t launch_unfused(const KParams &p, float *u_scratch, float *qrot, hipStream_t s);

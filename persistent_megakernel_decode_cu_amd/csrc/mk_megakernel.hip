@@ -3,6 +3,7 @@
 // checks co-residency and launches it cooperatively. The device code is in
 // mk_interp.h, instantiated by mk_interp_b{1,2,4,8}.hip.
 #include <algorithm>
+#include <mutex>
 
 #include "mk_device.h"
 
@@ -12,6 +13,39 @@ const void *interp_kernel_b1(int G);
 const void *interp_kernel_b2(int G);
 const void *interp_kernel_b4(int G);
 const void *interp_kernel_b8(int G);
+
+// Scratch for callers that cannot allocate (mk_decode_step_static): the
+// exchange words and counters of one step in a file-scope device array, one
+// copy per device, alive until the process ends and shared by every such
+// call on that device. Host code never passes the array's name to a kernel
+// (on the host it is only a stand-in): static_scratch_setup looks its device
+// address up once per device and static_scratch returns that address.
+static __device__ __align__(256) uint64_t scratch[STATIC_SCRATCH_BYTES / 8];
+
+namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};
+
+}  // namespace
+
+hipError_t static_scratch_setup(int device) {
+    if (device < 0 || device >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[device]) return hipSuccess;
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[device] = p;
+    return hipSuccess;
+}
+
+void *static_scratch(int device) {
+    if (device < 0 || device >= MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    return g_scratch_ptr[device];
+}
 
 namespace {
 
