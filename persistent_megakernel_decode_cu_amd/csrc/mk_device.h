@@ -203,9 +203,9 @@ __device__ __forceinline__ float wave_max(float v) {
 // in rounds of up to N_COMPUTE_WAVES blocks, one block per wave:
 //  1. each wave holding a block writes, for the G query heads of the group,
 //     the 16 scaled scores q_h . K_t / sqrt(64) into S[h][16 w + t] (-inf at
-//     positions past the new one) and the block's values into V[16 w + t][64]
-//     (bf16, zero past the new position: a missing position may hold any bit
-//     pattern);
+//     positions past the new one) and the block's values, transposed, into
+//     V[d][16 w + t] (bf16, zero past the new position: a missing position
+//     may hold any bit pattern);
 //  2. after a barrier, wave h < G folds the round into its running state of
 //     head h, lane = dim: M = max(M, max_t S), every state scaled by
 //     exp(M_old - M), L += sum_t exp(S - M), O += sum_t exp(S - M) V[t]
@@ -214,7 +214,8 @@ __device__ __forceinline__ float wave_max(float v) {
 // lane layout of a block follows the K/V page: lane l holds the 16-byte chunk
 // l of K and of V, i.e. dims 8 (l % 8) .. + 7 of positions l / 8 (t0) and
 // 8 + l / 8 (t1); a score is summed over the 8 lanes sharing a position.
-// (ATTN_ROUND_POS and the area's size attn_round_floats are in mk_isa.h)
+// (ATTN_ROUND_POS, ATTN_V_STRIDE and the area's size attn_round_floats are in
+// mk_isa.h)
 
 struct AttnRun {
     float O, M, L;  // head wave: running state of its head (lane = dim)
@@ -237,8 +238,17 @@ __device__ __forceinline__ void attn_block_write(const MK_LDS float *q, MK_LDS f
     MK_LDS float *S = area;
     MK_LDS uint16_t *V = (MK_LDS uint16_t *)(area + G * ATTN_ROUND_POS);
     const int j0 = ws * 16 + t0;
-    *(MK_LDS v4u *)(V + j0 * 64 + dd) = ok0 ? v0 : v4u{0u, 0u, 0u, 0u};
-    *(MK_LDS v4u *)(V + (j0 + 8) * 64 + dd) = ok1 ? v1 : v4u{0u, 0u, 0u, 0u};
+    if (!ok0) v0 = v4u{0u, 0u, 0u, 0u};
+    if (!ok1) v1 = v4u{0u, 0u, 0u, 0u};
+    const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w}, w1[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        MK_LDS uint16_t *row = V + (dd + 2 * e) * ATTN_V_STRIDE;
+        row[j0] = (uint16_t)(w0[e] & 0xffffu);
+        row[ATTN_V_STRIDE + j0] = (uint16_t)(w0[e] >> 16);
+        row[j0 + 8] = (uint16_t)(w1[e] & 0xffffu);
+        row[ATTN_V_STRIDE + j0 + 8] = (uint16_t)(w1[e] >> 16);
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         const v4f qa = *(const MK_LDS v4f *)(q + h * 64 + dd);
@@ -254,7 +264,8 @@ __device__ __forceinline__ void attn_block_write(const MK_LDS float *q, MK_LDS f
 
 // Step 2 for head h over the round's first npos positions (a multiple of
 // 16): each lane turns its positions' scores into weights exp(S - M) in
-// place, and the weights are then read back by every lane.
+// place; then lane d reads eight weights (the same for every lane) and the
+// eight values of its dim per step, in position order.
 __device__ __forceinline__ void attn_round_fold(MK_LDS float *S_h, const MK_LDS uint16_t *V, int npos, int lane,
                                                 AttnRun &r) {
     float mx = -INFINITY;
@@ -268,12 +279,20 @@ __device__ __forceinline__ void attn_round_fold(MK_LDS float *S_h, const MK_LDS 
         ls += e;
     }
     float o = r.O * scale;
-    for (int j = 0; j < npos; j += 4) {
-        const v4f p4 = *(const MK_LDS v4f *)(S_h + j);
-        o = fmaf(p4.x, bf2f(V[(j + 0) * 64 + lane]), o);
-        o = fmaf(p4.y, bf2f(V[(j + 1) * 64 + lane]), o);
-        o = fmaf(p4.z, bf2f(V[(j + 2) * 64 + lane]), o);
-        o = fmaf(p4.w, bf2f(V[(j + 3) * 64 + lane]), o);
+    const MK_LDS uint16_t *vrow = V + lane * ATTN_V_STRIDE;
+#pragma unroll 2
+    for (int j = 0; j < npos; j += 8) {
+        const v4f pa = *(const MK_LDS v4f *)(S_h + j);
+        const v4f pb = *(const MK_LDS v4f *)(S_h + j + 4);
+        const v4u v = *(const MK_LDS v4u *)(vrow + j);
+        o = fmaf(pa.x, bf_lo(v.x), o);
+        o = fmaf(pa.y, bf_hi(v.x), o);
+        o = fmaf(pa.z, bf_lo(v.y), o);
+        o = fmaf(pa.w, bf_hi(v.y), o);
+        o = fmaf(pb.x, bf_lo(v.z), o);
+        o = fmaf(pb.y, bf_hi(v.z), o);
+        o = fmaf(pb.z, bf_lo(v.w), o);
+        o = fmaf(pb.w, bf_hi(v.w), o);
     }
     r.L = fmaf(r.L, scale, wave_sum(ls));
     r.O = o;

@@ -1332,31 +1332,32 @@ __device__ __forceinline__ void run(const KParams &P, Ctx &c) {
         cur_next(P, c, ic);
     }
     Ins in{};
-    Acc<NB> acc;
-    RegAct ra;
-    bool first = true;
     int slot = 0;
-    for (;;) {
-        if (!first && !uni(leave<NB, G>(P, c, in, acc))) break;
-        first = false;
-        if (cc.op == OP_END) break;
+    while (uni(cc.op != OP_END)) {
+        // per-instruction accumulators and register activations: nothing of
+        // them lives from one instruction to the next (an attention tile never
+        // holds a matvec's registers). The record `in` stays outside, which
+        // keeps the compiler's view of the cursors uniform.
+        Acc<NB> acc;
+        RegAct ra;
         if (!uni(enter<NB, G>(P, c, cc, in, acc, ra))) break;
         if (cc.op == OP_ATTN) {
             if (!uni(attn_tile<G>(P, c, ic, cc, in, slot))) break;
-            continue;
+        } else {
+            for (;;) {
+                v4u buf[4];
+                take_any(slot, buf);
+                const bool empty = cc.u >= cc.nu;
+                if (!empty) consume_mv<NB>(P, c, cc, in, buf, acc, ra);
+                const bool last = empty || (cc.s == cc.sp - 1 && cc.u + NC >= cc.nu);
+                issue_any(slot, P, ic, c.lane);
+                cur_next(P, c, ic);
+                cur_next(P, c, cc);
+                slot = slot + 1 == D ? 0 : slot + 1;
+                if (uni(last)) break;
+            }
         }
-        for (;;) {
-            v4u buf[4];
-            take_any(slot, buf);
-            const bool empty = cc.u >= cc.nu;
-            if (!empty) consume_mv<NB>(P, c, cc, in, buf, acc, ra);
-            const bool last = empty || (cc.s == cc.sp - 1 && cc.u + NC >= cc.nu);
-            issue_any(slot, P, ic, c.lane);
-            cur_next(P, c, ic);
-            cur_next(P, c, cc);
-            slot = slot + 1 == D ? 0 : slot + 1;
-            if (uni(last)) break;
-        }
+        if (!uni(leave<NB, G>(P, c, in, acc))) break;
     }
     // no load may still be writing a slot register when the wave ends
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
