@@ -77,13 +77,25 @@ __device__ __forceinline__ uint32_t lds_add(MK_LDS uint32_t *p, uint32_t v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// The lane's index, recomputed where it is used by an opaque two-instruction
+// sequence the compiler neither hoists nor merges: lane-derived addresses are
+// then rebuilt next to their use instead of living across the whole kernel,
+// where register pressure spills them and each reload waits behind every
+// weight slice in flight.
+__device__ __forceinline__ int lane_id() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 struct Ctx {
     MK_LDS uint32_t *misc;
     const MK_LDS int32_t *q;  // this CU's queue, LDS_INSTR_WORDS words per instruction
     MK_LDS float *act;   // matvec inputs of all requests, or the attention staging
     MK_LDS float *xrow;  // residual rows of the instruction (O projection, down projection)
-    int cu, lane, w;
+    int cu, w;
     uint32_t nbar;
+    __device__ __forceinline__ int lane() const { return lane_id(); }
     uint32_t tag;        // copies of kernel arguments the helpers need: taking
     int64_t watchdog;    // the argument block's address would move it to
     int32_t *err;        // private memory
@@ -126,7 +138,7 @@ __device__ __forceinline__ bool lds_wait_ge(Ctx &c, MK_LDS uint32_t *p, uint32_t
 // barrier of the workgroup's waves (one arrival per wave)
 __device__ __forceinline__ bool cbar(Ctx &c, int pc) {
     c.nbar++;
-    if (c.lane == 0) lds_add(c.misc + M_ARRIVE, 1u);
+    if (c.lane() == 0) lds_add(c.misc + M_ARRIVE, 1u);
     return lds_wait_ge(c, c.misc + M_ARRIVE, (uint32_t)NC * c.nbar, pc);
 }
 
@@ -139,7 +151,7 @@ __device__ __forceinline__ bool cbar(Ctx &c, int pc) {
 __device__ __forceinline__ bool lbar(Ctx &c, int pc) {
     c.nbar++;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    if (c.lane == 0)
+    if (c.lane() == 0)
         __hip_atomic_fetch_add(c.misc + M_ARRIVE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     const uint32_t target = __builtin_amdgcn_readfirstlane((uint32_t)NC * c.nbar);
     int64_t spins = 0;
@@ -238,7 +250,7 @@ __device__ __forceinline__ bool tgather(Ctx &c, __amdgpu_buffer_rsrc_t r, int n,
 template <typename FN>
 __device__ __forceinline__ bool tgather_range(Ctx &c, __amdgpu_buffer_rsrc_t r, int lo, int hi, FN fn, int pc) {
     for (int base = lo; base < hi; base += 64 * 16) {
-        const int first = base + c.lane;
+        const int first = base + c.lane();
         const int n = first < hi ? min(16, (hi - first + 63) / 64) : 0;
         if (!tgather<16>(
                 c, r, n, [&](int k) { return (uint32_t)(first + 64 * k); },
@@ -259,7 +271,7 @@ __device__ __forceinline__ bool tgather_batch(Ctx &c, const uint64_t *src, int B
     const float invK = 1.0f / (float)K;
     constexpr int STRIDE = NC * 64;
     for (int base = 0; base < total; base += STRIDE * 16) {
-        const int first = base + c.w * 64 + c.lane;
+        const int first = base + c.w * 64 + c.lane();
         const int n = first < total ? min(16, (total - first + STRIDE - 1) / STRIDE) : 0;
         if (!tgather<16>(
                 c, r, n, [&](int k) { return (uint32_t)(first + STRIDE * k); },
@@ -560,7 +572,7 @@ constexpr bool ONE_ACC = NB > 1;
 __device__ __forceinline__ int token_of(const KParams &P, Ctx &c, int b, int pc) {
     int t = sload(P.tokens_in, b);
     if (t < 0 || t >= P.V) {
-        if (c.lane == 0) raise_err(c, ERR_RANGE, pc);
+        if (c.lane() == 0) raise_err(c, ERR_RANGE, pc);
         t = 0;
     }
     return t;
@@ -576,7 +588,7 @@ __device__ __forceinline__ void prefetch_norm_w(const KParams &P, const Ctx &c, 
     const int bytes = P.H * 2;
     MK_LDS char *dst = (MK_LDS char *)c.misc + P.nw_off;
     for (int kib = c.w; kib * 1024 < bytes; kib += 4) {
-        const int off = min(kib * 1024 + c.lane * 16, bytes - 16);
+        const int off = min(kib * 1024 + c.lane() * 16, bytes - 16);
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)((const char *)wn + off),
                                          (__attribute__((address_space(3))) void *)(dst + kib * 1024), 16, 0, 0);
     }
@@ -588,7 +600,7 @@ __device__ __forceinline__ void prefetch_norm_w(const KParams &P, const Ctx &c, 
 // one-kernel-per-op baseline's norm, so both paths agree bit for bit.
 template <int NB>
 __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &in, const uint16_t *wn, int xv) {
-    const int H = P.H, lane = c.lane, w = c.w;
+    const int H = P.H, lane = c.lane(), w = c.w;
     MK_LDS float *norm = (MK_LDS float *)(c.misc + M_NORM);
     const int first = w * 64 + lane;
     const int n = first < H ? (H - first + 255) / 256 : 0;  // this lane's elements
@@ -659,7 +671,7 @@ __device__ __forceinline__ bool stage_rows(const KParams &P, Ctx &c, const Ins &
     const int nr = in.r1 - in.r0;
     if (NB > 1 && xv != 0 && P.B * nr <= NC * 64) {  // every (request, row) word in one round
         const __amdgpu_buffer_rsrc_t r = tres(P.tx + (size_t)(xv - 1) * P.B * P.H, (uint32_t)(P.B * P.H));
-        const int L = c.w * 64 + c.lane;
+        const int L = c.w * 64 + c.lane();
         const int b = nr > 0 ? L / nr : 0, j = L - b * nr;
         return tgather<1>(
             c, r, L < P.B * nr ? 1 : 0, [&](int) { return (uint32_t)(b * P.H + in.r0 + j); },
@@ -669,11 +681,11 @@ __device__ __forceinline__ bool stage_rows(const KParams &P, Ctx &c, const Ins &
         MK_LDS float *xr = c.xrow + b * P.xrow_stride;
         if (xv == 0) {
             const int tok = P.has_embed ? token_of(P, c, b, in.pc) : 0;
-            for (int j = c.w * 64 + c.lane; j < nr; j += NC * 64) xr[j] = x_input(P, b, in.r0 + j, true, tok);
+            for (int j = c.w * 64 + c.lane(); j < nr; j += NC * 64) xr[j] = x_input(P, b, in.r0 + j, true, tok);
         } else {
             const __amdgpu_buffer_rsrc_t r = tres(P.tx + ((size_t)(xv - 1) * P.B + b) * P.H, (uint32_t)P.H);
             for (int j0 = c.w * 64; j0 < nr; j0 += NC * 64) {
-                const int j = j0 + c.lane;
+                const int j = j0 + c.lane();
                 if (!tgather<1>(
                         c, r, j < nr ? 1 : 0, [&](int) { return (uint32_t)(in.r0 + j); },
                         [&](int, float v) { xr[j] = v; }, in.pc))
@@ -721,7 +733,7 @@ __device__ __forceinline__ bool stage_copy(const KParams &P, Ctx &c, const Ins &
 // and the O projection reads only the merged outputs.
 template <int G>
 __device__ __forceinline__ bool stage_amerge(const KParams &P, Ctx &c, const Ins &in) {
-    const int nch = in.nch, lane = c.lane;
+    const int nch = in.nch, lane = c.lane();
     const int n = nch * G * ATTN_PART;
     const size_t pbase = (((size_t)in.layer * P.B + in.b) * P.nkv + in.g) * nch * G * ATTN_PART;
     const __amdgpu_buffer_rsrc_t rp = tres(P.tpart + pbase, (uint32_t)n);
@@ -732,20 +744,24 @@ __device__ __forceinline__ bool stage_amerge(const KParams &P, Ctx &c, const Ins
     if (!cbar(c, in.pc)) return false;
     if (c.w < G && nch <= MAX_ATTN_CHUNKS) {
         const int h = c.w;
-        float o[MAX_ATTN_CHUNKS], m[MAX_ATTN_CHUNKS], l[MAX_ATTN_CHUNKS];
-#pragma unroll
-        for (int cc = 0; cc < MAX_ATTN_CHUNKS; ++cc)
-            if (cc < nch) {
-                const MK_LDS float *src = c.act + (cc * G + h) * ATTN_PART;
-                o[cc] = src[lane];
-                m[cc] = src[64];
-                l[cc] = src[65];
-            }
         float O, M, L;
         merge_init(O, M, L);
+        // eight chunk states' reads at a time, then their merge steps in
+        // chunk order (the registers of all sixteen would spill)
+        for (int c0 = 0; c0 < nch; c0 += 8) {
+            float o[8], m[8], l[8];
 #pragma unroll
-        for (int cc = 0; cc < MAX_ATTN_CHUNKS; ++cc)
-            if (cc < nch) merge_step(O, M, L, o[cc], m[cc], l[cc]);
+            for (int k = 0; k < 8; ++k)
+                if (c0 + k < nch) {
+                    const MK_LDS float *src = c.act + ((c0 + k) * G + h) * ATTN_PART;
+                    o[k] = src[lane];
+                    m[k] = src[64];
+                    l[k] = src[65];
+                }
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (c0 + k < nch) merge_step(O, M, L, o[k], m[k], l[k]);
+        }
         const int QD = P.nq * P.d;
         tput(tres(P.to + ((size_t)in.layer * P.B + in.b) * QD, (uint32_t)QD), (uint32_t)((in.g * G + h) * 64 + lane),
              O / L, c.tag);
@@ -758,7 +774,7 @@ __device__ __forceinline__ bool stage_amerge(const KParams &P, Ctx &c, const Ins
 // the last chunk also appends that entry to the cache.
 template <int G>
 __device__ __forceinline__ bool stage_attn(const KParams &P, Ctx &c, const Ins &in) {
-    const int lane = c.lane;
+    const int lane = c.lane();
     const int QD = P.nq * P.d, QKVN = QD + 2 * P.nkv * P.d;
     const int b = in.b, g = in.g, p = in.p;
     const bool last = in.c == in.nch - 1;
@@ -817,7 +833,7 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
     in.mneed = rfl(mw[W_MNEED - 12]);
     in.wn = rfl64(nw[0], nw[1]);
     in.tr = P.trace ? P.trace + ((int64_t)c.cu * P.Q + pc) * TRACE_WORDS : nullptr;
-    const bool tracer = in.tr && c.w == 0 && c.lane == 0;
+    const bool tracer = in.tr && c.w == 0 && c.lane() == 0;
     if (tracer) in.tr[TR_START] = wall_clock64();
     // the previous instruction is finished, merges included: its LDS areas are free
     if (!lds_wait_ge(c, c.misc + M_DONE, (uint32_t)pc, pc)) return false;
@@ -839,7 +855,7 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
         case OP_ATTN: {
             const int p = in.b >= 0 && in.b < P.B ? (int)lds_ld_const(c.misc + M_KVLEN + in.b) : -1;
             if (p < 0 || p >= P.T * P.max_pages) {
-                if (c.lane == 0) raise_err(c, ERR_RANGE, pc);
+                if (c.lane() == 0) raise_err(c, ERR_RANGE, pc);
                 return false;
             }
             in.p = p;
@@ -849,7 +865,7 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
         }
         case OP_AMERGE: ok = stage_amerge<G>(P, c, in); break;
         default:
-            if (c.lane == 0) raise_err(c, ERR_OPCODE, pc);
+            if (c.lane() == 0) raise_err(c, ERR_OPCODE, pc);
             return false;
     }
     if (!ok) return false;
@@ -865,10 +881,10 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
         // batched kernels keep the LM head's running best of request b in the
         // wave's LDS slot (lane b reads and writes it), not in registers the
         // slice loop would have to spill
-        if (in.op == OP_LMHEAD && c.lane < P.B) {
+        if (in.op == OP_LMHEAD && c.lane() < P.B) {
             MK_LDS float *am = (MK_LDS float *)(c.misc + M_AMAX);
-            am[(c.w * MAX_B + c.lane) * 2] = -INFINITY;
-            ((MK_LDS int32_t *)am)[(c.w * MAX_B + c.lane) * 2 + 1] = 0x7fffffff;
+            am[(c.w * MAX_B + c.lane()) * 2] = -INFINITY;
+            ((MK_LDS int32_t *)am)[(c.w * MAX_B + c.lane()) * 2 + 1] = 0x7fffffff;
         }
     }
     acc.nan = false;
@@ -885,12 +901,12 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
         const MK_LDS uint16_t *nw = (const MK_LDS uint16_t *)((MK_LDS char *)c.misc + P.nw_off);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const v4f a = *(const MK_LDS v4f *)(c.act + j * 512 + c.lane * 4);
-            const v4f b = *(const MK_LDS v4f *)(c.act + j * 512 + 256 + c.lane * 4);
+            const v4f a = *(const MK_LDS v4f *)(c.act + j * 512 + c.lane() * 4);
+            const v4f b = *(const MK_LDS v4f *)(c.act + j * 512 + 256 + c.lane() * 4);
             ra.o[j][0] = a.x; ra.o[j][1] = a.y; ra.o[j][2] = a.z; ra.o[j][3] = a.w;
             ra.o[j][4] = b.x; ra.o[j][5] = b.y; ra.o[j][6] = b.z; ra.o[j][7] = b.w;
             if (normed) {
-                const v4u wq = *(const MK_LDS v4u *)(nw + (j * 64 + c.lane) * 8);
+                const v4u wq = *(const MK_LDS v4u *)(nw + (j * 64 + c.lane()) * 8);
                 const float wf[8] = {bf_lo(wq.x), bf_hi(wq.x), bf_lo(wq.y), bf_hi(wq.y),
                                      bf_lo(wq.z), bf_hi(wq.z), bf_lo(wq.w), bf_hi(wq.w)};
 #pragma unroll
@@ -944,7 +960,7 @@ __device__ __forceinline__ void emit_row(const KParams &P, Ctx &c, const Ins &in
 template <int NB>
 __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &k, const Ins &in, const v4u (&r)[4],
                                            Acc<NB> &acc, const RegAct &xr) {
-    const int lane = c.lane;
+    const int lane = c.lane();
     const int m = k.s >= k.spm ? 1 : 0, part = k.s - m * k.spm;
     if (NB == 1 && k.K == 2048) {
         float a = m ? acc.a1[0] : acc.a0[0];
@@ -1079,7 +1095,7 @@ __device__ __forceinline__ bool attn_round_sync(Ctx &c, const Ins &in, AttnRun &
     MK_LDS float *area = attn_area<G>(c);
     if (c.w < G)
         attn_round_fold(area + c.w * ATTN_ROUND_POS, (const MK_LDS uint16_t *)(area + G * ATTN_ROUND_POS),
-                        16 * min(NC, in.nblk - run.rounds * NC), c.lane, run);
+                        16 * min(NC, in.nblk - run.rounds * NC), c.lane(), run);
     run.rounds++;
     return run.rounds >= nround || uni(lbar(c, in.pc));
 }
@@ -1089,7 +1105,7 @@ __device__ __forceinline__ bool attn_round_sync(Ctx &c, const Ins &in, AttnRun &
 // and values go to the round area.
 template <int G>
 __device__ __forceinline__ void attn_write_block(Ctx &c, const Cur &k, const Ins &in, const v4u (&r)[4]) {
-    const int lane = c.lane;
+    const int lane = c.lane();
     const int blk = k.blo + k.u;
     v4u k0 = r[0], k1 = r[1], v0 = r[2], v1 = r[3];
     const int t0 = lane >> 3;
@@ -1114,7 +1130,7 @@ __device__ __forceinline__ void attn_write_block(Ctx &c, const Cur &k, const Ins
 __device__ __forceinline__ bool elect_last(const KParams &P, Ctx &c, const Ins &in) {
     const int32_t need = (int32_t)((int64_t)P.epoch * in.mneed);
     int32_t old = 0;
-    if (c.lane == 0)
+    if (c.lane() == 0)
         old = __hip_atomic_fetch_add(P.counters + (int64_t)in.mctr * CTR_STRIDE, 1, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
     old = __builtin_amdgcn_readfirstlane(old);  // lane 0's: every lane is active here
@@ -1147,7 +1163,7 @@ __device__ __forceinline__ bool wait_all_started(const KParams &P, Ctx &c, int32
 // Run by the last wave to finish an instruction's slices.
 template <int G>
 __device__ __forceinline__ bool finish(const KParams &P, Ctx &c, const Ins &in) {
-    const int lane = c.lane;
+    const int lane = c.lane();
     const uint32_t tag = P.tag;
     if (in.op == OP_LMHEAD) {
         const MK_LDS float *am = (const MK_LDS float *)(c.misc + M_AMAX);
@@ -1215,7 +1231,7 @@ __device__ __forceinline__ bool finish(const KParams &P, Ctx &c, const Ins &in) 
 
 template <int NB, int G>
 __device__ __forceinline__ bool leave(const KParams &P, Ctx &c, const Ins &in, Acc<NB> &acc) {
-    const int lane = c.lane;
+    const int lane = c.lane();
     if (in.op == OP_LMHEAD) {
         if constexpr (NB == 1) {  // batched kernels kept the running best there already
             MK_LDS float *am = (MK_LDS float *)(c.misc + M_AMAX);
@@ -1281,7 +1297,7 @@ __device__ __forceinline__ bool attn_tile(const KParams &P, Ctx &c, Cur &ic, Cur
             take_any(slot, buf);
             if (cc.u < cc.nu) attn_write_block<G>(c, cc, in, buf);
             took = true;
-            issue_any(slot, P, ic, c.lane);
+            issue_any(slot, P, ic, c.lane());
             cur_next(P, c, ic);
             cur_next(P, c, cc);
             slot = slot + 1 == D ? 0 : slot + 1;
@@ -1289,7 +1305,7 @@ __device__ __forceinline__ bool attn_tile(const KParams &P, Ctx &c, Cur &ic, Cur
         if (r < nround && !uni(attn_round_sync<G>(c, in, run))) return false;
     }
     if (c.w >= G) return true;
-    const int h = c.w, lane = c.lane;
+    const int h = c.w, lane = c.lane();
     const size_t pbase = ((((size_t)in.layer * P.B + in.b) * P.nkv + in.g) * in.nch + in.c) * G * ATTN_PART;
     const __amdgpu_buffer_rsrc_t rp = tres(P.tpart + pbase, (uint32_t)(G * ATTN_PART));
     tput(rp, (uint32_t)(h * ATTN_PART + lane), run.O, P.tag);
@@ -1319,16 +1335,16 @@ __device__ __forceinline__ void run(const KParams &P, Ctx &c) {
     Cur ic, cc;
     cur_load(P, c, ic, 0);
     cur_load(P, c, cc, 0);
-    issue<0>(P, ic, c.lane);
+    issue<0>(P, ic, c.lane());
     cur_next(P, c, ic);
-    issue<1>(P, ic, c.lane);
+    issue<1>(P, ic, c.lane());
     cur_next(P, c, ic);
     if constexpr (D > 2) {
-        issue<2>(P, ic, c.lane);
+        issue<2>(P, ic, c.lane());
         cur_next(P, c, ic);
     }
     if constexpr (D > 3) {
-        issue<3>(P, ic, c.lane);
+        issue<3>(P, ic, c.lane());
         cur_next(P, c, ic);
     }
     Ins in{};
@@ -1350,7 +1366,7 @@ __device__ __forceinline__ void run(const KParams &P, Ctx &c) {
                 const bool empty = cc.u >= cc.nu;
                 if (!empty) consume_mv<NB>(P, c, cc, in, buf, acc, ra);
                 const bool last = empty || (cc.s == cc.sp - 1 && cc.u + NC >= cc.nu);
-                issue_any(slot, P, ic, c.lane);
+                issue_any(slot, P, ic, c.lane());
                 cur_next(P, c, ic);
                 cur_next(P, c, cc);
                 slot = slot + 1 == D ? 0 : slot + 1;
@@ -1380,7 +1396,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(BLOCK_THREADS, BLOCK_THREA
     c.xrow = (MK_LDS float *)(lds + P.xrow_off);
     c.act = (MK_LDS float *)(lds + P.act_off);
     c.cu = blockIdx.x;
-    c.lane = threadIdx.x & 63;
     c.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     c.nbar = 0;
     c.tag = P.tag;

@@ -75,7 +75,7 @@ constexpr int BLOCK_THREADS = N_COMPUTE_WAVES * WAVE;
 constexpr int LDS_LIMIT = 160 * 1024;  // gfx950 LDS per workgroup
 constexpr int MISC_BYTES = 4096;
 constexpr int SLICE_BYTES = 4096;      // weight bytes one wave holds per register slice
-constexpr int PREFETCH_SLICES = 4;     // slices each wave keeps in flight
+constexpr int PREFETCH_SLICES = 2;     // slices each wave keeps in flight
 constexpr int ATTN_PART = 64 + 2;      // o[d], m, l of one head
 // an attention tile works in rounds of one 16-position K/V block per wave;
 // a round's LDS area for G query heads holds its scores [G][ATTN_ROUND_POS]

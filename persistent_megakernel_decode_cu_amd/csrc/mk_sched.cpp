@@ -244,9 +244,14 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
                 t.g = g;
                 t.nch = C;
                 t.merge = -1;
-                t.bytes = 0;  // streams nothing; charged below at the chunk states it gathers, to spread the merges
+                t.bytes = 0;  // streams nothing
                 t.cu = pick_least(cum);
-                cum[t.cu] += (int64_t)C * G * ATTN_PART * 8;
+                // charged at the whole O projection: a merge ends after the
+                // attention tiles, later than any other unit's inputs arrive,
+                // so its unit takes none of the O projection's rows (unless
+                // every unit carries a merge), which would otherwise end last
+                // and hold back the MLP
+                cum[t.cu] += (int64_t)H * QD * 2;
                 tiles.push_back(t);
             }
         matvec_op(OP_OPROJ, l, H, (int64_t)QD * 2, first);
