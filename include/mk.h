@@ -162,6 +162,26 @@ int mk_build_schedule(mk_handle *h, const mk_schedule_desc *s);
  * needs mk_build_schedule before the next step. */
 int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream);
 
+/* Runs n_steps consecutive greedy decode steps in one launch whose grid stays
+ * resident across them ("Inference MegaKernel", section "MPK compiler and
+ * runtime": the kernel stays resident between tokens; here the step count is
+ * fixed at the launch instead of a host shutdown flag). Step s embeds the
+ * token step s - 1 chose and attends over kv_lens + s entries, exactly as
+ * n_steps calls of mk_decode_step would; between steps no workgroup exits, so
+ * the next step's first weights stream while the previous step's LM head
+ * finishes. Needs MK_MODE_MEGAKERNEL and an embedding (has_embed == 1).
+ * io as for mk_decode_step, except: tokens_in [B] holds step 0's tokens;
+ * tokens_out is [n_steps][B] (step-major); kv_lens_out (optional) receives
+ * kv_lens + n_steps; logits_out and hidden_out (optional) receive the last
+ * step's values; every request's kv_lens + n_steps - 1 must be within the
+ * schedule's max_kv_len. The first call with a larger n_steps * B than
+ * before allocates a small device buffer (tagged tokens) and synchronises
+ * `stream`. Errors: as mk_decode_step, and MK_EINVAL for n_steps < 1 or
+ * above 2^20, a schedule in MK_MODE_UNFUSED, or a model without embedding.
+ * A device-side range error (a length past the page capacity) is reported
+ * like any other device error. */
+int mk_decode_steps(mk_handle *h, const mk_step_io *io, int32_t n_steps, void *stream);
+
 /* mk_decode_step for callers that cannot allocate device memory at the call
  * or around it (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc). It runs the same resident interpreter, but the

@@ -16,7 +16,7 @@ from typing import Mapping, Optional
 from . import _mk
 from ._mk import (MK_MODE_MEGAKERNEL, MK_MODE_UNFUSED, MkConfig, MkError, MkLayerWeights,  # noqa: F401
                   MkScheduleDesc, MkStepIO, MkWeights, Plan, mk_build_schedule, mk_create, mk_decode_step,
-                  mk_decode_step_static,
+                  mk_decode_step_static, mk_decode_steps,
                   mk_destroy, mk_get_schedule_info, mk_last_error, mk_read_trace, mk_sync_status)
 
 _MODES = {"megakernel": MK_MODE_MEGAKERNEL, "unfused": MK_MODE_UNFUSED}
@@ -94,9 +94,11 @@ class Decoder:
 
     def step(self, *, kv_lens, k_pool, v_pool, page_table, tokens_in=None, hidden_in=None, tokens_out=None,
              kv_lens_out=None, logits_out=None, hidden_out=None, stream: Optional[int] = None,
-             static_scratch: bool = False) -> None:
+             static_scratch: bool = False, n_steps: int = 1) -> None:
         """One step (mk_decode_step), or with ``static_scratch`` the
-        allocation-free mk_decode_step_static."""
+        allocation-free mk_decode_step_static, or with ``n_steps`` > 1 that
+        many greedy steps in one resident launch (mk_decode_steps; tokens_out
+        is then [n_steps, B])."""
         import torch
         s = self.shape
         B = self.batch
@@ -106,11 +108,17 @@ class Decoder:
             _ptr(kv_lens, "kv_lens", 4, (B,)), _ptr(k_pool, "k_pool", 2, pool_shape),
             _ptr(v_pool, "v_pool", 2, pool_shape), int(k_pool.shape[1]),
             _ptr(page_table, "page_table", 4, (B, self.cfg.max_pages_per_req)),
-            _ptr(tokens_out, "tokens_out", 4, (B,)), _ptr(kv_lens_out, "kv_lens_out", 4, (B,)),
+            _ptr(tokens_out, "tokens_out", 4, (n_steps, B) if n_steps > 1 else (B,)),
+            _ptr(kv_lens_out, "kv_lens_out", 4, (B,)),
             _ptr(logits_out, "logits_out", 4, (B, s.vocab)), _ptr(hidden_out, "hidden_out", 4, (B, s.hidden)))
         if stream is None:
             stream = torch.cuda.current_stream().cuda_stream
-        (mk_decode_step_static if static_scratch else mk_decode_step)(self.handle, io, stream)
+        if n_steps != 1:  # the library checks the count
+            if static_scratch:
+                raise ValueError("the allocation-free entry point runs one step per call")
+            mk_decode_steps(self.handle, io, int(n_steps), stream)
+        else:
+            (mk_decode_step_static if static_scratch else mk_decode_step)(self.handle, io, stream)
 
     def sync(self, stream: Optional[int] = None) -> None:
         import torch

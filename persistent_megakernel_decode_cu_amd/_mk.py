@@ -75,6 +75,7 @@ _SIGS = {
     "mk_build_schedule": (i32, [vp, ctypes.POINTER(MkScheduleDesc)]),
     "mk_decode_step": (i32, [vp, ctypes.POINTER(MkStepIO), vp]),
     "mk_decode_step_static": (i32, [vp, ctypes.POINTER(MkStepIO), vp]),
+    "mk_decode_steps": (i32, [vp, ctypes.POINTER(MkStepIO), i32, vp]),
     "mk_destroy": (None, [vp]),
     "mk_last_error": (ctypes.c_char_p, []),
     "mk_sync_status": (i32, [vp, vp]),
@@ -135,6 +136,10 @@ def mk_decode_step(handle: int, io: MkStepIO, stream: int = 0) -> None:
 
 def mk_decode_step_static(handle: int, io: MkStepIO, stream: int = 0) -> None:
     _check(lib().mk_decode_step_static(handle, ctypes.byref(io), stream))
+
+
+def mk_decode_steps(handle: int, io: MkStepIO, n_steps: int, stream: int = 0) -> None:
+    _check(lib().mk_decode_steps(handle, ctypes.byref(io), n_steps, stream))
 
 
 def mk_destroy(handle: int) -> None:

@@ -62,8 +62,11 @@ struct mk_handle {
     float *u = nullptr, *qrot = nullptr;
     uint64_t *tx = nullptr, *tqkv = nullptr, *to = nullptr, *tact = nullptr, *tpart = nullptr, *tlm = nullptr;
     uint32_t tag = 0;  // tag of the last step's activations (never 0 on the device)
+    uint64_t *ttok = nullptr;  // [ttok_cap] tagged tokens a resident launch hands from step to step
+    size_t ttok_cap = 0;
     int64_t *trace = nullptr;
-    int64_t epoch = 0;
+    int64_t epoch = 0;  // launches since the counters were last cleared (start counter)
+    int64_t steps = 0;  // decode steps since then (merge events)
     int32_t max_need = 1;
     int sticky = MK_OK;
 };
@@ -94,6 +97,8 @@ void free_schedule(mk_handle *h) {
     dfree(h->tact);
     dfree(h->tpart);
     dfree(h->tlm);
+    dfree(h->ttok);
+    h->ttok_cap = 0;
     dfree(h->trace);
     h->built = false;
 }
@@ -331,6 +336,7 @@ int mk_build_schedule(mk_handle *h, const mk_schedule_desc *s) {
         *h->host_err = 0;
         h->sticky = MK_OK;
         h->epoch = 0;
+        h->steps = 0;
         h->tag = 0;
         MK_HIP(hipDeviceSynchronize());
         h->built = true;
@@ -340,7 +346,7 @@ int mk_build_schedule(mk_handle *h, const mk_schedule_desc *s) {
     }
 }
 
-static int decode_step(mk_handle *h, const mk_step_io *io, void *stream, const StaticLayout *sl) {
+static int decode_step(mk_handle *h, const mk_step_io *io, void *stream, const StaticLayout *sl, int n_steps) {
     try {
         if (!h || !io) return set_error(MK_EINVAL, "null argument");
         if (!h->built) return set_error(MK_ENOSCHED, "mk_decode_step before mk_build_schedule");
@@ -359,7 +365,24 @@ static int decode_step(mk_handle *h, const mk_step_io *io, void *stream, const S
         if (io->n_pages < 1) return set_error(MK_EINVAL, "n_pages must be positive");
         hipStream_t st = (hipStream_t)stream;
         const mk::Plan &P = h->plan;
+        if (n_steps < 1) return set_error(MK_EINVAL, "n_steps must be positive");
+        if (n_steps > 1) {
+            if (P.desc.mode != MK_MODE_MEGAKERNEL)
+                return set_error(MK_EINVAL, "several steps per launch need the resident interpreter (MK_MODE_MEGAKERNEL)");
+            if (!c.has_embed) return set_error(MK_EINVAL, "several steps per launch need an embedding (greedy tokens feed back)");
+            if (n_steps > (1 << 20)) return set_error(MK_EINVAL, "n_steps above 2^20");
+            const size_t need = (size_t)n_steps * P.desc.batch;
+            if (need > h->ttok_cap) {
+                MK_HIP(hipStreamSynchronize(st));
+                dfree(h->ttok);
+                h->ttok_cap = 0;
+                if (int rc = dalloc(h->ttok, need)) return rc;
+                h->ttok_cap = need;
+            }
+        }
         mk::KParams k{};
+        k.n_steps = n_steps;
+        k.ttok = n_steps > 1 ? h->ttok : nullptr;
         if (sl) {
             // the static scratch keeps whatever the last call on this device
             // left there: clear the part this schedule uses (a fill kernel,
@@ -367,17 +390,27 @@ static int decode_step(mk_handle *h, const mk_step_io *io, void *stream, const S
             // step on cleared buffers
             MK_HIP(mk::fill_u32((uint32_t *)sl->base, sl->bytes / 4, 0u, st));
             k.epoch = 1;
+            k.step_epoch = 1;
             k.tag = 1;
         } else {
-            // epoch-based counters: re-zero before the int32 counts could wrap
-            if ((h->epoch + 1) * (int64_t)h->max_need >= ((int64_t)1 << 30)) {
+            // epoch-based counters (one start-counter epoch per launch, one
+            // merge epoch per step): re-zero before the int32 counts could wrap
+            if ((h->steps + n_steps) * (int64_t)h->max_need >= ((int64_t)1 << 30)) {
                 MK_HIP(mk::fill_u32((uint32_t *)h->counters, (size_t)(P.n_counters + 1) * mk::CTR_STRIDE, 0u, st));
                 h->epoch = 0;
+                h->steps = 0;
             }
             h->epoch++;
-            if (++h->tag == 0) h->tag = 1;  // the buffers start at tag 0, which no step uses
             k.epoch = (int32_t)h->epoch;
-            k.tag = h->tag;
+            k.step_epoch = (int32_t)(h->steps + 1);
+            h->steps += n_steps;
+            // step s of the launch tags its activations tag + s; tags only
+            // grow, so no word left by an earlier launch carries one of them
+            // (the buffers start at tag 0, which no step uses)
+            if ((uint64_t)h->tag + (uint64_t)n_steps > 0xffffffffull)
+                return set_error(MK_EINVAL, "activation tags exhausted; rebuild the schedule");
+            k.tag = h->tag + 1;
+            h->tag += (uint32_t)n_steps;
         }
         k.queue = h->queue;
         k.events = h->events;
@@ -448,7 +481,11 @@ static int decode_step(mk_handle *h, const mk_step_io *io, void *stream, const S
     }
 }
 
-int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream) { return decode_step(h, io, stream, nullptr); }
+int mk_decode_step(mk_handle *h, const mk_step_io *io, void *stream) { return decode_step(h, io, stream, nullptr, 1); }
+
+int mk_decode_steps(mk_handle *h, const mk_step_io *io, int32_t n_steps, void *stream) {
+    return decode_step(h, io, stream, nullptr, n_steps);
+}
 
 int mk_decode_step_static(mk_handle *h, const mk_step_io *io, void *stream) {
     try {
@@ -461,7 +498,7 @@ int mk_decode_step_static(mk_handle *h, const mk_step_io *io, void *stream) {
         if (!base) return set_error(MK_EHIP, "the static scratch of this device was not set up by mk_create");
         StaticLayout sl{};
         if (int rc = static_layout(h, (char *)base, &sl)) return rc;
-        return decode_step(h, io, stream, &sl);
+        return decode_step(h, io, stream, &sl, 1);
     } catch (...) {
         return set_error(MK_EINVAL, "internal error in mk_decode_step_static");
     }

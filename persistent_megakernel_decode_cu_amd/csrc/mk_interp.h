@@ -46,6 +46,7 @@ enum : int {
     M_FIN = 2,     // waves finished with an instruction's slices
     M_DONE = 3,    // instructions fully finished (incl. their merges)
     M_AFIN = 4,    // attention heads merged over the waves (G per instruction)
+    M_NQ = 5,      // instructions in the queue (the index of its END), found while copying it
     M_KVLEN = 8,   // [MAX_B] lengths of the requests (read once at start)
     M_NORM = 16,   // [4][MAX_B] sums of squares
     M_AMAX = 64,   // [NC][MAX_B][2] per-wave argmax (value, index)
@@ -88,12 +89,23 @@ __device__ __forceinline__ int lane_id() {
     return l;
 }
 
+// Lane lane ^ m's value (a cross-lane LDS permute addressed with lane_id():
+// the runtime's shuffle takes the lane index from a builtin the compiler
+// hoists to the kernel's start, where it is spilled and reloaded behind the
+// slices in flight).
+__device__ __forceinline__ int shfl_xor_i(int v, int m) {
+    return __builtin_amdgcn_ds_bpermute((lane_id() ^ m) << 2, v);
+}
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __int_as_float(shfl_xor_i(__float_as_int(v), m)); }
+
 struct Ctx {
     MK_LDS uint32_t *misc;
     const MK_LDS int32_t *q;  // this CU's queue, LDS_INSTR_WORDS words per instruction
     MK_LDS float *act;   // matvec inputs of all requests, or the attention staging
     MK_LDS float *xrow;  // residual rows of the instruction (O projection, down projection)
     int cu, w;
+    int nq;              // instructions in this unit's queue (the index of its END)
+    bool kv_pending;     // this wave appended a K/V entry in the current attention tile
     uint32_t nbar;
     __device__ __forceinline__ int lane() const { return lane_id(); }
     uint32_t tag;        // copies of kernel arguments the helpers need: taking
@@ -295,13 +307,19 @@ __device__ __forceinline__ bool tgather_batch(Ctx &c, const uint64_t *src, int B
 // of the unit. An instruction in which the wave has no unit still yields one
 // empty slice, so that the wave passes through its staging and merges.
 struct Cur {
+    int step;  // decode step of the launch (a resident launch runs several)
     int pc, op, layer, r0, nu, sp, spm, u, s, K;
     int b, g, blo, p;
     uint32_t rowb;
     uint64_t wa, wb;  // matvec: base of the op's first (gate) and second (up) weight matrix
 };
 
-__device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k, int pc) {
+// Instruction pc of step `step` (its END past the queue). The cursors never
+// cross a step's END themselves: the main loop restarts them at the next
+// step (logic for that here, in the slice loop's path, costs the whole step
+// dearly in code quality).
+__device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k, int pc, int step) {
+    k.step = step;
     k.pc = pc;
     k.op = OP_END;
     k.u = c.w;
@@ -312,7 +330,7 @@ __device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k,
     k.K = 0;
     k.rowb = 0;
     k.wa = k.wb = (uint64_t)(uintptr_t)P.wtab;
-    if (pc >= P.Q) return;
+    if (pc >= c.nq) return;
     const iv4 a = iw4(c, pc, W_OP), bw = iw4(c, pc, W_B), wq = iw4(c, pc, W_WA);
     k.op = rfl(a[0]);
     if (k.op == OP_END) return;
@@ -321,7 +339,7 @@ __device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k,
     if (k.op == OP_ATTN) {
         k.b = rfl(bw[0]);
         k.g = rfl(bw[1]);
-        int p = (int)lds_ld_const(c.misc + M_KVLEN + (k.b & (MAX_B - 1)));
+        int p = (int)lds_ld_const(c.misc + M_KVLEN + (k.b & (MAX_B - 1))) + step;
         if (p < 0 || p >= P.T * P.max_pages) p = 0;  // the staging raises the error
         k.p = p;
         int lo, hi;
@@ -351,7 +369,7 @@ __device__ __forceinline__ void cur_next(const KParams &P, const Ctx &c, Cur &k)
         }
         if (k.u < k.nu) return;
     }
-    cur_load(P, c, k, k.pc + 1);
+    cur_load(P, c, k, k.pc + 1, k.step);
 }
 
 // Buffer resource words for a byte range (gfx950 raw buffer, stride 0):
@@ -373,58 +391,73 @@ constexpr int SLOT_VGPR0 = 168;
 static_assert(SLOT_VGPR0 + 16 * D <= 256, "slots beyond the VGPR file");
 
 template <int K>
-__device__ __forceinline__ void slot_loads(uint32_t o, v4u ra, v4u rb);
+__device__ __forceinline__ void slot_loads(uint32_t o, v4u ra, v4u rb, bool coherent);
 template <int K>
 __device__ __forceinline__ void slot_take(v2u (&x)[8], int n_wait);
 
+
+// The four loads of a slot: weights non-temporal (streamed once); K/V blocks
+// device-coherent (sc1), since a resident launch appends entries on one XCD
+// and reads them back on another with no kernel boundary in between.
+#define MK_SLOT_LOADS_ASM(V0, V1, V2, V3, POL)                                        \
+    "s_nop 4\n\t"                                                                      \
+    "buffer_load_dwordx4 v[" V0 "], %0, %1, 0 offen " POL " ; slot_load\n\t"             \
+    "buffer_load_dwordx4 v[" V1 "], %0, %1, 0 offen offset:1024 " POL " ; slot_load\n\t" \
+    "buffer_load_dwordx4 v[" V2 "], %0, %2, 0 offen " POL " ; slot_load\n\t"             \
+    "buffer_load_dwordx4 v[" V3 "], %0, %2, 0 offen offset:1024 " POL " ; slot_load"
 template <>
-__device__ __forceinline__ void slot_loads<0>(uint32_t o, v4u ra, v4u rb) {
-    asm volatile(
-        "s_nop 4\n\t"
-        "buffer_load_dwordx4 v[168:171], %0, %1, 0 offen nt ; slot_load\n\t"
-        "buffer_load_dwordx4 v[172:175], %0, %1, 0 offen offset:1024 nt ; slot_load\n\t"
-        "buffer_load_dwordx4 v[176:179], %0, %2, 0 offen nt ; slot_load\n\t"
-        "buffer_load_dwordx4 v[180:183], %0, %2, 0 offen offset:1024 nt ; slot_load"
-        :
-        : "v"(o), "s"(ra), "s"(rb)
-        : "memory", "v168", "v169", "v170", "v171", "v172", "v173", "v174", "v175", "v176", "v177", "v178", "v179", "v180", "v181", "v182", "v183");
+__device__ __forceinline__ void slot_loads<0>(uint32_t o, v4u ra, v4u rb, bool coherent) {
+    if (coherent)
+        asm volatile(MK_SLOT_LOADS_ASM("168:171", "172:175", "176:179", "180:183", "sc1")
+                     :
+                     : "v"(o), "s"(ra), "s"(rb)
+                     : "memory", "v168", "v169", "v170", "v171", "v172", "v173", "v174", "v175", "v176", "v177", "v178", "v179", "v180", "v181", "v182", "v183");
+    else
+        asm volatile(MK_SLOT_LOADS_ASM("168:171", "172:175", "176:179", "180:183", "nt")
+                     :
+                     : "v"(o), "s"(ra), "s"(rb)
+                     : "memory", "v168", "v169", "v170", "v171", "v172", "v173", "v174", "v175", "v176", "v177", "v178", "v179", "v180", "v181", "v182", "v183");
 }
 template <>
-__device__ __forceinline__ void slot_loads<1>(uint32_t o, v4u ra, v4u rb) {
-    asm volatile(
-        "s_nop 4\n\t"
-        "buffer_load_dwordx4 v[184:187], %0, %1, 0 offen nt ; slot_load\n\t"
-        "buffer_load_dwordx4 v[188:191], %0, %1, 0 offen offset:1024 nt ; slot_load\n\t"
-        "buffer_load_dwordx4 v[192:195], %0, %2, 0 offen nt ; slot_load\n\t"
-        "buffer_load_dwordx4 v[196:199], %0, %2, 0 offen offset:1024 nt ; slot_load"
-        :
-        : "v"(o), "s"(ra), "s"(rb)
-        : "memory", "v184", "v185", "v186", "v187", "v188", "v189", "v190", "v191", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199");
+__device__ __forceinline__ void slot_loads<1>(uint32_t o, v4u ra, v4u rb, bool coherent) {
+    if (coherent)
+        asm volatile(MK_SLOT_LOADS_ASM("184:187", "188:191", "192:195", "196:199", "sc1")
+                     :
+                     : "v"(o), "s"(ra), "s"(rb)
+                     : "memory", "v184", "v185", "v186", "v187", "v188", "v189", "v190", "v191", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199");
+    else
+        asm volatile(MK_SLOT_LOADS_ASM("184:187", "188:191", "192:195", "196:199", "nt")
+                     :
+                     : "v"(o), "s"(ra), "s"(rb)
+                     : "memory", "v184", "v185", "v186", "v187", "v188", "v189", "v190", "v191", "v192", "v193", "v194", "v195", "v196", "v197", "v198", "v199");
 }
 template <>
-__device__ __forceinline__ void slot_loads<2>(uint32_t o, v4u ra, v4u rb) {
-    asm volatile(
-        "s_nop 4\n\t"
-        "buffer_load_dwordx4 v[200:203], %0, %1, 0 offen nt ; slot_load\n\t"
-        "buffer_load_dwordx4 v[204:207], %0, %1, 0 offen offset:1024 nt ; slot_load\n\t"
-        "buffer_load_dwordx4 v[208:211], %0, %2, 0 offen nt ; slot_load\n\t"
-        "buffer_load_dwordx4 v[212:215], %0, %2, 0 offen offset:1024 nt ; slot_load"
-        :
-        : "v"(o), "s"(ra), "s"(rb)
-        : "memory", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215");
+__device__ __forceinline__ void slot_loads<2>(uint32_t o, v4u ra, v4u rb, bool coherent) {
+    if (coherent)
+        asm volatile(MK_SLOT_LOADS_ASM("200:203", "204:207", "208:211", "212:215", "sc1")
+                     :
+                     : "v"(o), "s"(ra), "s"(rb)
+                     : "memory", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215");
+    else
+        asm volatile(MK_SLOT_LOADS_ASM("200:203", "204:207", "208:211", "212:215", "nt")
+                     :
+                     : "v"(o), "s"(ra), "s"(rb)
+                     : "memory", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v207", "v208", "v209", "v210", "v211", "v212", "v213", "v214", "v215");
 }
 template <>
-__device__ __forceinline__ void slot_loads<3>(uint32_t o, v4u ra, v4u rb) {
-    asm volatile(
-        "s_nop 4\n\t"
-        "buffer_load_dwordx4 v[216:219], %0, %1, 0 offen nt ; slot_load\n\t"
-        "buffer_load_dwordx4 v[220:223], %0, %1, 0 offen offset:1024 nt ; slot_load\n\t"
-        "buffer_load_dwordx4 v[224:227], %0, %2, 0 offen nt ; slot_load\n\t"
-        "buffer_load_dwordx4 v[228:231], %0, %2, 0 offen offset:1024 nt ; slot_load"
-        :
-        : "v"(o), "s"(ra), "s"(rb)
-        : "memory", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231");
+__device__ __forceinline__ void slot_loads<3>(uint32_t o, v4u ra, v4u rb, bool coherent) {
+    if (coherent)
+        asm volatile(MK_SLOT_LOADS_ASM("216:219", "220:223", "224:227", "228:231", "sc1")
+                     :
+                     : "v"(o), "s"(ra), "s"(rb)
+                     : "memory", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231");
+    else
+        asm volatile(MK_SLOT_LOADS_ASM("216:219", "220:223", "224:227", "228:231", "nt")
+                     :
+                     : "v"(o), "s"(ra), "s"(rb)
+                     : "memory", "v216", "v217", "v218", "v219", "v220", "v221", "v222", "v223", "v224", "v225", "v226", "v227", "v228", "v229", "v230", "v231");
 }
+#undef MK_SLOT_LOADS_ASM
 template <>
 __device__ __forceinline__ void slot_take<0>(v2u (&x)[8], int n_wait) {
     if (n_wait == 0)  // a constant at every call site
@@ -528,7 +561,7 @@ __device__ __forceinline__ void issue(const KParams &P, const Cur &k, int lane) 
             b = a + 2048;
         }
     }
-    slot_loads<K>((uint32_t)lane * 16, rsrc_words(a, na), rsrc_words(b, nb));
+    slot_loads<K>((uint32_t)lane * 16, rsrc_words(a, na), rsrc_words(b, nb), k.op == OP_ATTN && P.n_steps > 1);
 }
 
 // Waits until at most N vector memory operations are outstanding (N = 0 or
@@ -546,6 +579,8 @@ __device__ __forceinline__ void take_slot(v4u (&r)[4]) {
 // ------------------------------------------------------------ instruction
 
 struct Ins {
+    int step;  // decode step of the launch
+    int gpc;   // step * (queue length) + pc: the instruction's index in the LDS counts
     int pc, op, layer, r0, r1, flags, b, g, c, nch, p, merge, slot, nslot, mctr, mneed;
     int nblk;     // attention: K/V blocks of the tile
     uint64_t wn;  // norm weight of the op's input
@@ -569,10 +604,26 @@ struct Acc {
 template <int NB>
 constexpr bool ONE_ACC = NB > 1;
 
-__device__ __forceinline__ int token_of(const KParams &P, Ctx &c, int b, int pc) {
-    int t = sload(P.tokens_in, b);
+// Request b's input token: the caller's at the launch's first step, and at
+// each later step of a resident launch the token the previous step's LM
+// head published (polled like any tagged activation). -1 on abort.
+__device__ __forceinline__ int token_of(const KParams &P, Ctx &c, int b, const Ins &in) {
+    int t;
+    if (in.step == 0) {
+        t = sload(P.tokens_in, b);
+    } else {
+        float v = 0.0f;
+        const uint32_t tag = c.tag;
+        c.tag = tag - 1u;  // the previous step's
+        const bool ok = tgather<1>(
+            c, tres(P.ttok, (uint32_t)(P.n_steps * P.B)), 1,
+            [&](int) { return (uint32_t)((in.step - 1) * P.B + b); }, [&](int, float x) { v = x; }, in.pc);
+        c.tag = tag;
+        if (!ok) return -1;
+        t = __builtin_amdgcn_readfirstlane(__float_as_int(v));
+    }
     if (t < 0 || t >= P.V) {
-        if (c.lane() == 0) raise_err(c, ERR_RANGE, pc);
+        if (c.lane() == 0) raise_err(c, ERR_RANGE, in.pc);
         t = 0;
     }
     return t;
@@ -621,7 +672,8 @@ __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &
             if (batched) {
                 // gathered above
             } else if (xv == 0) {
-                const int tok = P.has_embed ? token_of(P, c, b, in.pc) : 0;
+                const int tok = P.has_embed ? token_of(P, c, b, in) : 0;
+                if (tok < 0) return false;
                 for (int i = first; i < H; i += 256) a[act_index(i)] = x_input(P, b, i, true, tok);
             } else {
                 const __amdgpu_buffer_rsrc_t r = tres(P.tx + ((size_t)(xv - 1) * P.B + b) * H, (uint32_t)H);
@@ -680,7 +732,8 @@ __device__ __forceinline__ bool stage_rows(const KParams &P, Ctx &c, const Ins &
     for (int b = 0; b < P.B; ++b) {
         MK_LDS float *xr = c.xrow + b * P.xrow_stride;
         if (xv == 0) {
-            const int tok = P.has_embed ? token_of(P, c, b, in.pc) : 0;
+            const int tok = P.has_embed ? token_of(P, c, b, in) : 0;
+            if (tok < 0) return false;
             for (int j = c.w * 64 + c.lane(); j < nr; j += NC * 64) xr[j] = x_input(P, b, in.r0 + j, true, tok);
         } else {
             const __amdgpu_buffer_rsrc_t r = tres(P.tx + ((size_t)(xv - 1) * P.B + b) * P.H, (uint32_t)P.H);
@@ -789,7 +842,7 @@ __device__ __forceinline__ bool stage_attn(const KParams &P, Ctx &c, const Ins &
             return false;
         float out = xi;
         if (t <= G) {  // queries and the key are rotated; the value is not
-            const float xp = __shfl_xor(xi, 32, 64);
+            const float xp = shfl_xor_f(xi, 32);
             out = rope_rotate(xi, xp, cs, lane < 32);
         }
         if (t < G) {
@@ -804,7 +857,15 @@ __device__ __forceinline__ bool stage_attn(const KParams &P, Ctx &c, const Ins &
                     page = 0;
                 }
                 uint16_t *pool = t == G ? P.k_pool : P.v_pool;
-                pool[(((size_t)in.layer * P.n_pages + page) * P.nkv + g) * 1024 + (p & 15) * 64 + lane] = hb;
+                const uint16_t *entry = pool + (((size_t)in.layer * P.n_pages + page) * P.nkv + g) * 1024 + (p & 15) * 64;
+                // one address for the wave, visibly (a buffer resource must be uniform)
+                const uint64_t ea = (uint64_t)(uintptr_t)entry;
+                uint16_t *dst = (uint16_t *)(uintptr_t)rfl64((int32_t)(uint32_t)ea, (int32_t)(uint32_t)(ea >> 32));
+                // device-coherent: the later steps of a resident launch read
+                // the entry back on other XCDs, with no kernel boundary
+                // between (the wave waits for it before it leaves the tile)
+                __builtin_amdgcn_raw_buffer_store_b16(hb, coherent_rsrc(dst, 128), (uint32_t)lane * 2, 0, CP_SC1);
+                c.kv_pending = true;
             }
         }
     }
@@ -815,6 +876,9 @@ template <int NB, int G>
 __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, Ins &in, Acc<NB> &acc, RegAct &ra) {
     const int pc = k.pc;
     in.pc = pc;
+    in.step = k.step;
+    in.gpc = k.step * c.nq + pc;
+    c.tag = P.tag + (uint32_t)k.step;
     const iv4 a = iw4(c, pc, W_OP), bw = iw4(c, pc, W_B), fw = iw4(c, pc, W_FLAGS), mw = iw4(c, pc, 12),
               nw = iw4(c, pc, W_WN);
     in.op = rfl(a[0]);
@@ -836,7 +900,7 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
     const bool tracer = in.tr && c.w == 0 && c.lane() == 0;
     if (tracer) in.tr[TR_START] = wall_clock64();
     // the previous instruction is finished, merges included: its LDS areas are free
-    if (!lds_wait_ge(c, c.misc + M_DONE, (uint32_t)pc, pc)) return false;
+    if (!lds_wait_ge(c, c.misc + M_DONE, (uint32_t)in.gpc, pc)) return false;
     bool ok = true;
     switch (in.op) {
         case OP_QKV:
@@ -853,7 +917,7 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
                  stage_copy<ACT16_DOWN<NB>, NB>(P, c, in, P.tact + (size_t)in.layer * P.B * P.F, P.F) && cbar(c, pc);
             break;
         case OP_ATTN: {
-            const int p = in.b >= 0 && in.b < P.B ? (int)lds_ld_const(c.misc + M_KVLEN + in.b) : -1;
+            const int p = in.b >= 0 && in.b < P.B ? (int)lds_ld_const(c.misc + M_KVLEN + in.b) + in.step : -1;
             if (p < 0 || p >= P.T * P.max_pages) {
                 if (c.lane() == 0) raise_err(c, ERR_RANGE, pc);
                 return false;
@@ -920,7 +984,8 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
 // Output of row `row` for request b (lane b), v0 the row's dot product, v1
 // the up projection's for UPGATE.
 __device__ __forceinline__ void emit_row(const KParams &P, Ctx &c, const Ins &in, int row, int b, float v0, float v1) {
-    const uint32_t tag = P.tag;
+    const uint32_t tag = c.tag;
+    const bool last_step = in.step == P.n_steps - 1;  // a resident launch returns its last step's logits and hidden
     switch (in.op) {
         case OP_QKV: {
             const int QKVN = (P.nq + 2 * P.nkv) * P.d;
@@ -938,11 +1003,11 @@ __device__ __forceinline__ void emit_row(const KParams &P, Ctx &c, const Ins &in
         case OP_DOWN: {
             const float nx = c.xrow[b * P.xrow_stride + (row - in.r0)] + v0;
             tput(tres(P.tx + ((size_t)(2 * in.layer + 1) * P.B + b) * P.H, (uint32_t)P.H), (uint32_t)row, nx, tag);
-            if ((in.flags & F_WRITE_HIDDEN) && P.hidden_out) P.hidden_out[(int64_t)b * P.H + row] = nx;
+            if ((in.flags & F_WRITE_HIDDEN) && P.hidden_out && last_step) P.hidden_out[(int64_t)b * P.H + row] = nx;
             break;
         }
         default:
-            if (P.logits_out) P.logits_out[(int64_t)b * P.V + row] = v0;
+            if (P.logits_out && last_step) P.logits_out[(int64_t)b * P.V + row] = v0;
             break;
     }
 }
@@ -1128,7 +1193,7 @@ __device__ __forceinline__ void attn_write_block(Ctx &c, const Cur &k, const Ins
 
 // Elects the last of the instruction's merge-event finishers (one per step).
 __device__ __forceinline__ bool elect_last(const KParams &P, Ctx &c, const Ins &in) {
-    const int32_t need = (int32_t)((int64_t)P.epoch * in.mneed);
+    const int32_t need = (int32_t)((int64_t)(P.step_epoch + in.step) * in.mneed);
     int32_t old = 0;
     if (c.lane() == 0)
         old = __hip_atomic_fetch_add(P.counters + (int64_t)in.mctr * CTR_STRIDE, 1, __ATOMIC_RELAXED,
@@ -1164,7 +1229,8 @@ __device__ __forceinline__ bool wait_all_started(const KParams &P, Ctx &c, int32
 template <int G>
 __device__ __forceinline__ bool finish(const KParams &P, Ctx &c, const Ins &in) {
     const int lane = c.lane();
-    const uint32_t tag = P.tag;
+    const uint32_t tag = c.tag;
+    const bool last_step = in.step == P.n_steps - 1;
     if (in.op == OP_LMHEAD) {
         const MK_LDS float *am = (const MK_LDS float *)(c.misc + M_AMAX);
         const __amdgpu_buffer_rsrc_t rl = tres(P.tlm, (uint32_t)(in.nslot * P.B * 2));
@@ -1184,7 +1250,7 @@ __device__ __forceinline__ bool finish(const KParams &P, Ctx &c, const Ins &in) 
         }
         if (!elect_last(P, c, in)) return true;
         if (in.tr && lane == 0) in.tr[TR_ELECT] = wall_clock64();
-        const int32_t started = P.kv_lens_out ? started_count(P) : 0;  // read now, checked before the write
+        const int32_t started = P.kv_lens_out && last_step ? started_count(P) : 0;  // read now, checked before the write
         // the argmax is a maximum under a total order: any combination order gives the same token
         if (!tgather_range(
                 c, rl, 0, in.nslot * P.B * 2, [&](int i, float v) { c.act[i] = v; }, in.pc))
@@ -1205,25 +1271,30 @@ __device__ __forceinline__ bool finish(const KParams &P, Ctx &c, const Ins &in) 
             }
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, 64);
-                const int oi = __shfl_xor(bi, o, 64);
+                const float ov = shfl_xor_f(bv, o);
+                const int oi = shfl_xor_i(bi, o);
                 if (amax_better(ov, oi, bv, bi)) {
                     bv = ov;
                     bi = oi;
                 }
             }
-            if (lane == 0) P.tokens_out[b] = bi;
+            if (lane == 0) {
+                P.tokens_out[(int64_t)in.step * P.B + b] = bi;
+                // the next step of a resident launch embeds this token
+                if (!last_step) tput(tres(P.ttok, (uint32_t)(P.n_steps * P.B)), (uint32_t)(in.step * P.B + b),
+                                     __int_as_float(bi), tag);
+            }
         }
-        if (P.kv_lens_out) {
+        if (P.kv_lens_out && last_step) {
             if (!wait_all_started(P, c, started, in.pc)) return false;
-            if (lane < P.B) P.kv_lens_out[lane] = (int32_t)c.misc[M_KVLEN + lane] + 1;
+            if (lane < P.B) P.kv_lens_out[lane] = (int32_t)c.misc[M_KVLEN + lane] + P.n_steps;
         }
         return true;
     }
     if ((in.flags & F_STEP_FINAL) && in.merge >= 0) {  // last layer's down projection without an LM head
         if (elect_last(P, c, in) && P.kv_lens_out) {
             if (!wait_all_started(P, c, started_count(P), in.pc)) return false;
-            if (lane < P.B) P.kv_lens_out[lane] = (int32_t)c.misc[M_KVLEN + lane] + 1;
+            if (lane < P.B) P.kv_lens_out[lane] = (int32_t)c.misc[M_KVLEN + lane] + P.n_steps;
         }
     }
     return true;
@@ -1245,10 +1316,10 @@ __device__ __forceinline__ bool leave(const KParams &P, Ctx &c, const Ins &in, A
     uint32_t old = 0;
     if (lane == 0) old = lds_add(c.misc + M_FIN, 1u);
     old = __builtin_amdgcn_readfirstlane(old);  // lane 0's: every lane is active here
-    if (in.tr && lane == 0 && old == (uint32_t)NC * in.pc) in.tr[TR_FIRST] = wall_clock64();
-    if (in.tr && lane == 0 && old == (uint32_t)NC * (in.pc + 1) - 1) in.tr[TR_LAST] = wall_clock64();
+    if (in.tr && lane == 0 && old == (uint32_t)NC * in.gpc) in.tr[TR_FIRST] = wall_clock64();
+    if (in.tr && lane == 0 && old == (uint32_t)NC * (in.gpc + 1) - 1) in.tr[TR_LAST] = wall_clock64();
     if (in.op == OP_ATTN) return true;  // the attention loop published the tile and ended it
-    if (old != (uint32_t)NC * (in.pc + 1) - 1) return true;
+    if (old != (uint32_t)NC * (in.gpc + 1) - 1) return true;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if (!finish<G>(P, c, in)) return false;
     if (in.tr && lane == 0) in.tr[TR_END] = wall_clock64();
@@ -1283,6 +1354,18 @@ __device__ __forceinline__ void issue_any(int k, const KParams &P, const Cur &cu
 // one empty slice. After the last round wave h < G publishes head h's
 // softmax state as the chunk's (o, m, l); the last head published ends the
 // instruction. False on abort.
+// A wave that appended the step's K/V entry waits for that store before it
+// leaves the tile, in a resident launch (after its part of the tile, so
+// the tile is not held up): every later instruction of this unit starts once
+// all its waves have left, so everything the unit publishes afterwards - and
+// with it the next step's token - follows the completed append. A single
+// step needs no wait: the kernel's end completes every store.
+__device__ __forceinline__ bool attn_tile_left(const KParams &P, Ctx &c) {
+    if (P.n_steps > 1 && c.kv_pending) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    c.kv_pending = false;
+    return true;
+}
+
 template <int G>
 __device__ __forceinline__ bool attn_tile(const KParams &P, Ctx &c, Cur &ic, Cur &cc, const Ins &in, int &slot) {
     AttnRun run;
@@ -1292,7 +1375,8 @@ __device__ __forceinline__ bool attn_tile(const KParams &P, Ctx &c, Cur &ic, Cur
     bool took = false;
     for (int r = 0; uni(r < nround || !took); ++r) {
         // this wave's block of round r, or the tile's one empty slice
-        if (uni(cc.pc == pc && cc.op == OP_ATTN && (cc.u >= cc.nu ? !took : cc.u == c.w + r * NC))) {
+        if (uni(cc.pc == pc && cc.step == in.step && cc.op == OP_ATTN &&
+                (cc.u >= cc.nu ? !took : cc.u == c.w + r * NC))) {
             v4u buf[4];
             take_any(slot, buf);
             if (cc.u < cc.nu) attn_write_block<G>(c, cc, in, buf);
@@ -1304,24 +1388,24 @@ __device__ __forceinline__ bool attn_tile(const KParams &P, Ctx &c, Cur &ic, Cur
         }
         if (r < nround && !uni(attn_round_sync<G>(c, in, run))) return false;
     }
-    if (c.w >= G) return true;
+    if (c.w >= G) return attn_tile_left(P, c);
     const int h = c.w, lane = c.lane();
     const size_t pbase = ((((size_t)in.layer * P.B + in.b) * P.nkv + in.g) * in.nch + in.c) * G * ATTN_PART;
     const __amdgpu_buffer_rsrc_t rp = tres(P.tpart + pbase, (uint32_t)(G * ATTN_PART));
-    tput(rp, (uint32_t)(h * ATTN_PART + lane), run.O, P.tag);
+    tput(rp, (uint32_t)(h * ATTN_PART + lane), run.O, c.tag);
     if (lane == 0) {
-        tput(rp, (uint32_t)(h * ATTN_PART + 64), run.M, P.tag);
-        tput(rp, (uint32_t)(h * ATTN_PART + 65), run.L, P.tag);
+        tput(rp, (uint32_t)(h * ATTN_PART + 64), run.M, c.tag);
+        tput(rp, (uint32_t)(h * ATTN_PART + 65), run.L, c.tag);
     }
     uint32_t m = 0;
     if (lane == 0) m = lds_add_local(c.misc + M_AFIN, 1u);
     m = __builtin_amdgcn_readfirstlane(m);
     // a tile's publishes all end before the next tile's begin, so the count
     // reaches a multiple of G exactly at its last publish
-    if ((m + 1) % G != 0) return true;
+    if ((m + 1) % G != 0) return attn_tile_left(P, c);
     if (in.tr && lane == 0) in.tr[TR_END] = wall_clock64();
     if (lane == 0) lds_add_local(c.misc + M_DONE, 1u);
-    return true;
+    return attn_tile_left(P, c);
 }
 
 // The wave's main loop. Slices are consumed in the order they were issued,
@@ -1329,51 +1413,70 @@ __device__ __forceinline__ bool attn_tile(const KParams &P, Ctx &c, Cur &ic, Cur
 // it, and a wait for all but the 4 (D - 1) newest loads is a wait for
 // exactly this slot. At an instruction boundary the wave leaves the previous instruction
 // and enters the next one while the slices already issued stay in flight.
+// A resident launch runs its steps one after the other: past a step's END
+// the slots hold empty loads, which the wave waits for before it restarts
+// its cursors at the next step's first instruction and refills its window
+// (that step's layer 0 waits for this step's token anyway).
 template <int NB, int G>
 __device__ __forceinline__ void run(const KParams &P, Ctx &c) {
     static_assert(D >= 2 && D <= 4, "two to four slots");
     Cur ic, cc;
-    cur_load(P, c, ic, 0);
-    cur_load(P, c, cc, 0);
-    issue<0>(P, ic, c.lane());
-    cur_next(P, c, ic);
-    issue<1>(P, ic, c.lane());
-    cur_next(P, c, ic);
-    if constexpr (D > 2) {
-        issue<2>(P, ic, c.lane());
-        cur_next(P, c, ic);
-    }
-    if constexpr (D > 3) {
-        issue<3>(P, ic, c.lane());
-        cur_next(P, c, ic);
-    }
     Ins in{};
-    int slot = 0;
-    while (uni(cc.op != OP_END)) {
-        // per-instruction accumulators and register activations: nothing of
-        // them lives from one instruction to the next (an attention tile never
-        // holds a matvec's registers). The record `in` stays outside, which
-        // keeps the compiler's view of the cursors uniform.
-        Acc<NB> acc;
-        RegAct ra;
-        if (!uni(enter<NB, G>(P, c, cc, in, acc, ra))) break;
-        if (cc.op == OP_ATTN) {
-            if (!uni(attn_tile<G>(P, c, ic, cc, in, slot))) break;
-        } else {
-            for (;;) {
-                v4u buf[4];
-                take_any(slot, buf);
-                const bool empty = cc.u >= cc.nu;
-                if (!empty) consume_mv<NB>(P, c, cc, in, buf, acc, ra);
-                const bool last = empty || (cc.s == cc.sp - 1 && cc.u + NC >= cc.nu);
-                issue_any(slot, P, ic, c.lane());
-                cur_next(P, c, ic);
-                cur_next(P, c, cc);
-                slot = slot + 1 == D ? 0 : slot + 1;
-                if (uni(last)) break;
+    bool ok = true;
+    for (int step = 0; uni(ok && step < P.n_steps); ++step) {
+        // a step starts with its first D slices issued; the slots the
+        // previous step left hold empty loads issued past its END
+        if (step > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        cur_load(P, c, ic, 0, step);
+        cur_load(P, c, cc, 0, step);
+        issue<0>(P, ic, c.lane());
+        cur_next(P, c, ic);
+        issue<1>(P, ic, c.lane());
+        cur_next(P, c, ic);
+        if constexpr (D > 2) {
+            issue<2>(P, ic, c.lane());
+            cur_next(P, c, ic);
+        }
+        if constexpr (D > 3) {
+            issue<3>(P, ic, c.lane());
+            cur_next(P, c, ic);
+        }
+        int slot = 0;
+        while (uni(cc.op != OP_END)) {
+            // per-instruction accumulators and register activations: nothing of
+            // them lives from one instruction to the next (an attention tile never
+            // holds a matvec's registers). The record `in` stays outside, which
+            // keeps the compiler's view of the cursors uniform.
+            Acc<NB> acc;
+            RegAct ra;
+            if (!uni(enter<NB, G>(P, c, cc, in, acc, ra))) {
+                ok = false;
+                break;
+            }
+            if (cc.op == OP_ATTN) {
+                if (!uni(attn_tile<G>(P, c, ic, cc, in, slot))) {
+                    ok = false;
+                    break;
+                }
+            } else {
+                for (;;) {
+                    v4u buf[4];
+                    take_any(slot, buf);
+                    const bool empty = cc.u >= cc.nu;
+                    if (!empty) consume_mv<NB>(P, c, cc, in, buf, acc, ra);
+                    const bool last = empty || (cc.s == cc.sp - 1 && cc.u + NC >= cc.nu);
+                    issue_any(slot, P, ic, c.lane());
+                    cur_next(P, c, ic);
+                    cur_next(P, c, cc);
+                    slot = slot + 1 == D ? 0 : slot + 1;
+                    if (uni(last)) break;
+                }
+            }
+            if (!uni(leave<NB, G>(P, c, in, acc))) {
+                ok = false;
+                break;
             }
         }
-        if (!uni(leave<NB, G>(P, c, in, acc))) break;
     }
     // no load may still be writing a slot register when the wave ends
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1403,7 +1506,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(BLOCK_THREADS, BLOCK_THREA
     c.err = P.err;
     c.host_err = P.host_err;
     c.pending_timeout = -1;
-    for (int i = threadIdx.x; i < MISC_BYTES / 4; i += BLOCK_THREADS) c.misc[i] = 0;
+    c.kv_pending = false;
+    for (int i = threadIdx.x; i < MISC_BYTES / 4; i += BLOCK_THREADS) c.misc[i] = i == M_NQ ? (uint32_t)P.Q : 0u;
     __syncthreads();
     // the CU's queue and the request lengths are read once, here: scalar
     // reads of them later in the step would miss in caches that the weight
@@ -1411,11 +1515,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(BLOCK_THREADS, BLOCK_THREA
     {
         MK_LDS int32_t *q = (MK_LDS int32_t *)(lds + P.queue_off);
         const int32_t *src = P.queue + (int64_t)c.cu * P.Q * INSTR_WORDS;
-        for (int i = threadIdx.x; i < P.Q * LDS_INSTR_WORDS; i += BLOCK_THREADS)
-            q[i] = src[(i / LDS_INSTR_WORDS) * INSTR_WORDS + i % LDS_INSTR_WORDS];
+        for (int i = threadIdx.x; i < P.Q * LDS_INSTR_WORDS; i += BLOCK_THREADS) {
+            const int32_t v = src[(i / LDS_INSTR_WORDS) * INSTR_WORDS + i % LDS_INSTR_WORDS];
+            q[i] = v;
+            if (i % LDS_INSTR_WORDS == W_OP && v == OP_END)
+                __hip_atomic_fetch_min(c.misc + M_NQ, (uint32_t)(i / LDS_INSTR_WORDS), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
         if (threadIdx.x < (unsigned)P.B) c.misc[M_KVLEN + threadIdx.x] = (uint32_t)P.kv_lens[threadIdx.x];
     }
     __syncthreads();
+    c.nq = (int)__builtin_amdgcn_readfirstlane(c.misc[M_NQ]);
     // the lengths are in LDS (their loads have returned): count this
     // workgroup as started
     if (threadIdx.x == 0)

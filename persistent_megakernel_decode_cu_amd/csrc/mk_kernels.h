@@ -11,9 +11,12 @@ struct KParams {
     const int32_t *queue;     // [n_cus, Q, INSTR_WORDS]
     const int32_t *events;    // [n_events, EV_WORDS] merge events
     int32_t *counters;        // [n_counters * CTR_STRIDE]
-    int32_t Q, epoch, n_cus;
+    int32_t Q, epoch, n_cus;  // epoch: launches so far, this one included (start counter)
     int32_t start_ctr;        // counter every workgroup bumps once it has read kv_lens
-    uint32_t tag;             // this step's tag on every exchanged activation (never 0)
+    uint32_t tag;             // the first step's tag on every exchanged activation (never 0); step s uses tag + s
+    int32_t n_steps;          // greedy decode steps this launch runs (the grid stays resident across them)
+    int32_t step_epoch;       // merge-event epoch of the first step (steps so far, this one included)
+    uint64_t *ttok;           // [n_steps][B] tagged tokens each step hands to the next, or null (one step)
     int32_t queue_off, xrow_off, act_off, nw_off;  // LDS byte offsets
     int32_t act_stride;       // floats per request in the activation area
     int32_t xrow_stride;      // floats per request in the residual-row area
