@@ -9,10 +9,16 @@ gated up/gate, down + residual), final norm, tied LM head and greedy argmax.
 The timed steps form one greedy chain: each step's token and length feed the
 next on the device, with no host synchronisation inside the timed region.
 
+By default the chain runs as resident launches of up to 64 steps each (the
+grid stays resident across a launch's steps, mk_decode_steps); the same
+chain with one launch per step is timed beside it
+(`megakernel_launch_per_step`).
+
 Prints one JSON line. `value` is microseconds per decode step (lower is
 better); `roofline` gives the achieved algorithmic HBM bandwidth of the
-megakernel launch against the 8 TB/s peak; `step_us` the 10th, 50th and 90th
-percentiles of single steps within the chain; `read_probe` the read rate
+timed chain against the 8 TB/s peak; `step_us` the 10th, 50th and 90th
+percentiles of the per-step time (of single steps with one launch per step;
+of each launch's average with resident launches); `read_probe` the read rate
 the interpreter's streaming shape reaches on a plain buffer, a second,
 achievable peak; `cpu_baseline` times the CPU oracle on consecutive steps of
 the same workload; `unfused` times the one-kernel-per-op baseline on the
@@ -86,6 +92,47 @@ def time_chain(dec, ds, cfg, steps, warmup, torch, per_step=None):
         bounds = [t0] + marks + [t1]
         per_step.extend(bounds[k].elapsed_time(bounds[k + 1]) for k in range(steps))
     return t0.elapsed_time(t1) / steps
+
+
+def time_resident(dec, ds, cfg, steps, warmup, torch, per_launch=64, per_step=None):
+    """The same greedy chain as resident launches (mk_decode_steps): the
+    warmup steps in one untimed launch, then `steps` timed steps in launches
+    of up to `per_launch` steps, each launch starting from the previous
+    launch's last token (two token buffers alternate; no host
+    synchronisation in the timed region). Returns ms per timed step; with a
+    list `per_step`, appends each launch's ms per step."""
+    stream = torch.cuda.current_stream()
+    B = ds.tokens.shape[0]
+    rows = max(per_launch, warmup, 1)
+    bufs = [torch.zeros((rows, B), dtype=torch.int32, device="cuda") for _ in range(2)]
+    bufs[1][rows - 1].copy_(ds.tokens)
+    state = {"k": 0, "last": (1, rows - 1)}
+
+    def launch(n):
+        src, row = state["last"]
+        out = bufs[state["k"] % 2]
+        dec.step(kv_lens=ds.kv_lens, k_pool=ds.k_pool, v_pool=ds.v_pool, page_table=ds.page_table,
+                 tokens_in=bufs[src][row], tokens_out=out[:n] if n > 1 else out[0], kv_lens_out=ds.kv_lens,
+                 n_steps=n, stream=stream.cuda_stream)
+        state["last"] = (state["k"] % 2, n - 1)
+        state["k"] += 1
+
+    if warmup > 0:
+        launch(warmup)
+    dec.sync(stream.cuda_stream)
+    sizes = [per_launch] * (steps // per_launch) + ([steps % per_launch] if steps % per_launch else [])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sizes) + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for k, n in enumerate(sizes):
+        launch(n)
+        ev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    dec.sync(stream.cuda_stream)
+    if per_step is not None:
+        per_step.extend(ev[k].elapsed_time(ev[k + 1]) / n for k, n in enumerate(sizes))
+    ds.tokens.copy_(bufs[state["last"][0]][state["last"][1]])
+    return ev[0].elapsed_time(ev[-1]) / steps
 
 
 def time_graph_chain(dec, ds, cfg, steps, warmup, torch):
@@ -253,7 +300,10 @@ def main():
     ap.add_argument("--workload", default="1b-kv1024")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="megakernel", choices=["megakernel", "unfused"])
+    ap.add_argument("--mode", default="resident", choices=["resident", "megakernel", "unfused"],
+                    help="resident: the megakernel with the grid resident across up to --per-launch steps "
+                         "(mk_decode_steps); megakernel: one launch per step; unfused: one kernel per op")
+    ap.add_argument("--per-launch", type=int, default=64, help="steps per resident launch")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run the plain copy kernel three times over this many bytes "
                          "(the reference for the rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
@@ -296,15 +346,22 @@ def main():
 
     result_modes = {}
     env = {}
-    modes = [args.mode] + ([] if args.no_unfused or args.mode == "unfused" else ["unfused"])
+    modes = [args.mode]
+    if args.mode == "resident":
+        modes.append("megakernel")
+    if not args.no_unfused and args.mode != "unfused":
+        modes.append("unfused")
     for mode in modes:
-        info = dec.build_schedule(B, mode=mode, max_kv_len=max_len)
+        info = dec.build_schedule(B, mode="megakernel" if mode == "resident" else mode, max_kv_len=max_len)
         ds.kv_lens.copy_(torch.from_numpy(st0.kv_lens))
         ds.tokens.copy_(torch.from_numpy(st0.tokens))
         per_step = []
         if mode == args.mode:
             env["before"] = gpu_env()
-        ms = time_chain(dec, ds, cfg, args.steps, args.warmup, torch, per_step)
+        if mode == "resident":
+            ms = time_resident(dec, ds, cfg, args.steps, args.warmup, torch, args.per_launch, per_step)
+        else:
+            ms = time_chain(dec, ds, cfg, args.steps, args.warmup, torch, per_step)
         if mode == args.mode:
             env["after"] = gpu_env()
         result_modes[mode] = (ms, info, per_step)
@@ -334,7 +391,7 @@ def main():
     # HBM traffic per launch, measured with rocprofv3 counters (see the summary
     # file); reported only while the kernel sources are the ones it was taken on
     traffic = None
-    if args.mode == "megakernel":
+    if args.mode in ("megakernel", "resident"):
         from persistent_megakernel_decode_cu_amd import profile_summary
         rec = profile_summary.read_traffic(os.path.join(ROOT, "profiles", f"traffic_megakernel_{cfg.name}.txt"))
         if rec is not None and rec[1] == profile_summary.digest():
@@ -358,12 +415,17 @@ def main():
                                + (f"{int(st0.kv_lens[0])}" if B == 1 else
                                   f"{int(st0.kv_lens.min())}-{int(st0.kv_lens.max())} (paged)")
                                + ", greedy chain",
-                   "mode": args.mode, "n_cus": info["n_cus"], "launches_per_step": info["launches_per_step"],
+                   "mode": args.mode, "n_cus": info["n_cus"],
+                   "launches_per_step": (round(1.0 / min(args.per_launch, args.steps), 4) if args.mode == "resident"
+                                         else info["launches_per_step"]),
+                   "steps_per_launch": min(args.per_launch, args.steps) if args.mode == "resident" else 1,
                    "lds_bytes_per_workgroup": info["lds_bytes"]},
         "hbm_gbps": round(achieved, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                     "bytes_per_launch": int(bytes_avg)},
+                     "bytes_per_step": int(bytes_avg),
+                     "bytes_per_launch": int(bytes_avg * (min(args.per_launch, args.steps)
+                                                          if args.mode == "resident" else 1))},
         "step_us": {"p10": pct(per_step, 10), "p50": pct(per_step, 50), "p90": pct(per_step, 90)},
     }
     if args.probe_bytes > 0:
@@ -373,6 +435,13 @@ def main():
         out["read_probe"] = {"gbps": round(pg, 1), "bytes": args.probe_bytes,
                              "frac_of_probe": round(achieved / pg, 4),
                              "shape": "1 workgroup x 8 waves per CU, 4 slices of 4 KiB in flight per wave"}
+    if "megakernel" in result_modes and args.mode == "resident":
+        mms, _, mper = result_modes["megakernel"]
+        out["megakernel_launch_per_step"] = {"us_per_step": round(mms * 1000.0, 2),
+                                             "hbm_gbps": round(bytes_avg / (mms * 1e-3) / 1e9, 1),
+                                             "step_us": {"p10": pct(mper, 10), "p50": pct(mper, 50),
+                                                         "p90": pct(mper, 90)},
+                                             "speedup_of_resident": round(mms / ms, 3)}
     if "unfused" in result_modes and args.mode != "unfused":
         ums, uinfo, _ = result_modes["unfused"]
         out["unfused"] = {"us_per_step": round(ums * 1000.0, 2), "launches_per_step": uinfo["launches_per_step"],
