@@ -12,9 +12,11 @@ decode step) and "hand-written whole-model MegaKernel / principle, schedule
 and dataflow" (the op bodies and the object table). The per-function
 citations and the readings of what the page leaves open are in oracle.c.
 
-Two builds of the same source exist: ``liboracle_f64.so`` (double, the
-default and the one parity is judged against) and ``liboracle_f32.so``
-(single precision throughout).
+Two builds of the same source exist: ``liboracle_f32.so`` (single
+precision throughout: the plain single-threaded fp32 forward pass that GPU
+parity, the stored chain fixtures, the smoke check and the CPU baseline use)
+and ``liboracle_f64.so`` (double; the pins run on both builds, and the f32
+build tracks the f64 one to 1e-4 on logits).
 
 Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
 against closed forms, special cases that reduce to a library routine, and
