@@ -125,6 +125,12 @@ __device__ __forceinline__ float dot8(v4u w, v4f a0, v4f a1) {
     return s;
 }
 
+// A pair of binary16 values (the operand of the packed fp16 dot product).
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ h2v as_h2(uint32_t w) { return __builtin_bit_cast(h2v, w); }
+// a bf16 pair (low, high half) as a binary16 pair, each rounded to nearest even
+__device__ __forceinline__ h2v bf_pair_h2(uint32_t w) { return h2v{(_Float16)bf_lo(w), (_Float16)bf_hi(w)}; }
+
 // dot8 with the weights already converted to fp32 (the same arithmetic)
 __device__ __forceinline__ float dot8f(const float (&w)[8], v4f a0, v4f a1) {
     float s = w[0] * a0.x;

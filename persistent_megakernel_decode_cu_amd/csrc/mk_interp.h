@@ -53,10 +53,13 @@ enum : int {
 };
 
 constexpr int NC = N_COMPUTE_WAVES;
-// at a padded batch of 8 the down projection's input is staged in LDS as
-// binary16 (8 requests' fp32 inputs of 8192 do not fit)
+// At a padded batch of 8 every matvec input is staged in LDS as binary16,
+// request b's K values contiguous at b K (8 requests' fp32 inputs of 8192
+// would not fit in LDS, and the batched products read each activation once
+// per weight row: binary16 halves those reads and feeds the packed fp16 dot
+// product). A norm's input is gathered as fp32 past that area first.
 template <int NB>
-constexpr bool ACT16_DOWN = NB == 8;
+constexpr bool ACT16 = NB == 8;
 constexpr int D = PREFETCH_SLICES;
 
 // Every lane reads the same LDS word; readfirstlane makes that visible to the
@@ -657,24 +660,28 @@ __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &
     const int n = first < H ? (H - first + 255) / 256 : 0;  // this lane's elements
     const int nmax = (H - w * 64 + 255) / 256;               // lane 0's: the most
     prefetch_norm_w(P, c, wn);
+    // the fp32 input of request b, element i: in the matvec layout, or with
+    // binary16 staging contiguous past the binary16 area
+    auto xs = [&](int b, int i) -> MK_LDS float & {
+        if constexpr (ACT16<NB>) return c.act[(NB * H) / 2 + b * H + i];
+        else return c.act[b * P.act_stride + act_index(i)];
+    };
     // several requests: every wave gathers, all requests in shared rounds
     const bool batched = NB > 1 && xv != 0;
     if (batched) {
         if (!tgather_batch(
-                c, P.tx + (size_t)(xv - 1) * P.B * H, P.B, H,
-                [&](int b, int i, float v) { c.act[b * P.act_stride + act_index(i)] = v; }, in.pc))
+                c, P.tx + (size_t)(xv - 1) * P.B * H, P.B, H, [&](int b, int i, float v) { xs(b, i) = v; }, in.pc))
             return false;
         if (!cbar(c, in.pc)) return false;
     }
     if (w < 4) {
         for (int b = 0; b < P.B; ++b) {
-            MK_LDS float *a = c.act + b * P.act_stride;
             if (batched) {
                 // gathered above
             } else if (xv == 0) {
                 const int tok = P.has_embed ? token_of(P, c, b, in) : 0;
                 if (tok < 0) return false;
-                for (int i = first; i < H; i += 256) a[act_index(i)] = x_input(P, b, i, true, tok);
+                for (int i = first; i < H; i += 256) xs(b, i) = x_input(P, b, i, true, tok);
             } else {
                 const __amdgpu_buffer_rsrc_t r = tres(P.tx + ((size_t)(xv - 1) * P.B + b) * H, (uint32_t)H);
                 // the loop bound is uniform: an early return from a loop whose
@@ -683,12 +690,12 @@ __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &
                 for (int k0 = 0; k0 < nmax; k0 += 16)
                     if (!tgather<16>(
                             c, r, n - k0, [&](int k) { return (uint32_t)(first + 256 * (k0 + k)); },
-                            [&](int k, float v) { a[act_index(first + 256 * (k0 + k))] = v; }, in.pc))
+                            [&](int k, float v) { xs(b, first + 256 * (k0 + k)) = v; }, in.pc))
                         return false;
             }
             float ss = 0.0f;
             for (int i = first; i < H; i += 256) {
-                const float v = a[act_index(i)];
+                const float v = xs(b, i);
                 ss = fmaf(v, v, ss);
             }
             ss = wave_sum(ss);
@@ -710,8 +717,12 @@ __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &
             float tot = 0.0f;
             for (int v = 0; v < 4; ++v) tot += norm[v * MAX_B + b];
             const float inv = 1.0f / sqrtf(tot / (float)H + P.eps);
-            MK_LDS float *a = c.act + b * P.act_stride;
-            for (int i = first; i < H; i += 256) a[act_index(i)] = a[act_index(i)] * inv * bf2f(nw[i]);
+            if constexpr (ACT16<NB>) {
+                MK_LDS uint16_t *a16 = (MK_LDS uint16_t *)c.act + b * H;
+                for (int i = first; i < H; i += 256) a16[i] = f2h(xs(b, i) * inv * bf2f(nw[i]));
+            } else {
+                for (int i = first; i < H; i += 256) xs(b, i) = xs(b, i) * inv * bf2f(nw[i]);
+            }
         }
     }
     return cbar(c, in.pc);
@@ -757,19 +768,19 @@ __device__ __forceinline__ bool stage_copy(const KParams &P, Ctx &c, const Ins &
         return tgather_batch(
             c, src, P.B, K,
             [&](int b, int i, float v) {
-                if (A16) ((MK_LDS uint16_t *)c.act + b * 2 * P.act_stride)[act16_index(i)] = f2h(v);
+                if (A16) ((MK_LDS uint16_t *)c.act + b * K)[i] = f2h(v);
                 else c.act[b * P.act_stride + act_index(i)] = v;
             },
             in.pc);
     const int per = K / NC;
     for (int b = 0; b < P.B; ++b) {
         MK_LDS float *a = c.act + b * P.act_stride;
-        MK_LDS uint16_t *a16 = (MK_LDS uint16_t *)c.act + b * 2 * P.act_stride;
+        MK_LDS uint16_t *a16 = (MK_LDS uint16_t *)c.act + b * K;
         const __amdgpu_buffer_rsrc_t r = tres(src + (size_t)b * K, (uint32_t)K);
         if (!tgather_range(
                 c, r, c.w * per, (c.w + 1) * per,
                 [&](int i, float v) {
-                    if (A16) a16[act16_index(i)] = f2h(v);
+                    if (A16) a16[i] = f2h(v);
                     else a[act_index(i)] = v;
                 },
                 in.pc))
@@ -910,11 +921,11 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
         case OP_LMHEAD: ok = stage_norm<NB>(P, c, in, (const uint16_t *)(uintptr_t)in.wn, 2 * P.L); break;
         case OP_OPROJ:
             ok = stage_rows<NB>(P, c, in, (in.flags & F_X_FROM_INPUT) ? 0 : 2 * in.layer) &&
-                 stage_copy<false, NB>(P, c, in, P.to + (size_t)in.layer * P.B * P.nq * P.d, P.nq * P.d) && cbar(c, pc);
+                 stage_copy<ACT16<NB>, NB>(P, c, in, P.to + (size_t)in.layer * P.B * P.nq * P.d, P.nq * P.d) && cbar(c, pc);
             break;
         case OP_DOWN:
             ok = stage_rows<NB>(P, c, in, 2 * in.layer + 1) &&
-                 stage_copy<ACT16_DOWN<NB>, NB>(P, c, in, P.tact + (size_t)in.layer * P.B * P.F, P.F) && cbar(c, pc);
+                 stage_copy<ACT16<NB>, NB>(P, c, in, P.tact + (size_t)in.layer * P.B * P.F, P.F) && cbar(c, pc);
             break;
         case OP_ATTN: {
             const int p = in.b >= 0 && in.b < P.B ? (int)lds_ld_const(c.misc + M_KVLEN + in.b) + in.step : -1;
@@ -1035,7 +1046,39 @@ __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &
                       v4f{xr.o[j][4], xr.o[j][5], xr.o[j][6], xr.o[j][7]});
         acc.a0[0] = m ? acc.a0[0] : a;
         acc.a1[0] = m ? a : acc.a1[0];
-    } else if (k.K >= (part + 1) * 2048) {
+    } else if (ACT16<NB> && k.K >= (part + 1) * 2048) {
+        // binary16 staging: the slice's weights as binary16 pairs once (bf16
+        // to binary16 with round-to-nearest-even; the weights' magnitudes lie
+        // far inside its range), then per request eight 16-byte activation
+        // reads and packed fp16 dot products accumulating in fp32
+        h2v wh[4][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            wh[j][0] = bf_pair_h2(r[j].x);
+            wh[j][1] = bf_pair_h2(r[j].y);
+            wh[j][2] = bf_pair_h2(r[j].z);
+            wh[j][3] = bf_pair_h2(r[j].w);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float a = ONE_ACC<NB> ? acc.a0[b] : (m ? acc.a1[b] : acc.a0[b]);
+            const MK_LDS uint16_t *ab = (const MK_LDS uint16_t *)c.act + b * k.K + part * 2048 + lane * 8;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const v4u x = *(const MK_LDS v4u *)(ab + j * 512);
+                a = __builtin_amdgcn_fdot2(wh[j][0], as_h2(x.x), a, false);
+                a = __builtin_amdgcn_fdot2(wh[j][1], as_h2(x.y), a, false);
+                a = __builtin_amdgcn_fdot2(wh[j][2], as_h2(x.z), a, false);
+                a = __builtin_amdgcn_fdot2(wh[j][3], as_h2(x.w), a, false);
+            }
+            if constexpr (ONE_ACC<NB>) {
+                acc.a0[b] = a;
+            } else {
+                acc.a0[b] = m ? acc.a0[b] : a;
+                acc.a1[b] = m ? a : acc.a1[b];
+            }
+        }
+    } else if (!ACT16<NB> && k.K >= (part + 1) * 2048) {
         // the slice's weights as fp32 once; then each request's activations
         // are read right before its products, so that few are live at once
         float wf[4][8];
@@ -1050,24 +1093,13 @@ __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &
             wf[j][6] = bf_lo(r[j].w);
             wf[j][7] = bf_hi(r[j].w);
         }
-        const bool act16 = ACT16_DOWN<NB> && in.op == OP_DOWN;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             float a = ONE_ACC<NB> ? acc.a0[b] : (m ? acc.a1[b] : acc.a0[b]);
-            if (act16) {
-                const MK_LDS uint16_t *ab = (const MK_LDS uint16_t *)c.act + b * 2 * P.act_stride + part * 2048 + lane * 8;
+            const MK_LDS float *ab = c.act + b * P.act_stride + part * 2048 + lane * 4;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const v4u x = *(const MK_LDS v4u *)(ab + j * 512);
-                    a += dot8f(wf[j], v4f{h_lo(x.x), h_hi(x.x), h_lo(x.y), h_hi(x.y)},
-                               v4f{h_lo(x.z), h_hi(x.z), h_lo(x.w), h_hi(x.w)});
-                }
-            } else {
-                const MK_LDS float *ab = c.act + b * P.act_stride + part * 2048 + lane * 4;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    a += dot8f(wf[j], *(const MK_LDS v4f *)(ab + j * 512), *(const MK_LDS v4f *)(ab + j * 512 + 256));
-            }
+            for (int j = 0; j < 4; ++j)
+                a += dot8f(wf[j], *(const MK_LDS v4f *)(ab + j * 512), *(const MK_LDS v4f *)(ab + j * 512 + 256));
             if constexpr (ONE_ACC<NB>) {
                 acc.a0[b] = a;
             } else {
@@ -1084,8 +1116,15 @@ __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &
                 const int base = ((ci >> 6) << 9) + ((ci & 63) << 2);
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
-                    const MK_LDS float *a = c.act + b * P.act_stride + base;
-                    const float d = dot8(r[j], *(const MK_LDS v4f *)a, *(const MK_LDS v4f *)(a + 256));
+                    float d;
+                    if constexpr (ACT16<NB>) {
+                        const v4u x = *(const MK_LDS v4u *)((const MK_LDS uint16_t *)c.act + b * k.K + ci * 8);
+                        d = dot8(r[j], v4f{h_lo(x.x), h_hi(x.x), h_lo(x.y), h_hi(x.y)},
+                                 v4f{h_lo(x.z), h_hi(x.z), h_lo(x.w), h_hi(x.w)});
+                    } else {
+                        const MK_LDS float *a = c.act + b * P.act_stride + base;
+                        d = dot8(r[j], *(const MK_LDS v4f *)a, *(const MK_LDS v4f *)(a + 256));
+                    }
                     if (ONE_ACC<NB> || m == 0) acc.a0[b] += d;
                     else acc.a1[b] += d;
                 }

@@ -332,9 +332,10 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
 
     // LDS layout (capacity obligation: everything a tile stages must fit)
     const int NBP = B <= 1 ? 1 : B <= 2 ? 2 : B <= 4 ? 4 : 8;  // requests the interpreter is compiled for
-    // at a padded batch of 8 the down projection's input is staged as
-    // binary16 (half the bytes); every other matvec input is fp32
-    const int kmax = NBP == 8 ? std::max({H, QD, (F + 1) / 2}) : std::max(H, std::max(F, QD));
+    // at a padded batch of 8 every matvec input is staged as binary16 (half
+    // the bytes), a norm's input first gathered as fp32 past it (1.5 H
+    // floats per request); otherwise every input is fp32
+    const int kmax = NBP == 8 ? std::max({(3 * H + 1) / 2, (QD + 1) / 2, (F + 1) / 2}) : std::max(H, std::max(F, QD));
     P.act_stride = (kmax + 511) / 512 * 512;
     P.xrow_stride = (max_rows_x + 3) / 4 * 4;
     // matvec inputs; attention staging (queries, new K/V entry) and one
