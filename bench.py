@@ -407,7 +407,9 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 weights, fp32 compute",
+        "dtype": ("bf16 weights, fp32 compute" if B <= 4 else
+                  "bf16 weights; matvec inputs staged as binary16 and multiplied by packed fp16 dot products "
+                  "accumulating in fp32 (padded batch 8); fp32 elsewhere"),
         "data": "synthetic (seeded random-init weights and K/V cache)",
         "config": {"workload": f"{cfg.name}: {cfg.n_layers}-layer Llama-3.2-1B shape (H {cfg.hidden}, "
                                f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}, F {cfg.ffn}, V {cfg.vocab}, "
