@@ -304,6 +304,8 @@ def main():
                     help="resident: the megakernel with the grid resident across up to --per-launch steps "
                          "(mk_decode_steps); megakernel: one launch per step; unfused: one kernel per op")
     ap.add_argument("--per-launch", type=int, default=64, help="steps per resident launch")
+    ap.add_argument("--no-launch-per-step", action="store_true",
+                    help="with --mode resident, skip the comparison chain of one launch per step")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after timing, run the plain copy kernel three times over this many bytes "
                          "(the reference for the rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
@@ -347,7 +349,7 @@ def main():
     result_modes = {}
     env = {}
     modes = [args.mode]
-    if args.mode == "resident":
+    if args.mode == "resident" and not args.no_launch_per_step:
         modes.append("megakernel")
     if not args.no_unfused and args.mode != "unfused":
         modes.append("unfused")

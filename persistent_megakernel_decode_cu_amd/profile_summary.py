@@ -89,7 +89,7 @@ def _counter_bytes(db: str, counter: str, kernel: str, copy_kernel: str, skip: i
 
 
 def traffic_text(fetch_db: str, write_db: str, kernel: str, copy_kernel: str, copy_bytes: int, commands,
-                 skip: int) -> str:
+                 skip: int, steps_per_launch: int = 1) -> str:
     f_mk, f_cp, nf = _counter_bytes(fetch_db, "FETCH_SIZE", kernel, copy_kernel, skip)
     w_mk, w_cp, nw = _counter_bytes(write_db, "WRITE_SIZE", kernel, copy_kernel, skip)
     ff, fw = f_cp / copy_bytes, w_cp / copy_bytes
@@ -104,6 +104,8 @@ def traffic_text(fetch_db: str, write_db: str, kernel: str, copy_kernel: str, co
              f"fetch_bytes_per_launch: {fetch:.0f}",
              f"write_bytes_per_launch: {write:.0f}",
              f"traffic_bytes_per_launch: {fetch + write:.0f}",
+             f"steps_per_launch: {steps_per_launch}",
+             f"traffic_bytes_per_step: {(fetch + write) / steps_per_launch:.0f}",
              f"source_digest: {digest()}"]
     return "\n".join(lines) + "\n"
 
@@ -130,7 +132,8 @@ def counters_text(dbs, kernel: str, commands, skip: int) -> str:
 
 
 def read_traffic(path: str):
-    """(traffic bytes per launch, source digest) of a traffic summary, or None."""
+    """(traffic bytes per decode step, source digest) of a traffic summary,
+    or None (a launch of a resident run covers steps_per_launch steps)."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -138,7 +141,8 @@ def read_traffic(path: str):
         k, _, v = line.partition(":")
         kv[k.strip()] = v.strip()
     try:
-        return float(kv["traffic_bytes_per_launch"]), kv["source_digest"]
+        steps = float(kv.get("steps_per_launch", "1").split()[0])
+        return float(kv["traffic_bytes_per_launch"]) / steps, kv["source_digest"]
     except (KeyError, ValueError):
         return None
 
@@ -156,6 +160,7 @@ def main(argv=None):
     b.add_argument("--copy-kernel", default="mk_copy_probe")
     b.add_argument("--copy-bytes", type=int, required=True)
     b.add_argument("--skip", type=int, default=1, help="leading dispatches of the kernel to leave out (warm-up)")
+    b.add_argument("--steps-per-launch", type=int, default=1, help="decode steps one launch of the kernel runs")
     b.add_argument("--command", action="append", required=True)
     c = sub.add_parser("counters")
     c.add_argument("dbs", nargs="+")
@@ -170,7 +175,7 @@ def main(argv=None):
         if len(args.command) != 2:
             ap.error("give --command twice: the FETCH_SIZE run, then the WRITE_SIZE run")
         sys.stdout.write(traffic_text(args.fetch, args.write, args.kernel, args.copy_kernel, args.copy_bytes,
-                                      args.command, args.skip))
+                                      args.command, args.skip, args.steps_per_launch))
     elif args.what == "counters":
         sys.stdout.write(counters_text(args.dbs, args.kernel, args.command, args.skip))
     else:
