@@ -304,6 +304,9 @@ def main():
                     help="resident: the megakernel with the grid resident across up to --per-launch steps "
                          "(mk_decode_steps); megakernel: one launch per step; unfused: one kernel per op")
     ap.add_argument("--per-launch", type=int, default=64, help="steps per resident launch")
+    ap.add_argument("--no-gpu-env", action="store_true",
+                    help="skip the amd-smi readings (a child process; for runs under a profiler, whose preloaded "
+                         "library counts the child's program start as an exec after GPU initialisation)")
     ap.add_argument("--no-launch-per-step", action="store_true",
                     help="with --mode resident, skip the comparison chain of one launch per step")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -358,13 +361,13 @@ def main():
         ds.kv_lens.copy_(torch.from_numpy(st0.kv_lens))
         ds.tokens.copy_(torch.from_numpy(st0.tokens))
         per_step = []
-        if mode == args.mode:
+        if mode == args.mode and not args.no_gpu_env:
             env["before"] = gpu_env()
         if mode == "resident":
             ms = time_resident(dec, ds, cfg, args.steps, args.warmup, torch, args.per_launch, per_step)
         else:
             ms = time_chain(dec, ds, cfg, args.steps, args.warmup, torch, per_step)
-        if mode == args.mode:
+        if mode == args.mode and not args.no_gpu_env:
             env["after"] = gpu_env()
         result_modes[mode] = (ms, info, per_step)
         print(f"# {mode}: {ms * 1000:.1f} us/step", file=sys.stderr, flush=True)
