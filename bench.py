@@ -318,6 +318,10 @@ def main():
                     help="skip the one-kernel-per-op chain replayed from a captured HIP graph")
     ap.add_argument("--probe-bytes", type=int, default=2 << 30,
                     help="bytes the register-slice read probe streams for the achievable-read-rate figure (0: skip)")
+    ap.add_argument("--attn-chunks", type=int, default=0,
+                    help="attention tiles per request on average (each kv head gets batch x this many); 0 = auto")
+    ap.add_argument("--attn-split", default="balanced", choices=["balanced", "per_request"],
+                    help="how each step shares a kv head's attention tiles out over the requests")
     ap.add_argument("--trace-layer", type=int, default=-1,
                     help="after timing, run three untimed steps of a traced megakernel schedule and print the "
                          "per-op timeline of this layer to stderr")
@@ -349,6 +353,7 @@ def main():
     max_len = int(st0.kv_lens.max()) + chain
     dec = gu.make_decoder(model, st0, wdev)
 
+    split = {"attn_chunks": args.attn_chunks, "attn_split": args.attn_split}
     result_modes = {}
     env = {}
     modes = [args.mode]
@@ -357,7 +362,7 @@ def main():
     if not args.no_unfused and args.mode != "unfused":
         modes.append("unfused")
     for mode in modes:
-        info = dec.build_schedule(B, mode="megakernel" if mode == "resident" else mode, max_kv_len=max_len)
+        info = dec.build_schedule(B, mode="megakernel" if mode == "resident" else mode, max_kv_len=max_len, **split)
         ds.kv_lens.copy_(torch.from_numpy(st0.kv_lens))
         ds.tokens.copy_(torch.from_numpy(st0.tokens))
         per_step = []
@@ -374,7 +379,7 @@ def main():
 
     graph_ms = None
     if "unfused" in result_modes and not args.no_graph_baseline:
-        dec.build_schedule(B, mode="unfused", max_kv_len=max_len)
+        dec.build_schedule(B, mode="unfused", max_kv_len=max_len, **split)
         ds.kv_lens.copy_(torch.from_numpy(st0.kv_lens))
         ds.tokens.copy_(torch.from_numpy(st0.tokens))
         graph_ms = time_graph_chain(dec, ds, cfg, args.steps, args.warmup, torch)
@@ -426,7 +431,8 @@ def main():
                    "launches_per_step": (round(1.0 / min(args.per_launch, args.steps), 4) if args.mode == "resident"
                                          else info["launches_per_step"]),
                    "steps_per_launch": min(args.per_launch, args.steps) if args.mode == "resident" else 1,
-                   "lds_bytes_per_workgroup": info["lds_bytes"]},
+                   "lds_bytes_per_workgroup": info["lds_bytes"],
+                   "attn_tiles_per_kv_head": B * info["attn_chunks"], "attn_split": args.attn_split},
         "hbm_gbps": round(achieved, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
@@ -461,12 +467,13 @@ def main():
     if args.trace_layer >= 0:
         # a separate traced schedule, outside the timed region
         from persistent_megakernel_decode_cu_amd import _mk, trace_summary
-        tinfo = dec.build_schedule(B, mode="megakernel", max_kv_len=max_len, trace=True)
+        tinfo = dec.build_schedule(B, mode="megakernel", max_kv_len=max_len, trace=True, **split)
         ds.kv_lens.copy_(torch.from_numpy(st0.kv_lens))
         ds.tokens.copy_(torch.from_numpy(st0.tokens))
         for _ in range(3):
             gu.run_step(dec, ds, cfg, want_logits=False)
-        plan = _mk.Plan(dec.cfg, _mk.MkScheduleDesc(B, tinfo["n_cus"], 0, max_len, 0, 1, 0, 0, 0))
+        plan = _mk.Plan(dec.cfg, _mk.MkScheduleDesc(B, tinfo["n_cus"], 0, max_len, args.attn_chunks, 1, 0,
+                                                    {"balanced": 0, "per_request": 1}[args.attn_split], 0))
         text = trace_summary.timeline(dec.trace(), trace_summary.decode_queue(plan.queue), args.trace_layer)
         for line in text.splitlines():
             print(f"# {line}", file=sys.stderr, flush=True)

@@ -67,6 +67,23 @@ typedef enum mk_mode {
     MK_MODE_UNFUSED = 1     /* one kernel launch per op (comparison baseline) */
 } mk_mode;
 
+/* How the attention work of a step is shared out ("Inference MegaKernel",
+ * shaojiemike.top, section "hand-written whole-model MegaKernel / limits": a
+ * queue fixed before the step cannot follow requests of different lengths).
+ * Each kv head has batch x attn_chunks attention tiles in the queues; which
+ * request and which K/V blocks a tile covers is computed on the device at
+ * every step from the requests' lengths then, the same way in both modes of
+ * mk_mode. Request b covers nb_b = ceil((kv_len_b + 1) / 16) blocks. */
+typedef enum mk_attn_split {
+    /* the smallest tile size s (blocks) with sum_b ceil(nb_b / s) <= tiles;
+     * request b gets ceil(nb_b / s) tiles, the spare ones go to the request
+     * with the most blocks (lowest index among equals); each request's
+     * blocks are cut evenly over its tiles */
+    MK_SPLIT_BALANCED = 0,
+    /* attn_chunks tiles per request, whatever its length */
+    MK_SPLIT_PER_REQUEST = 1
+} mk_attn_split;
+
 /* Model shape and capacity. Requirements: head_dim == 64; n_q_heads a
  * multiple of n_kv_heads with n_q_heads / n_kv_heads <= 8; hidden, ffn and
  * n_q_heads * head_dim each a multiple of 512 or equal to 256; page_tokens
@@ -78,8 +95,9 @@ typedef struct mk_config {
     float rms_eps, rope_theta;
     int32_t max_batch;
     int32_t page_tokens;        /* K/V positions per page, 16 */
-    int32_t max_pages_per_req;  /* page-table columns; a request may hold up
-                                   to max_pages_per_req * page_tokens positions */
+    int32_t max_pages_per_req;  /* page-table columns, 1..65535; a request may
+                                   hold up to max_pages_per_req * page_tokens
+                                   positions */
     int32_t device;             /* HIP device ordinal */
 } mk_config;
 
@@ -106,10 +124,14 @@ typedef struct mk_schedule_desc {
     int32_t mode;            /* mk_mode */
     int32_t max_kv_len;      /* the largest kv_lens[b] a step will see; sizes
                                 the attention split; <= capacity - 1 */
-    int32_t attn_chunks;     /* K/V chunks per (request, kv head); 0 = auto */
+    int32_t attn_chunks;     /* attention tiles per request, on average: each kv
+                                head gets batch x attn_chunks tiles; 0 = auto */
     int32_t trace;           /* 1: record per-instruction device timestamps */
     int64_t watchdog_spins;  /* bound of every device wait loop; 0 = default */
-    int32_t reserved0;       /* must be 0 */
+    int32_t attn_split;      /* how a kv head's tiles are shared out over the
+                                requests, on the device at every step, from
+                                the current lengths: MK_SPLIT_BALANCED (0)
+                                or MK_SPLIT_PER_REQUEST (1) */
     int32_t reserved1;       /* must be 0 */
 } mk_schedule_desc;
 
@@ -275,6 +297,17 @@ int mk_debug_copy_probe(const void *src_dev, void *dst_dev, size_t bytes, void *
  * MK_EINVAL, MK_EHIP. */
 int mk_debug_litmus(int pairs, int n_words, int rounds, int mode, int32_t *data_dev, int32_t *flags_dev,
                     int32_t *res_dev);
+
+/* The attention split (mk_attn_split) as the device computes it, for
+ * n_cases batches of `batch` requests: kv_lens_dev [n_cases][batch] int32
+ * (each clamped to 0..capacity - 1, as a step does); `tiles` per kv head
+ * (batch <= tiles <= 128, a multiple of batch for MK_SPLIT_PER_REQUEST);
+ * out_dev [n_cases][4 tiles + batch + 1] int32: per tile its request, first
+ * block, end block and 1 on a request's last tile, then the first tile of
+ * each request and `tiles`. One wave per case; synchronous. Errors:
+ * MK_EINVAL, MK_EHIP. */
+int mk_debug_attn_split(const int32_t *kv_lens_dev, int n_cases, int batch, int tiles, int mode, int capacity,
+                        int32_t *out_dev);
 
 /* Dependency-hop latency: a cooperative grid of n_cus one-wave workgroups
  * runs `rounds` grid-wide hops (wait for every workgroup's previous round,

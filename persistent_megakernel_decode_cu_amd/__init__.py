@@ -20,6 +20,7 @@ from ._mk import (MK_MODE_MEGAKERNEL, MK_MODE_UNFUSED, MkConfig, MkError, MkLaye
                   mk_destroy, mk_get_schedule_info, mk_last_error, mk_read_trace, mk_sync_status)
 
 _MODES = {"megakernel": MK_MODE_MEGAKERNEL, "unfused": MK_MODE_UNFUSED}
+_SPLITS = {"balanced": 0, "per_request": 1}  # MK_SPLIT_BALANCED, MK_SPLIT_PER_REQUEST
 _LAYER_KEYS = ("attn_norm", "wqkv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")
 
 
@@ -85,8 +86,10 @@ class Decoder:
         self.batch = 0
 
     def build_schedule(self, batch: int, mode: str = "megakernel", max_kv_len: int = 0, attn_chunks: int = 0,
-                       n_cus: int = 0, trace: bool = False, watchdog_spins: int = 0) -> dict:
-        desc = MkScheduleDesc(batch, n_cus, _MODES[mode], max_kv_len, attn_chunks, int(trace), watchdog_spins, 0, 0)
+                       n_cus: int = 0, trace: bool = False, watchdog_spins: int = 0,
+                       attn_split: str = "balanced") -> dict:
+        desc = MkScheduleDesc(batch, n_cus, _MODES[mode], max_kv_len, attn_chunks, int(trace), watchdog_spins,
+                              _SPLITS[attn_split], 0)
         mk_build_schedule(self.handle, desc)
         self.batch = batch
         self.mode = mode

@@ -41,7 +41,7 @@ class MkWeights(ctypes.Structure):
 
 class MkScheduleDesc(ctypes.Structure):
     _fields_ = [("batch", i32), ("n_cus", i32), ("mode", i32), ("max_kv_len", i32),
-                ("attn_chunks", i32), ("trace", i32), ("watchdog_spins", i64), ("reserved0", i32),
+                ("attn_chunks", i32), ("trace", i32), ("watchdog_spins", i64), ("attn_split", i32),
                 ("reserved1", i32)]
 
 
@@ -84,6 +84,7 @@ _SIGS = {
     "mk_debug_copy_scratch": (i32, [vp, i32, vp, ctypes.c_size_t]),
     "mk_debug_copy_probe": (i32, [vp, vp, ctypes.c_size_t, vp]),
     "mk_debug_litmus": (i32, [i32, i32, i32, i32, vp, vp, vp]),
+    "mk_debug_attn_split": (i32, [vp, i32, i32, i32, i32, i32, vp]),
     "mk_debug_hop_probe": (i32, [vp, ctypes.c_size_t, vp, ctypes.c_size_t, i32, i32, i32, vp]),
     "mk_debug_ll_probe": (i32, [vp, ctypes.c_size_t, i32, i32, i32, i32, vp]),
     "mk_debug_regstream_probe": (i32, [vp, ctypes.c_size_t, i32, i32, i32, vp]),
@@ -178,6 +179,11 @@ def mk_debug_copy_scratch(handle: int, which: str, n_floats: int) -> np.ndarray:
 
 def mk_debug_copy_probe(src_ptr: int, dst_ptr: int, nbytes: int, stream: int = 0) -> None:
     _check(lib().mk_debug_copy_probe(src_ptr, dst_ptr, nbytes, stream))
+
+
+def mk_debug_attn_split(kv_lens_ptr: int, n_cases: int, batch: int, tiles: int, mode: int, capacity: int,
+                        out_ptr: int) -> None:
+    _check(lib().mk_debug_attn_split(kv_lens_ptr, n_cases, batch, tiles, mode, capacity, out_ptr))
 
 
 def mk_debug_regstream_probe(src_ptr: int, nbytes: int, blocks: int, threads: int, depth: int, out_ptr: int) -> None:

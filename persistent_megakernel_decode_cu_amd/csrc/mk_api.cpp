@@ -465,6 +465,7 @@ static int decode_step(mk_handle *h, const mk_step_io *io, void *stream, const S
         k.tpart = sl ? sl->tpart : h->tpart;
         k.tlm = sl ? sl->tlm : h->tlm;
         k.attn_chunks = P.attn_chunks;
+        k.attn_split = P.desc.attn_split;
         k.err = h->err;
         k.host_err = h->host_err_dev;
         k.trace = h->trace;
@@ -593,6 +594,17 @@ int mk_debug_litmus(int pairs, int n_words, int rounds, int mode, int32_t *data_
         !res_dev)
         return set_error(MK_EINVAL, "bad litmus arguments");
     MK_HIP(mk::litmus(pairs, n_words, rounds, mode, data_dev, flags_dev, res_dev));
+    return MK_OK;
+}
+
+int mk_debug_attn_split(const int32_t *kv_lens_dev, int n_cases, int batch, int tiles, int mode, int capacity,
+                        int32_t *out_dev) {
+    if (!kv_lens_dev || !out_dev || n_cases < 1 || n_cases > 65535 || batch < 1 || batch > mk::MAX_B ||
+        tiles < batch || tiles > mk::MAX_ATTN_TILES || capacity < 1 || capacity > 65535 * 16 ||
+        (mode != mk::SPLIT_BALANCED && mode != mk::SPLIT_PER_REQUEST) ||
+        (mode == mk::SPLIT_PER_REQUEST && tiles % batch != 0))
+        return set_error(MK_EINVAL, "bad attention split arguments");
+    MK_HIP(mk::split_probe(kv_lens_dev, n_cases, batch, tiles, mode, capacity, out_dev));
     return MK_OK;
 }
 

@@ -321,6 +321,112 @@ __device__ __forceinline__ void merge_init(float &O, float &M, float &L) {
     L = 0.0f;
 }
 
+// ------------------------------------------------------------ attention split
+// "Inference MegaKernel" (shaojiemike.top), section "hand-written whole-model
+// MegaKernel / limits": a queue fixed before the step cannot follow requests
+// whose lengths differ. The queue here stays fixed - each kv head has T
+// attention instructions ("tiles") - but what each tile does is decided on
+// the device at every step, from the requests' current lengths: every wave
+// that needs the split computes it from the same inputs, so all agree
+// without exchanging anything.
+//
+// Request b covers nb[b] = ceil((p_b + 1) / 16) K/V blocks (positions
+// 0..p_b). Balanced: s is the smallest tile size, in blocks, for which
+// ceil(nb[b] / s) tiles per request fit in T; request b gets that many tiles,
+// the T - sum spare tiles go to the request with the most blocks (the lowest
+// index of those), and each request's blocks are cut evenly over its tiles,
+// tile j of n getting [j nb / n, (j + 1) nb / n). Per request: T / B tiles
+// each. Tiles are numbered request by request; the last tile of a request
+// holds its block of position p_b.
+
+// blocks of a request whose newest position is p (clamped to the capacity;
+// an out-of-range length is reported by the attention staging)
+__device__ __forceinline__ int attn_nblocks(int p, int cap) {
+    p = p < 0 ? 0 : (p >= cap ? cap - 1 : p);
+    return (p + 16) >> 4;
+}
+
+// n[b]: tiles of request b (0 for b >= B). Every lane of the wave takes
+// part (the search for s tries 64 sizes at once) and gets the same counts;
+// nb and B are the same on every lane; 1 <= B <= T <= MAX_ATTN_TILES.
+__device__ __forceinline__ void attn_split_counts(const int (&nb)[MAX_B], int B, int T, bool balanced, int lane,
+                                                  int (&n)[MAX_B]) {
+    if (!balanced) {
+#pragma unroll
+        for (int b = 0; b < MAX_B; ++b) n[b] = b < B ? T / B : 0;
+        return;
+    }
+    int N = 0, mx = 0, bm = 0;
+#pragma unroll
+    for (int b = 0; b < MAX_B; ++b)
+        if (b < B) {
+            N += nb[b];
+            if (nb[b] > mx) {
+                mx = nb[b];
+                bm = b;
+            }
+        }
+    // f(s) = sum ceil(nb / s) does not increase with s; f(mx) = B <= T, and
+    // f(s) <= N / s + B <= T once s >= N / (T - B); f(s) >= N / s > T below
+    // ceil(N / T). Each pass tries 64 sizes spread over [lo, hi] (the last
+    // one hi) and keeps the gap below the first that fits.
+    int lo = max(1, (N + T - 1) / T), hi = mx;
+    if (T > B) hi = min(hi, (N + T - B - 1) / (T - B));
+    while (lo < hi) {
+        const int stride = (hi - lo + 62) / 63;
+        const int cand = min(hi, lo + stride * lane);
+        int f = 0;
+#pragma unroll
+        for (int b = 0; b < MAX_B; ++b)
+            if (b < B) f += (nb[b] + cand - 1) / cand;
+        const uint64_t ok = __builtin_amdgcn_ballot_w64(f <= T);
+        const int k = (int)__builtin_ctzll(ok);  // lane 63 holds hi, which fits
+        const int ck = __builtin_amdgcn_readlane(cand, k);
+        lo = k == 0 ? ck : __builtin_amdgcn_readlane(cand, k - 1) + 1;
+        hi = ck;
+    }
+    int used = 0;
+#pragma unroll
+    for (int b = 0; b < MAX_B; ++b) {
+        n[b] = b < B ? (nb[b] + lo - 1) / lo : 0;
+        used += n[b];
+    }
+#pragma unroll
+    for (int b = 0; b < MAX_B; ++b)
+        if (b == bm) n[b] += T - used;
+}
+
+// Tile t (< sum n): its request b, blocks [lo, hi) of it, and whether it is
+// the request's last tile.
+__device__ __forceinline__ void attn_split_tile(const int (&nb)[MAX_B], const int (&n)[MAX_B], int t, int &b, int &lo,
+                                                int &hi, bool &last) {
+    int first = 0, rb = -1, rn = 1, rnb = 0, rf = 0;
+#pragma unroll
+    for (int j = 0; j < MAX_B; ++j) {
+        if (rb < 0 && t < first + n[j]) {
+            rb = j;
+            rn = n[j];
+            rnb = nb[j];
+            rf = first;
+        }
+        first += n[j];
+    }
+    const int jj = t - rf;
+    b = rb;
+    lo = jj * rnb / rn;
+    hi = (jj + 1) * rnb / rn;
+    last = jj == rn - 1;
+}
+
+// first tile of request b
+__device__ __forceinline__ int attn_split_first(const int (&n)[MAX_B], int b) {
+    int f = 0;
+#pragma unroll
+    for (int j = 0; j < MAX_B; ++j)
+        if (j < b) f += n[j];
+    return f;
+}
+
 // (value, index) order of the greedy pick: larger value, then lower index
 __device__ __forceinline__ bool amax_better(float v, int i, float bv, int bi) {
     return v > bv || (v == bv && i < bi);

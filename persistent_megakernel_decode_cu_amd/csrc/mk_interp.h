@@ -50,9 +50,17 @@ enum : int {
     M_KVLEN = 8,   // [MAX_B] lengths of the requests (read once at start)
     M_NORM = 16,   // [4][MAX_B] sums of squares
     M_AMAX = 64,   // [NC][MAX_B][2] per-wave argmax (value, index)
+    // the attention split of a step, one of two areas by
+    // the step's parity: the first tile of each request ([MAX_B + 1], at 0),
+    // then per tile its request (| 256 on a request's last tile) and its
+    // blocks lo | hi << 16 (two words, at SPLIT_TILE)
+    M_SPLIT = 256,
+    SPLIT_TILE = 16,
+    SPLIT_WORDS = SPLIT_TILE + 2 * MAX_ATTN_TILES,
 };
 
 constexpr int NC = N_COMPUTE_WAVES;
+static_assert(M_AMAX + NC * MAX_B * 2 <= M_SPLIT && M_SPLIT + 2 * SPLIT_WORDS <= MISC_BYTES / 4, "LDS misc area");
 // At a padded batch of 8 every matvec input is staged in LDS as binary16,
 // request b's K values contiguous at b K (8 requests' fp32 inputs of 8192
 // would not fit in LDS, and the batched products read each activation once
@@ -218,10 +226,39 @@ static_assert(W_OP == 0 && W_LAYER == 1 && W_R0 == 2 && W_R1 == 3 && W_B == 4 &&
                   W_WN + 4 <= LDS_INSTR_WORDS,
               "instruction record layout read by iw4");
 
-__device__ __forceinline__ void chunk_blocks(int p, int c, int nch, int *lo, int *hi) {
-    const int nb = (p + 1 + 15) >> 4;
-    *lo = (int)((int64_t)c * nb / nch);
-    *hi = (int)((int64_t)(c + 1) * nb / nch);
+// The attention split of a step (mk_device.h): every wave writes it, from
+// the lengths all waves read, into the step's area at its own start of the
+// step (the same values whichever wave writes last), and reads back only
+// what it wrote itself. The area of step s is rewritten at step s + 2, which
+// no wave starts before every wave has finished step s. The interpreter for
+// a single request has no table (its split is the even cut of its blocks).
+__device__ __forceinline__ MK_LDS uint32_t *split_area(const Ctx &c, int step) {
+    return c.misc + M_SPLIT + (step & 1) * SPLIT_WORDS;
+}
+// a word of the step's split, as this wave wrote it
+__device__ __forceinline__ uint32_t split_word(const Ctx &c, int step, int i) {
+    return __builtin_amdgcn_readfirstlane(split_area(c, step)[i]);
+}
+template <int NB>
+__device__ __forceinline__ void split_build(const KParams &P, Ctx &c, int step) {
+    if constexpr (NB == 1) return;  // one request: the cursors cut its blocks evenly themselves
+    const int lane = lane_id(), T = P.B * P.attn_chunks, cap = P.T * P.max_pages;
+    int nb[MAX_B], n[MAX_B];
+#pragma unroll
+    for (int b = 0; b < MAX_B; ++b)
+        nb[b] = b < P.B ? attn_nblocks((int)lds_ld_const(c.misc + M_KVLEN + b) + step, cap) : 0;
+    attn_split_counts(nb, P.B, T, P.attn_split == SPLIT_BALANCED, lane, n);
+    MK_LDS uint32_t *a = split_area(c, step);
+    for (int t = lane; t < T; t += WAVE) {
+        int b, lo, hi;
+        bool last;
+        attn_split_tile(nb, n, t, b, lo, hi, last);
+        a[SPLIT_TILE + 2 * t] = (uint32_t)b | (last ? 256u : 0u);
+        a[SPLIT_TILE + 2 * t + 1] = (uint32_t)lo | ((uint32_t)hi << 16);
+    }
+    if (lane <= P.B) a[lane] = (uint32_t)attn_split_first(n, lane);
+    // the wave's lanes read one another's words: its LDS accesses stay in order
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 }
 
 // Reads the tagged words idx(k), k < n (n <= N, per lane), until each
@@ -321,6 +358,7 @@ struct Cur {
 // cross a step's END themselves: the main loop restarts them at the next
 // step (logic for that here, in the slice loop's path, costs the whole step
 // dearly in code quality).
+template <int NB>
 __device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k, int pc, int step) {
     k.step = step;
     k.pc = pc;
@@ -340,13 +378,26 @@ __device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k,
     k.layer = rfl(a[1]);
     k.r0 = rfl(a[2]);
     if (k.op == OP_ATTN) {
-        k.b = rfl(bw[0]);
         k.g = rfl(bw[1]);
-        int p = (int)lds_ld_const(c.misc + M_KVLEN + (k.b & (MAX_B - 1))) + step;
-        if (p < 0 || p >= P.T * P.max_pages) p = 0;  // the staging raises the error
-        k.p = p;
+        const int t = rfl(bw[2]), cap = P.T * P.max_pages;
         int lo, hi;
-        chunk_blocks(p, rfl(bw[2]), rfl(bw[3]), &lo, &hi);
+        if constexpr (NB == 1) {  // one request: tile t of T takes blocks [t nb / T, (t + 1) nb / T)
+            const int T = rfl(bw[3]), nb = attn_nblocks((int)lds_ld_const(c.misc + M_KVLEN) + step, cap);
+            k.b = 0;
+            // 64-bit: the compiler keeps this division on the scalar unit (a
+            // 32-bit one it moves to the vector unit, which measured slower
+            // in the slice loop this is inlined into)
+            lo = (int)((int64_t)t * nb / T);
+            hi = (int)((int64_t)(t + 1) * nb / T);
+        } else {
+            const uint32_t w0 = split_word(c, step, SPLIT_TILE + 2 * t), w1 = split_word(c, step, SPLIT_TILE + 2 * t + 1);
+            k.b = (int)(w0 & (MAX_B - 1));
+            lo = (int)(w1 & 0xffffu);
+            hi = (int)(w1 >> 16);
+        }
+        int p = (int)lds_ld_const(c.misc + M_KVLEN + k.b) + step;
+        if (p < 0 || p >= cap) p = 0;  // the staging raises the error
+        k.p = p;
         k.blo = lo;
         k.nu = hi - lo;
     } else if (k.op == OP_AMERGE) {
@@ -363,6 +414,7 @@ __device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k,
     // an unknown opcode yields one empty slice; its staging raises the error
 }
 
+template <int NB>
 __device__ __forceinline__ void cur_next(const KParams &P, const Ctx &c, Cur &k) {
     if (k.op == OP_END) return;
     if (k.u < k.nu) {
@@ -372,7 +424,7 @@ __device__ __forceinline__ void cur_next(const KParams &P, const Ctx &c, Cur &k)
         }
         if (k.u < k.nu) return;
     }
-    cur_load(P, c, k, k.pc + 1, k.step);
+    cur_load<NB>(P, c, k, k.pc + 1, k.step);
 }
 
 // Buffer resource words for a byte range (gfx950 raw buffer, stride 0):
@@ -586,6 +638,7 @@ struct Ins {
     int gpc;   // step * (queue length) + pc: the instruction's index in the LDS counts
     int pc, op, layer, r0, r1, flags, b, g, c, nch, p, merge, slot, nslot, mctr, mneed;
     int nblk;     // attention: K/V blocks of the tile
+    bool alast;   // attention: the tile holds its request's newest position (and appends it)
     uint64_t wn;  // norm weight of the op's input
     int64_t *tr;
 };
@@ -789,47 +842,73 @@ __device__ __forceinline__ bool stage_copy(const KParams &P, Ctx &c, const Ins &
     return true;
 }
 
-// AMERGE: the chunk states (o, m, l) that the attention tiles of request b
-// and kv head g published are gathered into LDS (the activation area, which
-// no other part of a merge uses) by all waves, then merged in
-// chunk order, one wave per query head of the group (lane = dim), and
-// o = O / L is published for the O projection: one gather round per merge,
-// and the O projection reads only the merged outputs.
+// AMERGE: the softmax states (o, m, l) that the attention tiles of request
+// b and kv head g published - the request's tiles of this step's split, in
+// tile order - are gathered into LDS (the activation area, which no other
+// part of a merge uses) by all waves, MAX_ATTN_CHUNKS tiles at a time, and
+// merged in tile order, one wave per query head of the group (lane = dim);
+// then o = O / L is published for the O projection, which reads only the
+// merged outputs.
+
+// nc gathered states (in LDS) into head h's running state, in tile order:
+// eight states' reads at a time, then their merge steps (the registers of
+// all sixteen would spill)
 template <int G>
-__device__ __forceinline__ bool stage_amerge(const KParams &P, Ctx &c, const Ins &in) {
-    const int nch = in.nch, lane = c.lane();
-    const int n = nch * G * ATTN_PART;
-    const size_t pbase = (((size_t)in.layer * P.B + in.b) * P.nkv + in.g) * nch * G * ATTN_PART;
-    const __amdgpu_buffer_rsrc_t rp = tres(P.tpart + pbase, (uint32_t)n);
-    const int per = (n + NC - 1) / NC;
-    if (!tgather_range(
-            c, rp, c.w * per, min(n, (c.w + 1) * per), [&](int i, float v) { c.act[i] = v; }, in.pc))
-        return false;
-    if (!cbar(c, in.pc)) return false;
-    if (c.w < G && nch <= MAX_ATTN_CHUNKS) {
-        const int h = c.w;
-        float O, M, L;
-        merge_init(O, M, L);
-        // eight chunk states' reads at a time, then their merge steps in
-        // chunk order (the registers of all sixteen would spill)
-        for (int c0 = 0; c0 < nch; c0 += 8) {
-            float o[8], m[8], l[8];
+__device__ __forceinline__ void merge_states(const Ctx &c, int nc, int h, int lane, float &O, float &M, float &L) {
+    for (int k0 = 0; k0 < nc; k0 += 8) {
+        float o[8], m[8], l[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (c0 + k < nch) {
-                    const MK_LDS float *src = c.act + ((c0 + k) * G + h) * ATTN_PART;
-                    o[k] = src[lane];
-                    m[k] = src[64];
-                    l[k] = src[65];
-                }
+        for (int k = 0; k < 8; ++k)
+            if (k0 + k < nc) {
+                const MK_LDS float *src = c.act + ((k0 + k) * G + h) * ATTN_PART;
+                o[k] = src[lane];
+                m[k] = src[64];
+                l[k] = src[65];
+            }
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (c0 + k < nch) merge_step(O, M, L, o[k], m[k], l[k]);
-        }
-        const int QD = P.nq * P.d;
-        tput(tres(P.to + ((size_t)in.layer * P.B + in.b) * QD, (uint32_t)QD), (uint32_t)((in.g * G + h) * 64 + lane),
-             O / L, c.tag);
+        for (int k = 0; k < 8; ++k)
+            if (k0 + k < nc) merge_step(O, M, L, o[k], m[k], l[k]);
     }
+}
+
+template <int NB, int G>
+__device__ __forceinline__ bool stage_amerge(const KParams &P, Ctx &c, const Ins &in) {
+    const int T = in.nch, lane = c.lane(), QD = P.nq * P.d;
+    const __amdgpu_buffer_rsrc_t ro = tres(P.to + ((size_t)in.layer * P.B + in.b) * QD, (uint32_t)QD);
+    if constexpr (NB == 1) {
+        // one request: its T (<= MAX_ATTN_CHUNKS) tiles in one gather (the
+        // round loop below measured slower here)
+        const int n = T * G * ATTN_PART, per = (n + NC - 1) / NC;
+        const __amdgpu_buffer_rsrc_t rp = tres(P.tpart + ((size_t)in.layer * P.nkv + in.g) * n, (uint32_t)n);
+        if (!tgather_range(
+                c, rp, c.w * per, min(n, (c.w + 1) * per), [&](int i, float v) { c.act[i] = v; }, in.pc))
+            return false;
+        if (!cbar(c, in.pc)) return false;
+        if (c.w < G && T <= MAX_ATTN_CHUNKS) {
+            float O, M, L;
+            merge_init(O, M, L);
+            merge_states<G>(c, T, c.w, lane, O, M, L);
+            tput(ro, (uint32_t)((in.g * G + c.w) * 64 + lane), O / L, c.tag);
+        }
+        return true;
+    }
+    const int first = (int)split_word(c, in.step, in.b), nt = (int)split_word(c, in.step, in.b + 1) - first;
+    const size_t base = (((size_t)in.layer * P.nkv + in.g) * T + first) * G * ATTN_PART;
+    float O, M, L;
+    merge_init(O, M, L);
+    for (int c0 = 0; uni(c0 < nt); c0 += MAX_ATTN_CHUNKS) {
+        const int nc = min(MAX_ATTN_CHUNKS, nt - c0);
+        const int n = nc * G * ATTN_PART, per = (n + NC - 1) / NC;
+        const __amdgpu_buffer_rsrc_t rp = tres(P.tpart + base + (size_t)c0 * G * ATTN_PART, (uint32_t)n);
+        if (!tgather_range(
+                c, rp, c.w * per, min(n, (c.w + 1) * per), [&](int i, float v) { c.act[i] = v; }, in.pc))
+            return false;
+        if (!cbar(c, in.pc)) return false;
+        if (c.w < G) merge_states<G>(c, nc, c.w, lane, O, M, L);
+        // the head waves have read these states before the next ones land
+        if (c0 + MAX_ATTN_CHUNKS < nt && !cbar(c, in.pc)) return false;
+    }
+    if (c.w < G) tput(ro, (uint32_t)((in.g * G + c.w) * 64 + lane), O / L, c.tag);
     return true;
 }
 
@@ -841,7 +920,7 @@ __device__ __forceinline__ bool stage_attn(const KParams &P, Ctx &c, const Ins &
     const int lane = c.lane();
     const int QD = P.nq * P.d, QKVN = QD + 2 * P.nkv * P.d;
     const int b = in.b, g = in.g, p = in.p;
-    const bool last = in.c == in.nch - 1;
+    const bool last = in.alast;
     MK_LDS uint16_t *kvn = (MK_LDS uint16_t *)(c.act + G * 64);
     const __amdgpu_buffer_rsrc_t r = tres(P.tqkv + ((size_t)in.layer * P.B + b) * QKVN, (uint32_t)QKVN);
     const float2 cs = P.rope[(int64_t)p * 32 + (lane & 31)];
@@ -928,17 +1007,24 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
                  stage_copy<ACT16<NB>, NB>(P, c, in, P.tact + (size_t)in.layer * P.B * P.F, P.F) && cbar(c, pc);
             break;
         case OP_ATTN: {
-            const int p = in.b >= 0 && in.b < P.B ? (int)lds_ld_const(c.misc + M_KVLEN + in.b) + in.step : -1;
+            // the cursor's request and blocks of this tile at this step
+            in.b = k.b;
+            in.nblk = k.nu;
+            // the tile holding the request's newest position appends it
+            if constexpr (NB == 1)
+                in.alast = in.c == in.nch - 1;
+            else
+                in.alast = (split_word(c, in.step, SPLIT_TILE + 2 * in.c) & 256u) != 0;
+            const int p = (int)lds_ld_const(c.misc + M_KVLEN + k.b) + in.step;
             if (p < 0 || p >= P.T * P.max_pages) {
                 if (c.lane() == 0) raise_err(c, ERR_RANGE, pc);
                 return false;
             }
             in.p = p;
-            in.nblk = k.nu;  // the cursor's blocks of this tile at this length
             ok = stage_attn<G>(P, c, in);
             break;
         }
-        case OP_AMERGE: ok = stage_amerge<G>(P, c, in); break;
+        case OP_AMERGE: ok = stage_amerge<NB, G>(P, c, in); break;
         default:
             if (c.lane() == 0) raise_err(c, ERR_OPCODE, pc);
             return false;
@@ -1405,7 +1491,7 @@ __device__ __forceinline__ bool attn_tile_left(const KParams &P, Ctx &c) {
     return true;
 }
 
-template <int G>
+template <int NB, int G>
 __device__ __forceinline__ bool attn_tile(const KParams &P, Ctx &c, Cur &ic, Cur &cc, const Ins &in, int &slot) {
     AttnRun run;
     attn_run_init(run);
@@ -1421,15 +1507,15 @@ __device__ __forceinline__ bool attn_tile(const KParams &P, Ctx &c, Cur &ic, Cur
             if (cc.u < cc.nu) attn_write_block<G>(c, cc, in, buf);
             took = true;
             issue_any(slot, P, ic, c.lane());
-            cur_next(P, c, ic);
-            cur_next(P, c, cc);
+            cur_next<NB>(P, c, ic);
+            cur_next<NB>(P, c, cc);
             slot = slot + 1 == D ? 0 : slot + 1;
         }
         if (r < nround && !uni(attn_round_sync<G>(c, in, run))) return false;
     }
     if (c.w >= G) return attn_tile_left(P, c);
     const int h = c.w, lane = c.lane();
-    const size_t pbase = ((((size_t)in.layer * P.B + in.b) * P.nkv + in.g) * in.nch + in.c) * G * ATTN_PART;
+    const size_t pbase = (((size_t)in.layer * P.nkv + in.g) * in.nch + in.c) * G * ATTN_PART;
     const __amdgpu_buffer_rsrc_t rp = tres(P.tpart + pbase, (uint32_t)(G * ATTN_PART));
     tput(rp, (uint32_t)(h * ATTN_PART + lane), run.O, c.tag);
     if (lane == 0) {
@@ -1466,19 +1552,20 @@ __device__ __forceinline__ void run(const KParams &P, Ctx &c) {
         // a step starts with its first D slices issued; the slots the
         // previous step left hold empty loads issued past its END
         if (step > 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        cur_load(P, c, ic, 0, step);
-        cur_load(P, c, cc, 0, step);
+        split_build<NB>(P, c, step);
+        cur_load<NB>(P, c, ic, 0, step);
+        cur_load<NB>(P, c, cc, 0, step);
         issue<0>(P, ic, c.lane());
-        cur_next(P, c, ic);
+        cur_next<NB>(P, c, ic);
         issue<1>(P, ic, c.lane());
-        cur_next(P, c, ic);
+        cur_next<NB>(P, c, ic);
         if constexpr (D > 2) {
             issue<2>(P, ic, c.lane());
-            cur_next(P, c, ic);
+            cur_next<NB>(P, c, ic);
         }
         if constexpr (D > 3) {
             issue<3>(P, ic, c.lane());
-            cur_next(P, c, ic);
+            cur_next<NB>(P, c, ic);
         }
         int slot = 0;
         while (uni(cc.op != OP_END)) {
@@ -1493,7 +1580,7 @@ __device__ __forceinline__ void run(const KParams &P, Ctx &c) {
                 break;
             }
             if (cc.op == OP_ATTN) {
-                if (!uni(attn_tile<G>(P, c, ic, cc, in, slot))) {
+                if (!uni(attn_tile<NB, G>(P, c, ic, cc, in, slot))) {
                     ok = false;
                     break;
                 }
@@ -1505,8 +1592,8 @@ __device__ __forceinline__ void run(const KParams &P, Ctx &c) {
                     if (!empty) consume_mv<NB>(P, c, cc, in, buf, acc, ra);
                     const bool last = empty || (cc.s == cc.sp - 1 && cc.u + NC >= cc.nu);
                     issue_any(slot, P, ic, c.lane());
-                    cur_next(P, c, ic);
-                    cur_next(P, c, cc);
+                    cur_next<NB>(P, c, ic);
+                    cur_next<NB>(P, c, cc);
                     slot = slot + 1 == D ? 0 : slot + 1;
                     if (uni(last)) break;
                 }

@@ -23,12 +23,12 @@ namespace mk {
 enum Op : int32_t {
     OP_END = 0,
     OP_QKV = 1,     // rows [r0,r1) of Wqkv . rmsnorm(x_{2l})             -> qkv_l
-    OP_ATTN = 2,    // request b, kv head g, K/V chunk c of nch            -> o_l (merged by the last chunk)
+    OP_ATTN = 2,    // kv head g, tile c of nch: request and K/V blocks split at run time -> a softmax state
     OP_OPROJ = 3,   // rows [r0,r1) of Wo . o_l, plus residual x_{2l}       -> x_{2l+1}
     OP_UPGATE = 4,  // rows [r0,r1) of Wgate, Wup . rmsnorm(x_{2l+1}), SiLU -> act_l
     OP_DOWN = 5,    // rows [r0,r1) of Wdown . act_l, plus residual x_{2l+1} -> x_{2l+2}
     OP_LMHEAD = 6,  // rows [r0,r1) of E . rmsnorm_final(x_{2L}), argmax   -> logits, token
-    OP_AMERGE = 7,  // request b, kv head g: merge the chunks' softmax states -> o_l
+    OP_AMERGE = 7,  // request b, kv head g: merge its tiles' softmax states -> o_l
     OP_COUNT = 8
 };
 
@@ -92,10 +92,15 @@ constexpr int MAX_B = 8;
 constexpr int TRACE_WORDS = 8;  // MK_TRACE_WORDS of mk.h
 enum : int { TR_START = 0, TR_READY = 1, TR_END = 2, TR_FIRST = 3, TR_LAST = 4, TR_ELECT = 5, TR_GATHER = 6 };
 constexpr int MAX_G = 8;
-// K/V chunks per (request, kv head), merged by one AMERGE instruction
+// Attention tiles: each kv head has batch x attn_chunks of them, shared out
+// over the requests at every step (the attention split of mk_device.h); an
+// AMERGE merges one request's tiles, MAX_ATTN_CHUNKS at a time
 constexpr int MAX_ATTN_CHUNKS = 16;
-// chunks the automatic choice stops at
+constexpr int MAX_ATTN_TILES = MAX_B * MAX_ATTN_CHUNKS;
+// chunks per request the automatic choice stops at
 constexpr int AUTO_ATTN_CHUNKS = 16;
+// attention split modes (mk_schedule_desc::attn_split)
+enum : int32_t { SPLIT_BALANCED = 0, SPLIT_PER_REQUEST = 1 };
 
 // device error word: code << 28 | cu << 16 | pc
 enum : int32_t { ERR_TIMEOUT = 1, ERR_OPCODE = 2, ERR_RANGE = 3, ERR_NAN = 4 };

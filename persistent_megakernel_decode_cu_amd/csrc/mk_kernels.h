@@ -42,16 +42,17 @@ struct KParams {
     uint64_t *tx;      // [2L][B][H]: x_1 .. x_{2L} (x_v at index v - 1)
     uint64_t *tqkv;    // [L][B][(nq + 2 nkv) d]
     uint64_t *tact;    // [L][B][F]
-    uint64_t *tpart;   // [L][B][nkv][chunks][G][ATTN_PART] attention chunk partials
+    uint64_t *tpart;   // [L][nkv][B chunks][G][ATTN_PART] attention tile states
     uint64_t *to;      // [L][B][nq d] merged attention outputs
     uint64_t *tlm;     // [lm slots][B][2] argmax partials (value, index)
-    int32_t attn_chunks;
+    int32_t attn_chunks;  // tiles per request, on average: each kv head has B attn_chunks tiles
+    int32_t attn_split;   // SPLIT_BALANCED or SPLIT_PER_REQUEST
     // one-kernel-per-op baseline scratch (fp32, overwritten in place)
     float *x;          // [B, H] residual stream
     float *qkv;        // [B, (nq + 2 nkv) d]
     float *o;          // [B, nq d] attention output
     float *act;        // [B, F] gated MLP activation
-    float *attn_part;  // [B, nkv, chunks, G, ATTN_PART_STRIDE]
+    float *attn_part;  // [nkv, B chunks, G, ATTN_PART_STRIDE]
     float *lm_part;    // [lm slots, B, 2]
     int32_t *err;      // device error word
     int32_t *host_err; // mapped host mirror of the error word
@@ -73,6 +74,7 @@ hipError_t megakernel_occupancy(int B, int G, int lds_bytes, int *blocks_per_cu)
 hipError_t launch_unfused(const KParams &p, float *u_scratch, float *qrot, hipStream_t s);
 hipError_t copy_probe(const void *src, void *dst, size_t bytes, hipStream_t s);
 hipError_t litmus(int pairs, int n, int rounds, int mode, int32_t *data, int32_t *flags, int32_t *res);
+hipError_t split_probe(const int32_t *kv, int n_cases, int B, int T, int mode, int cap, int32_t *out);
 hipError_t hop_probe(int32_t *ctr, float *xbuf, int n_cus, int rounds, int variant, int32_t *res);
 hipError_t ll_probe(uint64_t *buf, int n_cus, int per, int copies, int rounds, int32_t *res);
 hipError_t regstream_probe(const void *src, size_t bytes, int blocks, int threads, int depth, uint32_t *out);

@@ -300,6 +300,34 @@ hipError_t litmus(int pairs, int n, int rounds, int mode, int32_t *data, int32_t
     return hipDeviceSynchronize();
 }
 
+// The attention split of mk_device.h for a batch of kv lengths per case, one
+// wave per case.
+__global__ __launch_bounds__(64) void mk_split_probe(const int32_t *kv, int B, int T, int mode, int cap, int32_t *out) {
+    const int cs = blockIdx.x, lane = threadIdx.x;
+    int nb[MAX_B], n[MAX_B];
+#pragma unroll
+    for (int b = 0; b < MAX_B; ++b) nb[b] = b < B ? attn_nblocks(kv[(int64_t)cs * B + b], cap) : 0;
+    attn_split_counts(nb, B, T, mode == SPLIT_BALANCED, lane, n);
+    int32_t *o = out + (int64_t)cs * (4 * T + B + 1);
+    for (int t = lane; t < T; t += 64) {
+        int b, lo, hi;
+        bool last;
+        attn_split_tile(nb, n, t, b, lo, hi, last);
+        o[4 * t] = b;
+        o[4 * t + 1] = lo;
+        o[4 * t + 2] = hi;
+        o[4 * t + 3] = last ? 1 : 0;
+    }
+    if (lane <= B) o[4 * T + lane] = attn_split_first(n, lane);
+}
+
+hipError_t split_probe(const int32_t *kv, int n_cases, int B, int T, int mode, int cap, int32_t *out) {
+    hipLaunchKernelGGL(mk_split_probe, dim3(n_cases), dim3(64), 0, nullptr, kv, B, T, mode, cap, out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return hipDeviceSynchronize();
+}
+
 // Plain device copy of n16 16-byte words: each word is read once and written
 // once, so its traffic counters calibrate those of the other kernels.
 __global__ __launch_bounds__(256) void mk_copy_probe(const v4u *src, v4u *dst, size_t n16) {

@@ -92,35 +92,12 @@ int check_config(const mk_config &c) {
         return set_error(MK_EINVAL, "hidden, ffn and n_q_heads*head_dim must each be 256 or a multiple of 512");
     if (c.page_tokens != 16) return set_error(MK_EINVAL, "page_tokens must be 16");
     if (c.max_batch < 1 || c.max_batch > MAX_B) return set_error(MK_EINVAL, "max_batch must be in 1..8");
-    if (c.max_pages_per_req < 1) return set_error(MK_EINVAL, "max_pages_per_req must be positive");
+    if (c.max_pages_per_req < 1 || c.max_pages_per_req > 65535)
+        return set_error(MK_EINVAL, "max_pages_per_req must be in 1..65535");
     if (c.has_embed != 0 && c.has_embed != 1) return set_error(MK_EINVAL, "has_embed must be 0 or 1");
     if (c.has_embed && c.vocab < 1) return set_error(MK_EINVAL, "vocab must be positive with an embedding");
     if (!(c.rms_eps >= 0.0f) || !(c.rope_theta > 0.0f)) return set_error(MK_EINVAL, "bad rms_eps or rope_theta");
     return MK_OK;
-}
-
-void attn_chunk_blocks(int kv_len, int page_tokens, int c, int nch, int *lo, int *hi) {
-    const int nb = (kv_len + 1 + page_tokens - 1) / page_tokens;  // blocks covering positions 0..kv_len
-    *lo = (int)((int64_t)c * nb / nch);
-    *hi = (int)((int64_t)(c + 1) * nb / nch);
-}
-
-int64_t instr_stream_bytes(const mk_config &cfg, const int32_t *ins, int kv_len) {
-    const int64_t H = cfg.hidden, F = cfg.ffn, QD = (int64_t)cfg.n_q_heads * cfg.head_dim;
-    const int64_t rows = ins[W_R1] - ins[W_R0];
-    switch (ins[W_OP]) {
-        case OP_QKV: return rows * H * 2;
-        case OP_OPROJ: return rows * QD * 2;
-        case OP_UPGATE: return rows * H * 2 * 2;
-        case OP_DOWN: return rows * F * 2;
-        case OP_LMHEAD: return rows * H * 2;
-        case OP_ATTN: {
-            int lo, hi;
-            attn_chunk_blocks(kv_len, cfg.page_tokens, ins[W_C], ins[W_NCH], &lo, &hi);
-            return (int64_t)(hi - lo) * 2 * cfg.page_tokens * cfg.head_dim * 2;
-        }
-        default: return 0;
-    }
 }
 
 int unfused_launches(const mk_config &cfg) {
@@ -139,7 +116,9 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     if (S < 1) return set_error(MK_EINVAL, "n_cus must be positive");
     if (desc.mode != MK_MODE_MEGAKERNEL && desc.mode != MK_MODE_UNFUSED)
         return set_error(MK_EINVAL, "unknown mode");
-    if (desc.reserved0 != 0 || desc.reserved1 != 0) return set_error(MK_EINVAL, "reserved fields must be 0");
+    if (desc.attn_split != SPLIT_BALANCED && desc.attn_split != SPLIT_PER_REQUEST)
+        return set_error(MK_EINVAL, "unknown attn_split");
+    if (desc.reserved1 != 0) return set_error(MK_EINVAL, "reserved fields must be 0");
     const int T = cfg.page_tokens, cap = cfg.max_pages_per_req * T;
     int maxlen = desc.max_kv_len > 0 ? desc.max_kv_len : cap - 1;
     if (maxlen > cap - 1 || maxlen < 0)
@@ -153,10 +132,14 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     // about one K/V block per wave on half the waves (one wave per SIMD,
     // which then has the vector unit to itself): attention is short
     // arithmetic on few units, so it is spread wide; with more requests there
-    // are more tiles already, and half the chunk cap
-    int C = desc.attn_chunks > 0 ? desc.attn_chunks
-                                 : std::min(B <= 2 ? AUTO_ATTN_CHUNKS : AUTO_ATTN_CHUNKS / 2,
-                                            std::max(1, ceil_div(nb_max, N_COMPUTE_WAVES / 2)));
+    // are more tiles already, and half the chunk cap, and no more tiles than
+    // compute units (a unit's second tile would start only after its first,
+    // while the balanced split already evens out the tiles' sizes)
+    int C = desc.attn_chunks > 0
+                ? desc.attn_chunks
+                : std::min(B <= 2 ? AUTO_ATTN_CHUNKS : AUTO_ATTN_CHUNKS / 2,
+                           std::max(1, ceil_div(nb_max, N_COMPUTE_WAVES / 2)));
+    if (desc.attn_chunks <= 0 && B > 2) C = std::min(C, std::max(1, S / (B * cfg.n_kv_heads)));
     C = std::min(C, nb_max);
     P.attn_chunks = C;
     P.n_cus = S;
@@ -212,28 +195,31 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
         // units carrying attention chunks get fewer of its rows.
         std::fill(cum.begin(), cum.end(), 0);
         matvec_op(OP_QKV, l, QKV, (int64_t)H * 2, first);
-        // attention chunks, each publishing its softmax state; then one
-        // merge per (request, kv head), on the least-loaded unit
-        for (int b = 0; b < B; ++b)
-            for (int g = 0; g < nkv; ++g) {
-                for (int c = 0; c < C; ++c) {
-                    Tile t;
-                    t.op = OP_ATTN;
-                    t.layer = l;
-                    t.b = b;
-                    t.g = g;
-                    t.c = c;
-                    t.nch = C;
-                    t.merge = -1;
-                    t.slot = c;
-                    t.nslot = C;
-                    int lo, hi;
-                    attn_chunk_blocks(maxlen, T, c, C, &lo, &hi);
-                    t.bytes = (int64_t)(hi - lo) * 2 * T * d * 2;
-                    t.cu = pick_least(cum);
-                    cum[t.cu] += t.bytes;
-                    tiles.push_back(t);
-                }
+        // B x C attention tiles per kv head, each publishing one softmax
+        // state: which request and K/V blocks a tile takes is decided on the
+        // device at every step (the attention split), so each is charged an
+        // equal share of the batch's K/V at max_kv_len; then one merge per
+        // (request, kv head), on the least-loaded unit
+        const int TT = B * C;
+        for (int g = 0; g < nkv; ++g)
+            for (int c = 0; c < TT; ++c) {
+                // a single request's split is fixed: tile c of its blocks
+                const int64_t blocks = B == 1 ? (int64_t)(c + 1) * nb_max / TT - (int64_t)c * nb_max / TT
+                                              : (int64_t)ceil_div((int64_t)B * nb_max, TT);
+                Tile t;
+                t.op = OP_ATTN;
+                t.layer = l;
+                t.b = -1;
+                t.g = g;
+                t.c = c;
+                t.nch = TT;
+                t.merge = -1;
+                t.slot = c;
+                t.nslot = TT;
+                t.bytes = blocks * 2 * T * d * 2;
+                t.cu = pick_least(cum);
+                cum[t.cu] += t.bytes;
+                tiles.push_back(t);
             }
         for (int b = 0; b < B; ++b)
             for (int g = 0; g < nkv; ++g) {
@@ -242,7 +228,7 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
                 t.layer = l;
                 t.b = b;
                 t.g = g;
-                t.nch = C;
+                t.nch = TT;
                 t.merge = -1;
                 t.bytes = 0;  // streams nothing
                 t.cu = pick_least(cum);
@@ -339,10 +325,12 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     P.act_stride = (kmax + 511) / 512 * 512;
     P.xrow_stride = (max_rows_x + 3) / 4 * 4;
     // matvec inputs; attention staging (queries, new K/V entry) and one
-    // round's scores and values; an AMERGE's chunk states; LM-head partials
+    // round's scores and values; an AMERGE's tile states (MAX_ATTN_CHUNKS at
+    // a time); LM-head partials
     const int64_t act_floats =
         std::max<int64_t>({(int64_t)NBP * P.act_stride, (int64_t)G * 64 + 64 + attn_round_floats(G),
-                           (int64_t)C * G * ATTN_PART, (int64_t)P.n_lm_slots * B * 2});
+                           (int64_t)std::min(B * C, MAX_ATTN_CHUNKS) * G * ATTN_PART,
+                           (int64_t)P.n_lm_slots * B * 2});
     auto up256 = [](int64_t x) { return (x + 255) / 256 * 256; };
     const int64_t queue_off = MISC_BYTES;  // the CU's queue, LDS_INSTR_WORDS words per instruction
     const int64_t xrow_off = queue_off + up256((int64_t)Q * LDS_INSTR_WORDS * 4);

@@ -33,13 +33,6 @@ struct Plan {
 // Shape checks shared by mk_create and the planner.
 int check_config(const mk_config &cfg);
 
-// Bytes one instruction streams (weights or K/V blocks) for a request whose
-// current length is `kv_len` (only ATTN depends on it).
-int64_t instr_stream_bytes(const mk_config &cfg, const int32_t *ins, int kv_len);
-
-// K/V blocks [lo, hi) of chunk c out of nch for a request of length n+1.
-void attn_chunk_blocks(int kv_len, int page_tokens, int c, int nch, int *lo, int *hi);
-
 int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &out);
 
 // Number of kernel launches of one unfused step.

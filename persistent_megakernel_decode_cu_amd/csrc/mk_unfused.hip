@@ -154,9 +154,18 @@ __global__ __launch_bounds__(UF_THREADS) void uf_rope_append(KParams P, int laye
     }
 }
 
-// One (chunk, kv head, request) per workgroup of N_COMPUTE_WAVES waves that
-// take K/V blocks round-robin and merge their states in wave order: the same
-// split and lane layout as an attention tile of the resident interpreter.
+// The attention split of the step (mk_device.h), computed by each wave that
+// needs it from the request lengths.
+__device__ __forceinline__ void uf_split(const KParams &P, int T, int lane, int (&nb)[MAX_B], int (&n)[MAX_B]) {
+#pragma unroll
+    for (int b = 0; b < MAX_B; ++b) nb[b] = b < P.B ? attn_nblocks(P.kv_lens[b], P.T * P.max_pages) : 0;
+    attn_split_counts(nb, P.B, T, P.attn_split == SPLIT_BALANCED, lane, n);
+}
+
+// One attention tile (tile c of kv head g: the request and K/V blocks the
+// split gives it) per workgroup of N_COMPUTE_WAVES waves that take K/V
+// blocks round-robin and merge their states in wave order: the same split
+// and lane layout as an attention tile of the resident interpreter.
 constexpr int UF_ATTN_THREADS = N_COMPUTE_WAVES * 64;
 
 template <int G>
@@ -164,14 +173,16 @@ __global__ __launch_bounds__(UF_ATTN_THREADS) void uf_attn(KParams P, int layer,
     constexpr int NW = N_COMPUTE_WAVES;
     __shared__ float q[MAX_G * 64];
     __shared__ float area[attn_round_floats(MAX_G)];
-    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, nch = gridDim.x;
+    const int c = blockIdx.x, g = blockIdx.y, T = gridDim.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int nb[MAX_B], n[MAX_B], b, blo, bhi;
+    bool last;
+    uf_split(P, T, lane, nb, n);
+    attn_split_tile(nb, n, c, b, blo, bhi, last);
     const int p = P.kv_lens[b];
     if (p < 0 || p >= P.T * P.max_pages) return;  // flagged by uf_rope_append
     for (int i = threadIdx.x; i < G * 64; i += UF_ATTN_THREADS) q[i] = qrot[(int64_t)b * P.nq * 64 + (g * G) * 64 + i];
     __syncthreads();
-    const int nb = (p + 1 + 15) >> 4;
-    const int blo = (int)((int64_t)c * nb / nch), bhi = (int)((int64_t)(c + 1) * nb / nch);
     const size_t layer_pool = (size_t)P.n_pages * P.nkv * 16 * 64;
     MK_LDS float *ar = (MK_LDS float *)area;
     AttnRun run;
@@ -198,7 +209,7 @@ __global__ __launch_bounds__(UF_ATTN_THREADS) void uf_attn(KParams P, int layer,
         __syncthreads();
     }
     if (wave < G) {
-        float *dst = P.attn_part + ((((int64_t)b * P.nkv + g) * nch + c) * G + wave) * ATTN_PART_STRIDE;
+        float *dst = P.attn_part + (((int64_t)g * T + c) * G + wave) * ATTN_PART_STRIDE;
         dst[lane] = run.O;
         if (lane == 0) {
             dst[64] = run.M;
@@ -207,26 +218,21 @@ __global__ __launch_bounds__(UF_ATTN_THREADS) void uf_attn(KParams P, int layer,
     }
 }
 
-// Chunk states of each head merged in chunk order, then o = O / L: one wave
-// per query head of the kv group, every chunk's state loaded before the merge.
-__global__ __launch_bounds__(64 * MAX_G) void uf_attn_merge(KParams P, int nch) {
+// The states of each request's tiles merged in tile order, then o = O / L:
+// one wave per query head of the kv group.
+__global__ __launch_bounds__(64 * MAX_G) void uf_attn_merge(KParams P, int T) {
     const int g = blockIdx.x, b = blockIdx.y, lane = threadIdx.x & 63, hq = threadIdx.x >> 6;
     const int G = P.nq / P.nkv;
-    if (hq >= G) return;
-    float o[MAX_ATTN_CHUNKS], m[MAX_ATTN_CHUNKS], l[MAX_ATTN_CHUNKS];
-#pragma unroll
-    for (int c = 0; c < MAX_ATTN_CHUNKS; ++c)
-        if (c < nch) {
-            const float *src = P.attn_part + ((((int64_t)b * P.nkv + g) * nch + c) * G + hq) * ATTN_PART_STRIDE;
-            o[c] = src[lane];
-            m[c] = src[64];
-            l[c] = src[65];
-        }
+    if (hq >= G) return;  // whole waves: the block has 64 G threads
+    int nb[MAX_B], n[MAX_B];
+    uf_split(P, T, lane, nb, n);
+    const int first = attn_split_first(n, b), nt = attn_split_first(n, b + 1) - first;
     float O, M, L;
     merge_init(O, M, L);
-#pragma unroll
-    for (int c = 0; c < MAX_ATTN_CHUNKS; ++c)
-        if (c < nch) merge_step(O, M, L, o[c], m[c], l[c]);
+    for (int c = first; c < first + nt; ++c) {
+        const float *src = P.attn_part + (((int64_t)g * T + c) * G + hq) * ATTN_PART_STRIDE;
+        merge_step(O, M, L, src[lane], src[64], src[65]);
+    }
     P.o[(int64_t)b * P.nq * P.d + (g * G + hq) * 64 + lane] = O / L;
 }
 
@@ -311,7 +317,7 @@ hipError_t launch_unfused(const KParams &p, float *u, float *qrot, hipStream_t s
         hipError_t e_ = (x);                      \
         if (e_ != hipSuccess) return e_;          \
     } while (0)
-    const int nch = p.attn_chunks;
+    const int nt = p.B * p.attn_chunks;  // attention tiles per kv head
     for (int l = 0; l < p.L; ++l) {
         const int first = l == 0 ? F_X_FROM_INPUT : 0;
         const bool last = l == p.L - 1;
@@ -321,7 +327,7 @@ hipError_t launch_unfused(const KParams &p, float *u, float *qrot, hipStream_t s
         hipLaunchKernelGGL(uf_rope_append, dim3(p.B), dim3(UF_THREADS), 0, s, p, l, qrot);
         MK_TRY(hipGetLastError());
         {
-            const dim3 grid(nch, p.nkv, p.B), blk(UF_ATTN_THREADS);
+            const dim3 grid(nt, p.nkv), blk(UF_ATTN_THREADS);
             switch (p.nq / p.nkv) {
                 case 1: hipLaunchKernelGGL(uf_attn<1>, grid, blk, 0, s, p, l, (const float *)qrot); break;
                 case 2: hipLaunchKernelGGL(uf_attn<2>, grid, blk, 0, s, p, l, (const float *)qrot); break;
@@ -334,7 +340,7 @@ hipError_t launch_unfused(const KParams &p, float *u, float *qrot, hipStream_t s
             }
         }
         MK_TRY(hipGetLastError());
-        hipLaunchKernelGGL(uf_attn_merge, dim3(p.nkv, p.B), dim3(64 * (p.nq / p.nkv)), 0, s, p, nch);
+        hipLaunchKernelGGL(uf_attn_merge, dim3(p.nkv, p.B), dim3(64 * (p.nq / p.nkv)), 0, s, p, nt);
         MK_TRY(hipGetLastError());
         MK_TRY(uf_mv_any(p, OP_OPROJ, l, first, p.o, s));
         hipLaunchKernelGGL(uf_norm, dim3(p.B), dim3(UF_THREADS), 0, s, p, l, 3, 0, u);

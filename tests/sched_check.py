@@ -7,7 +7,7 @@ producer (a tile, or the elected last finisher of a merge event). So:
 
 * ``decode``: reads the [S, Q, 32] int32 queues and the merge-event table.
 * ``validate``: every op's rows are covered exactly once per layer (so every
-  element has exactly one producer), every attention chunk exists once, the
+  element has exactly one producer), every attention tile exists once, the
   merge events have the right members and slots, each queue is a
   subsequence of one global order, and every element an instruction reads is
   produced earlier in that order -- which rules out deadlock: the earliest
@@ -128,18 +128,14 @@ def dependencies(shape, batch: int, ins):
                 writers[("act", i.layer)].append((b * F + i.r0, b * F + i.r1, node))
             elif i.op == I["OP_DOWN"]:
                 writers[("x", 2 * i.layer + 2)].append((b * H + i.r0, b * H + i.r1, node))
-        if i.op == I["OP_ATTN"]:  # one softmax state per (request, kv head, chunk)
-            lo = (i.b * nkv + i.g) * i.nch + i.c
+        if i.op == I["OP_ATTN"]:  # one softmax state per (kv head, tile)
+            lo = i.g * i.nch + i.c
             writers[("opart", i.layer)].append((lo, lo + 1, node))
         if i.op == I["OP_AMERGE"]:  # the merged outputs of (request, kv head)
             lo = i.b * QD + i.g * G * d
             writers[("o", i.layer)].append((lo, lo + G * d, node))
     for k in writers:
         writers[k].sort()
-    n_chunks = defaultdict(int)
-    for i in ins:
-        if i.op == I["OP_ATTN"]:
-            n_chunks[i.layer] = i.nch
 
     def producers(buf, lo, hi):
         out = set()
@@ -162,16 +158,15 @@ def dependencies(shape, batch: int, ins):
                 if not first:
                     need |= producers(("x", 2 * i.layer), b * H, (b + 1) * H)
             elif i.op == I["OP_ATTN"]:
-                if b != i.b:
-                    continue
+                # the split decides on the device which request a tile
+                # serves: any request's queries and K/V entry of head g
                 g = i.g
                 for lo, n in ((g * G * d, G * d), (QD + g * d, d), (QD + nkv * d + g * d, d)):
                     need |= producers(("qkv", i.layer), b * QKV + lo, b * QKV + lo + n)
-            elif i.op == I["OP_AMERGE"]:  # every chunk state of its (request, kv head)
+            elif i.op == I["OP_AMERGE"]:  # its request's tiles: any of head g's
                 if b != i.b:
                     continue
-                lo = (i.b * nkv + i.g) * i.nch
-                need |= producers(("opart", i.layer), lo, lo + i.nch)
+                need |= producers(("opart", i.layer), i.g * i.nch, (i.g + 1) * i.nch)
             elif i.op == I["OP_OPROJ"]:  # the merged outputs of the request
                 need |= producers(("o", i.layer), b * QD, (b + 1) * QD)
                 if not first:
@@ -187,7 +182,7 @@ def dependencies(shape, batch: int, ins):
     return deps, members
 
 
-def validate(shape, batch: int, queue: np.ndarray, events: np.ndarray, attn_chunks: int, max_kv_len: int):
+def validate(shape, batch: int, queue: np.ndarray, events: np.ndarray, attn_chunks: int, max_kv_len: int = 0):
     """Raises ScheduleError on the first violation; returns the decoded list."""
     I = ISA
     ins = decode(queue)
@@ -206,11 +201,11 @@ def validate(shape, batch: int, queue: np.ndarray, events: np.ndarray, attn_chun
     merges = defaultdict(list)
     for i in ins:
         if i.op == I["OP_ATTN"]:
-            attn[i.layer].append((i.b, i.g, i.c))
-            _req(i.nch == attn_chunks, "ATTN instruction with a different chunk count")
+            attn[i.layer].append((i.g, i.c))
+            _req(i.nch == batch * attn_chunks, "ATTN instruction with a different tile count")
         elif i.op == I["OP_AMERGE"]:
             merges[i.layer].append((i.b, i.g))
-            _req(i.nch == attn_chunks, "AMERGE instruction with a different chunk count")
+            _req(i.nch == batch * attn_chunks, "AMERGE instruction with a different tile count")
         else:
             rows[(i.op, i.layer)].append((i.r0, i.r1))
     for l in range(L):
@@ -218,7 +213,7 @@ def validate(shape, batch: int, queue: np.ndarray, events: np.ndarray, attn_chun
         _cover(rows[(I["OP_OPROJ"], l)], H, f"OPROJ layer {l}")
         _cover(rows[(I["OP_UPGATE"], l)], F, f"UPGATE layer {l}")
         _cover(rows[(I["OP_DOWN"], l)], H, f"DOWN layer {l}")
-        want = sorted((b, g, c) for b in range(batch) for g in range(nkv) for c in range(attn_chunks))
+        want = sorted((g, c) for g in range(nkv) for c in range(batch * attn_chunks))
         _req(sorted(attn[l]) == want, f"attention tiles of layer {l} incomplete or duplicated")
         want_m = sorted((b, g) for b in range(batch) for g in range(nkv))
         _req(sorted(merges[l]) == want_m, f"attention merges of layer {l} incomplete or duplicated")
@@ -240,8 +235,8 @@ def validate(shape, batch: int, queue: np.ndarray, events: np.ndarray, attn_chun
     for i in ins:
         _req(i.merge < ne, "merge of an unknown event")
         if i.op == I["OP_ATTN"]:
-            _req(i.merge < 0, "attention tiles publish chunk states without a merge event")
-            _req(1 <= i.nch <= ISA["MAX_ATTN_CHUNKS"], "attention chunk count out of range")
+            _req(i.merge < 0, "attention tiles publish their states without a merge event")
+            _req(batch <= i.nch <= ISA["MAX_B"] * ISA["MAX_ATTN_CHUNKS"], "attention tile count out of range")
         if i.op == I["OP_LMHEAD"]:
             _req(i.merge >= 0, "LM-head tiles need the argmax merge")
     # every input is produced earlier in the global order
@@ -250,11 +245,6 @@ def validate(shape, batch: int, queue: np.ndarray, events: np.ndarray, attn_chun
         for kind, v in deps[i.seq]:
             at = v if kind == "i" else last_member[v]
             _req(at < i.seq, f"instruction {i.seq} (op {i.op}, layer {i.layer}) reads data produced at {at}")
-    # the block holding the new position belongs to the last chunk
-    nb = (max_kv_len + 1 + 15) // 16
-    c_last = attn_chunks - 1
-    _req((c_last * nb) // attn_chunks <= nb - 1 < ((c_last + 1) * nb) // attn_chunks,
-         "the new K/V position is not in the last chunk")
     return ins
 
 

@@ -78,9 +78,13 @@ def test_capacity_checks():
     assert e.value.code == _mk.MK_ECAPACITY
     # the one-kernel-per-op mode has no such limit
     _mk.Plan(cfg_of(wide, max_batch=8, pages=258), _mk.MkScheduleDesc(8, 256, 1, 0, 0, 0, 0, 0, 0))
-    with pytest.raises(_mk.MkError) as e:   # reserved fields
-        _mk.Plan(cfg_of(w), _mk.MkScheduleDesc(1, 8, 0, 0, 0, 0, 0, 1, 0))
+    with pytest.raises(_mk.MkError) as e:   # reserved field
+        _mk.Plan(cfg_of(w), _mk.MkScheduleDesc(1, 8, 0, 0, 0, 0, 0, 0, 1))
     assert e.value.code == _mk.MK_EINVAL
+    with pytest.raises(_mk.MkError) as e:   # unknown attention split
+        _mk.Plan(cfg_of(w), _mk.MkScheduleDesc(1, 8, 0, 0, 0, 0, 0, 2, 0))
+    assert e.value.code == _mk.MK_EINVAL
+    _mk.Plan(cfg_of(w), _mk.MkScheduleDesc(1, 8, 0, 0, 0, 0, 0, 1, 0))  # per-request split
 
 
 def test_head_grouping_of_the_resident_interpreter():

@@ -167,32 +167,37 @@ def test_1b_batch8_paged(mode, oracle32):
     print(f"1b batch 8 {mode}: max |dlogit| = {diff:.3g}")
 
 
-def _outputs(cfg, m, st, wdev, mode, n_cus=0, attn_chunks=0):
+def _outputs(cfg, m, st, wdev, mode, n_cus=0, attn_chunks=0, attn_split="balanced"):
     ds = gu.DevState(st)
     dec = gu.make_decoder(m, st, wdev)
-    dec.build_schedule(st.batch, mode=mode, max_kv_len=int(st.kv_lens.max()), n_cus=n_cus,
-                       attn_chunks=attn_chunks)
+    info = dec.build_schedule(st.batch, mode=mode, max_kv_len=int(st.kv_lens.max()), n_cus=n_cus,
+                              attn_chunks=attn_chunks, attn_split=attn_split)
     g = gu.run_step(dec, ds, cfg, want_hidden=True)
     g["k_pool"] = ds.k_pool.cpu().numpy()
     g["v_pool"] = ds.v_pool.cpu().numpy()
+    g["attn_chunks"] = info["attn_chunks"]
     dec.close()
     return g
 
 
-@pytest.mark.parametrize("n_cus,attn_chunks", [(1, 0), (3, 2), (8, 0), (37, 3), (256, 0)])
-def test_megakernel_equals_unfused_bitwise(n_cus, attn_chunks):
+@pytest.mark.parametrize("n_cus,attn_chunks,split", [(1, 0, "balanced"), (3, 2, "balanced"), (8, 0, "balanced"),
+                                                     (37, 3, "balanced"), (37, 3, "per_request"),
+                                                     (256, 0, "balanced"), (256, 16, "balanced")])
+def test_megakernel_equals_unfused_bitwise(n_cus, attn_chunks, split):
     """Both paths perform the same floating-point operations in the same order
     (norm partition, chunk order of every dot product, attention split and
     merge order, explicit FMAs in RoPE), so their outputs agree exactly, for
-    any grid size and chunking."""
+    any grid size, tile count and split mode. At 16 tiles per request (64 per
+    kv head) the longest request's merge takes more than one gather round."""
     cfg = synthetic.Workload(11, "tiny-b4-paged", n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2,
                              head_dim=64, ffn=1024, vocab=4096, has_embed=True, batch=4,
                              kv_len_range=(1, 300), steps=2, paged_random=True)
     cfg, m, st = inputs(cfg)
     wdev = gu.upload_model(m)
-    print(f"bitwise n_cus={n_cus} chunks={attn_chunks}", flush=True)
-    u = _outputs(cfg, m, st, wdev, "unfused", attn_chunks=attn_chunks)
-    k = _outputs(cfg, m, st, wdev, "megakernel", n_cus=n_cus, attn_chunks=attn_chunks)
+    print(f"bitwise n_cus={n_cus} chunks={attn_chunks} split={split}", flush=True)
+    k = _outputs(cfg, m, st, wdev, "megakernel", n_cus=n_cus, attn_chunks=attn_chunks, attn_split=split)
+    # the same attention tiles (the automatic count depends on the grid size)
+    u = _outputs(cfg, m, st, wdev, "unfused", attn_chunks=k["attn_chunks"], attn_split=split)
     for key in ("tokens", "kv_lens", "logits", "hidden", "k_pool", "v_pool"):
         a, b = u[key], k[key]
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), (
@@ -202,8 +207,8 @@ def test_megakernel_equals_unfused_bitwise(n_cus, attn_chunks):
 def test_megakernel_equals_unfused_bitwise_1b_layer():
     cfg, m, st = inputs("1b-layer-kv512")
     wdev = gu.upload_model(m)
-    u = _outputs(cfg, m, st, wdev, "unfused")
     k = _outputs(cfg, m, st, wdev, "megakernel")
+    u = _outputs(cfg, m, st, wdev, "unfused", attn_chunks=k["attn_chunks"])
     for key in ("kv_lens", "hidden", "k_pool", "v_pool"):
         assert np.array_equal(u[key].view(np.uint8), k[key].view(np.uint8)), key
 

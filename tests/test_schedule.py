@@ -63,13 +63,18 @@ def test_streamed_bytes_match_the_byte_model():
 def test_auto_chunks_about_one_block_per_wave():
     # attention is spread so that about one 16-position K/V block goes to
     # each of half a tile's 8 waves (one wave per SIMD), up to a chunk cap
-    # that halves above batch 2
+    # that halves above batch 2, where there are also no more attention
+    # tiles than compute units
     for name in ("tiny-2l", "1b-kv1024", "1b-kv8192", "1b-b8-paged"):
         w, B, maxlen, p = plan_for(name, 256)
         nb = (maxlen + 1 + 15) // 16
         cap = sched_check.ISA["AUTO_ATTN_CHUNKS"] // (1 if B <= 2 else 2)
         want = min(nb, cap, max(1, -(-nb // 4)))
+        if B > 2:
+            want = min(want, max(1, 256 // (B * w.n_kv_heads)))
         assert p.info.attn_chunks == want, (name, p.info.attn_chunks, want)
+        if B > 2:
+            assert B * p.info.attn_chunks * w.n_kv_heads <= 256
 
 
 def test_attention_chunks_above_the_limit_are_rejected():
