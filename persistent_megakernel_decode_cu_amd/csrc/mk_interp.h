@@ -313,19 +313,19 @@ __device__ __forceinline__ bool tgather_range(Ctx &c, __amdgpu_buffer_rsrc_t r, 
 }
 
 // Gathers the flattened tagged vector src[0, B K) (B requests of K words)
-// with every wave of the workgroup, 16 words per lane and round, handing
+// with every wave of the workgroup, W words per lane and round, handing
 // word (b, i) to put(b, i, v): the gathers of all requests share their
 // rounds, where one gather per request would pay one round trip each.
-template <typename PUT>
+template <int W = 16, typename PUT>
 __device__ __forceinline__ bool tgather_batch(Ctx &c, const uint64_t *src, int B, int K, PUT put, int pc) {
     const int total = B * K;
     const __amdgpu_buffer_rsrc_t r = tres(src, (uint32_t)total);
     const float invK = 1.0f / (float)K;
     constexpr int STRIDE = NC * 64;
-    for (int base = 0; base < total; base += STRIDE * 16) {
+    for (int base = 0; base < total; base += STRIDE * W) {
         const int first = base + c.w * 64 + c.lane();
-        const int n = first < total ? min(16, (total - first + STRIDE - 1) / STRIDE) : 0;
-        if (!tgather<16>(
+        const int n = first < total ? min(W, (total - first + STRIDE - 1) / STRIDE) : 0;
+        if (!tgather<W>(
                 c, r, n, [&](int k) { return (uint32_t)(first + STRIDE * k); },
                 [&](int k, float v) {
                     const int j = first + STRIDE * k;
@@ -701,10 +701,96 @@ __device__ __forceinline__ void prefetch_norm_w(const KParams &P, const Ctx &c, 
     }
 }
 
+// The batched norm (several requests, x_v with v > 0): request b's words
+// are gathered by its NC / NB waves, each holding the baseline partition's
+// "virtual waves" v0 .. v0 + VPW - 1 (elements i = 64 v + lane + 256 k) in
+// registers, so the sums of squares run in the baseline's order straight
+// from the gathered words; the fp32 words also land in the staging area for
+// the scaling pass. Words of the wave, in gather order j: virtual wave
+// v0 + j % VPW, k = j / VPW.
+template <int NB>
+__device__ __forceinline__ bool norm_gather_batched(const KParams &P, Ctx &c, const Ins &in, int xv) {
+    static_assert(NB == 2 || NB == 4 || NB == 8, "batched norm");
+    constexpr int R = NC / NB, VPW = 4 / R;  // waves per request; virtual waves per wave
+    const int H = P.H, lane = c.lane(), b = c.w / R, v0 = (c.w % R) * VPW;
+    if (b >= P.B) return true;
+    const int nw = VPW * (H / 256);  // words per lane (H is a multiple of 256)
+    const __amdgpu_buffer_rsrc_t r = tres(P.tx + ((size_t)(xv - 1) * P.B + b) * H, (uint32_t)H);
+    auto xs = [&](int i) -> MK_LDS float & {
+        if constexpr (ACT16<NB>) return c.act[(NB * H) / 2 + b * H + i];
+        else return c.act[b * P.act_stride + act_index(i)];
+    };
+    auto elem = [&](int j) { return 64 * (v0 + j % VPW + 4 * (j / VPW)) + lane; };
+    float ss[VPW];
+#pragma unroll
+    for (int v = 0; v < VPW; ++v) ss[v] = 0.0f;
+    for (int j0 = 0; j0 < nw; j0 += 16) {  // uniform bound; 16 is a multiple of VPW
+        float x[16];
+        if (!tgather<16>(
+                c, r, min(16, nw - j0), [&](int k) { return (uint32_t)elem(j0 + k); },
+                [&](int k, float v) { x[k] = v; }, in.pc))
+            return false;
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            if (j0 + k < nw) {
+                ss[k % VPW] = fmaf(x[k], x[k], ss[k % VPW]);
+                xs(elem(j0 + k)) = x[k];
+            }
+    }
+    MK_LDS float *norm = (MK_LDS float *)(c.misc + M_NORM);
+#pragma unroll
+    for (int v = 0; v < VPW; ++v) {
+        const float t = wave_sum(ss[v]);
+        if (lane == 0) norm[(v0 + v) * MAX_B + b] = t;
+    }
+    return true;
+}
+
+// ... and the scaling pass of the batched norm: request b's R waves split its
+// elements in chunks of 8 (16-byte LDS accesses), scaled by its inverse RMS
+// (the four partial sums added in the baseline's order) and the norm weight.
+template <int NB>
+__device__ __forceinline__ void norm_scale_batched(const KParams &P, Ctx &c) {
+    constexpr int R = NC / NB;
+    const int H = P.H, lane = c.lane(), b = c.w / R, r = c.w % R;
+    if (b >= P.B) return;
+    const MK_LDS float *norm = (const MK_LDS float *)(c.misc + M_NORM);
+    float tot = 0.0f;
+    for (int v = 0; v < 4; ++v) tot += norm[v * MAX_B + b];
+    const float inv = 1.0f / sqrtf(tot / (float)H + P.eps);
+    const MK_LDS uint16_t *nwl = (const MK_LDS uint16_t *)((MK_LDS char *)c.misc + P.nw_off);
+    const int per = H / 8 / R;  // chunks of this wave
+    for (int ci = r * per + lane; ci < (r + 1) * per; ci += 64) {
+        const v4u wv = *(const MK_LDS v4u *)(nwl + ci * 8);
+        const float wn[8] = {bf_lo(wv.x), bf_hi(wv.x), bf_lo(wv.y), bf_hi(wv.y),
+                             bf_lo(wv.z), bf_hi(wv.z), bf_lo(wv.w), bf_hi(wv.w)};
+        if constexpr (ACT16<NB>) {
+            const MK_LDS float *xs = c.act + (NB * H) / 2 + b * H + ci * 8;
+            const v4f a = *(const MK_LDS v4f *)xs, e = *(const MK_LDS v4f *)(xs + 4);
+            const float xv[8] = {a.x, a.y, a.z, a.w, e.x, e.y, e.z, e.w};
+            uint32_t h[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                h[q] = (uint32_t)f2h(xv[2 * q] * inv * wn[2 * q]) |
+                       ((uint32_t)f2h(xv[2 * q + 1] * inv * wn[2 * q + 1]) << 16);
+            *(MK_LDS v4u *)((MK_LDS uint16_t *)c.act + b * H + ci * 8) = v4u{h[0], h[1], h[2], h[3]};
+        } else {
+            // act_index: chunk ci's first four values, then its last four 256 floats on
+            MK_LDS float *xs = c.act + b * P.act_stride + act_index(ci * 8);
+            v4f a = *(MK_LDS v4f *)xs, e = *(MK_LDS v4f *)(xs + 256);
+            a = v4f{a.x * inv * wn[0], a.y * inv * wn[1], a.z * inv * wn[2], a.w * inv * wn[3]};
+            e = v4f{e.x * inv * wn[4], e.y * inv * wn[5], e.z * inv * wn[6], e.w * inv * wn[7]};
+            *(MK_LDS v4f *)xs = a;
+            *(MK_LDS v4f *)(xs + 256) = e;
+        }
+    }
+}
+
 // act[b] <- rmsnorm(x_v[b]) * wn in the matvec layout (x_0: the layer-0
-// input). Waves 0..3 each gather the elements i = 64 w + lane + 256 k and
-// sum their squares in that order, which is the reduction of the
-// one-kernel-per-op baseline's norm, so both paths agree bit for bit.
+// input). The elements i = 64 w + lane + 256 k of each request are summed
+// as four "virtual waves" w = 0..3 in that order, then added w by w, which is
+// the reduction of the one-kernel-per-op baseline's norm, so both paths
+// agree bit for bit.
 template <int NB>
 __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &in, const uint16_t *wn, int xv) {
     const int H = P.H, lane = c.lane(), w = c.w;
@@ -713,25 +799,25 @@ __device__ __forceinline__ bool stage_norm(const KParams &P, Ctx &c, const Ins &
     const int n = first < H ? (H - first + 255) / 256 : 0;  // this lane's elements
     const int nmax = (H - w * 64 + 255) / 256;               // lane 0's: the most
     prefetch_norm_w(P, c, wn);
+    if constexpr (NB > 1) {
+        if (xv != 0) {
+            if (!norm_gather_batched<NB>(P, c, in, xv)) return false;
+            // the norm-weight copies (waves 0..3) have landed
+            if (w < 4) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (!cbar(c, in.pc)) return false;
+            norm_scale_batched<NB>(P, c);
+            return cbar(c, in.pc);
+        }
+    }
     // the fp32 input of request b, element i: in the matvec layout, or with
     // binary16 staging contiguous past the binary16 area
     auto xs = [&](int b, int i) -> MK_LDS float & {
         if constexpr (ACT16<NB>) return c.act[(NB * H) / 2 + b * H + i];
         else return c.act[b * P.act_stride + act_index(i)];
     };
-    // several requests: every wave gathers, all requests in shared rounds
-    const bool batched = NB > 1 && xv != 0;
-    if (batched) {
-        if (!tgather_batch(
-                c, P.tx + (size_t)(xv - 1) * P.B * H, P.B, H, [&](int b, int i, float v) { xs(b, i) = v; }, in.pc))
-            return false;
-        if (!cbar(c, in.pc)) return false;
-    }
     if (w < 4) {
         for (int b = 0; b < P.B; ++b) {
-            if (batched) {
-                // gathered above
-            } else if (xv == 0) {
+            if (xv == 0) {
                 const int tok = P.has_embed ? token_of(P, c, b, in) : 0;
                 if (tok < 0) return false;
                 for (int i = first; i < H; i += 256) xs(b, i) = x_input(P, b, i, true, tok);
@@ -817,8 +903,10 @@ __device__ __forceinline__ bool stage_rows(const KParams &P, Ctx &c, const Ins &
 // the 16-bit layout); src: tagged [B][K]
 template <bool A16, int NB>
 __device__ __forceinline__ bool stage_copy(const KParams &P, Ctx &c, const Ins &in, const uint64_t *src, int K) {
+    // batch 8: the down projection's eight inputs of F words are the
+    // largest gather; twice the words in flight per round halve its rounds
     if (NB > 1)
-        return tgather_batch(
+        return tgather_batch<A16 ? 32 : 16>(
             c, src, P.B, K,
             [&](int b, int i, float v) {
                 if (A16) ((MK_LDS uint16_t *)c.act + b * K)[i] = f2h(v);
