@@ -1197,6 +1197,91 @@ __device__ __forceinline__ void emit_row(const KParams &P, Ctx &c, const Ins &in
     }
 }
 
+// The eight requests' dot products of a unit summed over the wave's 64
+// lanes together: three exchanges with the lanes 32, 16 and 8 apart, each
+// halving the values a lane carries, then a sum over 8 adjacent lanes;
+// request b's total ends in lanes 8 b .. 8 b + 7. (Eight separate wave sums
+// and eight one-lane emits per unit cost several times the unit's products
+// at this batch.)
+__device__ __forceinline__ float reduce8(const float (&v)[8]) {
+    const int lane = lane_id();
+    const bool h5 = (lane & 32) != 0, h4 = (lane & 16) != 0, h3 = (lane & 8) != 0;
+    float a[4], e[2];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = (h5 ? v[k + 4] : v[k]) + shfl_xor_f(h5 ? v[k] : v[k + 4], 32);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) e[k] = (h4 ? a[k + 2] : a[k]) + shfl_xor_f(h4 ? a[k] : a[k + 2], 16);
+    return sum8lanes((h3 ? e[1] : e[0]) + shfl_xor_f(h3 ? e[0] : e[1], 8));
+}
+
+// Row `row`'s outputs of the eight requests, written by lanes 8 b (request
+// b = lane / 8, the value pair its lane group holds); the buffer resources
+// span all requests so that they stay uniform.
+__device__ __forceinline__ void emit_rows8(const KParams &P, Ctx &c, const Ins &in, int row, float v0, float v1) {
+    const int lane = lane_id(), b = lane >> 3;
+    if ((lane & 7) != 0 || b >= P.B) return;
+    const uint32_t tag = c.tag;
+    const bool last_step = in.step == P.n_steps - 1;
+    switch (in.op) {
+        case OP_QKV: {
+            const int QKVN = (P.nq + 2 * P.nkv) * P.d;
+            tput(tres(P.tqkv + (size_t)in.layer * P.B * QKVN, (uint32_t)(P.B * QKVN)), (uint32_t)(b * QKVN + row), v0,
+                 tag);
+            break;
+        }
+        case OP_OPROJ: {
+            const float nx = c.xrow[b * P.xrow_stride + (row - in.r0)] + v0;
+            tput(tres(P.tx + (size_t)(2 * in.layer) * P.B * P.H, (uint32_t)(P.B * P.H)), (uint32_t)(b * P.H + row), nx,
+                 tag);
+            break;
+        }
+        case OP_UPGATE:
+            tput(tres(P.tact + (size_t)in.layer * P.B * P.F, (uint32_t)(P.B * P.F)), (uint32_t)(b * P.F + row),
+                 silu(v0) * v1, tag);
+            break;
+        case OP_DOWN: {
+            const float nx = c.xrow[b * P.xrow_stride + (row - in.r0)] + v0;
+            tput(tres(P.tx + (size_t)(2 * in.layer + 1) * P.B * P.H, (uint32_t)(P.B * P.H)), (uint32_t)(b * P.H + row),
+                 nx, tag);
+            if ((in.flags & F_WRITE_HIDDEN) && P.hidden_out && last_step) P.hidden_out[(int64_t)b * P.H + row] = nx;
+            break;
+        }
+        default: {
+            if (P.logits_out && last_step) P.logits_out[(int64_t)b * P.V + row] = v0;
+            // the wave's running best of request b (its rows rise, so ties
+            // keep the lowest index)
+            MK_LDS float *am = (MK_LDS float *)(c.misc + M_AMAX);
+            const int at = (c.w * MAX_B + b) * 2;
+            if (v0 > am[at]) {
+                am[at] = v0;
+                ((MK_LDS int32_t *)am)[at + 1] = row;
+            }
+            break;
+        }
+    }
+}
+
+// End of a slice at a padded batch of 8: at the end of an UPGATE unit's gate
+// half its eight sums are parked in acc.g (request b's in lanes 8 b ..), at
+// the end of a unit its outputs are written.
+template <int NB>
+__device__ __forceinline__ void unit_end8(const KParams &P, Ctx &c, const Cur &k, const Ins &in, Acc<NB> &acc) {
+    static_assert(NB == 8 && ONE_ACC<NB>, "batch-8 epilogue");
+    const bool gate_done = in.op == OP_UPGATE && k.s == k.spm - 1;
+    if (!gate_done && k.s != k.sp - 1) return;
+    const float s = reduce8(acc.a0);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc.a0[b] = 0.0f;
+    if (gate_done) {
+        acc.g = s;
+        return;
+    }
+    const bool up = in.op == OP_UPGATE;
+    const float v0 = up ? acc.g : s;
+    if (in.op == OP_LMHEAD && __builtin_amdgcn_ballot_w64((lane_id() >> 3) < P.B && v0 != v0) != 0) acc.nan = true;
+    emit_rows8(P, c, in, k.r0 + k.u, v0, up ? s : 0.0f);
+}
+
 // Slice (part, m) of unit u: the lane's 16-byte chunks ci = 256 part + 64 j +
 // lane, j < 4, times the activations of those chunks, added in j order to
 // the unit's dot product (m: gate or up matrix of UPGATE). Three forms with
@@ -1233,13 +1318,26 @@ __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &
             wh[j][2] = bf_pair_h2(r[j].z);
             wh[j][3] = bf_pair_h2(r[j].w);
         }
+        // request b + 1's four activation reads are issued before request
+        // b's products, so that LDS latency overlaps the arithmetic instead
+        // of being waited out read by read
+        const MK_LDS uint16_t *a0p = (const MK_LDS uint16_t *)c.act + part * 2048 + lane * 8;
+        v4u xn[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xn[j] = *(const MK_LDS v4u *)(a0p + j * 512);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             float a = ONE_ACC<NB> ? acc.a0[b] : (m ? acc.a1[b] : acc.a0[b]);
-            const MK_LDS uint16_t *ab = (const MK_LDS uint16_t *)c.act + b * k.K + part * 2048 + lane * 8;
+            v4u xc[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xc[j] = xn[j];
+            if (b + 1 < NB) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) xn[j] = *(const MK_LDS v4u *)(a0p + (b + 1) * k.K + j * 512);
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const v4u x = *(const MK_LDS v4u *)(ab + j * 512);
+                const v4u x = xc[j];
                 a = __builtin_amdgcn_fdot2(wh[j][0], as_h2(x.x), a, false);
                 a = __builtin_amdgcn_fdot2(wh[j][1], as_h2(x.y), a, false);
                 a = __builtin_amdgcn_fdot2(wh[j][2], as_h2(x.z), a, false);
@@ -1304,6 +1402,10 @@ __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &
                 }
             }
         }
+    }
+    if constexpr (NB == 8) {
+        unit_end8(P, c, k, in, acc);
+        return;
     }
     if constexpr (ONE_ACC<NB>) {
         if (in.op == OP_UPGATE && k.s == k.spm - 1) {  // the unit's gate half is complete
