@@ -1456,35 +1456,41 @@ __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &
     }
 }
 
-// The attention tile's LDS area of a round: after the staged queries
-// ([G][64] fp32) and the new K/V entry (bf16 [2][64], 64 floats' room).
-template <int G>
-__device__ __forceinline__ MK_LDS float *attn_area(const Ctx &c) {
-    return c.act + G * 64 + 64;
+// The attention tile's LDS area of round r: after the staged queries
+// ([G][64] fp32) and the new K/V entry (bf16 [2][64], 64 floats' room). The
+// interpreters for several requests, whose tiles run several rounds,
+// alternate between two areas.
+template <int NB, int G>
+__device__ __forceinline__ MK_LDS float *attn_area(const Ctx &c, int r) {
+    return c.act + G * 64 + 64 + (NB > 1 ? (r & 1) * attn_round_floats(G) : 0);
 }
 
 // Ends round run.rounds of an attention tile for this wave: a barrier (every
-// wave holding a block of the round has written it), the fold of the round
-// by the head waves, and between rounds a second barrier (the fold has read
-// the round before the next one overwrites it). Every wave goes through
-// every round of the tile, with a block or without. False on abort.
-template <int G>
+// wave holding a block of the round has written it), then the fold of the
+// round by the head waves. With one area a second barrier follows between
+// rounds (the fold has read the round before the next one overwrites it);
+// with two, the next round's blocks go to the other area while the head
+// waves fold, and round r + 2 reuses this one only after the barrier of
+// round r + 1, which the head waves reach once they have folded round r.
+// Every wave goes through every round of the tile, with a block or without.
+// False on abort.
+template <int NB, int G>
 __device__ __forceinline__ bool attn_round_sync(Ctx &c, const Ins &in, AttnRun &run) {
     const int nround = (in.nblk + NC - 1) / NC;
     if (!uni(lbar(c, in.pc))) return false;
-    MK_LDS float *area = attn_area<G>(c);
+    MK_LDS float *area = attn_area<NB, G>(c, run.rounds);
     if (c.w < G)
         attn_round_fold(area + c.w * ATTN_ROUND_POS, (const MK_LDS uint16_t *)(area + G * ATTN_ROUND_POS),
                         16 * min(NC, in.nblk - run.rounds * NC), c.lane(), run);
     run.rounds++;
-    return run.rounds >= nround || uni(lbar(c, in.pc));
+    return NB > 1 || run.rounds >= nround || uni(lbar(c, in.pc));
 }
 
 // One K/V block of an attention tile (the wave's block of its round): the
 // new entry replaces whatever the cache slot held, then the block's scores
 // and values go to the round area.
-template <int G>
-__device__ __forceinline__ void attn_write_block(Ctx &c, const Cur &k, const Ins &in, const v4u (&r)[4]) {
+template <int NB, int G>
+__device__ __forceinline__ void attn_write_block(Ctx &c, const Cur &k, const Ins &in, const v4u (&r)[4], int round) {
     const int lane = c.lane();
     const int blk = k.blo + k.u;
     v4u k0 = r[0], k1 = r[1], v0 = r[2], v1 = r[3];
@@ -1503,7 +1509,7 @@ __device__ __forceinline__ void attn_write_block(Ctx &c, const Cur &k, const Ins
         }
     }
     const int pos0 = blk * 16 + t0;
-    attn_block_write<G>(c.act, attn_area<G>(c), c.w, lane, k0, k1, v0, v1, pos0 <= in.p, pos0 + 8 <= in.p);
+    attn_block_write<G>(c.act, attn_area<NB, G>(c, round), c.w, lane, k0, k1, v0, v1, pos0 <= in.p, pos0 + 8 <= in.p);
 }
 
 // Elects the last of the instruction's merge-event finishers (one per step).
@@ -1694,14 +1700,14 @@ __device__ __forceinline__ bool attn_tile(const KParams &P, Ctx &c, Cur &ic, Cur
                 (cc.u >= cc.nu ? !took : cc.u == c.w + r * NC))) {
             v4u buf[4];
             take_any(slot, buf);
-            if (cc.u < cc.nu) attn_write_block<G>(c, cc, in, buf);
+            if (cc.u < cc.nu) attn_write_block<NB, G>(c, cc, in, buf, r);
             took = true;
             issue_any(slot, P, ic, c.lane());
             cur_next<NB>(P, c, ic);
             cur_next<NB>(P, c, cc);
             slot = slot + 1 == D ? 0 : slot + 1;
         }
-        if (r < nround && !uni(attn_round_sync<G>(c, in, run))) return false;
+        if (r < nround && !uni(attn_round_sync<NB, G>(c, in, run))) return false;
     }
     if (c.w >= G) return attn_tile_left(P, c);
     const int h = c.w, lane = c.lane();

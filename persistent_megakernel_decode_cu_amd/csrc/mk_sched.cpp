@@ -325,10 +325,10 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     P.act_stride = (kmax + 511) / 512 * 512;
     P.xrow_stride = (max_rows_x + 3) / 4 * 4;
     // matvec inputs; attention staging (queries, new K/V entry) and one
-    // round's scores and values; an AMERGE's tile states (MAX_ATTN_CHUNKS at
-    // a time); LM-head partials
+    // round's scores and values (two rounds' above batch 1); an AMERGE's tile
+    // states (MAX_ATTN_CHUNKS at a time); LM-head partials
     const int64_t act_floats =
-        std::max<int64_t>({(int64_t)NBP * P.act_stride, (int64_t)G * 64 + 64 + attn_round_floats(G),
+        std::max<int64_t>({(int64_t)NBP * P.act_stride, (int64_t)G * 64 + 64 + (NBP > 1 ? 2 : 1) * attn_round_floats(G),
                            (int64_t)std::min(B * C, MAX_ATTN_CHUNKS) * G * ATTN_PART,
                            (int64_t)P.n_lm_slots * B * 2});
     auto up256 = [](int64_t x) { return (x + 255) / 256 * 256; };
