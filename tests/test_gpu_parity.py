@@ -213,6 +213,21 @@ def test_megakernel_equals_unfused_bitwise_1b_layer():
         assert np.array_equal(u[key].view(np.uint8), k[key].view(np.uint8)), key
 
 
+def test_megakernel_equals_unfused_bitwise_1b_layer_batch4():
+    # batch 4 with 1B widths: the batched input gathers of 1024-word blocks
+    # (O projection, down projection), the per-request norm staging and the
+    # balanced split over uneven paged requests, against the baseline
+    cfg = synthetic.Workload(41, "1b-layer-b4-paged", n_layers=1, hidden=2048, n_q_heads=32, n_kv_heads=8,
+                             head_dim=64, ffn=8192, vocab=0, has_embed=False, batch=4, kv_len_range=(5, 700),
+                             steps=1, paged_random=True)
+    cfg, m, st = inputs(cfg)
+    wdev = gu.upload_model(m)
+    k = _outputs(cfg, m, st, wdev, "megakernel")
+    u = _outputs(cfg, m, st, wdev, "unfused", attn_chunks=k["attn_chunks"])
+    for key in ("kv_lens", "hidden", "k_pool", "v_pool"):
+        assert np.array_equal(u[key].view(np.uint8), k[key].view(np.uint8)), key
+
+
 @pytest.mark.parametrize("batch", [1, 4])
 @pytest.mark.parametrize("mode", ["unfused", "megakernel"])
 def test_argmax_ties_take_the_lowest_index(mode, batch, oracle32):
