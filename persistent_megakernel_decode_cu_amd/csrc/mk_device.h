@@ -205,104 +205,140 @@ __device__ __forceinline__ float wave_max(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// Attention over one tile's K/V blocks (16 positions of one kv head each),
-// in rounds of up to N_COMPUTE_WAVES blocks, one block per wave:
-//  1. each wave holding a block writes, for the G query heads of the group,
-//     the 16 scaled scores q_h . K_t / sqrt(64) into S[h][16 w + t] (-inf at
-//     positions past the new one) and the block's values, transposed, into
-//     V[d][16 w + t] (bf16, zero past the new position: a missing position
-//     may hold any bit pattern);
-//  2. after a barrier, wave h < G folds the round into its running state of
-//     head h, lane = dim: M = max(M, max_t S), every state scaled by
-//     exp(M_old - M), L += sum_t exp(S - M), O += sum_t exp(S - M) V[t]
-//     (positions in ascending order).
-// The tile's (O, M, L) is the chunk's softmax state (O unnormalised). The
-// lane layout of a block follows the K/V page: lane l holds the 16-byte chunk
-// l of K and of V, i.e. dims 8 (l % 8) .. + 7 of positions l / 8 (t0) and
-// 8 + l / 8 (t1); a score is summed over the 8 lanes sharing a position.
-// (ATTN_ROUND_POS, ATTN_V_STRIDE and the area's size attn_round_floats are in
-// mk_isa.h)
-
-struct AttnRun {
-    float O, M, L;  // head wave: running state of its head (lane = dim)
-    int rounds;     // rounds of the current tile this wave has gone through
-};
-
-__device__ __forceinline__ void attn_run_init(AttnRun &r) {
-    r.O = 0.0f;
-    r.M = -1e30f;
-    r.L = 0.0f;
-    r.rounds = 0;
+// Cross-lane exchanges among the 8 lane groups of a wave (lanes 8 apart):
+// the value of lane l ^ 8 (rows of 16 lanes rotated by 8), and the gfx950
+// lane swaps, which hand back (a with its upper 32 lanes replaced by b's
+// lower 32, b with its lower 32 replaced by a's upper 32) and the same with
+// rows of 16 lanes (a's odd rows against b's even rows).
+__device__ __forceinline__ float xor8(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float swap32_add(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap16_add(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_max(float a) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap16_max(float a) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// maximum of a value that is the same on the 8 lanes of each group, over
+// the groups; every lane gets it
+__device__ __forceinline__ float group_max(float v) {
+    v = swap32_max(v);
+    v = swap16_max(v);
+    return fmaxf(v, xor8(v));
 }
 
-// Step 1 for the block of wave slot `ws` of a round; q: the group's rotated
-// queries [G][64] fp32; area: the round's LDS area.
+// Attention over one tile's K/V blocks (16 positions of one kv head each),
+// wave by wave: wave w folds blocks w, w + N_COMPUTE_WAVES, ... of the tile,
+// in order, into an online-softmax state per query head of the group, kept
+// in registers. The lane layout of a block follows the K/V page: lane l holds
+// the 16-byte chunk l of K and of V, i.e. dims dd = 8 (l % 8) .. dd + 7 of
+// positions t0 = l / 8 and t0 + 8; a position's score q_h . K_t / sqrt(64)
+// is the sum over its 8 lanes. Per block and head the wave's running
+// maximum M (the same on every lane) rises to the block's, every sum is
+// scaled by exp(M_old - M_new), and each lane adds exp(S - M) and
+// exp(S - M) V over ITS two positions to its L and to O over its 8 dims;
+// positions past the new one score -inf and their values count as zero (a
+// missing position may hold any bit pattern). At the end of the tile the 8
+// lane groups are added, which gives the wave's state (o[64], m, l) of each
+// head; the tile's state is then the merge of the waves' states in wave
+// order (merge_step below). No barrier between blocks; the O of the tile is
+// unnormalised.
 template <int G>
-__device__ __forceinline__ void attn_block_write(const MK_LDS float *q, MK_LDS float *area, int ws, int lane, v4u k0,
-                                                 v4u k1, v4u v0, v4u v1, bool ok0, bool ok1) {
-    const int dd = (lane & 7) * 8, t0 = lane >> 3;
-    MK_LDS float *S = area;
-    MK_LDS uint16_t *V = (MK_LDS uint16_t *)(area + G * ATTN_ROUND_POS);
-    const int j0 = ws * 16 + t0;
+struct AttnAcc {
+    float O[G][8];  // per lane: head h, dims dd .. dd + 7, over the lane's positions
+    float L[G];     // per lane: the lane's positions' weights (the same on its group's 8 lanes)
+    float M[G];     // the wave's running maximum score
+};
+
+template <int G>
+__device__ __forceinline__ void attn_acc_init(AttnAcc<G> &a) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a.O[h][i] = 0.0f;
+        a.L[h] = 0.0f;
+        a.M[h] = -1e30f;
+    }
+}
+
+// One block into the wave's state; q: the group's rotated queries [G][64]
+// fp32 in LDS; ok0 / ok1: positions t0 and t0 + 8 are at or before the new
+// one.
+template <int G>
+__device__ __forceinline__ void attn_acc_block(AttnAcc<G> &a, const MK_LDS float *q, int lane, v4u k0, v4u k1,
+                                               v4u v0, v4u v1, bool ok0, bool ok1) {
+    const int dd = (lane & 7) * 8;
     if (!ok0) v0 = v4u{0u, 0u, 0u, 0u};
     if (!ok1) v1 = v4u{0u, 0u, 0u, 0u};
-    const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w}, w1[4] = {v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        MK_LDS uint16_t *row = V + (dd + 2 * e) * ATTN_V_STRIDE;
-        row[j0] = (uint16_t)(w0[e] & 0xffffu);
-        row[ATTN_V_STRIDE + j0] = (uint16_t)(w0[e] >> 16);
-        row[j0 + 8] = (uint16_t)(w1[e] & 0xffffu);
-        row[ATTN_V_STRIDE + j0 + 8] = (uint16_t)(w1[e] >> 16);
-    }
+    const float va[8] = {bf_lo(v0.x), bf_hi(v0.x), bf_lo(v0.y), bf_hi(v0.y),
+                         bf_lo(v0.z), bf_hi(v0.z), bf_lo(v0.w), bf_hi(v0.w)};
+    const float vb[8] = {bf_lo(v1.x), bf_hi(v1.x), bf_lo(v1.y), bf_hi(v1.y),
+                         bf_lo(v1.z), bf_hi(v1.z), bf_lo(v1.w), bf_hi(v1.w)};
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         const v4f qa = *(const MK_LDS v4f *)(q + h * 64 + dd);
         const v4f qb = *(const MK_LDS v4f *)(q + h * 64 + dd + 4);
-        const float s0 = sum8lanes(dot8(k0, qa, qb)) * 0.125f;  // 1 / sqrt(64)
-        const float s1 = sum8lanes(dot8(k1, qa, qb)) * 0.125f;
-        if ((lane & 7) == (h & 7)) {
-            S[h * ATTN_ROUND_POS + j0] = ok0 ? s0 : -INFINITY;
-            S[h * ATTN_ROUND_POS + j0 + 8] = ok1 ? s1 : -INFINITY;
-        }
+        float s0 = sum8lanes(dot8(k0, qa, qb)) * 0.125f;  // 1 / sqrt(64)
+        float s1 = sum8lanes(dot8(k1, qa, qb)) * 0.125f;
+        if (!ok0) s0 = -INFINITY;
+        if (!ok1) s1 = -INFINITY;
+        const float Mn = fmaxf(a.M[h], group_max(fmaxf(s0, s1)));
+        const float sc = __expf(a.M[h] - Mn);
+        const float p0 = __expf(s0 - Mn), p1 = __expf(s1 - Mn);
+        a.L[h] = fmaf(a.L[h], sc, p0 + p1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a.O[h][i] = fmaf(p1, vb[i], fmaf(p0, va[i], a.O[h][i] * sc));
+        a.M[h] = Mn;
     }
 }
 
-// Step 2 for head h over the round's first npos positions (a multiple of
-// 16): each lane turns its positions' scores into weights exp(S - M) in
-// place; then lane d reads eight weights (the same for every lane) and the
-// eight values of its dim per step, in position order.
-__device__ __forceinline__ void attn_round_fold(MK_LDS float *S_h, const MK_LDS uint16_t *V, int npos, int lane,
-                                                AttnRun &r) {
-    float mx = -INFINITY;
-    for (int j = lane; j < npos; j += 64) mx = fmaxf(mx, S_h[j]);
-    const float Mn = fmaxf(r.M, wave_max(mx));
-    const float scale = __expf(r.M - Mn);
-    float ls = 0.0f;
-    for (int j = lane; j < npos; j += 64) {
-        const float e = __expf(S_h[j] - Mn);
-        S_h[j] = e;
-        ls += e;
+// The wave's state of every head, added over the 8 lane groups by halving:
+// lanes 32 apart add dims 0-3 (lower half) or 4-7 (upper half) of their 8,
+// then rows 16 apart two of those, then lanes 8 apart one (each sum of two
+// lanes is the same on both). Lane l ends with dim 8 (l % 8) + l / 8 in
+// o[h] (and in l[h] the head's weight sum, on every lane).
+template <int G>
+__device__ __forceinline__ void attn_acc_finish(const AttnAcc<G> &a, int lane, float (&o)[G], float (&l)[G]) {
+    const bool hi8 = (lane & 8) != 0;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float o4[4], o2[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = swap32_add(a.O[h][i], a.O[h][i + 4]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) o2[i] = swap16_add(o4[i], o4[i + 2]);
+        const float keep = hi8 ? o2[1] : o2[0], send = hi8 ? o2[0] : o2[1];
+        o[h] = keep + xor8(send);
+        float s = swap32_add(a.L[h], a.L[h]);
+        s = swap16_add(s, s);
+        l[h] = s + xor8(s);
     }
-    float o = r.O * scale;
-    const MK_LDS uint16_t *vrow = V + lane * ATTN_V_STRIDE;
-#pragma unroll 2
-    for (int j = 0; j < npos; j += 8) {
-        const v4f pa = *(const MK_LDS v4f *)(S_h + j);
-        const v4f pb = *(const MK_LDS v4f *)(S_h + j + 4);
-        const v4u v = *(const MK_LDS v4u *)(vrow + j);
-        o = fmaf(pa.x, bf_lo(v.x), o);
-        o = fmaf(pa.y, bf_hi(v.x), o);
-        o = fmaf(pa.z, bf_lo(v.y), o);
-        o = fmaf(pa.w, bf_hi(v.y), o);
-        o = fmaf(pb.x, bf_lo(v.z), o);
-        o = fmaf(pb.y, bf_hi(v.z), o);
-        o = fmaf(pb.z, bf_lo(v.w), o);
-        o = fmaf(pb.w, bf_hi(v.w), o);
+}
+
+// The wave's finished states into st[(w G + h) ATTN_PART + ...] (o[64], m, l).
+template <int G>
+__device__ __forceinline__ void attn_acc_store(const AttnAcc<G> &a, const float (&o)[G], const float (&l)[G],
+                                               MK_LDS float *st, int w, int lane) {
+    const int dim = (lane & 7) * 8 + (lane >> 3);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        MK_LDS float *d = st + (w * G + h) * ATTN_PART;
+        d[dim] = o[h];
+        if (lane == 0) {
+            d[64] = a.M[h];
+            d[65] = l[h];
+        }
     }
-    r.L = fmaf(r.L, scale, wave_sum(ls));
-    r.O = o;
-    r.M = Mn;
 }
 
 // Softmax-state merge, one source at a time in a fixed order: (O, M, L)

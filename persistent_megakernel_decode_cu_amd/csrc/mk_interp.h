@@ -382,13 +382,13 @@ __device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k,
         const int t = rfl(bw[2]), cap = P.T * P.max_pages;
         int lo, hi;
         if constexpr (NB == 1) {  // one request: tile t of T takes blocks [t nb / T, (t + 1) nb / T)
-            const int T = rfl(bw[3]), nb = attn_nblocks((int)lds_ld_const(c.misc + M_KVLEN) + step, cap);
+            const int nb = attn_nblocks((int)lds_ld_const(c.misc + M_KVLEN) + step, cap);
+            const uint32_t T = (uint32_t)rfl(bw[3]), rT = (uint32_t)rfl(a[3]);
             k.b = 0;
-            // 64-bit: the compiler keeps this division on the scalar unit (a
-            // 32-bit one it moves to the vector unit, which measured slower
-            // in the slice loop this is inlined into)
-            lo = (int)((int64_t)t * nb / T);
-            hi = (int)((int64_t)(t + 1) * nb / T);
+            // n / T as the high word of n ceil(2^32 / T) (the queue holds the
+            // multiplier): exact, since n <= 16 * 65536 and T <= 16
+            lo = (int)(T == 1 ? (uint32_t)t * nb : __umulhi((uint32_t)t * nb, rT));
+            hi = (int)(T == 1 ? (uint32_t)(t + 1) * nb : __umulhi((uint32_t)(t + 1) * nb, rT));
         } else {
             const uint32_t w0 = split_word(c, step, SPLIT_TILE + 2 * t), w1 = split_word(c, step, SPLIT_TILE + 2 * t + 1);
             k.b = (int)(w0 & (MAX_B - 1));
@@ -1456,41 +1456,18 @@ __device__ __forceinline__ void consume_mv(const KParams &P, Ctx &c, const Cur &
     }
 }
 
-// The attention tile's LDS area of round r: after the staged queries
-// ([G][64] fp32) and the new K/V entry (bf16 [2][64], 64 floats' room). The
-// interpreters for several requests, whose tiles run several rounds,
-// alternate between two areas.
-template <int NB, int G>
-__device__ __forceinline__ MK_LDS float *attn_area(const Ctx &c, int r) {
-    return c.act + G * 64 + 64 + (NB > 1 ? (r & 1) * attn_round_floats(G) : 0);
+// The LDS area of an attention tile's wave states ([N_COMPUTE_WAVES][G]
+// [ATTN_PART]): after the staged queries ([G][64] fp32) and the new K/V
+// entry (bf16 [2][64], 64 floats' room).
+template <int G>
+__device__ __forceinline__ MK_LDS float *attn_states(const Ctx &c) {
+    return c.act + G * 64 + 64;
 }
 
-// Ends round run.rounds of an attention tile for this wave: a barrier (every
-// wave holding a block of the round has written it), then the fold of the
-// round by the head waves. With one area a second barrier follows between
-// rounds (the fold has read the round before the next one overwrites it);
-// with two, the next round's blocks go to the other area while the head
-// waves fold, and round r + 2 reuses this one only after the barrier of
-// round r + 1, which the head waves reach once they have folded round r.
-// Every wave goes through every round of the tile, with a block or without.
-// False on abort.
-template <int NB, int G>
-__device__ __forceinline__ bool attn_round_sync(Ctx &c, const Ins &in, AttnRun &run) {
-    const int nround = (in.nblk + NC - 1) / NC;
-    if (!uni(lbar(c, in.pc))) return false;
-    MK_LDS float *area = attn_area<NB, G>(c, run.rounds);
-    if (c.w < G)
-        attn_round_fold(area + c.w * ATTN_ROUND_POS, (const MK_LDS uint16_t *)(area + G * ATTN_ROUND_POS),
-                        16 * min(NC, in.nblk - run.rounds * NC), c.lane(), run);
-    run.rounds++;
-    return NB > 1 || run.rounds >= nround || uni(lbar(c, in.pc));
-}
-
-// One K/V block of an attention tile (the wave's block of its round): the
-// new entry replaces whatever the cache slot held, then the block's scores
-// and values go to the round area.
-template <int NB, int G>
-__device__ __forceinline__ void attn_write_block(Ctx &c, const Cur &k, const Ins &in, const v4u (&r)[4], int round) {
+// One K/V block of an attention tile into the wave's softmax state: the new
+// entry replaces whatever the cache slot held.
+template <int G>
+__device__ __forceinline__ void attn_fold_block(Ctx &c, const Cur &k, const Ins &in, const v4u (&r)[4], AttnAcc<G> &a) {
     const int lane = c.lane();
     const int blk = k.blo + k.u;
     v4u k0 = r[0], k1 = r[1], v0 = r[2], v1 = r[3];
@@ -1509,7 +1486,7 @@ __device__ __forceinline__ void attn_write_block(Ctx &c, const Cur &k, const Ins
         }
     }
     const int pos0 = blk * 16 + t0;
-    attn_block_write<G>(c.act, attn_area<NB, G>(c, round), c.w, lane, k0, k1, v0, v1, pos0 <= in.p, pos0 + 8 <= in.p);
+    attn_acc_block<G>(a, c.act, lane, k0, k1, v0, v1, pos0 <= in.p, pos0 + 8 <= in.p);
 }
 
 // Elects the last of the instruction's merge-event finishers (one per step).
@@ -1667,14 +1644,15 @@ __device__ __forceinline__ void issue_any(int k, const KParams &P, const Cur &cu
     }
 }
 
-// An attention tile, outside the matvec slice loop (its barriers and head
-// state would otherwise share that loop's registers): the wave takes its
-// blocks (units w, w + NC, ...: one per round) from the slice stream in
-// order, keeping the stream D slices ahead, and goes through every round of
-// the tile, with a block or without; a wave without any block consumes its
-// one empty slice. After the last round wave h < G publishes head h's
-// softmax state as the chunk's (o, m, l); the last head published ends the
-// instruction. False on abort.
+// An attention tile, outside the matvec slice loop (its softmax state
+// would otherwise share that loop's registers): the wave takes its blocks
+// (units w, w + NC, ...) from the slice stream in order, keeping the stream
+// D slices ahead, and folds each into its own state, with no barrier; a
+// wave without any block consumes its one empty slice. The waves holding
+// blocks then leave their states in LDS, and after one barrier wave h < G
+// merges head h's states in wave order and publishes the result as the
+// tile's (o, m, l); the last head published ends the instruction. False on
+// abort.
 // A wave that appended the step's K/V entry waits for that store before it
 // leaves the tile, in a resident launch (after its part of the tile, so
 // the tile is not held up): every later instruction of this unit starts once
@@ -1689,34 +1667,41 @@ __device__ __forceinline__ bool attn_tile_left(const KParams &P, Ctx &c) {
 
 template <int NB, int G>
 __device__ __forceinline__ bool attn_tile(const KParams &P, Ctx &c, Cur &ic, Cur &cc, const Ins &in, int &slot) {
-    AttnRun run;
-    attn_run_init(run);
-    const int nround = (in.nblk + NC - 1) / NC;
-    const int pc = in.pc;
-    bool took = false;
-    for (int r = 0; uni(r < nround || !took); ++r) {
-        // this wave's block of round r, or the tile's one empty slice
-        if (uni(cc.pc == pc && cc.step == in.step && cc.op == OP_ATTN &&
-                (cc.u >= cc.nu ? !took : cc.u == c.w + r * NC))) {
-            v4u buf[4];
-            take_any(slot, buf);
-            if (cc.u < cc.nu) attn_write_block<NB, G>(c, cc, in, buf, r);
-            took = true;
-            issue_any(slot, P, ic, c.lane());
-            cur_next<NB>(P, c, ic);
-            cur_next<NB>(P, c, cc);
-            slot = slot + 1 == D ? 0 : slot + 1;
-        }
-        if (r < nround && !uni(attn_round_sync<NB, G>(c, in, run))) return false;
+    AttnAcc<G> a;
+    attn_acc_init(a);
+    const int pc = in.pc, lane = c.lane();
+    // the cursor leaves the instruction after the wave's last block (or its
+    // empty slice)
+    while (uni(cc.pc == pc && cc.step == in.step && cc.op == OP_ATTN)) {
+        v4u buf[4];
+        take_any(slot, buf);
+        if (cc.u < cc.nu) attn_fold_block<G>(c, cc, in, buf, a);
+        issue_any(slot, P, ic, lane);
+        cur_next<NB>(P, c, ic);
+        cur_next<NB>(P, c, cc);
+        slot = slot + 1 == D ? 0 : slot + 1;
     }
+    MK_LDS float *st = attn_states<G>(c);
+    if (c.w < in.nblk) {
+        float o[G], l[G];
+        attn_acc_finish<G>(a, lane, o, l);
+        attn_acc_store<G>(a, o, l, st, c.w, lane);
+    }
+    if (!uni(lbar(c, pc))) return false;
     if (c.w >= G) return attn_tile_left(P, c);
-    const int h = c.w, lane = c.lane();
+    const int h = c.w, nw = min(NC, in.nblk);
+    float O, M, L;
+    merge_init(O, M, L);
+    for (int w = 0; w < nw; ++w) {
+        const MK_LDS float *s = st + (w * G + h) * ATTN_PART;
+        merge_step(O, M, L, s[lane], s[64], s[65]);
+    }
     const size_t pbase = (((size_t)in.layer * P.nkv + in.g) * in.nch + in.c) * G * ATTN_PART;
     const __amdgpu_buffer_rsrc_t rp = tres(P.tpart + pbase, (uint32_t)(G * ATTN_PART));
-    tput(rp, (uint32_t)(h * ATTN_PART + lane), run.O, c.tag);
+    tput(rp, (uint32_t)(h * ATTN_PART + lane), O, c.tag);
     if (lane == 0) {
-        tput(rp, (uint32_t)(h * ATTN_PART + 64), run.M, c.tag);
-        tput(rp, (uint32_t)(h * ATTN_PART + 65), run.L, c.tag);
+        tput(rp, (uint32_t)(h * ATTN_PART + 64), M, c.tag);
+        tput(rp, (uint32_t)(h * ATTN_PART + 65), L, c.tag);
     }
     uint32_t m = 0;
     if (lane == 0) m = lds_add_local(c.misc + M_AFIN, 1u);

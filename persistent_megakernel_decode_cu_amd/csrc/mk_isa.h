@@ -77,14 +77,9 @@ constexpr int MISC_BYTES = 4096;
 constexpr int SLICE_BYTES = 4096;      // weight bytes one wave holds per register slice
 constexpr int PREFETCH_SLICES = 2;     // slices each wave keeps in flight
 constexpr int ATTN_PART = 64 + 2;      // o[d], m, l of one head
-// an attention tile works in rounds of one 16-position K/V block per wave;
-// a round's LDS area for G query heads holds its scores [G][ATTN_ROUND_POS]
-// fp32, then its values transposed, [64 dims][ATTN_V_STRIDE] bf16 (each dim's
-// row padded by 16 bytes, so that eight lanes reading eight rows at one
-// column hit different banks)
-constexpr int ATTN_ROUND_POS = N_COMPUTE_WAVES * 16;
-constexpr int ATTN_V_STRIDE = ATTN_ROUND_POS + 8;  // bf16 per dim row
-constexpr int attn_round_floats(int G) { return G * ATTN_ROUND_POS + 64 * ATTN_V_STRIDE / 2; }
+// an attention tile leaves one softmax state per wave and query head in LDS
+// before the waves' states are merged
+constexpr int attn_state_floats(int G) { return N_COMPUTE_WAVES * G * ATTN_PART; }
 constexpr int MAX_B = 8;
 // device-clock stamps per instruction in a traced step: start, inputs staged,
 // end (merges included), first wave done with its slices, last wave done,

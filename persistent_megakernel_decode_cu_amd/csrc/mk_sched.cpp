@@ -213,6 +213,8 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
                 t.g = g;
                 t.c = c;
                 t.nch = TT;
+                // ceil(2^32 / TT): a single request's interpreter divides by TT with it
+                t.r1 = TT > 1 ? (int32_t)(uint32_t)(((1ull << 32) + TT - 1) / TT) : 0;
                 t.merge = -1;
                 t.slot = c;
                 t.nslot = TT;
@@ -229,6 +231,8 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
                 t.b = b;
                 t.g = g;
                 t.nch = TT;
+                // ceil(2^32 / TT): a single request's interpreter divides by TT with it
+                t.r1 = TT > 1 ? (int32_t)(uint32_t)(((1ull << 32) + TT - 1) / TT) : 0;
                 t.merge = -1;
                 t.bytes = 0;  // streams nothing
                 t.cu = pick_least(cum);
@@ -324,11 +328,11 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     const int kmax = NBP == 8 ? std::max({(3 * H + 1) / 2, (QD + 1) / 2, (F + 1) / 2}) : std::max(H, std::max(F, QD));
     P.act_stride = (kmax + 511) / 512 * 512;
     P.xrow_stride = (max_rows_x + 3) / 4 * 4;
-    // matvec inputs; attention staging (queries, new K/V entry) and one
-    // round's scores and values (two rounds' above batch 1); an AMERGE's tile
-    // states (MAX_ATTN_CHUNKS at a time); LM-head partials
+    // matvec inputs; attention staging (queries, new K/V entry) and the
+    // tile's wave states; an AMERGE's tile states (MAX_ATTN_CHUNKS at a
+    // time); LM-head partials
     const int64_t act_floats =
-        std::max<int64_t>({(int64_t)NBP * P.act_stride, (int64_t)G * 64 + 64 + (NBP > 1 ? 2 : 1) * attn_round_floats(G),
+        std::max<int64_t>({(int64_t)NBP * P.act_stride, (int64_t)G * 64 + 64 + attn_state_floats(G),
                            (int64_t)std::min(B * C, MAX_ATTN_CHUNKS) * G * ATTN_PART,
                            (int64_t)P.n_lm_slots * B * 2});
     auto up256 = [](int64_t x) { return (x + 255) / 256 * 256; };

@@ -163,16 +163,17 @@ __device__ __forceinline__ void uf_split(const KParams &P, int T, int lane, int 
 }
 
 // One attention tile (tile c of kv head g: the request and K/V blocks the
-// split gives it) per workgroup of N_COMPUTE_WAVES waves that take K/V
-// blocks round-robin and merge their states in wave order: the same split
-// and lane layout as an attention tile of the resident interpreter.
+// split gives it) per workgroup of N_COMPUTE_WAVES waves: wave w folds blocks
+// blo + w, blo + w + N_COMPUTE_WAVES, ... into its own softmax state and the
+// head waves merge the waves' states in wave order - the same split, lane
+// layout and order as an attention tile of the resident interpreter.
 constexpr int UF_ATTN_THREADS = N_COMPUTE_WAVES * 64;
 
 template <int G>
 __global__ __launch_bounds__(UF_ATTN_THREADS) void uf_attn(KParams P, int layer, const float *qrot) {
     constexpr int NW = N_COMPUTE_WAVES;
     __shared__ float q[MAX_G * 64];
-    __shared__ float area[attn_round_floats(MAX_G)];
+    __shared__ float st[attn_state_floats(MAX_G)];
     const int c = blockIdx.x, g = blockIdx.y, T = gridDim.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int nb[MAX_B], n[MAX_B], b, blo, bhi;
@@ -184,36 +185,39 @@ __global__ __launch_bounds__(UF_ATTN_THREADS) void uf_attn(KParams P, int layer,
     for (int i = threadIdx.x; i < G * 64; i += UF_ATTN_THREADS) q[i] = qrot[(int64_t)b * P.nq * 64 + (g * G) * 64 + i];
     __syncthreads();
     const size_t layer_pool = (size_t)P.n_pages * P.nkv * 16 * 64;
-    MK_LDS float *ar = (MK_LDS float *)area;
-    AttnRun run;
-    attn_run_init(run);
+    MK_LDS float *sts = (MK_LDS float *)st;
+    AttnAcc<G> a;
+    attn_acc_init(a);
     const int t0 = lane >> 3;
-    // rounds of NW blocks, block blo + NW r + w on wave w, as the resident
-    // interpreter hands them out
-    for (int r0 = blo; r0 < bhi; r0 += NW) {
-        const int blk = r0 + wave;
-        if (blk < bhi) {
-            int page = P.page_table[(int64_t)b * P.max_pages + blk];
-            if (page < 0 || page >= P.n_pages) page = 0;
-            const size_t off = (size_t)layer * layer_pool + ((size_t)page * P.nkv + g) * 1024;
-            const v4u *kb = (const v4u *)(P.k_pool + off);
-            const v4u *vb = (const v4u *)(P.v_pool + off);
-            const int pos0 = blk * 16 + t0;
-            attn_block_write<G>((const MK_LDS float *)q, ar, wave, lane, kb[lane], kb[64 + lane], vb[lane],
-                                vb[64 + lane], pos0 <= p, pos0 + 8 <= p);
-        }
-        __syncthreads();
-        if (wave < G)
-            attn_round_fold(ar + wave * ATTN_ROUND_POS, (const MK_LDS uint16_t *)(ar + G * ATTN_ROUND_POS),
-                            16 * min(NW, bhi - r0), lane, run);
-        __syncthreads();
+    for (int blk = blo + wave; blk < bhi; blk += NW) {
+        int page = P.page_table[(int64_t)b * P.max_pages + blk];
+        if (page < 0 || page >= P.n_pages) page = 0;
+        const size_t off = (size_t)layer * layer_pool + ((size_t)page * P.nkv + g) * 1024;
+        const v4u *kb = (const v4u *)(P.k_pool + off);
+        const v4u *vb = (const v4u *)(P.v_pool + off);
+        const int pos0 = blk * 16 + t0;
+        attn_acc_block<G>(a, (const MK_LDS float *)q, lane, kb[lane], kb[64 + lane], vb[lane], vb[64 + lane],
+                          pos0 <= p, pos0 + 8 <= p);
     }
+    if (blo + wave < bhi) {
+        float o[G], l[G];
+        attn_acc_finish<G>(a, lane, o, l);
+        attn_acc_store<G>(a, o, l, sts, wave, lane);
+    }
+    __syncthreads();
     if (wave < G) {
+        const int nw = min(NW, bhi - blo);
+        float O, M, L;
+        merge_init(O, M, L);
+        for (int w = 0; w < nw; ++w) {
+            const MK_LDS float *s = sts + (w * G + wave) * ATTN_PART;
+            merge_step(O, M, L, s[lane], s[64], s[65]);
+        }
         float *dst = P.attn_part + (((int64_t)g * T + c) * G + wave) * ATTN_PART_STRIDE;
-        dst[lane] = run.O;
+        dst[lane] = O;
         if (lane == 0) {
-            dst[64] = run.M;
-            dst[65] = run.L;
+            dst[64] = M;
+            dst[65] = L;
         }
     }
 }
