@@ -640,6 +640,10 @@ struct Ins {
     int nblk;     // attention: K/V blocks of the tile
     bool alast;   // attention: the tile holds its request's newest position (and appends it)
     uint64_t wn;  // norm weight of the op's input
+    // a matvec's tagged output: the layer's vector of every request (request
+    // b's row r is word b * os + r of B * os)
+    uint64_t *ob;
+    int os;
     int64_t *tr;
 };
 
@@ -1074,6 +1078,28 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
     in.mctr = rfl(mw[W_MCTR - 12]);
     in.mneed = rfl(mw[W_MNEED - 12]);
     in.wn = rfl64(nw[0], nw[1]);
+    switch (in.op) {
+        case OP_QKV:
+            in.os = (P.nq + 2 * P.nkv) * P.d;
+            in.ob = P.tqkv + (size_t)in.layer * P.B * in.os;
+            break;
+        case OP_OPROJ:
+            in.os = P.H;
+            in.ob = P.tx + (size_t)(2 * in.layer) * P.B * P.H;
+            break;
+        case OP_UPGATE:
+            in.os = P.F;
+            in.ob = P.tact + (size_t)in.layer * P.B * P.F;
+            break;
+        case OP_DOWN:
+            in.os = P.H;
+            in.ob = P.tx + (size_t)(2 * in.layer + 1) * P.B * P.H;
+            break;
+        default:
+            in.os = 0;
+            in.ob = nullptr;
+            break;
+    }
     in.tr = P.trace ? P.trace + ((int64_t)c.cu * P.Q + pc) * TRACE_WORDS : nullptr;
     const bool tracer = in.tr && c.w == 0 && c.lane() == 0;
     if (tracer) in.tr[TR_START] = wall_clock64();
@@ -1169,32 +1195,21 @@ __device__ __forceinline__ bool enter(const KParams &P, Ctx &c, const Cur &k, In
 // Output of row `row` for request b (lane b), v0 the row's dot product, v1
 // the up projection's for UPGATE.
 __device__ __forceinline__ void emit_row(const KParams &P, Ctx &c, const Ins &in, int row, int b, float v0, float v1) {
-    const uint32_t tag = c.tag;
     const bool last_step = in.step == P.n_steps - 1;  // a resident launch returns its last step's logits and hidden
+    float v;
     switch (in.op) {
-        case OP_QKV: {
-            const int QKVN = (P.nq + 2 * P.nkv) * P.d;
-            tput(tres(P.tqkv + ((size_t)in.layer * P.B + b) * QKVN, (uint32_t)QKVN), (uint32_t)row, v0, tag);
+        case OP_QKV: v = v0; break;
+        case OP_OPROJ: v = c.xrow[b * P.xrow_stride + (row - in.r0)] + v0; break;
+        case OP_UPGATE: v = silu(v0) * v1; break;
+        case OP_DOWN:
+            v = c.xrow[b * P.xrow_stride + (row - in.r0)] + v0;
+            if ((in.flags & F_WRITE_HIDDEN) && P.hidden_out && last_step) P.hidden_out[(int64_t)b * P.H + row] = v;
             break;
-        }
-        case OP_OPROJ: {
-            const float nx = c.xrow[b * P.xrow_stride + (row - in.r0)] + v0;
-            tput(tres(P.tx + ((size_t)(2 * in.layer) * P.B + b) * P.H, (uint32_t)P.H), (uint32_t)row, nx, tag);
-            break;
-        }
-        case OP_UPGATE:
-            tput(tres(P.tact + ((size_t)in.layer * P.B + b) * P.F, (uint32_t)P.F), (uint32_t)row, silu(v0) * v1, tag);
-            break;
-        case OP_DOWN: {
-            const float nx = c.xrow[b * P.xrow_stride + (row - in.r0)] + v0;
-            tput(tres(P.tx + ((size_t)(2 * in.layer + 1) * P.B + b) * P.H, (uint32_t)P.H), (uint32_t)row, nx, tag);
-            if ((in.flags & F_WRITE_HIDDEN) && P.hidden_out && last_step) P.hidden_out[(int64_t)b * P.H + row] = nx;
-            break;
-        }
         default:
             if (P.logits_out && last_step) P.logits_out[(int64_t)b * P.V + row] = v0;
-            break;
+            return;
     }
+    tput(tres(in.ob, (uint32_t)(P.B * in.os)), (uint32_t)(b * in.os + row), v, c.tag);
 }
 
 // The eight requests' dot products of a unit summed over the wave's 64
@@ -1215,37 +1230,21 @@ __device__ __forceinline__ float reduce8(const float (&v)[8]) {
 }
 
 // Row `row`'s outputs of the eight requests, written by lanes 8 b (request
-// b = lane / 8, the value pair its lane group holds); the buffer resources
-// span all requests so that they stay uniform.
+// b = lane / 8, the value pair its lane group holds), through the
+// instruction's output resource, which spans all requests (uniform).
 __device__ __forceinline__ void emit_rows8(const KParams &P, Ctx &c, const Ins &in, int row, float v0, float v1) {
     const int lane = lane_id(), b = lane >> 3;
     if ((lane & 7) != 0 || b >= P.B) return;
-    const uint32_t tag = c.tag;
     const bool last_step = in.step == P.n_steps - 1;
+    float v;
     switch (in.op) {
-        case OP_QKV: {
-            const int QKVN = (P.nq + 2 * P.nkv) * P.d;
-            tput(tres(P.tqkv + (size_t)in.layer * P.B * QKVN, (uint32_t)(P.B * QKVN)), (uint32_t)(b * QKVN + row), v0,
-                 tag);
+        case OP_QKV: v = v0; break;
+        case OP_OPROJ: v = c.xrow[b * P.xrow_stride + (row - in.r0)] + v0; break;
+        case OP_UPGATE: v = silu(v0) * v1; break;
+        case OP_DOWN:
+            v = c.xrow[b * P.xrow_stride + (row - in.r0)] + v0;
+            if ((in.flags & F_WRITE_HIDDEN) && P.hidden_out && last_step) P.hidden_out[(int64_t)b * P.H + row] = v;
             break;
-        }
-        case OP_OPROJ: {
-            const float nx = c.xrow[b * P.xrow_stride + (row - in.r0)] + v0;
-            tput(tres(P.tx + (size_t)(2 * in.layer) * P.B * P.H, (uint32_t)(P.B * P.H)), (uint32_t)(b * P.H + row), nx,
-                 tag);
-            break;
-        }
-        case OP_UPGATE:
-            tput(tres(P.tact + (size_t)in.layer * P.B * P.F, (uint32_t)(P.B * P.F)), (uint32_t)(b * P.F + row),
-                 silu(v0) * v1, tag);
-            break;
-        case OP_DOWN: {
-            const float nx = c.xrow[b * P.xrow_stride + (row - in.r0)] + v0;
-            tput(tres(P.tx + (size_t)(2 * in.layer + 1) * P.B * P.H, (uint32_t)(P.B * P.H)), (uint32_t)(b * P.H + row),
-                 nx, tag);
-            if ((in.flags & F_WRITE_HIDDEN) && P.hidden_out && last_step) P.hidden_out[(int64_t)b * P.H + row] = nx;
-            break;
-        }
         default: {
             if (P.logits_out && last_step) P.logits_out[(int64_t)b * P.V + row] = v0;
             // the wave's running best of request b (its rows rise, so ties
@@ -1256,9 +1255,10 @@ __device__ __forceinline__ void emit_rows8(const KParams &P, Ctx &c, const Ins &
                 am[at] = v0;
                 ((MK_LDS int32_t *)am)[at + 1] = row;
             }
-            break;
+            return;
         }
     }
+    tput(tres(in.ob, (uint32_t)(P.B * in.os)), (uint32_t)(b * in.os + row), v, c.tag);
 }
 
 // End of a slice at a padded batch of 8: at the end of an UPGATE unit's gate
