@@ -244,7 +244,10 @@ def bench_layer(args, cfg, torch, np, gu, synthetic):
     wdev = gu.upload_model(model)
     ds = gu.DevState(st0)
     dec = gu.make_decoder(model, st0, wdev)
-    info = dec.build_schedule(1, mode=args.mode, max_kv_len=int(st0.kv_lens.max()) + 1)
+    # one step per launch (a layer has no token to hand to a next step), so
+    # the default resident mode times the megakernel's single launches
+    mode = "megakernel" if args.mode == "resident" else args.mode
+    info = dec.build_schedule(1, mode=mode, max_kv_len=int(st0.kv_lens.max()) + 1)
     stream = torch.cuda.current_stream()
     hidden = torch.empty((1, cfg.hidden), dtype=torch.float32, device="cuda")
     kv_out = torch.empty_like(ds.kv_lens)
@@ -282,7 +285,7 @@ def bench_layer(args, cfg, torch, np, gu, synthetic):
         "config": {"workload": f"{cfg.name}: one Llama-3.2-1B-shaped layer (H 2048, 32q/8kv x 64, F 8192), "
                                f"batch 1, K/V length {int(st0.kv_lens[0])}, no embedding or LM head; median of "
                                f"{args.steps} single steps, each after a 512 MB cache-evicting write",
-                   "mode": args.mode, "n_cus": info["n_cus"], "launches_per_step": info["launches_per_step"]},
+                   "mode": mode, "n_cus": info["n_cus"], "launches_per_step": info["launches_per_step"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None, "bytes_per_launch": int(nbytes)},
         "step_us": {"p10": pct(times["cold"], 10), "p50": cold_us, "p90": pct(times["cold"], 90)},
