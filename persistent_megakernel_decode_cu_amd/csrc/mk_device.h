@@ -253,11 +253,20 @@ __device__ __forceinline__ float group_max(float v) {
 // head; the tile's state is then the merge of the waves' states in wave
 // order (merge_step below). No barrier between blocks; the O of the tile is
 // unnormalised.
+// Above four heads per group the 8 dims x G heads of deferred sums would
+// not fit beside the interpreter's other registers: there each block's
+// products are summed over the lane groups at once (the halving below), so
+// that a lane carries one dim per head and the weight sums are whole.
+template <int G>
+constexpr bool ATTN_SUM_PER_BLOCK = G > 4;
+template <int G>
+constexpr int ATTN_ACC_DIMS = ATTN_SUM_PER_BLOCK<G> ? 1 : 8;
+
 template <int G>
 struct AttnAcc {
-    float O[G][8];  // per lane: head h, dims dd .. dd + 7, over the lane's positions
-    float L[G];     // per lane: the lane's positions' weights (the same on its group's 8 lanes)
-    float M[G];     // the wave's running maximum score
+    float O[G][ATTN_ACC_DIMS<G>];  // head h: dims dd .. dd + 7 over the lane's positions (or the lane's dim, summed)
+    float L[G];                    // the lane's positions' weights (or the wave's, summed)
+    float M[G];                    // the wave's running maximum score
 };
 
 template <int G>
@@ -265,10 +274,33 @@ __device__ __forceinline__ void attn_acc_init(AttnAcc<G> &a) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a.O[h][i] = 0.0f;
+        for (int i = 0; i < ATTN_ACC_DIMS<G>; ++i) a.O[h][i] = 0.0f;
         a.L[h] = 0.0f;
         a.M[h] = -1e30f;
     }
+}
+
+// Eight values per lane (dims dd .. dd + 7 of the lane's group) added over
+// the 8 lane groups by halving: lanes 32 apart add dims 0-3 (lower half) or
+// 4-7 (upper half), then rows 16 apart two of those, then lanes 8 apart one
+// (each sum of two lanes is the same on both). Lane l ends with dim
+// 8 (l % 8) + l / 8.
+__device__ __forceinline__ float group_sum_dims(const float (&v)[8], int lane) {
+    const bool hi8 = (lane & 8) != 0;
+    float v4[4], v2[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v4[i] = swap32_add(v[i], v[i + 4]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) v2[i] = swap16_add(v4[i], v4[i + 2]);
+    const float keep = hi8 ? v2[1] : v2[0], send = hi8 ? v2[0] : v2[1];
+    return keep + xor8(send);
+}
+// a value that is the same on the 8 lanes of each group, summed over the
+// groups (the same halving), on every lane
+__device__ __forceinline__ float group_sum(float v) {
+    v = swap32_add(v, v);
+    v = swap16_add(v, v);
+    return v + xor8(v);
 }
 
 // One block into the wave's state; q: the group's rotated queries [G][64]
@@ -295,33 +327,35 @@ __device__ __forceinline__ void attn_acc_block(AttnAcc<G> &a, const MK_LDS float
         const float Mn = fmaxf(a.M[h], group_max(fmaxf(s0, s1)));
         const float sc = __expf(a.M[h] - Mn);
         const float p0 = __expf(s0 - Mn), p1 = __expf(s1 - Mn);
-        a.L[h] = fmaf(a.L[h], sc, p0 + p1);
+        if constexpr (ATTN_SUM_PER_BLOCK<G>) {
+            float t[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a.O[h][i] = fmaf(p1, vb[i], fmaf(p0, va[i], a.O[h][i] * sc));
+            for (int i = 0; i < 8; ++i) t[i] = fmaf(p1, vb[i], p0 * va[i]);
+            a.O[h][0] = fmaf(a.O[h][0], sc, group_sum_dims(t, lane));
+            a.L[h] = fmaf(a.L[h], sc, group_sum(p0 + p1));
+        } else {
+            a.L[h] = fmaf(a.L[h], sc, p0 + p1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a.O[h][i] = fmaf(p1, vb[i], fmaf(p0, va[i], a.O[h][i] * sc));
+        }
         a.M[h] = Mn;
     }
 }
 
-// The wave's state of every head, added over the 8 lane groups by halving:
-// lanes 32 apart add dims 0-3 (lower half) or 4-7 (upper half) of their 8,
-// then rows 16 apart two of those, then lanes 8 apart one (each sum of two
-// lanes is the same on both). Lane l ends with dim 8 (l % 8) + l / 8 in
-// o[h] (and in l[h] the head's weight sum, on every lane).
+// The wave's state of every head: lane l's o[h] holds dim 8 (l % 8) + l / 8
+// and l[h] the head's weight sum, on every lane (the deferred sums added
+// over the lane groups now, or already whole).
 template <int G>
 __device__ __forceinline__ void attn_acc_finish(const AttnAcc<G> &a, int lane, float (&o)[G], float (&l)[G]) {
-    const bool hi8 = (lane & 8) != 0;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        float o4[4], o2[2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o4[i] = swap32_add(a.O[h][i], a.O[h][i + 4]);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) o2[i] = swap16_add(o4[i], o4[i + 2]);
-        const float keep = hi8 ? o2[1] : o2[0], send = hi8 ? o2[0] : o2[1];
-        o[h] = keep + xor8(send);
-        float s = swap32_add(a.L[h], a.L[h]);
-        s = swap16_add(s, s);
-        l[h] = s + xor8(s);
+        if constexpr (ATTN_SUM_PER_BLOCK<G>) {
+            o[h] = a.O[h][0];
+            l[h] = a.L[h];
+        } else {
+            o[h] = group_sum_dims(a.O[h], lane);
+            l[h] = group_sum(a.L[h]);
+        }
     }
 }
 

@@ -71,12 +71,12 @@ def check_appended(ds, ost, cfg, before, kv_rel=0.0):
         before[name] = g.copy()
 
 
-def run_compare(cfg, m, st, oracle32, mode, steps=1, check_kv=True, kv_rel=0.0):
+def run_compare(cfg, m, st, oracle32, mode, steps=1, check_kv=True, kv_rel=0.0, attn_chunks=0):
     wdev = gu.upload_model(m)
     ds = gu.DevState(st)
     dec = gu.make_decoder(m, st, wdev)
     maxlen = int(st.kv_lens.max()) + steps - 1
-    dec.build_schedule(st.batch, mode=mode, max_kv_len=maxlen)
+    dec.build_schedule(st.batch, mode=mode, max_kv_len=maxlen, attn_chunks=attn_chunks)
     ost = st.copy()
     before = {"k": st.k_pool.copy(), "v": st.v_pool.copy()}
     worst = 0.0
@@ -135,6 +135,23 @@ def test_tiny_gqa8_first_position(mode, oracle32):
                              ffn=512, vocab=1000, has_embed=True, batch=2, kv_len=0, steps=1)
     cfg, m, st = inputs(cfg)
     run_compare(cfg, m, st, oracle32, mode)
+
+
+def _gqa8_long():
+    return synthetic.Workload(14, "tiny-g8-long", n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=1, head_dim=64,
+                              ffn=512, vocab=1000, has_embed=True, batch=2, kv_len_range=(200, 900), steps=2,
+                              paged_random=True)
+
+
+@pytest.mark.parametrize("mode", ["unfused", "megakernel"])
+@pytest.mark.parametrize("attn_chunks", [1, 0])
+def test_tiny_gqa8_long_cache(mode, attn_chunks, oracle32):
+    """Eight query heads per kv head over uneven cached lengths: with one tile
+    per request every wave folds several pages (the per-page lane-group sums
+    that groups of more than four heads use), with the automatic count
+    several tiles per request."""
+    cfg, m, st = inputs(_gqa8_long())
+    run_compare(cfg, m, st, oracle32, mode, steps=2, attn_chunks=attn_chunks)
 
 
 @pytest.mark.parametrize("mode", ["unfused", "megakernel"])
@@ -202,6 +219,16 @@ def test_megakernel_equals_unfused_bitwise(n_cus, attn_chunks, split):
         a, b = u[key], k[key]
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), (
             f"{key} differs: max |diff| {np.max(np.abs(a.astype(np.float64) - b.astype(np.float64)))}")
+
+
+@pytest.mark.parametrize("attn_chunks", [1, 3])
+def test_megakernel_equals_unfused_bitwise_gqa8(attn_chunks):
+    cfg, m, st = inputs(_gqa8_long())
+    wdev = gu.upload_model(m)
+    k = _outputs(cfg, m, st, wdev, "megakernel", attn_chunks=attn_chunks)
+    u = _outputs(cfg, m, st, wdev, "unfused", attn_chunks=attn_chunks)
+    for key in ("tokens", "kv_lens", "logits", "hidden", "k_pool", "v_pool"):
+        assert np.array_equal(u[key].view(np.uint8), k[key].view(np.uint8)), key
 
 
 def test_megakernel_equals_unfused_bitwise_1b_layer():
