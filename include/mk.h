@@ -125,7 +125,9 @@ typedef struct mk_schedule_desc {
     int32_t max_kv_len;      /* the largest kv_lens[b] a step will see; sizes
                                 the attention split; <= capacity - 1 */
     int32_t attn_chunks;     /* attention tiles per request, on average: each kv
-                                head gets batch x attn_chunks tiles; 0 = auto */
+                                head gets batch x attn_chunks tiles; 0 = auto;
+                                at most 32, batch x attn_chunks at most 128
+                                (else MK_EINVAL) */
     int32_t trace;           /* 1: record per-instruction device timestamps */
     int64_t watchdog_spins;  /* bound of every device wait loop; 0 = default */
     int32_t attn_split;      /* how a kv head's tiles are shared out over the

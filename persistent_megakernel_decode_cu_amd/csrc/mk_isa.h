@@ -89,10 +89,12 @@ enum : int { TR_START = 0, TR_READY = 1, TR_END = 2, TR_FIRST = 3, TR_LAST = 4, 
 constexpr int MAX_G = 8;
 // Attention tiles: each kv head has batch x attn_chunks of them, shared out
 // over the requests at every step (the attention split of mk_device.h); an
-// AMERGE merges one request's tiles, MAX_ATTN_CHUNKS at a time
-constexpr int MAX_ATTN_CHUNKS = 16;
-constexpr int MAX_ATTN_TILES = MAX_B * MAX_ATTN_CHUNKS;
-// chunks per request the automatic choice stops at
+// AMERGE merges one request's tiles, MAX_ATTN_CHUNKS at a time. The split's
+// LDS tables hold up to MAX_ATTN_TILES tiles per kv head.
+constexpr int MAX_ATTN_CHUNKS = 32;
+constexpr int MAX_ATTN_TILES = 128;
+// chunks per request the automatic choice gives short K/V (one block per
+// wave on half a tile's waves) stops at
 constexpr int AUTO_ATTN_CHUNKS = 16;
 // attention split modes (mk_schedule_desc::attn_split)
 enum : int32_t { SPLIT_BALANCED = 0, SPLIT_PER_REQUEST = 1 };

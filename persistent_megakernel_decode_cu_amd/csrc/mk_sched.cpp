@@ -129,16 +129,24 @@ int build_plan(const mk_config &cfg, const mk_schedule_desc &desc, Plan &P) {
     // prefetch window (N_COMPUTE_WAVES waves x PREFETCH_SLICES blocks)
     if (desc.attn_chunks > MAX_ATTN_CHUNKS)
         return set_error(MK_EINVAL, "attn_chunks above " + std::to_string(MAX_ATTN_CHUNKS));
+    if ((int64_t)B * desc.attn_chunks > MAX_ATTN_TILES)
+        return set_error(MK_EINVAL, "batch x attn_chunks above " + std::to_string(MAX_ATTN_TILES));
     // about one K/V block per wave on half the waves (one wave per SIMD,
     // which then has the vector unit to itself): attention is short
     // arithmetic on few units, so it is spread wide; with more requests there
     // are more tiles already, and half the chunk cap, and no more tiles than
     // compute units (a unit's second tile would start only after its first,
-    // while the balanced split already evens out the tiles' sizes)
+    // while the balanced split already evens out the tiles' sizes). Long K/V
+    // at batch <= 2: two blocks per wave, up to one tile per compute unit
+    // (1b-kv8192: 32 tiles per request took 953 us per step against 1041 at
+    // 16, 1088 at 48; at 1b-kv1024 16 stays best)
     int C = desc.attn_chunks > 0
                 ? desc.attn_chunks
                 : std::min(B <= 2 ? AUTO_ATTN_CHUNKS : AUTO_ATTN_CHUNKS / 2,
                            std::max(1, ceil_div(nb_max, N_COMPUTE_WAVES / 2)));
+    if (desc.attn_chunks <= 0 && B <= 2)
+        C = std::max(C, std::min({MAX_ATTN_CHUNKS, ceil_div(nb_max, 2 * N_COMPUTE_WAVES),
+                                  std::max(1, S / (B * cfg.n_kv_heads))}));
     if (desc.attn_chunks <= 0 && B > 2) C = std::min(C, std::max(1, S / (B * cfg.n_kv_heads)));
     C = std::min(C, nb_max);
     P.attn_chunks = C;

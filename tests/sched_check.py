@@ -236,7 +236,7 @@ def validate(shape, batch: int, queue: np.ndarray, events: np.ndarray, attn_chun
         _req(i.merge < ne, "merge of an unknown event")
         if i.op == I["OP_ATTN"]:
             _req(i.merge < 0, "attention tiles publish their states without a merge event")
-            _req(batch <= i.nch <= ISA["MAX_B"] * ISA["MAX_ATTN_CHUNKS"], "attention tile count out of range")
+            _req(batch <= i.nch <= ISA["MAX_ATTN_TILES"], "attention tile count out of range")
         if i.op == I["OP_LMHEAD"]:
             _req(i.merge >= 0, "LM-head tiles need the argmax merge")
     # every input is produced earlier in the global order

@@ -199,13 +199,15 @@ def _outputs(cfg, m, st, wdev, mode, n_cus=0, attn_chunks=0, attn_split="balance
 
 @pytest.mark.parametrize("n_cus,attn_chunks,split", [(1, 0, "balanced"), (3, 2, "balanced"), (8, 0, "balanced"),
                                                      (37, 3, "balanced"), (37, 3, "per_request"),
-                                                     (256, 0, "balanced"), (256, 16, "balanced")])
+                                                     (256, 0, "balanced"), (256, 16, "balanced"),
+                                                     (256, 32, "balanced")])
 def test_megakernel_equals_unfused_bitwise(n_cus, attn_chunks, split):
     """Both paths perform the same floating-point operations in the same order
     (norm partition, chunk order of every dot product, attention split and
     merge order, explicit FMAs in RoPE), so their outputs agree exactly, for
-    any grid size, tile count and split mode. At 16 tiles per request (64 per
-    kv head) the longest request's merge takes more than one gather round."""
+    any grid size, tile count and split mode. At 16 and more tiles per
+    request the longest request's merge can take more than one gather
+    round."""
     cfg = synthetic.Workload(11, "tiny-b4-paged", n_layers=2, hidden=256, n_q_heads=4, n_kv_heads=2,
                              head_dim=64, ffn=1024, vocab=4096, has_embed=True, batch=4,
                              kv_len_range=(1, 300), steps=2, paged_random=True)

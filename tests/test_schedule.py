@@ -64,14 +64,18 @@ def test_auto_chunks_about_one_block_per_wave():
     # attention is spread so that about one 16-position K/V block goes to
     # each of half a tile's 8 waves (one wave per SIMD), up to a chunk cap
     # that halves above batch 2, where there are also no more attention
-    # tiles than compute units
+    # tiles than compute units; long K/V at batch <= 2 goes to two blocks per
+    # wave, up to one tile per compute unit
     for name in ("tiny-2l", "1b-kv1024", "1b-kv8192", "1b-b8-paged"):
         w, B, maxlen, p = plan_for(name, 256)
         nb = (maxlen + 1 + 15) // 16
         cap = sched_check.ISA["AUTO_ATTN_CHUNKS"] // (1 if B <= 2 else 2)
-        want = min(nb, cap, max(1, -(-nb // 4)))
+        want = min(cap, max(1, -(-nb // 4)))
+        if B <= 2:
+            want = max(want, min(sched_check.ISA["MAX_ATTN_CHUNKS"], -(-nb // 16), max(1, 256 // (B * w.n_kv_heads))))
         if B > 2:
             want = min(want, max(1, 256 // (B * w.n_kv_heads)))
+        want = min(want, nb)
         assert p.info.attn_chunks == want, (name, p.info.attn_chunks, want)
         if B > 2:
             assert B * p.info.attn_chunks * w.n_kv_heads <= 256
@@ -81,6 +85,13 @@ def test_attention_chunks_above_the_limit_are_rejected():
     with pytest.raises(_mk.MkError) as ex:
         plan_for("1b-kv1024", 256, chunks=sched_check.ISA["MAX_ATTN_CHUNKS"] + 1)
     assert ex.value.code == _mk.MK_EINVAL
+    # batch 8: the per-request cap is allowed, but not more tiles per kv head
+    # than the split's tables hold
+    with pytest.raises(_mk.MkError) as ex:
+        plan_for("1b-b8-paged", 256, chunks=sched_check.ISA["MAX_ATTN_TILES"] // 8 + 1)
+    assert ex.value.code == _mk.MK_EINVAL
+    w, B, maxlen, p = plan_for("1b-b8-paged", 256, chunks=sched_check.ISA["MAX_ATTN_TILES"] // 8)
+    assert p.info.attn_chunks * B <= sched_check.ISA["MAX_ATTN_TILES"]
 
 
 @pytest.mark.parametrize("name,n_cus,steps", [("tiny-2l", 8, 2000), ("tiny-2l", 256, 50),
