@@ -54,11 +54,6 @@ __device__ __forceinline__ float coherent_load4f(__amdgpu_buffer_rsrc_t r, uint3
 __device__ __forceinline__ void coherent_store4f(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, CP_SC1);
 }
-__device__ __forceinline__ void coherent_store16f(__amdgpu_buffer_rsrc_t r, uint32_t off, v4f v) {
-    __builtin_amdgcn_raw_buffer_store_b128(v4u{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
-                                               __float_as_uint(v.w)},
-                                           r, off, 0, CP_SC1);
-}
 
 // Tagged activations: one 64-bit word per value, low half the fp32 bits,
 // high half the tag of the step that wrote it. A single 64-bit access is
@@ -71,10 +66,6 @@ __device__ __forceinline__ v2u tget(__amdgpu_buffer_rsrc_t r, uint32_t idx) {
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tres(const uint64_t *base, uint32_t words) {
     return coherent_rsrc(base, words * 8u);
-}
-// ordinary (cached) buffer resource over `bytes` bytes; loads beyond return 0
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t plain_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -151,12 +142,6 @@ __device__ __forceinline__ int act_index(int i) {
     const int ci = i >> 3, e8 = i & 7;
     return ((((ci >> 6) << 1) + (e8 >> 2)) << 8) + ((ci & 63) << 2) + (e8 & 3);
 }
-// 16-bit form of the same layout: chunk ci's 8 values are one 16-byte LDS
-// read of lane ci % 64 in pass ci / 64
-__device__ __forceinline__ int act16_index(int i) {
-    const int ci = i >> 3;
-    return ((ci >> 6) << 9) + ((ci & 63) << 3) + (i & 7);
-}
 
 // Rotate-half RoPE of element i (lane) of a 64-wide head: x_i cos - x_{i+32}
 // sin for i < 32, x_i cos + x_{i-32} sin above; xp is the partner element.
@@ -187,23 +172,6 @@ __device__ __forceinline__ float sum8lanes(float v) {
     return v;
 }
 
-// Maximum over the 64 lanes of a wave, returned to every lane: the row
-// shifts and row broadcasts of wave_sum, with -inf where a lane has no
-// source (max is exact, so the combination order does not matter).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_max_src(float v) {
-    return __int_as_float(
-        __builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
-}
-__device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, dpp_max_src<0x111, 0xf>(v));
-    v = fmaxf(v, dpp_max_src<0x112, 0xf>(v));
-    v = fmaxf(v, dpp_max_src<0x114, 0xf>(v));
-    v = fmaxf(v, dpp_max_src<0x118, 0xf>(v));
-    v = fmaxf(v, dpp_max_src<0x142, 0xa>(v));
-    v = fmaxf(v, dpp_max_src<0x143, 0xc>(v));
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
 
 // Cross-lane exchanges among the 8 lane groups of a wave (lanes 8 apart):
 // the value of lane l ^ 8 (rows of 16 lanes rotated by 8), and the gfx950

@@ -205,9 +205,6 @@ __device__ __forceinline__ uint32_t lds_add_local(MK_LDS uint32_t *p, uint32_t v
 __device__ __forceinline__ int32_t iw(const Ctx &c, int pc, int w) {
     return __builtin_amdgcn_readfirstlane(c.q[pc * LDS_INSTR_WORDS + w]);
 }
-__device__ __forceinline__ uint64_t iw64(const Ctx &c, int pc, int w) {
-    return (uint64_t)(uint32_t)iw(c, pc, w) | ((uint64_t)(uint32_t)iw(c, pc, w + 1) << 32);
-}
 
 // Words [w0, w0 + 4) of instruction pc as one 16-byte LDS read (every lane
 // the same address): the reads of a record issue together and wait once,
