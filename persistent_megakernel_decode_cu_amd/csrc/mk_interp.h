@@ -1283,8 +1283,7 @@ __device__ __forceinline__ void unit_end8(const KParams &P, Ctx &c, const Cur &k
 // lane, j < 4, times the activations of those chunks, added in j order to
 // the unit's dot product (m: gate or up matrix of UPGATE). Three forms with
 // the same arithmetic: at batch 1 with K = 2048 the activations sit in
-// registers, loaded once per instruction into the attention state's output
-// registers (xr.o[j], free during a matvec); a full slice converts its
+// registers (xr.o[j]), loaded once per instruction; a full slice converts its
 // weights once and reads each request's activations from LDS right before
 // that request's products (at a padded batch of 8 the down projection's
 // input is staged as binary16, the only way 8 requests' 8192-wide inputs fit

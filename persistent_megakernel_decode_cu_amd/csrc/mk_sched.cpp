@@ -31,7 +31,7 @@
 //      which makes every queue consistent with one order and so rules out
 //      deadlock while all workgroups are co-resident (progress obligation);
 //   4. encode each queue as [Q, 32] int32 words (mk_isa.h) and lay out the
-//      LDS of a workgroup (residual rows, activations, attention rounds).
+//      LDS of a workgroup (residual rows, activations, attention states).
 #include "mk_sched.h"
 
 #include <algorithm>

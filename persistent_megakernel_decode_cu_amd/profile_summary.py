@@ -9,9 +9,10 @@ mk_copy_probe of a known size.
         --kernel mk_megakernel --copy-bytes N --command "..." --command "..."
     python -m persistent_megakernel_decode_cu_amd.profile_summary counters DB [DB ...] --command "..."
 
-`digest()` fingerprints the kernel sources; a traffic summary records it, so
-that a reader can tell whether the kernels changed after the counters were
-taken.
+`digest()` fingerprints the kernel sources' code (comments and blank lines
+left out, so that a comment edit does not disown a measurement); a traffic
+summary records it, so that a reader can tell whether the kernels changed
+after the counters were taken.
 """
 from __future__ import annotations
 
@@ -19,6 +20,7 @@ import argparse
 import collections
 import hashlib
 import os
+import re
 import sqlite3
 import statistics
 import sys
@@ -27,8 +29,17 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 
 
+def _code(text: str) -> str:
+    """The source without its comments, trailing blanks and blank lines (the
+    sources hold no comment markers inside string literals)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def digest() -> str:
-    """sha256 over the HIP/C++ sources and the public header, in name order."""
+    """sha256 over the code of the HIP/C++ sources and the public header, in
+    name order."""
     h = hashlib.sha256()
     csrc = os.path.join(_HERE, "csrc")
     files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)
@@ -36,8 +47,8 @@ def digest() -> str:
     files.append(os.path.join(_ROOT, "include", "mk.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
