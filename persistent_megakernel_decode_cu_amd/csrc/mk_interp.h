@@ -383,7 +383,7 @@ __device__ __forceinline__ void cur_load(const KParams &P, const Ctx &c, Cur &k,
             const uint32_t T = (uint32_t)rfl(bw[3]), rT = (uint32_t)rfl(a[3]);
             k.b = 0;
             // n / T as the high word of n ceil(2^32 / T) (the queue holds the
-            // multiplier): exact, since n <= 16 * 65536 and T <= 16
+            // multiplier): exact, since n <= 32 * 65536 and T <= 32
             lo = (int)(T == 1 ? (uint32_t)t * nb : __umulhi((uint32_t)t * nb, rT));
             hi = (int)(T == 1 ? (uint32_t)(t + 1) * nb : __umulhi((uint32_t)(t + 1) * nb, rT));
         } else {

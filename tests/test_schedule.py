@@ -152,3 +152,25 @@ def test_trace_decoder_follows_the_queue_encoding():
     assert (ts.W_OP, ts.W_LAYER, ts.OP_END) == (ISA["W_OP"], ISA["W_LAYER"], ISA["OP_END"])
     ops = {v: k[3:] for k, v in ISA.items() if k.startswith("OP_") and k not in ("OP_END", "OP_COUNT")}
     assert ts.OP_NAMES == ops
+
+
+@pytest.mark.parametrize("name", ["1b-kv1024", "1b-kv8192", "tiny-2l"])
+def test_batch1_tile_multiplier_divides_exactly(name):
+    """A single request's attention tile t of T covers blocks [t nb / T,
+    (t + 1) nb / T); the interpreter divides by T as the high word of
+    n ceil(2^32 / T), the multiplier the queue carries in the R1 word of each
+    attention instruction. The multiplier is checked against its definition,
+    and the quotient against integer division for every n the device can
+    form (n <= T x 65536 blocks)."""
+    w, B, maxlen, p = plan_for(name, 256)
+    assert B == 1
+    q = p.queue.reshape(-1, sched_check.ISA["INSTR_WORDS"])
+    attn = q[q[:, sched_check.ISA["W_OP"]] == sched_check.ISA["OP_ATTN"]]
+    T = int(attn[0, sched_check.ISA["W_NCH"]])
+    assert T == p.info.attn_chunks and np.all(attn[:, sched_check.ISA["W_NCH"]] == T)
+    mult = attn[:, sched_check.ISA["W_R1"]].astype(np.uint32)
+    want = 0 if T == 1 else -(-(1 << 32) // T)
+    assert np.all(mult == np.uint32(want))
+    if T > 1:
+        n = np.arange(0, T * 65536 + 1, dtype=np.uint64)
+        assert np.array_equal((n * np.uint64(want)) >> np.uint64(32), n // np.uint64(T))
