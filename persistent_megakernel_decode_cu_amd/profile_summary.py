@@ -39,8 +39,15 @@ def _code(text: str) -> str:
 
 def digest() -> str:
     """sha256 over the code of the HIP/C++ sources and the public header, in
-    name order."""
+    name order, and the compiler flags that shape the kernels (without the
+    include paths, which differ between machines)."""
     h = hashlib.sha256()
+    if __package__:
+        from . import build
+    else:  # run as a script
+        sys.path.insert(0, _ROOT)
+        from persistent_megakernel_decode_cu_amd import build
+    h.update(repr(([f for f in build.COMMON if not os.path.isabs(f)], sorted(build.EXTRA.items()))).encode())
     csrc = os.path.join(_HERE, "csrc")
     files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)
                    if f.endswith((".h", ".hip", ".cpp")))
